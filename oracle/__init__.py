@@ -1,0 +1,121 @@
+"""CPU oracle for C = alpha*A*B + beta*C with binary16 A, B (test infrastructure).
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, the smoke check in __graft_entry__ and
+the CPU-baseline leg of bench.py may import this package.  It shares no code
+with the GPU path (mixed_precision_gemm_amd) and never imports it.
+
+The arithmetic is in ref_gemm.c (plain fp64 triple loop, own binary16 decoder
+and encoder); this module only marshals numpy arrays through ctypes.  See the
+header of ref_gemm.c for what each function follows on the pages.
+"""
+import ctypes
+import os
+import numpy as np
+
+from . import build as _build
+
+ROW_MAJOR, COL_MAJOR = 0, 1
+OUT_F16, OUT_F32 = 0, 1
+
+_lib = None
+
+
+def load_library(path):
+    """Opens an oracle shared library at `path` and declares its functions."""
+    lib = ctypes.CDLL(path)
+    i64, dbl, vp = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+    lib.oracle_dec16.argtypes = [ctypes.c_uint16]
+    lib.oracle_dec16.restype = dbl
+    lib.oracle_enc16.argtypes = [dbl]
+    lib.oracle_enc16.restype = ctypes.c_uint16
+    lib.oracle_gemm.argtypes = [i64, i64, i64, i64,
+                                ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                i64, i64, i64, i64, i64, i64,
+                                vp, vp, vp, dbl, dbl, vp, i64, vp, vp,
+                                ctypes.c_int]
+    lib.oracle_gemm.restype = ctypes.c_int
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        _lib = load_library(_build.LIB)
+    return _lib
+
+
+def dec16(bits, lib=None) -> np.ndarray:
+    """binary16 bit patterns (any int array) -> float64, element by element."""
+    lib = lib or _load()
+    flat = np.asarray(bits, dtype=np.uint16).ravel()
+    out = np.array([lib.oracle_dec16(int(h)) for h in flat], dtype=np.float64)
+    return out.reshape(np.shape(bits))
+
+
+def enc16(values, lib=None) -> np.ndarray:
+    """float64 values -> binary16 bit patterns (round to nearest, ties even)."""
+    lib = lib or _load()
+    flat = np.asarray(values, dtype=np.float64).ravel()
+    out = np.array([lib.oracle_enc16(float(v)) for v in flat], dtype=np.uint16)
+    return out.reshape(np.shape(values))
+
+
+def _as_u16(x) -> np.ndarray:
+    a = np.ascontiguousarray(x)
+    if a.dtype == np.float16:
+        a = a.view(np.uint16)
+    if a.dtype != np.uint16:
+        raise TypeError(f"expected binary16 storage, got {a.dtype}")
+    return a
+
+
+def gemm(M, N, K, A, B, C=None, *, alpha=1.0, beta=0.0,
+         layout_a=ROW_MAJOR, layout_b=ROW_MAJOR, out_type=OUT_F16,
+         lda=None, ldb=None, ldc=None, batch=1,
+         stride_a=0, stride_b=0, stride_c=0, rows=None, nthreads=None,
+         lib=None):
+    """Reference result and error scale, each shaped (batch, nrows, N).
+
+    A, B: flat binary16 storage (uint16 or float16 numpy arrays) in the
+    layouts given; C: binary16 (out_type OUT_F16) or float32 storage, read
+    only when beta != 0.  alpha, beta are rounded to fp32 first, as the
+    library receives them.  rows: optional row indices (sampled rows).
+    lib: an alternative library handle from load_library (tests only).
+    """
+    lib = lib or _load()
+    lda = lda if lda is not None else (K if layout_a == ROW_MAJOR else M)
+    ldb = ldb if ldb is not None else (N if layout_b == ROW_MAJOR else K)
+    ldc = ldc if ldc is not None else N
+    a = _as_u16(A)
+    b = _as_u16(B)
+    c = None
+    if beta != 0.0:
+        if C is None:
+            raise ValueError("beta != 0 needs C")
+        c = np.ascontiguousarray(C)
+        if out_type == OUT_F16:
+            c = _as_u16(c)
+        elif c.dtype != np.float32:
+            raise TypeError("fp32 C expected")
+    rows_arr = None
+    nrows = M
+    if rows is not None:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows = rows_arr.size
+    shape = (max(batch, 0), max(nrows, 0), max(N, 0))   # C rejects negatives
+    ref = np.zeros(shape, dtype=np.float64)
+    scale = np.zeros(shape, dtype=np.float64)
+    if nthreads is None:
+        nthreads = os.cpu_count() or 1
+    alpha32 = float(np.float32(alpha))
+    beta32 = float(np.float32(beta))
+    ptr = lambda x: None if x is None else x.ctypes.data
+    rc = lib.oracle_gemm(batch, M, N, K, layout_a, layout_b, out_type,
+                         lda, ldb, ldc, stride_a, stride_b, stride_c,
+                         ptr(a), ptr(b), ptr(c), alpha32, beta32,
+                         ptr(rows_arr), nrows, ptr(ref), ptr(scale), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm failed with {rc}")
+    return ref, scale

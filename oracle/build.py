@@ -1,0 +1,26 @@
+"""Builds the CPU oracle library (oracle/liboracle.so) with gcc.
+
+Test infrastructure only: the library is the checker, not the product.
+Compiled without fast-math so the k loop is summed exactly as written.
+"""
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "ref_gemm.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+
+def build(verbose: bool = False) -> str:
+    cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c11",
+           "-Wall", "-Wextra", "-shared", "-fPIC", "-pthread",
+           SRC, "-o", LIB + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,357 @@
+"""Pins for the CPU oracle (no GPU).
+
+The oracle (oracle/ref_gemm.c) is the plain definition of
+C = alpha*A*B + beta*C in fp64.  These tests pin it to things other than
+itself: numpy's binary16 conversions, exact rational arithmetic on tiny
+inputs (brute force), numpy's int64 matrix product on integer inputs, the
+binary16 landmarks the pages state (tests/golden/), and closed forms.  The
+logical matrices are built first and laid out into storage with numpy
+transposes, so the oracle's own index formulas are checked, not retyped.
+"""
+import itertools
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import COL_MAJOR, OUT_F16, OUT_F32, ROW_MAJOR
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+LAYOUTS = [(ROW_MAJOR, ROW_MAJOR), (ROW_MAJOR, COL_MAJOR),
+           (COL_MAJOR, ROW_MAJOR), (COL_MAJOR, COL_MAJOR)]
+
+
+# ---------------------------------------------------------------- helpers
+
+def to_storage(logical: np.ndarray, layout: int, ld: int, fill=0):
+    """Lays a logical rows x cols fp16 matrix out with leading dimension ld.
+    Row-major: ld >= cols, element (r, c) at r*ld + c.  Column-major: the
+    transpose is stored row-major, element (r, c) at r + c*ld."""
+    mat = logical if layout == ROW_MAJOR else logical.T
+    rows, cols = mat.shape
+    store = np.full((rows, ld), fill, dtype=np.float16)
+    store[:, :cols] = mat
+    return store.ravel()
+
+
+def stack_batches(mats, layout, ld, fill=0):
+    parts = [to_storage(m, layout, ld, fill) for m in mats]
+    return np.concatenate(parts), parts[0].size
+
+
+def exact_product(A_log, B_log, C_log, alpha, beta):
+    """alpha * A @ B + beta * C in exact rationals; also the error scale
+    |alpha| sum|a b| + |beta| |c|.  C_log is ignored when beta == 0."""
+    M, K = A_log.shape
+    N = B_log.shape[1]
+    fa = [[Fraction(float(A_log[i, k])) for k in range(K)] for i in range(M)]
+    fb = [[Fraction(float(B_log[k, j])) for j in range(N)] for k in range(K)]
+    al, be = Fraction(float(np.float32(alpha))), Fraction(float(np.float32(beta)))
+    ref = np.empty((M, N), dtype=object)
+    sc = np.empty((M, N), dtype=object)
+    for i in range(M):
+        for j in range(N):
+            s = sum((fa[i][k] * fb[k][j] for k in range(K)), Fraction(0))
+            t = sum((abs(fa[i][k] * fb[k][j]) for k in range(K)), Fraction(0))
+            c = Fraction(float(C_log[i, j])) if beta != 0 else Fraction(0)
+            ref[i, j] = al * s + be * c
+            sc[i, j] = abs(al) * t + abs(be) * abs(c)
+    return ref, sc
+
+
+def rand_f16(rng, shape):
+    return (rng.uniform(-1, 1, size=shape)).astype(np.float16)
+
+
+# ------------------------------------------------------- binary16 decoding
+
+def test_dec16_exhaustive_against_numpy():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.dec16(bits)
+    want = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    # signed zeros keep their sign
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def test_binary16_landmarks_golden():
+    path = os.path.join(GOLDEN, "binary16_landmarks.txt")
+    rows = []
+    with open(path) as fh:
+        for line in fh:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            parts = line.split()
+            rows.append((int(parts[0], 16), float(parts[1])))
+    assert len(rows) >= 10
+    for bits, value in rows:
+        got = float(oracle.dec16(np.array([bits]))[0])
+        assert got == value and np.signbit(got) == np.signbit(value), hex(bits)
+        if not np.isinf(value):
+            assert int(oracle.enc16(np.array([value]))[0]) == bits, hex(bits)
+
+
+# ------------------------------------------------------- binary16 encoding
+
+def _encode_probe_values():
+    rng = np.random.default_rng(1)
+    finite = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
+    nxt = np.nextafter(finite[:-1], np.inf)
+    mids = (finite[:-1] + finite[1:]) / 2          # exact ties in double
+    vals = [finite, mids, np.nextafter(mids, np.inf), np.nextafter(mids, -np.inf),
+            nxt,
+            np.exp2(rng.uniform(-30, 17, 20000)),
+            np.array([65504.0, 65519.99999, 65520.0, 65520.00001, 65536.0,
+                      1e9, 2.0 ** -25, 2.0 ** -25 * 1.0000001, 2.0 ** -24 * 1.5,
+                      2.0 ** -24 * 2.5, 2.0 ** -14 - 2.0 ** -25, 1e-300])]
+    v = np.concatenate(vals)
+    return np.concatenate([v, -v])
+
+
+def test_enc16_matches_numpy_round_to_nearest_even():
+    v = _encode_probe_values()
+    got = oracle.enc16(v)
+    with np.errstate(over="ignore"):
+        want = v.astype(np.float16).view(np.uint16)   # numpy: RNE from double
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(v[i], hex(got[i]), hex(want[i])) for i in bad[:5]]
+
+
+def test_enc16_specials():
+    got = oracle.enc16(np.array([np.inf, -np.inf, np.nan, -0.0, 0.0]))
+    assert got[0] == 0x7C00 and got[1] == 0xFC00
+    assert (got[2] & 0x7C00) == 0x7C00 and (got[2] & 0x3FF) != 0
+    assert got[3] == 0x8000 and got[4] == 0x0000
+
+
+# ------------------------------------------------ exact brute force (tiny)
+
+def _run_case(lib, M, N, K, la, lb, out_type, alpha, beta, batch, pad, rng):
+    A_log = [rand_f16(rng, (M, K)) for _ in range(batch)]
+    B_log = [rand_f16(rng, (K, N)) for _ in range(batch)]
+    if out_type == OUT_F16:
+        C_log = [rand_f16(rng, (M, N)) for _ in range(batch)]
+    else:
+        C_log = [rng.uniform(-4, 4, (M, N)).astype(np.float32) for _ in range(batch)]
+    lda = (K if la == ROW_MAJOR else M) + pad
+    ldb = (N if lb == ROW_MAJOR else K) + pad
+    ldc = N + pad
+    A, sa = stack_batches(A_log, la, lda, fill=np.nan)
+    B, sb = stack_batches(B_log, lb, ldb, fill=np.nan)
+    cst = []
+    for c in C_log:
+        s = np.full((M, ldc), np.nan, dtype=c.dtype)
+        s[:, :N] = c
+        cst.append(s.ravel())
+    C = np.concatenate(cst)
+    ref, sc = oracle.gemm(M, N, K, A, B, C, alpha=alpha, beta=beta,
+                          layout_a=la, layout_b=lb, out_type=out_type,
+                          lda=lda, ldb=ldb, ldc=ldc, batch=batch,
+                          stride_a=sa, stride_b=sb, stride_c=M * ldc,
+                          nthreads=2, lib=lib)
+    for b in range(batch):
+        ex, exs = exact_product(A_log[b], B_log[b], C_log[b], alpha, beta)
+        for i in range(M):
+            for j in range(N):
+                tol = float(exs[i, j]) * 2.0 ** -50
+                assert abs(Fraction(ref[b, i, j]) - ex[i, j]) <= Fraction(tol), \
+                    (M, N, K, la, lb, out_type, alpha, beta, b, i, j)
+                assert abs(Fraction(sc[b, i, j]) - exs[i, j]) <= Fraction(tol)
+
+
+ALPHA_BETA = [(1.0, 0.0), (-0.5, 2.0), (0.0, 1.0)]
+
+
+def _brute_force(lib, shapes, full_combos):
+    rng = np.random.default_rng(7)
+    n = 0
+    for idx, (M, N, K) in enumerate(shapes):
+        for li, (la, lb) in enumerate(LAYOUTS):
+            if full_combos:
+                combos = [(o, ab) for o in (OUT_F16, OUT_F32) for ab in ALPHA_BETA]
+            else:
+                k = idx * 4 + li
+                combos = [((OUT_F16, OUT_F32)[k % 2], ALPHA_BETA[k % 3])]
+            for out_type, (alpha, beta) in combos:
+                batch = 1 + (n % 2)
+                pad = n % 3
+                _run_case(lib, M, N, K, la, lb, out_type, alpha, beta, batch,
+                          pad, rng)
+                n += 1
+    return n
+
+
+def test_brute_force_all_small_shapes():
+    shapes = list(itertools.product(range(1, 9), repeat=3))
+    assert _brute_force(None, shapes, full_combos=False) == 512 * 4
+
+
+def test_brute_force_odd_shapes_all_combinations():
+    shapes = [(1, 1, 1), (3, 5, 7), (17, 9, 33)]
+    _brute_force(None, shapes, full_combos=True)
+
+
+# -------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+@pytest.mark.parametrize("K", [1, 7, 64, 2048, 4097])
+def test_all_ones_gives_K(la, lb, K):
+    M, N = 5, 3
+    A = to_storage(np.ones((M, K), np.float16), la, K if la == ROW_MAJOR else M)
+    B = to_storage(np.ones((K, N), np.float16), lb, N if lb == ROW_MAJOR else K)
+    ref, sc = oracle.gemm(M, N, K, A, B, layout_a=la, layout_b=lb)
+    assert np.all(ref == K) and np.all(sc == K)
+    # the fp16 output is the round-to-nearest-even of K (4097 -> 4096)
+    enc = oracle.enc16(ref.ravel())
+    assert np.all(enc == np.float16(K).view(np.uint16))
+    if K == 4097:
+        assert np.all(enc == 0x6C00)
+
+
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+def test_identity_returns_other_operand(la, lb):
+    rng = np.random.default_rng(3)
+    M, N = 37, 23
+    Bm = rand_f16(rng, (M, N))
+    eye = np.eye(M, dtype=np.float16)
+    ref, _ = oracle.gemm(M, N, M, to_storage(eye, la, M), to_storage(Bm, lb, N if lb == ROW_MAJOR else M),
+                         layout_a=la, layout_b=lb)
+    assert np.array_equal(ref[0], Bm.astype(np.float64))
+    Am = rand_f16(rng, (M, N))
+    eyeN = np.eye(N, dtype=np.float16)
+    ref, _ = oracle.gemm(M, N, N, to_storage(Am, la, N if la == ROW_MAJOR else M), to_storage(eyeN, lb, N),
+                         layout_a=la, layout_b=lb)
+    assert np.array_equal(ref[0], Am.astype(np.float64))
+
+
+def test_rank_one_K1_is_a_single_exact_product():
+    rng = np.random.default_rng(4)
+    M, N = 19, 11
+    a = rand_f16(rng, (M, 1))
+    b = rand_f16(rng, (1, N))
+    alpha = -1.75
+    ref, _ = oracle.gemm(M, N, 1, to_storage(a, ROW_MAJOR, 1), to_storage(b, ROW_MAJOR, N), alpha=alpha)
+    want = alpha * np.outer(a.astype(np.float64), b.astype(np.float64))
+    assert np.array_equal(ref[0], want)
+
+
+# ------------------------------------------------------------ integer exact
+
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+def test_integer_inputs_match_int64_matmul(la, lb):
+    rng = np.random.default_rng(5)
+    M, N, K, batch = 33, 41, 113, 3
+    Ai = rng.integers(-3, 4, (batch, M, K))
+    Bi = rng.integers(-3, 4, (batch, K, N))
+    Ci = rng.integers(-8, 9, (batch, M, N))
+    lda = (K if la == ROW_MAJOR else M) + 5
+    ldb = (N if lb == ROW_MAJOR else K) + 2
+    A, sa = stack_batches([m.astype(np.float16) for m in Ai], la, lda, fill=np.nan)
+    B, sb = stack_batches([m.astype(np.float16) for m in Bi], lb, ldb, fill=np.nan)
+    C = Ci.astype(np.float16).ravel()
+    ref, sc = oracle.gemm(M, N, K, A, B, C, alpha=1.0, beta=1.0, layout_a=la,
+                          layout_b=lb, lda=lda, ldb=ldb, batch=batch,
+                          stride_a=sa, stride_b=sb, stride_c=M * N)
+    want = np.matmul(Ai, Bi) + Ci
+    assert np.array_equal(ref, want.astype(np.float64))
+    want_s = np.matmul(np.abs(Ai), np.abs(Bi)) + np.abs(Ci)
+    assert np.array_equal(sc, want_s.astype(np.float64))
+
+
+def test_fp32_c_is_read_as_fp32():
+    rng = np.random.default_rng(6)
+    M, N, K = 4, 6, 3
+    A = np.zeros(M * K, np.float16)
+    B = np.zeros(K * N, np.float16)
+    C = rng.uniform(-1, 1, M * N).astype(np.float32)
+    ref, _ = oracle.gemm(M, N, K, A, B, C, alpha=1.0, beta=-3.0, out_type=OUT_F32)
+    assert np.array_equal(ref.ravel(), -3.0 * C.astype(np.float64))
+
+
+# -------------------------------------------------------------- invariants
+
+def test_beta_zero_never_reads_c():
+    rng = np.random.default_rng(8)
+    M, N, K = 9, 7, 5
+    A = rand_f16(rng, M * K)
+    B = rand_f16(rng, K * N)
+    C = np.full(M * N, np.nan, np.float16)
+    ref, sc = oracle.gemm(M, N, K, A, B, C, alpha=1.0, beta=0.0)
+    assert np.all(np.isfinite(ref)) and np.all(np.isfinite(sc))
+
+
+def test_alpha_zero_gives_beta_c():
+    rng = np.random.default_rng(9)
+    M, N, K = 6, 5, 4
+    A = rand_f16(rng, M * K)
+    B = rand_f16(rng, K * N)
+    C = rand_f16(rng, M * N)
+    ref, _ = oracle.gemm(M, N, K, A, B, C, alpha=0.0, beta=0.5)
+    assert np.array_equal(ref.ravel(), 0.5 * C.astype(np.float64))
+
+
+def test_row_subset_and_threads_are_consistent():
+    rng = np.random.default_rng(10)
+    M, N, K = 50, 30, 70
+    A = rand_f16(rng, M * K)
+    B = rand_f16(rng, K * N)
+    full1, s1 = oracle.gemm(M, N, K, A, B, nthreads=1)
+    full8, s8 = oracle.gemm(M, N, K, A, B, nthreads=8)
+    assert np.array_equal(full1, full8) and np.array_equal(s1, s8)
+    rows = [49, 0, 17, 17, 3]
+    sub, ssub = oracle.gemm(M, N, K, A, B, rows=rows, nthreads=3)
+    assert np.array_equal(sub[0], full1[0][rows])
+    assert np.array_equal(ssub[0], s1[0][rows])
+
+
+def test_layout_only_changes_storage():
+    """NN with B vs NT with B materialised transposed: identical references."""
+    rng = np.random.default_rng(11)
+    M, N, K = 21, 13, 29
+    Am = rand_f16(rng, (M, K))
+    Bm = rand_f16(rng, (K, N))
+    r_nn, _ = oracle.gemm(M, N, K, to_storage(Am, ROW_MAJOR, K), to_storage(Bm, ROW_MAJOR, N))
+    r_nt, _ = oracle.gemm(M, N, K, to_storage(Am, ROW_MAJOR, K), to_storage(Bm, COL_MAJOR, K),
+                          layout_b=COL_MAJOR)
+    r_tt, _ = oracle.gemm(M, N, K, to_storage(Am, COL_MAJOR, M), to_storage(Bm, COL_MAJOR, K),
+                          layout_a=COL_MAJOR, layout_b=COL_MAJOR)
+    assert np.array_equal(r_nn, r_nt) and np.array_equal(r_nn, r_tt)
+
+
+def test_degenerate_sizes():
+    A = np.zeros(0, np.float16)
+    ref, sc = oracle.gemm(0, 5, 3, A, np.zeros(15, np.float16))
+    assert ref.shape == (1, 0, 5)
+    C = np.arange(6, dtype=np.float16)
+    ref, _ = oracle.gemm(2, 3, 0, A, A, C, beta=2.0)       # K = 0: beta * C
+    assert np.array_equal(ref.ravel(), 2.0 * C.astype(np.float64))
+    with pytest.raises(RuntimeError):
+        oracle.gemm(-1, 3, 3, A, A)
+
+
+def test_fp32_accumulation_beats_fp16_accumulation():
+    """The hand-written GEMM kernel page (§6.2) reports that summing a
+    4096-long fp16 dot product in fp16 gives tens of times the relative error
+    of fp32 accumulation.  Measured here against the oracle's exact-product
+    fp64 sum; documents why the accumulators are fp32 (not a gate on the GPU)."""
+    rng = np.random.default_rng(12)
+    K = 4096
+    ratios = []
+    for _ in range(8):
+        a = rng.uniform(0, 1, K).astype(np.float16)
+        b = rng.uniform(0, 1, K).astype(np.float16)
+        ref, _ = oracle.gemm(1, 1, K, a, b, layout_b=COL_MAJOR)
+        exact = ref[0, 0, 0]
+        s16 = np.float16(0)
+        s32 = np.float32(0)
+        for x, y in zip(a, b):
+            p = np.float32(x) * np.float32(y)      # exact in fp32
+            s16 = np.float16(s16 + np.float16(p))
+            s32 = np.float32(s32 + p)
+        ratios.append(abs(float(s16) - exact) / max(abs(float(s32) - exact), 1e-30))
+    assert np.median(ratios) > 10.0

@@ -1,0 +1,77 @@
+"""Planted mistakes in a copy of the CPU oracle must fail its pins (no GPU).
+
+Each mutant is the oracle's C source with one plausible slip (a transposed
+operand, a wrong index or stride, a dropped term, a wrong sign, an off-by-one
+k loop, a wrong rounding rule), built with gcc into a temporary library.  The
+pins of tests/test_oracle.py are re-run against it and at least one must
+fail; the unmodified source must pass the same pins.
+"""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import build as oracle_build
+
+from test_oracle import _brute_force, _encode_probe_values
+
+MUTANTS = {
+    "transposed_A_row_major": ("A[i * j->lda + k]", "A[k * j->lda + i]"),
+    "transposed_B_col_major": ("B[k + n * j->ldb]", "B[n + k * j->ldb]"),
+    "dropped_beta_term": ("out[n] = j->alpha * s + j->beta * cin;",
+                          "out[n] = j->alpha * s;"),
+    "wrong_sign_beta": ("out[n] = j->alpha * s + j->beta * cin;",
+                        "out[n] = j->alpha * s - j->beta * cin;"),
+    "short_k_loop": ("for (int64_t k = 0; k < K; ++k) {\n                double p",
+                     "for (int64_t k = 0; k < K - 1; ++k) {\n                double p"),
+    "c_row_stride": ("i * j->ldc + n", "i * j->N + n"),
+    "b_batch_stride": ("j->B + b * j->stride_b", "j->B + b * j->stride_a"),
+    "scale_without_abs": ("t += fabs(p);", "t += p;"),
+    "subnormal_exponent": ("mag = ldexp((double)f, -24);", "mag = ldexp((double)f, -25);"),
+    "ties_away_from_zero": ("double r = nearbyint(n);", "double r = floor(n + 0.5);"),
+}
+
+SHAPES = [(1, 1, 1), (2, 3, 4), (3, 5, 7), (4, 1, 6)]
+
+
+def _pins_pass(lib) -> bool:
+    try:
+        bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+        got = oracle.dec16(bits, lib=lib)
+        want = bits.view(np.float16).astype(np.float64)
+        ok = ~np.isnan(want)
+        assert np.array_equal(got[ok], want[ok])
+        v = _encode_probe_values()
+        with np.errstate(over="ignore"):
+            assert np.array_equal(oracle.enc16(v, lib=lib),
+                                  v.astype(np.float16).view(np.uint16))
+        _brute_force(lib, SHAPES, full_combos=True)
+    except (AssertionError, ValueError, OverflowError):
+        return False   # a pin failed (or met a NaN/inf where a number was due)
+    return True
+
+
+def _build_variant(tmp_path, name, src):
+    c = tmp_path / f"{name}.c"
+    so = tmp_path / f"{name}.so"
+    c.write_text(src)
+    subprocess.run(["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c11",
+                    "-shared", "-fPIC", "-pthread", str(c), "-o", str(so), "-lm"],
+                   check=True)
+    return oracle.load_library(str(so))
+
+
+def test_unmodified_oracle_passes(tmp_path):
+    src = open(oracle_build.SRC).read()
+    assert _pins_pass(_build_variant(tmp_path, "clean", src))
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, name):
+    old, new = MUTANTS[name]
+    src = open(oracle_build.SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique"
+    lib = _build_variant(tmp_path, name, src.replace(old, new))
+    assert not _pins_pass(lib), f"pins did not catch {name}"
