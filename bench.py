@@ -1,0 +1,131 @@
+"""Benchmark of the fp16 -> fp32-accumulate GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--layout nn|nt]
+                    [--shape M N K] [--no-cpu-baseline]
+
+A step is one C = A*B + C GEMM (the whole hot path: staging, MFMA K loop,
+epilogue) on the square workload M = N = K = 8192, fp16 A, B, C uniform
+[-1, 1) from seed 0, alpha = beta = 1, fp16 output, with A, B and C resident
+in HBM before timing starts.  W untimed warm-up steps, then K timed steps
+bracketed by device synchronisation; the kernel's own duration is measured
+with HIP events recorded on the stream the kernel is launched on.  Prints one
+JSON line (value = TFLOP/s, 2*M*N*K flops per step).
+
+The CPU baseline is the oracle (a plain fp64 triple loop on the host cores),
+timed on a bounded sample of the same workload: a fixed set of rows of C.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_F16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 dense fp16 flop/clk/CU
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--layout", choices=["nn", "nt"], default="nn")
+    ap.add_argument("--shape", type=int, nargs=3, default=[8192, 8192, 8192])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=2048)
+    return ap.parse_args()
+
+
+def cpu_baseline(case, nrows):
+    """Times the oracle on `nrows` rows of C (fixed, spread over M)."""
+    import numpy as np
+    import torch
+    import oracle
+    u16 = lambda t: t.view(torch.int16).numpy().view(np.uint16)
+    rows = np.linspace(0, case.M - 1, num=min(nrows, case.M)).astype(np.int64)
+    threads = min(16, os.cpu_count() or 1)
+    t0 = time.perf_counter()
+    oracle.gemm(case.M, case.N, case.K, u16(case.A), u16(case.B), u16(case.C),
+                alpha=case.alpha, beta=case.beta, layout_a=case.layout_a,
+                layout_b=case.layout_b, rows=rows, nthreads=threads)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows.size * case.N * case.K
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"{rows.size} of {case.M} rows of C (all {case.N} columns, "
+                      f"full K={case.K}), {dt:.1f} s wall including operand decode"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this GEMM is built and measured on "
+              "a single MI355X (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gemm_inputs as gi
+    import mixed_precision_gemm_amd as mpg
+
+    M, N, K = args.shape
+    lb = gi.COL_MAJOR if args.layout == "nt" else gi.ROW_MAJOR
+    case = gi.make_case(M, N, K, layout_b=lb, alpha=1.0, beta=1.0, seed=0)
+    dev = torch.device("cuda:0")
+    dA, dB, dC = case.A.to(dev), case.B.to(dev), case.C.to(dev)
+    plan = mpg.Plan(M, N, K, case.layout_a, case.layout_b, case.out_type,
+                    case.lda, case.ldb, case.ldc)
+    stream = torch.cuda.current_stream(dev)
+    print(f"# kernel {plan.kernel}, {M}x{N}x{K} {args.layout.upper()}", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        plan.run(dA, dB, dC, 1.0, 1.0, stream=stream)
+    torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        plan.run(dA, dB, dC, 1.0, 1.0, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_events = ev0.elapsed_time(ev1)
+    ms_per_step = ms_events / args.steps
+    flops = 2.0 * M * N * K
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    plan.close()
+
+    out = {
+        "metric": "FP16 GEMM TFLOP/s (fp32 acc) at M=N=K=8192; % of MFMA FP16 peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"gemm {M}x{N}x{K} {args.layout.upper()} alpha=1 beta=1, "
+                               "fp16 A/B/C uniform[-1,1) seed 0, fp32 accumulation, fp16 out",
+                   "M": M, "N": N, "K": K, "layout": args.layout.upper(),
+                   "kernel": plan.kernel},
+        "pct_of_peak": round(100.0 * tflops / PEAK_F16_TFLOPS, 2),
+        "wall_s_timed": round(wall, 4),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_F16_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(case, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,136 @@
+/*
+ * gemm_f16f32.h -- C ABI of the MI355X (gfx950) mixed-precision GEMM.
+ *
+ *   C = alpha * A * B + beta * C
+ *
+ * A and B hold IEEE binary16 values; products are accumulated in fp32; C
+ * (read when beta != 0, then written) is binary16 or fp32.  Any M, N, K from
+ * 1 to several thousand; A and B each row- or column-major; strided batches.
+ *
+ * Pages this interface follows (titles as printed on them):
+ *   [GEMM]    "手写GEMM内核：矩阵乘法性能优化的完整工程实践" (hand-written GEMM
+ *             kernel): §1.3 fixes the problem -- fp16 inputs and output, fp32
+ *             accumulation, arbitrary M, N, K from 1 to thousands; §3.4 fixes
+ *             the edge rule -- out-of-range elements of partial tiles,
+ *             including the K remainder, contribute zero.
+ *   [CATLASS] CATLASS template library page: §2.1 gives C = A * B + C as the
+ *             operation; §1.1 and §1.3 make the row/column-major layout of
+ *             each operand a parameter, row-major (m, n) at m * ld + n.
+ *   [OPS]     CUDA operator practice page (Softmax and GEMM): §3.2 writes C
+ *             row-major; §5.2 warns that 32-bit index products overflow, so
+ *             every extent and offset here is 64-bit.
+ * alpha and beta are the BLAS-style generalisation of [CATLASS] §2.1.
+ *
+ * Semantics (all indices 0-based, all extents and strides in ELEMENTS):
+ *   A(b,i,k) = A[b*stride_a + i*lda + k]  (GEMM_ROW_MAJOR, lda >= K)
+ *            = A[b*stride_a + i + k*lda]  (GEMM_COL_MAJOR, lda >= M)
+ *   B(b,k,j) = B[b*stride_b + k*ldb + j]  (GEMM_ROW_MAJOR, ldb >= N)
+ *            = B[b*stride_b + k + j*ldb]  (GEMM_COL_MAJOR, ldb >= K)
+ *   C(b,i,j) = C[b*stride_c + i*ldc + j]  (always row-major, ldc >= N)
+ *   C(b,i,j) <- fp32(alpha) * sum_k A(b,i,k) B(b,k,j) + fp32(beta) * C(b,i,j)
+ * The sum is taken in fp32 in an order the kernel chooses; the fp32 result is
+ * rounded once to binary16 (round to nearest even, overflow to +-inf) for a
+ * binary16 C, or stored as is for an fp32 C.  When beta == 0, C is not read
+ * (NaN or garbage in C does not propagate).  Elements of A, B or C lying in
+ * the padding of a leading dimension are never read and never written.
+ * A column-major C is obtained by the caller by swapping operands
+ * (C^T = B^T A^T).
+ *
+ * Ownership: the caller owns A, B, C and the stream.  A plan owns host
+ * memory only (no device memory, no scratch), is immutable after creation,
+ * and may be run concurrently on several streams.  gemm_f16f32_run is
+ * asynchronous on the given stream: A, B, C must stay valid until the stream
+ * has passed the launched kernel.  The launch copies what it needs from the
+ * plan, so a plan may be destroyed as soon as gemm_f16f32_run returns.
+ *
+ * Errors: every function returns a status code (GEMM_OK == 0 or a negative
+ * GEMM_ERR_*); no exception crosses this boundary and there is no global
+ * error state.  Faults raised by the device while the kernel runs are
+ * reported by the HIP runtime at the caller's next synchronisation.
+ */
+#ifndef GEMM_F16F32_H
+#define GEMM_F16F32_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct gemm_f16f32_plan_s *gemm_f16f32_plan_t; /* opaque, host only */
+
+enum { GEMM_ROW_MAJOR = 0, GEMM_COL_MAJOR = 1 };  /* storage of A and of B */
+enum { GEMM_OUT_F16 = 0, GEMM_OUT_F32 = 1 };      /* element type of C     */
+
+enum {
+    GEMM_OK = 0,
+    GEMM_ERR_INVALID_ARG = -1,  /* argument violates a rule stated below    */
+    GEMM_ERR_UNSUPPORTED = -2,  /* valid but outside what the kernels cover */
+    GEMM_ERR_HIP = -3,          /* the HIP runtime refused the launch       */
+    GEMM_ERR_NOMEM = -4         /* host allocation for the plan failed      */
+};
+
+/*
+ * Validates a problem description and chooses the kernel for it.  No device
+ * work and no HIP call is made; the call can be made on a machine without a
+ * GPU.
+ *   out                 receives the new plan (set to NULL on failure).
+ *   M, N, K             extents; negative -> INVALID_ARG.  M == 0 or N == 0
+ *                       makes a plan whose run is a no-op; K == 0 makes
+ *                       C <- beta * C.
+ *   layout_a, layout_b  GEMM_ROW_MAJOR or GEMM_COL_MAJOR, else INVALID_ARG.
+ *   out_type            GEMM_OUT_F16 or GEMM_OUT_F32, else INVALID_ARG.
+ *   lda, ldb, ldc       leading dimensions, >= the minimum given in the
+ *                       header comment and >= 1, else INVALID_ARG.
+ *   batch               >= 1, else INVALID_ARG.
+ *   stride_a/b/c        element distance between consecutive batch items;
+ *                       ignored when batch == 1; must be >= 0, and
+ *                       stride_c must be at least M*ldc (batch items of C may
+ *                       not overlap), else INVALID_ARG.
+ * Offsets that do not fit the kernels' 32-bit per-tile addressing
+ * (an operand's leading dimension above 2^22 elements) -> UNSUPPORTED.
+ */
+int gemm_f16f32_plan(gemm_f16f32_plan_t *out,
+                     int64_t M, int64_t N, int64_t K,
+                     int layout_a, int layout_b, int out_type,
+                     int64_t lda, int64_t ldb, int64_t ldc,
+                     int64_t batch, int64_t stride_a, int64_t stride_b,
+                     int64_t stride_c);
+
+/*
+ * Runs a plan: launches one kernel on `stream` and returns without waiting.
+ *   A, B   device pointers to binary16 storage (const), described by the plan.
+ *   C      device pointer to binary16 or fp32 storage, read (beta != 0) and
+ *          written.
+ *   alpha, beta  fp32 scalars, by value.
+ *   stream a hipStream_t; NULL means the default stream.
+ * Rules: plan != NULL; A, B, C non-NULL unless the plan's M*N == 0 (then the
+ * call is a no-op and returns GEMM_OK) -- else INVALID_ARG.  The address range
+ * of C must not overlap those of A or B -> INVALID_ARG.  Pointer alignment is
+ * never an error: 16-byte-aligned operands whose leading dimensions are
+ * multiples of 8 take the 128-bit load path, others a narrow-load path with
+ * the same results up to summation order.  A failed launch -> GEMM_ERR_HIP.
+ */
+int gemm_f16f32_run(gemm_f16f32_plan_t plan,
+                    const void *A, const void *B, void *C,
+                    float alpha, float beta, void *stream);
+
+/* Frees a plan.  NULL is a no-op.  Returns GEMM_OK. */
+int gemm_f16f32_destroy(gemm_f16f32_plan_t plan);
+
+/* A static, NUL-terminated description of a status code (never NULL). */
+const char *gemm_f16f32_status_string(int status);
+
+/*
+ * Name of the kernel configuration the plan chose (tile sizes, layout path,
+ * "vec16" when the shapes allow 128-bit loads, else "narrow"), as a
+ * NUL-terminated string owned by the plan (valid until it is destroyed), or
+ * "none" for a no-op plan and "invalid" for NULL.  Diagnostic only.
+ */
+const char *gemm_f16f32_plan_kernel(gemm_f16f32_plan_t plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_F16F32_H */

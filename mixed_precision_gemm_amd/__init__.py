@@ -1,0 +1,185 @@
+"""Python binding of the MI355X fp16 -> fp32-accumulate GEMM library.
+
+Thin ctypes marshalling over the C ABI declared in include/gemm_f16f32.h: the
+functions below carry the same names and arguments as the C entry points, and
+every step of the computation runs in the HIP kernels of libmpgemm.so.  There
+is no fallback: if the library is missing, loading raises.  torch is used only
+for device buffers and streams (in `gemm`, the convenience wrapper).
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmpgemm.so")
+
+GEMM_ROW_MAJOR, GEMM_COL_MAJOR = 0, 1
+GEMM_OUT_F16, GEMM_OUT_F32 = 0, 1
+GEMM_OK = 0
+GEMM_ERR_INVALID_ARG = -1
+GEMM_ERR_UNSUPPORTED = -2
+GEMM_ERR_HIP = -3
+GEMM_ERR_NOMEM = -4
+
+EXPORTED = ("gemm_f16f32_plan", "gemm_f16f32_run", "gemm_f16f32_destroy",
+            "gemm_f16f32_status_string", "gemm_f16f32_plan_kernel")
+
+_lib = None
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {gemm_f16f32_status_string(status)} ({status})")
+        self.status = status
+
+
+def library() -> ctypes.CDLL:
+    """Loads libmpgemm.so (built by mixed_precision_gemm_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m mixed_precision_gemm_amd.build` (no fallback exists)")
+        lib = ctypes.CDLL(LIB_PATH)
+        i64, vp = ctypes.c_int64, ctypes.c_void_p
+        lib.gemm_f16f32_plan.argtypes = [ctypes.POINTER(vp), i64, i64, i64,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         i64, i64, i64, i64, i64, i64, i64]
+        lib.gemm_f16f32_plan.restype = ctypes.c_int
+        lib.gemm_f16f32_run.argtypes = [vp, vp, vp, vp, ctypes.c_float,
+                                        ctypes.c_float, vp]
+        lib.gemm_f16f32_run.restype = ctypes.c_int
+        lib.gemm_f16f32_destroy.argtypes = [vp]
+        lib.gemm_f16f32_destroy.restype = ctypes.c_int
+        lib.gemm_f16f32_status_string.argtypes = [ctypes.c_int]
+        lib.gemm_f16f32_status_string.restype = ctypes.c_char_p
+        lib.gemm_f16f32_plan_kernel.argtypes = [vp]
+        lib.gemm_f16f32_plan_kernel.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+# ----------------------------------------------------------- C entry points
+
+def gemm_f16f32_plan(M, N, K, layout_a, layout_b, out_type, lda, ldb, ldc,
+                     batch=1, stride_a=0, stride_b=0, stride_c=0):
+    """Returns (status, plan_handle); the handle is None unless status == 0."""
+    h = ctypes.c_void_p()
+    st = library().gemm_f16f32_plan(ctypes.byref(h), M, N, K, layout_a, layout_b,
+                                    out_type, lda, ldb, ldc, batch, stride_a,
+                                    stride_b, stride_c)
+    return st, (h.value if st == GEMM_OK else None)
+
+
+def gemm_f16f32_run(plan, A, B, C, alpha, beta, stream=None):
+    """A, B, C: device addresses (ints); stream: hipStream_t as int or None."""
+    return library().gemm_f16f32_run(plan, A, B, C, alpha, beta, stream)
+
+
+def gemm_f16f32_destroy(plan):
+    return library().gemm_f16f32_destroy(plan)
+
+
+def gemm_f16f32_status_string(status):
+    return library().gemm_f16f32_status_string(status).decode()
+
+
+def gemm_f16f32_plan_kernel(plan):
+    return library().gemm_f16f32_plan_kernel(plan).decode()
+
+
+# ------------------------------------------------------- convenience layer
+
+class Plan:
+    """Owns a plan handle; `run` launches on a stream (torch's current one by
+    default)."""
+
+    def __init__(self, M, N, K, layout_a=GEMM_ROW_MAJOR, layout_b=GEMM_ROW_MAJOR,
+                 out_type=GEMM_OUT_F16, lda=None, ldb=None, ldc=None, batch=1,
+                 stride_a=0, stride_b=0, stride_c=0):
+        lda = lda if lda is not None else (K if layout_a == GEMM_ROW_MAJOR else M)
+        ldb = ldb if ldb is not None else (N if layout_b == GEMM_ROW_MAJOR else K)
+        ldc = ldc if ldc is not None else N
+        st, h = gemm_f16f32_plan(M, N, K, layout_a, layout_b, out_type, lda, ldb,
+                                 ldc, batch, stride_a, stride_b, stride_c)
+        if st != GEMM_OK:
+            raise GemmError(st, "gemm_f16f32_plan")
+        self.handle = h
+        self.shape = (M, N, K)
+        self.kernel = gemm_f16f32_plan_kernel(h)
+
+    def run(self, A, B, C, alpha=1.0, beta=0.0, stream=None):
+        """A, B, C: torch tensors (device) or raw device addresses."""
+        ptr = lambda t: t if isinstance(t, int) or t is None else t.data_ptr()
+        if stream is None:
+            import torch
+            stream = torch.cuda.current_stream().cuda_stream
+        elif not isinstance(stream, int):
+            stream = stream.cuda_stream
+        st = gemm_f16f32_run(self.handle, ptr(A), ptr(B), ptr(C), alpha, beta,
+                             stream)
+        if st != GEMM_OK:
+            raise GemmError(st, "gemm_f16f32_run")
+
+    def close(self):
+        if self.handle is not None:
+            gemm_f16f32_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+def _layout_of(t, rows, cols):
+    """(layout, ld) of a 2-D (or batched 3-D) torch view, or None."""
+    s_r, s_c = t.stride(-2), t.stride(-1)
+    if s_c == 1 and (s_r >= max(cols, 1) or rows <= 1):
+        return GEMM_ROW_MAJOR, max(s_r, cols, 1)
+    if s_r == 1 and (s_c >= max(rows, 1) or cols <= 1):
+        return GEMM_COL_MAJOR, max(s_c, rows, 1)
+    return None
+
+
+def gemm(A, B, C=None, alpha=1.0, beta=0.0, out_dtype=None):
+    """C = alpha * A @ B + beta * C for fp16 CUDA tensors A (.., M, K) and
+    B (.., K, N); layouts and leading dimensions come from the strides.
+    Returns C (allocated when None; fp16 unless out_dtype is torch.float32)."""
+    import torch
+    if A.dtype != torch.float16 or B.dtype != torch.float16:
+        raise TypeError("A and B must be float16")
+    batched = A.dim() == 3
+    M, K = A.shape[-2:]
+    K2, N = B.shape[-2:]
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    batch = A.shape[0] if batched else 1
+    la = _layout_of(A, M, K)
+    lb = _layout_of(B, K, N)
+    if la is None:
+        A = A.contiguous(); la = _layout_of(A, M, K)
+    if lb is None:
+        B = B.contiguous(); lb = _layout_of(B, K, N)
+    if C is None:
+        dt = out_dtype or torch.float16
+        C = torch.empty((batch, M, N) if batched else (M, N), dtype=dt, device=A.device)
+        beta = 0.0
+    out_type = GEMM_OUT_F32 if C.dtype == torch.float32 else GEMM_OUT_F16
+    if C.stride(-1) != 1:
+        raise ValueError("C must be row-major")
+    ldc = max(C.stride(-2), N, 1)
+    sa = A.stride(0) if batched else 0
+    sb = B.stride(0) if batched else 0
+    sc = C.stride(0) if batched else 0
+    with Plan(M, N, K, la[0], lb[0], out_type, la[1], lb[1], ldc, batch,
+              sa, sb, sc) as p:
+        p.run(A, B, C, alpha, beta)
+    return C

@@ -1,0 +1,48 @@
+// Internal plan structure and tile table shared by the planner (host C++)
+// and the launcher (HIP).  Not part of the C ABI.
+#pragma once
+
+#include <stdint.h>
+
+namespace mpgemm {
+
+// Workgroup tile shapes.  BM x BN is the output tile of one workgroup, BK the
+// K depth of one LDS stage, WGM x WGN the grid of 64-lane waves that split the
+// output tile.  Each wave owns (BM/WGM) x (BN/WGN) outputs as 32 x 32 MFMA
+// accumulator blocks.
+enum TileId : int {
+    TILE_256x256 = 0,   // compute-bound square-ish problems
+    TILE_128x128 = 1,   // medium problems: more workgroups to fill 256 CUs
+    TILE_64x64 = 2,     // small and batched-small products
+    TILE_32x64 = 3,     // skinny M (tokens) problems
+    NUM_TILES = 4
+};
+
+struct TileShape {
+    int bm, bn, bk, wgm, wgn;
+    const char *name;
+};
+
+constexpr TileShape kTiles[NUM_TILES] = {
+    {256, 256, 64, 2, 2, "256x256x64"},
+    {128, 128, 64, 2, 2, "128x128x64"},
+    {64, 64, 64, 2, 2, "64x64x64"},
+    {32, 64, 64, 1, 2, "32x64x64"},
+};
+
+constexpr int kNumCUs = 256;
+
+}  // namespace mpgemm
+
+struct gemm_f16f32_plan_s {
+    int64_t M, N, K;
+    int layout_a, layout_b, out_type;
+    int64_t lda, ldb, ldc;
+    int64_t batch, stride_a, stride_b, stride_c;
+    int tile;              // mpgemm::TileId
+    int vec_ok;            // shapes allow 128-bit loads (pointers checked at run)
+    int64_t tiles_m, tiles_n;
+    int group_m;           // tile rows per rasterisation group
+    int64_t extent_a, extent_b, extent_c;  // elements spanned by each operand
+    char kernel_name[64];
+};

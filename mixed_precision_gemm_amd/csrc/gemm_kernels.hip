@@ -1,0 +1,476 @@
+// fp16 x fp16 -> fp32-accumulate GEMM kernels for gfx950 (MI355X), and the
+// C-ABI entry point that launches them.
+//
+// Pages cited (titles as printed):
+//   [GEMM]    "手写GEMM内核：矩阵乘法性能优化的完整工程实践" (hand-written GEMM kernel)
+//   [OPS]     CUDA operator practice page (Softmax and GEMM)
+//   [CATLASS] CATLASS template library page
+//
+// Structure of one workgroup (the pages' three-level data flow, [CATLASS] §2.2
+// and [GEMM] §3, rebuilt for CDNA4):
+//   * it owns one BM x BN tile of C ([GEMM] §3.1, [CATLASS] §2.1) and walks K in
+//     steps of BK, keeping the fp32 accumulators in registers for the whole K
+//     loop ([GEMM] §3.2, §6.2);
+//   * each K step stages an A tile (BM x BK) and a B tile (BK x BN) from global
+//     memory into one slot of a two-slot LDS ring with 128-bit buffer loads
+//     ([OPS] §3.5, [GEMM] §4.1); the loads for step k+1 are issued before the
+//     MFMAs of step k and written to the other slot after them ([GEMM] §5.1,
+//     §5.4: issue the future, wait for the past);
+//   * out-of-range elements (rows >= M or N, the K remainder) are loaded as
+//     zeros through the buffer descriptor's range check, so the main loop has
+//     no data-dependent branch ([GEMM] §3.4: zero padding, not predication);
+//   * both operands are stored K-contiguous in LDS -- an MN-contiguous operand
+//     is transposed in registers on its way in -- with the 16-byte vectors of a
+//     row XOR-swizzled by the row index so that ds_read_b128 of MFMA fragments
+//     and ds_write_b128 are free of bank conflicts ([OPS] §3.3 and [GEMM] §4.3
+//     pad rows instead; the swizzle costs no LDS);
+//   * 64-lane waves read their fragments with ds_read_b128 and accumulate with
+//     v_mfma_f32_32x32x16_f16 (fp16 products, fp32 sums; [GEMM] §2.3, §6.2);
+//   * the epilogue forms alpha*acc + beta*C in fp32, rounds once to fp16 (RNE)
+//     or stores fp32, and masks the tile edges ([CATLASS] §2.1, [OPS] §3.2).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_f16f32.h"
+#include "gemm_internal.h"
+
+using namespace mpgemm;
+
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Byte offset that fails the buffer range check: the load returns zeros.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+// Word 3 of a gfx9 buffer descriptor: 32-bit data format, raw addressing.
+constexpr int kRsrcWord3 = 0x00020000;
+
+struct GemmArgs {
+    const _Float16 *A;
+    const _Float16 *B;
+    void *C;
+    int64_t M, N, K;
+    int64_t lda, ldb, ldc;
+    int64_t sa, sb, sc;
+    int64_t extent_a, extent_b;   // elements per batch item reachable from its base
+    float alpha, beta;
+    int tiles_m, tiles_n;
+    int group_m;
+    int total_tiles;
+    int out_f32;
+    int c_vec;                    // C rows allow 4-element vector access
+};
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    const int32_t n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int32_t)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, kRsrcWord3);
+}
+
+// XOR swizzle of the 16-byte vector index within an LDS row of VPR vectors.
+// For VPR = 8 (BK = 64, rows of 128 B): any 8 consecutive rows read at the same
+// vector column hit 8 distinct 16-byte bank groups of a 128-byte window, and
+// any 16 consecutive rows hit 16 distinct groups of a 256-byte window.
+template <int VPR>
+__device__ __host__ constexpr int swz(int row) {
+    if constexpr (VPR == 8) {
+        return (row ^ (row >> 3)) & 7;
+    } else {
+        return ((row >> 1) ^ (row >> 3)) & (VPR - 1);
+    }
+}
+
+// Transposes an 8 x 8 block of fp16: in[c] holds row c (8 elements along the
+// contiguous dimension), out[e] receives column e (8 elements, one per row).
+__device__ inline void transpose8x8(const u32x4 in[8], u32x4 out[8]) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {       // dword d of an input row: elements 2d, 2d+1
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {   // dword e of an output row: rows 2e, 2e+1
+            const uint32_t lo = in[2 * e][d];
+            const uint32_t hi = in[2 * e + 1][d];
+            out[2 * d][e] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+            out[2 * d + 1][e] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+        }
+    }
+}
+
+// Loader of one operand tile (R rows of the MN dimension x BK) into LDS rows
+// that are K-contiguous.  KC: the operand's storage is K-contiguous (row-major
+// A, column-major B).  VEC: 128-bit loads (every 8-vector wholly in or out).
+template <int R, int BK, int NT, bool KC, bool VEC>
+struct TileLoader {
+    static constexpr int VPR = BK / 8;                         // vectors per LDS row
+    static constexpr int UNITS = KC || !VEC ? R * VPR : (R / 8) * VPR;  // per stage
+    static constexpr int PER_THREAD = (UNITS + NT - 1) / NT;
+    static constexpr int REGS = KC || !VEC ? PER_THREAD : PER_THREAD * 8;
+
+    u32x4 stage[REGS];
+    uint32_t off[PER_THREAD];   // byte offset of the unit, relative to the K-step base
+    int kin[PER_THREAD];        // K index (relative to the step) of the unit
+    bool live[PER_THREAD];      // unit exists and its MN rows are in range
+
+    // Per-tile set-up.  r0: first MN row of the tile; rtot: M or N; ld: leading
+    // dimension in elements.
+    __device__ void init(int tid, int64_t r0, int64_t rtot, int64_t ld) {
+#pragma unroll
+        for (int q = 0; q < PER_THREAD; ++q) {
+            const int idx = q * NT + tid;
+            live[q] = idx < UNITS;
+            if constexpr (KC) {
+                const int r = idx / VPR, kv = idx % VPR;
+                off[q] = (uint32_t)((r * ld + kv * 8) * 2);
+                kin[q] = kv * 8;
+                live[q] = live[q] && (r0 + r < rtot);
+            } else if constexpr (VEC) {
+                const int rb = idx % (R / 8), kb = idx / (R / 8);
+                off[q] = (uint32_t)((kb * 8 * ld + rb * 8) * 2);
+                kin[q] = kb * 8;
+                live[q] = live[q] && (r0 + rb * 8 < rtot);
+            } else {
+                const int r = idx % R, kv = idx / R;
+                off[q] = (uint32_t)((r + kv * 8 * ld) * 2);
+                kin[q] = kv * 8;
+                live[q] = live[q] && (r0 + r < rtot);
+            }
+        }
+    }
+
+    // Issues the global loads of the K step whose first K index is k0.
+    // base points at element (r0, k0) of the operand.
+    __device__ void load(const _Float16 *base, int64_t bytes_left, int64_t k0,
+                         int64_t K, int64_t ld) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, bytes_left);
+#pragma unroll
+        for (int q = 0; q < PER_THREAD; ++q) {
+            if constexpr (VEC && KC) {
+                const uint32_t o = (live[q] && k0 + kin[q] < K) ? off[q] : kOutOfRange;
+                stage[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0));
+            } else if constexpr (VEC) {
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const uint32_t o = (live[q] && k0 + kin[q] + c < K)
+                                           ? off[q] + (uint32_t)(c * ld * 2) : kOutOfRange;
+                    stage[q * 8 + c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0));
+                }
+            } else {
+                // Narrow path: eight 16-bit loads, each range-checked on its own.
+                uint32_t h[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const bool ok = live[q] && (k0 + kin[q] + e < K);
+                    const uint32_t step = KC ? (uint32_t)(e * 2) : (uint32_t)(e * ld * 2);
+                    const uint32_t o = ok ? off[q] + step : kOutOfRange;
+                    h[e] = __builtin_amdgcn_raw_buffer_load_b16(rs, o, 0, 0);
+                }
+                u32x4 v;
+                v[0] = h[0] | (h[1] << 16);
+                v[1] = h[2] | (h[3] << 16);
+                v[2] = h[4] | (h[5] << 16);
+                v[3] = h[6] | (h[7] << 16);
+                stage[q] = v;
+            }
+        }
+    }
+
+    // Writes the staged registers into an LDS slot holding R rows of VPR vectors.
+    __device__ void store(u32x4 *lds, int tid) {
+#pragma unroll
+        for (int q = 0; q < PER_THREAD; ++q) {
+            const int idx = q * NT + tid;
+            if (UNITS % NT != 0 && idx >= UNITS) continue;
+            if constexpr (KC) {
+                const int r = idx / VPR, kv = idx % VPR;
+                lds[r * VPR + (kv ^ swz<VPR>(r))] = stage[q];
+            } else if constexpr (VEC) {
+                const int rb = idx % (R / 8), kb = idx / (R / 8);
+                u32x4 t[8];
+                transpose8x8(&stage[q * 8], t);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int r = rb * 8 + e;
+                    lds[r * VPR + (kb ^ swz<VPR>(r))] = t[e];
+                }
+            } else {
+                const int r = idx % R, kv = idx / R;
+                lds[r * VPR + (kv ^ swz<VPR>(r))] = stage[q];
+            }
+        }
+    }
+};
+
+// Maps a workgroup id to (batch item, tile row, tile column).  Workgroups are
+// dispatched round-robin over the 8 XCDs, each with its own L2; the id is first
+// remapped so that each XCD receives a contiguous run of logical tile ids, and
+// logical ids walk C in groups of group_m tile rows so that the tiles resident
+// on one XCD at a time share A rows and B columns in that XCD's L2.
+__device__ inline void tile_coords(const GemmArgs &p, int wg, int &b, int &tm, int &tn) {
+    constexpr int kXcds = 8;
+    const int total = p.total_tiles;
+    const int q = total / kXcds, rem = total % kXcds;
+    const int xcd = wg % kXcds, local = wg / kXcds;
+    const int logical = xcd * q + (xcd < rem ? xcd : rem) + local;
+    const int per = p.tiles_m * p.tiles_n;
+    b = logical / per;
+    const int t = logical - b * per;
+    const int width = p.group_m * p.tiles_n;
+    const int group = t / width;
+    const int first_m = group * p.group_m;
+    const int gsz = min(p.tiles_m - first_m, p.group_m);
+    const int tw = t - group * width;
+    tm = first_m + tw % gsz;
+    tn = tw / gsz;
+}
+
+template <int BM, int BN, int BK, int WGM, int WGN, bool AK, bool BKC, bool VEC>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
+    constexpr int NT = 64 * WGM * WGN;
+    constexpr int VPR = BK / 8;
+    constexpr int WTM = BM / WGM, WTN = BN / WGN;
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int SLOT = (BM + BN) * VPR;          // 16-byte vectors per ring slot
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be 32-aligned");
+    static_assert(BK % 16 == 0, "BK must be a multiple of the MFMA K (16)");
+
+    __shared__ u32x4 lds[2 * SLOT];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WGN, wn = wave % WGN;
+
+    int b, tm, tn;
+    tile_coords(p, blockIdx.x, b, tm, tn);
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+    const _Float16 *Ab = p.A + b * p.sa;
+    const _Float16 *Bb = p.B + b * p.sb;
+    // Per-tile bases and K-step strides (elements) of each operand.
+    const int64_t a_tile = AK ? m0 * p.lda : m0;
+    const int64_t a_kstep = AK ? BK : BK * p.lda;
+    const int64_t b_tile = BKC ? n0 * p.ldb : n0;
+    const int64_t b_kstep = BKC ? BK : BK * p.ldb;
+
+    TileLoader<BM, BK, NT, AK, VEC> la;
+    TileLoader<BN, BK, NT, BKC, VEC> lb;
+    la.init(tid, m0, p.M, p.lda);
+    lb.init(tid, n0, p.N, p.ldb);
+
+    floatx16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int64_t nk = (p.K + BK - 1) / BK;
+
+    auto issue = [&](int64_t kt) {
+        const int64_t k0 = kt * BK;
+        const int64_t ao = a_tile + kt * a_kstep, bo = b_tile + kt * b_kstep;
+        la.load(Ab + ao, (p.extent_a - ao) * 2, k0, p.K, p.lda);
+        lb.load(Bb + bo, (p.extent_b - bo) * 2, k0, p.K, p.ldb);
+    };
+
+    if (nk > 0) {
+        issue(0);
+        la.store(lds, tid);
+        lb.store(lds + BM * VPR, tid);
+    }
+    __syncthreads();
+
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        const int cur = (int)(kt & 1);
+        const bool more = kt + 1 < nk;
+        if (more) issue(kt + 1);
+
+        const u32x4 *sa = lds + cur * SLOT;
+        const u32x4 *sb = sa + BM * VPR;
+#pragma unroll
+        for (int s = 0; s < BK / 16; ++s) {
+            const int kv = 2 * s + (lane >> 5);
+            half8 af[FM], bf[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int r = wm * WTM + i * 32 + (lane & 31);
+                af[i] = __builtin_bit_cast(half8, sa[r * VPR + (kv ^ swz<VPR>(r))]);
+            }
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int r = wn * WTN + j * 32 + (lane & 31);
+                bf[j] = __builtin_bit_cast(half8, sb[r * VPR + (kv ^ swz<VPR>(r))]);
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    // src0 = B fragment (rows n), src1 = A fragment (columns m):
+                    // the block accumulates C^T, so each lane ends up holding
+                    // runs of 4 consecutive n of one row m of C.
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
+        }
+
+        if (more) {
+            u32x4 *dst = lds + (cur ^ 1) * SLOT;
+            la.store(dst, tid);
+            lb.store(dst + BM * VPR, tid);
+        }
+        __syncthreads();
+    }
+
+    // Epilogue.  Accumulator register r of lane l in block (i, j) holds
+    // C(m, n) with m = l % 32 and n = 8*(r/4) + 4*(l/32) + r%4 (block-local).
+    const float alpha = p.alpha, beta = p.beta;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int64_t m = m0 + wm * WTM + i * 32 + (lane & 31);
+        if (m >= p.M) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int64_t n = n0 + wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
+                if (n >= p.N) continue;
+                const int64_t off = b * p.sc + m * p.ldc + n;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = alpha * acc[i][j][4 * g + e];
+                const bool full = p.c_vec && (n + 4 <= p.N);
+                if (p.out_f32) {
+                    float *C = (float *)p.C + off;
+                    if (full) {
+                        if (beta != 0.0f) {
+                            const floatx4 c = *(const floatx4 *)C;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) v[e] += beta * c[e];
+                        }
+                        floatx4 o = {v[0], v[1], v[2], v[3]};
+                        *(floatx4 *)C = o;
+                    } else {
+                        for (int e = 0; e < 4 && n + e < p.N; ++e) {
+                            float o = v[e];
+                            if (beta != 0.0f) o += beta * C[e];
+                            C[e] = o;
+                        }
+                    }
+                } else {
+                    _Float16 *C = (_Float16 *)p.C + off;
+                    if (full) {
+                        if (beta != 0.0f) {
+                            const half4 c = *(const half4 *)C;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) v[e] += beta * (float)c[e];
+                        }
+                        half4 o = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+                        *(half4 *)C = o;
+                    } else {
+                        for (int e = 0; e < 4 && n + e < p.N; ++e) {
+                            float o = v[e];
+                            if (beta != 0.0f) o += beta * (float)C[e];
+                            C[e] = (_Float16)o;
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+typedef void (*KernelFn)(GemmArgs);
+
+template <int T, bool AK, bool BKC, bool VEC>
+constexpr KernelFn pick() {
+    return gemm_kernel<kTiles[T].bm, kTiles[T].bn, kTiles[T].bk, kTiles[T].wgm,
+                       kTiles[T].wgn, AK, BKC, VEC>;
+}
+
+// Kernel table indexed [tile][A K-contiguous][B K-contiguous][vec].
+template <int T>
+constexpr void fill_tile(KernelFn (&t)[2][2][2]) {
+    t[0][0][0] = pick<T, false, false, false>();
+    t[0][0][1] = pick<T, false, false, true>();
+    t[0][1][0] = pick<T, false, true, false>();
+    t[0][1][1] = pick<T, false, true, true>();
+    t[1][0][0] = pick<T, true, false, false>();
+    t[1][0][1] = pick<T, true, false, true>();
+    t[1][1][0] = pick<T, true, true, false>();
+    t[1][1][1] = pick<T, true, true, true>();
+}
+
+struct KernelTable {
+    KernelFn k[NUM_TILES][2][2][2];
+    KernelTable() {
+        fill_tile<TILE_256x256>(k[TILE_256x256]);
+        fill_tile<TILE_128x128>(k[TILE_128x128]);
+        fill_tile<TILE_64x64>(k[TILE_64x64]);
+        fill_tile<TILE_32x64>(k[TILE_32x64]);
+    }
+};
+
+const KernelTable &kernels() {
+    static const KernelTable t;
+    return t;
+}
+
+bool ranges_overlap(uintptr_t a, int64_t a_bytes, uintptr_t b, int64_t b_bytes) {
+    if (a_bytes <= 0 || b_bytes <= 0) return false;
+    return a < b + (uintptr_t)b_bytes && b < a + (uintptr_t)a_bytes;
+}
+
+}  // namespace
+
+extern "C" int gemm_f16f32_run(gemm_f16f32_plan_t plan, const void *A,
+                               const void *B, void *C, float alpha, float beta,
+                               void *stream) {
+    if (!plan) return GEMM_ERR_INVALID_ARG;
+    const gemm_f16f32_plan_s &p = *plan;
+    if (p.M == 0 || p.N == 0) return GEMM_OK;
+    if (!C) return GEMM_ERR_INVALID_ARG;
+    if (p.K > 0 && (!A || !B)) return GEMM_ERR_INVALID_ARG;
+    const int64_t cbytes = p.extent_c * (p.out_type == GEMM_OUT_F32 ? 4 : 2);
+    if (p.K > 0 && (ranges_overlap((uintptr_t)C, cbytes, (uintptr_t)A, p.extent_a * 2) ||
+                    ranges_overlap((uintptr_t)C, cbytes, (uintptr_t)B, p.extent_b * 2)))
+        return GEMM_ERR_INVALID_ARG;
+
+    const bool vec = p.vec_ok && ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0);
+    const int64_t celem = p.out_type == GEMM_OUT_F32 ? 4 : 2;
+    const bool c_vec = (p.ldc % 4 == 0) && (p.stride_c % 4 == 0) &&
+                       ((uintptr_t)C % (4 * celem) == 0);
+
+    GemmArgs a;
+    a.A = (const _Float16 *)A;
+    a.B = (const _Float16 *)B;
+    a.C = C;
+    a.M = p.M; a.N = p.N; a.K = p.K;
+    a.lda = p.lda; a.ldb = p.ldb; a.ldc = p.ldc;
+    a.sa = p.stride_a; a.sb = p.stride_b; a.sc = p.stride_c;
+    // Elements reachable from each batch item's base (the range check of the
+    // buffer descriptor never lets a load leave the operand).
+    a.extent_a = p.layout_a == GEMM_ROW_MAJOR ? (p.M - 1) * p.lda + p.K
+                                              : (p.K - 1) * p.lda + p.M;
+    a.extent_b = p.layout_b == GEMM_ROW_MAJOR ? (p.K - 1) * p.ldb + p.N
+                                              : (p.N - 1) * p.ldb + p.K;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.tiles_m = (int)p.tiles_m;
+    a.tiles_n = (int)p.tiles_n;
+    a.group_m = p.group_m;
+    a.total_tiles = (int)(p.tiles_m * p.tiles_n * p.batch);
+    a.out_f32 = p.out_type == GEMM_OUT_F32;
+    a.c_vec = c_vec;
+
+    const TileShape &ts = kTiles[p.tile];
+    const int ak = p.layout_a == GEMM_ROW_MAJOR;   // A K-contiguous
+    const int bkc = p.layout_b == GEMM_COL_MAJOR;  // B K-contiguous
+    KernelFn fn = kernels().k[p.tile][ak][bkc][vec ? 1 : 0];
+    void *args[] = {&a};
+    hipError_t e = hipLaunchKernel((const void *)fn, dim3((unsigned)a.total_tiles),
+                                   dim3(64 * ts.wgm * ts.wgn), args, 0,
+                                   (hipStream_t)stream);
+    return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}

@@ -1,0 +1,148 @@
+// Host-side planner of the fp16 -> fp32-accumulate GEMM: argument validation,
+// tile choice and grid shape.  Makes no HIP call, so it runs (and is tested)
+// on machines without a GPU.
+//
+// Pages cited (titles as printed):
+//   [GEMM]    "手写GEMM内核：矩阵乘法性能优化的完整工程实践" (hand-written GEMM kernel)
+//   [OPS]     CUDA operator practice page (Softmax and GEMM)
+//   [CATLASS] CATLASS template library page
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "gemm_f16f32.h"
+#include "gemm_internal.h"
+
+using namespace mpgemm;
+
+namespace {
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Elements spanned by one operand over the whole batch (0 when empty).
+int64_t operand_extent(int64_t rows, int64_t cols, int64_t ld, int64_t batch,
+                       int64_t stride) {
+    if (rows == 0 || cols == 0) return 0;
+    return (batch - 1) * stride + (rows - 1) * ld + cols;
+}
+
+// Tile choice.  [GEMM] §1.3 rules out autotuning and run-time selection among
+// many kernels; the choice here is a fixed rule on the shape.  [OPS] §4.3
+// asks that the grid fill the device, so the largest tile that still gives at
+// least one workgroup per compute unit is taken; skinny M (token counts of a
+// linear layer) takes the 32-row tile.
+int choose_tile(int64_t M, int64_t N, int64_t batch) {
+    if (M <= 32) return TILE_32x64;
+    auto count = [&](int t) {
+        return ceil_div(M, kTiles[t].bm) * ceil_div(N, kTiles[t].bn) * batch;
+    };
+    if (count(TILE_256x256) >= kNumCUs) return TILE_256x256;
+    if (count(TILE_128x128) >= kNumCUs / 2) return TILE_128x128;
+    return TILE_64x64;
+}
+
+}  // namespace
+
+extern "C" int gemm_f16f32_plan(gemm_f16f32_plan_t *out, int64_t M, int64_t N,
+                                int64_t K, int layout_a, int layout_b,
+                                int out_type, int64_t lda, int64_t ldb,
+                                int64_t ldc, int64_t batch, int64_t stride_a,
+                                int64_t stride_b, int64_t stride_c) {
+    if (!out) return GEMM_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_ARG;
+    if (layout_a != GEMM_ROW_MAJOR && layout_a != GEMM_COL_MAJOR)
+        return GEMM_ERR_INVALID_ARG;
+    if (layout_b != GEMM_ROW_MAJOR && layout_b != GEMM_COL_MAJOR)
+        return GEMM_ERR_INVALID_ARG;
+    if (out_type != GEMM_OUT_F16 && out_type != GEMM_OUT_F32)
+        return GEMM_ERR_INVALID_ARG;
+    if (batch < 1) return GEMM_ERR_INVALID_ARG;
+    const int64_t min_lda = layout_a == GEMM_ROW_MAJOR ? K : M;
+    const int64_t min_ldb = layout_b == GEMM_ROW_MAJOR ? N : K;
+    if (lda < 1 || lda < min_lda) return GEMM_ERR_INVALID_ARG;
+    if (ldb < 1 || ldb < min_ldb) return GEMM_ERR_INVALID_ARG;
+    if (ldc < 1 || ldc < N) return GEMM_ERR_INVALID_ARG;
+    if (batch > 1) {
+        if (stride_a < 0 || stride_b < 0 || stride_c < 0)
+            return GEMM_ERR_INVALID_ARG;
+        if (M > 0 && N > 0 && stride_c < M * ldc) return GEMM_ERR_INVALID_ARG;
+    } else {
+        stride_a = stride_b = stride_c = 0;
+    }
+    // Per-tile lane offsets are 32-bit byte offsets: a tile spans at most
+    // 256 rows (or 64 K steps) of an operand, so leading dimensions up to 2^22
+    // elements keep them below 2^31.
+    const int64_t kMaxLd = int64_t(1) << 22;
+    if (lda > kMaxLd || ldb > kMaxLd || ldc > kMaxLd) return GEMM_ERR_UNSUPPORTED;
+    if (batch > (int64_t(1) << 24)) return GEMM_ERR_UNSUPPORTED;
+
+    gemm_f16f32_plan_s *p = new (std::nothrow) gemm_f16f32_plan_s();
+    if (!p) return GEMM_ERR_NOMEM;
+    p->M = M; p->N = N; p->K = K;
+    p->layout_a = layout_a; p->layout_b = layout_b; p->out_type = out_type;
+    p->lda = lda; p->ldb = ldb; p->ldc = ldc;
+    p->batch = batch;
+    p->stride_a = stride_a; p->stride_b = stride_b; p->stride_c = stride_c;
+    p->extent_a = operand_extent(layout_a == GEMM_ROW_MAJOR ? M : K,
+                                 layout_a == GEMM_ROW_MAJOR ? K : M, lda, batch,
+                                 stride_a);
+    p->extent_b = operand_extent(layout_b == GEMM_ROW_MAJOR ? K : N,
+                                 layout_b == GEMM_ROW_MAJOR ? N : K, ldb, batch,
+                                 stride_b);
+    p->extent_c = operand_extent(M, N, ldc, batch, stride_c);
+    if (M == 0 || N == 0) {
+        p->tile = -1;
+        snprintf(p->kernel_name, sizeof p->kernel_name, "none");
+        *out = p;
+        return GEMM_OK;
+    }
+    // 128-bit loads need every 8-element vector along an operand's contiguous
+    // dimension to be either wholly inside or wholly outside the matrix, and
+    // every row (and batch item) to start on a 16-byte boundary.
+    const int64_t contig_a = layout_a == GEMM_ROW_MAJOR ? K : M;
+    const int64_t contig_b = layout_b == GEMM_ROW_MAJOR ? N : K;
+    p->vec_ok = (contig_a % 8 == 0) && (lda % 8 == 0) && (stride_a % 8 == 0) &&
+                (contig_b % 8 == 0) && (ldb % 8 == 0) && (stride_b % 8 == 0);
+    p->tile = choose_tile(M, N, batch);
+    // The narrow-load path stages eight 16-bit loads per vector; at the
+    // 256 x 256 tile that exceeds the register budget, so it stops at 128.
+    if (!p->vec_ok && p->tile == TILE_256x256) p->tile = TILE_128x128;
+    const TileShape &ts = kTiles[p->tile];
+    p->tiles_m = ceil_div(M, ts.bm);
+    p->tiles_n = ceil_div(N, ts.bn);
+    if (p->tiles_m * p->tiles_n * batch > 0x7fffffff) {
+        delete p;
+        return GEMM_ERR_UNSUPPORTED;
+    }
+    p->group_m = 8;
+    snprintf(p->kernel_name, sizeof p->kernel_name, "gemm_%s_%c%c_%s",
+             ts.name, layout_a == GEMM_ROW_MAJOR ? 'n' : 't',
+             layout_b == GEMM_ROW_MAJOR ? 'n' : 't',
+             p->vec_ok ? "vec16" : "narrow");
+    *out = p;
+    return GEMM_OK;
+}
+
+extern "C" int gemm_f16f32_destroy(gemm_f16f32_plan_t plan) {
+    delete plan;
+    return GEMM_OK;
+}
+
+extern "C" const char *gemm_f16f32_status_string(int status) {
+    switch (status) {
+    case GEMM_OK: return "GEMM_OK";
+    case GEMM_ERR_INVALID_ARG: return "GEMM_ERR_INVALID_ARG: an argument violates the documented rules";
+    case GEMM_ERR_UNSUPPORTED: return "GEMM_ERR_UNSUPPORTED: valid, but outside what the kernels cover";
+    case GEMM_ERR_HIP: return "GEMM_ERR_HIP: the HIP runtime refused the launch";
+    case GEMM_ERR_NOMEM: return "GEMM_ERR_NOMEM: host allocation failed";
+    default: return "unknown status";
+    }
+}
+
+extern "C" const char *gemm_f16f32_plan_kernel(gemm_f16f32_plan_t plan) {
+    if (!plan) return "invalid";
+    return plan->kernel_name;
+}

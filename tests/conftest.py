@@ -21,3 +21,13 @@ def gpu_available() -> bool:
 def oracle_mod():
     import oracle
     return oracle
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_test(request):
+    """Names each GPU test on stderr (flushed) before it touches the device,
+    so a run that ends abruptly still shows which case was running."""
+    if request.node.get_closest_marker("gpu") is not None:
+        sys.stderr.write(f"\n[gpu-test] {request.node.nodeid}\n")
+        sys.stderr.flush()
+    yield

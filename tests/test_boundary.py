@@ -1,0 +1,130 @@
+"""C-ABI boundary tests that need no GPU.
+
+The library must load and export every function include/*.h declares; the
+planner (which makes no HIP call) must enforce every documented rule; run must
+reject bad arguments before it reaches the HIP runtime.
+"""
+import glob
+import os
+import re
+
+import pytest
+
+import mixed_precision_gemm_amd as mpg
+from mixed_precision_gemm_amd import (GEMM_COL_MAJOR, GEMM_ERR_INVALID_ARG,
+                                      GEMM_ERR_UNSUPPORTED, GEMM_OK,
+                                      GEMM_OUT_F16, GEMM_OUT_F32,
+                                      GEMM_ROW_MAJOR)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"\b(gemm_\w+)\s*\(", text):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert names, "no declarations found"
+    lib = mpg.library()
+    for n in sorted(names):
+        assert hasattr(lib, n), n
+    assert names == set(mpg.EXPORTED)
+
+
+def plan(M=64, N=64, K=64, la=GEMM_ROW_MAJOR, lb=GEMM_ROW_MAJOR, out=GEMM_OUT_F16,
+         lda=None, ldb=None, ldc=None, batch=1, sa=0, sb=0, sc=0):
+    lda = lda if lda is not None else (K if la == GEMM_ROW_MAJOR else M)
+    ldb = ldb if ldb is not None else (N if lb == GEMM_ROW_MAJOR else K)
+    ldc = ldc if ldc is not None else N
+    st, h = mpg.gemm_f16f32_plan(M, N, K, la, lb, out, lda, ldb, ldc, batch, sa, sb, sc)
+    if h is not None:
+        mpg.gemm_f16f32_destroy(h)
+    return st
+
+
+def test_valid_plans():
+    assert plan() == GEMM_OK
+    for la in (0, 1):
+        for lb in (0, 1):
+            for out in (0, 1):
+                assert plan(127, 257, 33, la, lb, out) == GEMM_OK
+    assert plan(1, 4096, 4096) == GEMM_OK
+    assert plan(64, 64, 64, batch=512, sa=4096, sb=4096, sc=4096) == GEMM_OK
+    # degenerate extents are valid
+    assert plan(0, 5, 5, ldc=5) == GEMM_OK
+    assert plan(5, 0, 5, ldb=1, ldc=1) == GEMM_OK
+    assert plan(5, 5, 0, lda=1) == GEMM_OK
+
+
+@pytest.mark.parametrize("kw", [
+    dict(M=-1), dict(N=-1), dict(K=-1),
+    dict(la=2), dict(lb=-1), dict(out=7),
+    dict(lda=63), dict(ldb=63), dict(ldc=63),
+    dict(la=GEMM_COL_MAJOR, M=100, lda=99),
+    dict(lb=GEMM_COL_MAJOR, K=100, ldb=99),
+    dict(batch=0), dict(batch=2, sa=-1, sb=0, sc=64 * 64),
+    dict(batch=2, sa=0, sb=0, sc=64 * 64 - 1),     # C batch items overlap
+])
+def test_invalid_plans(kw):
+    assert plan(**kw) == GEMM_ERR_INVALID_ARG
+
+
+def test_unsupported_leading_dimension():
+    assert plan(lda=(1 << 22) + 8) == GEMM_ERR_UNSUPPORTED
+
+
+def test_null_out_pointer():
+    lib = mpg.library()
+    assert lib.gemm_f16f32_plan(None, 1, 1, 1, 0, 0, 0, 1, 1, 1, 1, 0, 0, 0) == GEMM_ERR_INVALID_ARG
+
+
+def test_destroy_null_and_status_strings():
+    assert mpg.gemm_f16f32_destroy(None) == GEMM_OK
+    for st in (0, -1, -2, -3, -4):
+        s = mpg.gemm_f16f32_status_string(st)
+        assert s.startswith("GEMM_")
+    assert mpg.gemm_f16f32_status_string(12345) == "unknown status"
+    assert mpg.gemm_f16f32_plan_kernel(None) == "invalid"
+
+
+def test_kernel_choice_by_regime():
+    def kern(*a, **k):
+        p = mpg.Plan(*a, **k)
+        name = p.kernel
+        p.close()
+        return name
+    assert kern(8192, 8192, 8192).startswith("gemm_256x256")
+    assert kern(8192, 8192, 8192, layout_b=GEMM_COL_MAJOR).endswith("nt_vec16")
+    assert kern(16, 4096, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_32x64")
+    assert "narrow" in kern(127, 257, 33)
+    assert kern(0, 8, 8) == "none"
+
+
+def test_run_rejects_bad_arguments_before_launch():
+    with mpg.Plan(64, 64, 64) as p:
+        h = p.handle
+        assert mpg.gemm_f16f32_run(None, 16, 16, 16, 1.0, 0.0, None) == GEMM_ERR_INVALID_ARG
+        assert mpg.gemm_f16f32_run(h, 0, 1 << 20, 1 << 24, 1.0, 0.0, None) == GEMM_ERR_INVALID_ARG
+        assert mpg.gemm_f16f32_run(h, 1 << 20, 0, 1 << 24, 1.0, 0.0, None) == GEMM_ERR_INVALID_ARG
+        assert mpg.gemm_f16f32_run(h, 1 << 20, 1 << 21, 0, 1.0, 0.0, None) == GEMM_ERR_INVALID_ARG
+        # C overlapping A or B (addresses only; nothing is launched)
+        base = 1 << 30
+        assert mpg.gemm_f16f32_run(h, base, base + (1 << 20), base + 100, 1.0, 0.0, None) == GEMM_ERR_INVALID_ARG
+        assert mpg.gemm_f16f32_run(h, base + (1 << 20), base, base + 100, 1.0, 0.0, None) == GEMM_ERR_INVALID_ARG
+    # an empty product is a no-op even with NULL pointers
+    with mpg.Plan(0, 64, 64) as p:
+        assert mpg.gemm_f16f32_run(p.handle, 0, 0, 0, 1.0, 0.0, None) == GEMM_OK
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(mpg, "_lib", None)
+    monkeypatch.setattr(mpg, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(ImportError):
+        mpg.library()

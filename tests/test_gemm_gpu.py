@@ -1,0 +1,280 @@
+"""GPU parity of the HIP GEMM against the CPU oracle, through the C ABI.
+
+Each test draws seeded inputs (gemm_inputs), runs the library's kernel on
+cuda:0, and compares with the oracle element by element under the acceptance
+bound of tests/parity.py -- on every element for shapes the oracle finishes
+in seconds, on sampled rows (first, last, tile boundaries, random) at the full
+workload sizes.  Cases whose exact result is representable are compared bit
+for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gemm_inputs as gi
+import mixed_precision_gemm_amd as mpg
+from gemm_inputs import COL_MAJOR, OUT_F16, OUT_F32, ROW_MAJOR
+from parity import (c_logical, check_bound, oracle_for, parity, run_case,
+                    sample_rows, to_device)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+LAYOUTS = [(ROW_MAJOR, ROW_MAJOR), (ROW_MAJOR, COL_MAJOR),
+           (COL_MAJOR, ROW_MAJOR), (COL_MAJOR, COL_MAJOR)]
+LNAME = {(0, 0): "NN", (0, 1): "NT", (1, 0): "TN", (1, 1): "TT"}
+
+
+# ------------------------------------------------------------ workloads
+
+def test_square_256_nn():
+    """M = N = K = 256, uniform [-1, 1), alpha 1, beta 0, fp16 C."""
+    case = gi.make_case(256, 256, 256, seed=0)
+    parity(case, what="256^3 NN")
+
+
+@pytest.mark.parametrize("shape", [(1, 4096, 4096), (1000, 1000, 1000),
+                                   (127, 257, 33), (4097, 63, 1025)])
+def test_edge_shapes(shape):
+    M, N, K = shape
+    case = gi.make_case(M, N, K, seed=0)
+    parity(case, what=f"edge {shape}")
+
+
+@pytest.mark.parametrize("la,lb", [(ROW_MAJOR, ROW_MAJOR), (ROW_MAJOR, COL_MAJOR)])
+@pytest.mark.parametrize("n", [1024, 2048])
+def test_square_beta1_full(n, la, lb):
+    case = gi.make_case(n, n, n, layout_a=la, layout_b=lb, alpha=1.0, beta=1.0, seed=0)
+    parity(case, what=f"{n}^3 {LNAME[(la, lb)]} beta=1")
+
+
+@pytest.mark.parametrize("lb", [ROW_MAJOR, COL_MAJOR])
+@pytest.mark.parametrize("n", [4096, 8192])
+def test_square_beta1_sampled(n, lb):
+    """Full-size square GEMMs (the headline size at 8192) on sampled rows."""
+    case = gi.headline_case(n, layout_b=lb)
+    rows = sample_rows(n)
+    parity(case, rows=rows, what=f"{n}^3 {LNAME[(0, lb)]} beta=1 sampled")
+
+
+@pytest.mark.parametrize("N", [4096, 11008, 12288])
+@pytest.mark.parametrize("M", [16, 128, 2048, 8192])
+def test_linear_layer_shapes(M, N):
+    case = gi.linear_case(M, N)
+    rows = None if M <= 128 else sample_rows(M, n_random=96)
+    parity(case, rows=rows, what=f"linear M={M} N={N}")
+
+
+@pytest.mark.parametrize("kind", ["sq64", "qk"])
+def test_batched_small(kind):
+    case = gi.batched_case(kind)
+    parity(case, what=f"batched {kind}")
+
+
+# ----------------------------------------------------- layouts and types
+
+SWEEP = [(1, 1, 1), (2, 3, 5), (8, 8, 8), (31, 33, 17), (32, 64, 64),
+         (33, 65, 63), (64, 64, 128), (65, 127, 129), (100, 36, 72),
+         (129, 255, 200), (257, 129, 96), (300, 300, 65)]
+
+
+@pytest.mark.parametrize("out_type", [OUT_F16, OUT_F32])
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+def test_layout_sweep(la, lb, out_type):
+    for i, (M, N, K) in enumerate(SWEEP):
+        for alpha, beta in ((1.0, 0.0), (-0.5, 2.0)):
+            case = gi.make_case(M, N, K, layout_a=la, layout_b=lb,
+                                out_type=out_type, alpha=alpha, beta=beta,
+                                seed=100 + i)
+            parity(case, what=f"{LNAME[(la, lb)]} out={out_type} {M}x{N}x{K} a={alpha} b={beta}")
+
+
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+def test_padded_leading_dims_and_batch(la, lb):
+    for M, N, K in [(40, 48, 56), (37, 41, 43), (256, 64, 96)]:
+        lda = (K if la == ROW_MAJOR else M) + 8
+        ldb = (N if lb == ROW_MAJOR else K) + 16
+        ldc = N + 8
+        case = gi.make_case(M, N, K, layout_a=la, layout_b=lb, lda=lda, ldb=ldb,
+                            ldc=ldc, batch=3, beta=1.0, seed=7)
+        parity(case, what=f"padded {LNAME[(la, lb)]} {M}x{N}x{K}")
+
+
+# --------------------------------------------------------- exact cases
+
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+def test_integer_inputs_bit_exact_f16(la, lb):
+    """A, B in {-3..3}, K <= 113, C in {-8..8}, beta = 1: every partial sum is
+    an integer below 2^11, so the fp16 result is exact in any order."""
+    for M, N, K in [(64, 64, 64), (200, 136, 113), (33, 47, 100)]:
+        case = gi.make_case(M, N, K, layout_a=la, layout_b=lb, beta=1.0,
+                            dist_a="integer", dist_b="integer", dist_c="integer",
+                            seed=3)
+        dC = run_case(case)
+        got = c_logical(case, dC.cpu())
+        ref, _ = oracle_for(case)
+        assert np.array_equal(got, ref), (M, N, K)
+
+
+@pytest.mark.parametrize("la,lb", [(ROW_MAJOR, ROW_MAJOR), (ROW_MAJOR, COL_MAJOR)])
+def test_integer_inputs_bit_exact_f32(la, lb):
+    """A, B in {-8..8}, K = 4096: |C| <= 262144 < 2^24, exact in fp32."""
+    case = gi.make_case(512, 512, 4096, layout_a=la, layout_b=lb, out_type=OUT_F32,
+                        dist_a="integer", dist_b="integer", int_range=(-8, 8), seed=4)
+    dC = run_case(case)
+    got = c_logical(case, dC.cpu())
+    ref, _ = oracle_for(case)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("K", [1, 7, 64, 2048, 4097])
+def test_all_ones_gives_K(K):
+    case = gi.make_case(96, 80, K, dist_a="ones", dist_b="ones", seed=0)
+    dC = run_case(case)
+    got = dC.cpu().reshape(96, 80)
+    want = torch.full((96, 80), float(K), dtype=torch.float16)   # RNE of K
+    assert torch.equal(got, want)
+
+
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+def test_identity_returns_other_operand(la, lb):
+    n, N = 160, 72
+    g = torch.Generator().manual_seed(5)
+    Bm = (torch.rand(n, N, generator=g) * 2 - 1).half()
+    eye = torch.eye(n, dtype=torch.float16)
+    A = eye if la == ROW_MAJOR else eye.t().contiguous()
+    B = Bm if lb == ROW_MAJOR else Bm.t().contiguous()
+    lda = n
+    ldb = N if lb == ROW_MAJOR else n
+    C = torch.zeros(n, N, dtype=torch.float16, device="cuda")
+    with mpg.Plan(n, N, n, la, lb, OUT_F16, lda, ldb, N) as p:
+        p.run(A.cuda(), B.cuda(), C)
+    assert torch.equal(C.cpu(), Bm)
+
+
+def test_fragment_layout_one_hot():
+    """Batch of 32x32x16 products of one-hot matrices: item t has A = e_i e_k^T
+    and B = e_k' e_j^T; C must be e_i e_j^T when k == k' and zero otherwise.
+    Pins which lane and register of the MFMA fragments hold which (i, j, k)."""
+    items = []
+    for i in range(32):
+        for j in range(32):
+            k = (i * 5 + j) % 16
+            items.append((i, j, k, k))
+            if (i + j) % 8 == 0:
+                items.append((i, j, k, (k + 1 + i % 15) % 16))
+    T = len(items)
+    A = torch.zeros(T, 32, 16, dtype=torch.float16)
+    B = torch.zeros(T, 16, 32, dtype=torch.float16)
+    for t, (i, j, k, k2) in enumerate(items):
+        A[t, i, k] = 1.0
+        B[t, k2, j] = 1.0
+    C = torch.full((T, 32, 32), 7.0, dtype=torch.float16, device="cuda")
+    with mpg.Plan(32, 32, 16, ROW_MAJOR, ROW_MAJOR, OUT_F16, 16, 32, 32, T,
+                  32 * 16, 16 * 32, 32 * 32) as p:
+        p.run(A.cuda(), B.cuda(), C)
+    C = C.cpu()
+    for t, (i, j, k, k2) in enumerate(items):
+        want = torch.zeros(32, 32, dtype=torch.float16)
+        if k == k2:
+            want[i, j] = 1.0
+        assert torch.equal(C[t], want), (t, i, j, k, k2)
+
+
+def test_overflow_rounds_to_infinity():
+    """|sum| = 2 * 200 * 200 = 80000 >= 65520 -> +-inf in fp16."""
+    A = torch.full((64, 2), 200.0, dtype=torch.float16)
+    B = torch.full((2, 64), 200.0, dtype=torch.float16)
+    B[:, 32:] = -200.0
+    C = torch.zeros(64, 64, dtype=torch.float16, device="cuda")
+    with mpg.Plan(64, 64, 2, lda=2, ldb=64, ldc=64) as p:
+        p.run(A.cuda(), B.cuda(), C)
+    C = C.cpu().float()
+    assert torch.all(C[:, :32] == float("inf"))
+    assert torch.all(C[:, 32:] == float("-inf"))
+
+
+# ---------------------------------------------- reads and writes respected
+
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+def test_nan_in_padding_and_c_not_read_when_beta_zero(la, lb):
+    M, N, K = 70, 90, 50
+    lda = (K if la == ROW_MAJOR else M) + 6
+    ldb = (N if lb == ROW_MAJOR else K) + 6
+    case = gi.make_case(M, N, K, layout_a=la, layout_b=lb, lda=lda, ldb=ldb, seed=9)
+    # NaN in every padding element of A and B, NaN in all of C (beta = 0)
+    A = case.A.reshape(-1, lda).clone()
+    A[:, (K if la == ROW_MAJOR else M):] = float("nan")
+    B = case.B.reshape(-1, ldb).clone()
+    B[:, (N if lb == ROW_MAJOR else K):] = float("nan")
+    case.A, case.B = A.reshape(-1), B.reshape(-1)
+    case.C = torch.full_like(case.C, float("nan"))
+    dC = run_case(case)
+    got = c_logical(case, dC.cpu())
+    assert np.isfinite(got).all()
+    ref, scale = oracle_for(case)
+    check_bound(got, ref, scale, OUT_F16, "nan padding")
+
+
+def test_writes_stay_inside_c():
+    """Sentinels in C's ld padding, in the rows after M and in the batch gap
+    must survive."""
+    M, N, K, ldc, batch = 77, 45, 64, 56, 2
+    stride_c = (M + 3) * ldc
+    case = gi.make_case(M, N, K, batch=batch, seed=11)
+    sentinel = -1234.0
+    C = torch.full((batch * stride_c,), sentinel, dtype=torch.float16, device="cuda")
+    with mpg.Plan(M, N, K, ldc=ldc, batch=batch, stride_a=case.stride_a,
+                  stride_b=case.stride_b, stride_c=stride_c) as p:
+        p.run(case.A.cuda(), case.B.cuda(), C)
+    C = C.cpu().reshape(batch, M + 3, ldc)
+    assert torch.all(C[:, :, N:] == sentinel)
+    assert torch.all(C[:, M:, :] == sentinel)
+    assert not torch.any(C[:, :M, :N] == sentinel)
+
+
+def test_misaligned_pointers_take_the_narrow_path():
+    M, N, K = 96, 64, 128
+    case = gi.make_case(M, N, K, beta=1.0, seed=12)
+    A = torch.zeros(case.A.numel() + 1, dtype=torch.float16, device="cuda")
+    B = torch.zeros(case.B.numel() + 3, dtype=torch.float16, device="cuda")
+    C = torch.zeros(case.C.numel() + 1, dtype=torch.float16, device="cuda")
+    A[1:] = case.A.cuda()
+    B[3:] = case.B.cuda()
+    C[1:] = case.C.cuda()
+    run_case(case, A[1:], B[3:], C[1:])
+    got = c_logical(case, C[1:].cpu())
+    ref, scale = oracle_for(case)
+    check_bound(got, ref, scale, OUT_F16, "misaligned")
+
+
+def test_degenerate_extents():
+    # K = 0: C <- beta * C
+    case = gi.make_case(50, 40, 0, beta=0.5, lda=1, seed=13)
+    dC = run_case(case)
+    assert torch.equal(dC.cpu(), (case.C.float() * 0.5).half())
+    # M = 0: no-op, even with null pointers
+    with mpg.Plan(0, 40, 30) as p:
+        assert mpg.gemm_f16f32_run(p.handle, 0, 0, 0, 1.0, 0.0, None) == 0
+    # alpha = 0: beta * C
+    case = gi.make_case(33, 65, 17, alpha=0.0, beta=2.0, seed=14)
+    dC = run_case(case)
+    assert torch.equal(dC.cpu(), (case.C.float() * 2.0).half())
+
+
+# ---------------------------------------------------------- determinism
+
+def test_run_to_run_bitwise_determinism():
+    """Same plan, same inputs: bitwise identical output, also on another
+    stream (a missing barrier shows up as run-to-run differences)."""
+    case = gi.make_case(1536, 1280, 1000, beta=1.0, seed=15)
+    dA, dB, dC0 = to_device(case)
+    outs = []
+    s2 = torch.cuda.Stream()
+    for stream in (None, None, s2):
+        dC = dC0.clone()
+        torch.cuda.synchronize()
+        run_case(case, dA, dB, dC, stream=stream)
+        torch.cuda.synchronize()
+        outs.append(dC.cpu())
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
