@@ -11,24 +11,39 @@ namespace mpgemm {
 // output tile.  Each wave owns (BM/WGM) x (BN/WGN) outputs as 32 x 32 MFMA
 // accumulator blocks.
 enum TileId : int {
-    TILE_256x256 = 0,   // compute-bound square-ish problems
-    TILE_128x128 = 1,   // medium problems: more workgroups to fill 256 CUs
-    TILE_64x64 = 2,     // small and batched-small products
-    TILE_32x64 = 3,     // skinny M (tokens) problems
-    NUM_TILES = 4
+    TILE_256x256 = 0,        // compute-bound square-ish problems
+    TILE_128x128 = 1,        // medium problems: more workgroups to fill 256 CUs
+    TILE_64x64 = 2,          // small and batched-small products
+    TILE_32x64 = 3,          // skinny M (tokens) problems
+    TILE_128x128_STAGED = 4, // narrow-load fallback of the two direct tiles
+    NUM_TILES = 5
 };
 
+// Two kernel families share the tile table:
+//   KIND_DIRECT: an S-slot LDS ring filled by direct-to-LDS buffer loads (no
+//                register staging), for 16-byte-aligned operands;
+//   KIND_STAGED: a two-slot ring filled through registers (global -> VGPR ->
+//                LDS), used for the small tiles and for the narrow-load path.
+enum KernelKind : int { KIND_DIRECT = 0, KIND_STAGED = 1 };
+
 struct TileShape {
-    int bm, bn, bk, wgm, wgn;
+    int bm, bn, bk, wgm, wgn, stages, kind;
     const char *name;
 };
 
 constexpr TileShape kTiles[NUM_TILES] = {
-    {256, 256, 64, 2, 2, "256x256x64"},
-    {128, 128, 64, 2, 2, "128x128x64"},
-    {64, 64, 64, 2, 2, "64x64x64"},
-    {32, 64, 64, 1, 2, "32x64x64"},
+    {256, 256, 32, 2, 2, 4, KIND_DIRECT, "256x256x32s4"},
+    {128, 128, 32, 2, 2, 4, KIND_DIRECT, "128x128x32s4"},
+    {64, 64, 64, 2, 2, 2, KIND_STAGED, "64x64x64"},
+    {32, 64, 64, 1, 2, 2, KIND_STAGED, "32x64x64"},
+    {128, 128, 64, 2, 2, 2, KIND_STAGED, "128x128x64"},
 };
+
+// Tile of the staged kernel that serves operands the direct kernel cannot
+// take (unaligned rows or pointers).
+constexpr int narrow_tile(int t) {
+    return kTiles[t].kind == KIND_DIRECT ? TILE_128x128_STAGED : t;
+}
 
 constexpr int kNumCUs = 256;
 
@@ -39,9 +54,8 @@ struct gemm_f16f32_plan_s {
     int layout_a, layout_b, out_type;
     int64_t lda, ldb, ldc;
     int64_t batch, stride_a, stride_b, stride_c;
-    int tile;              // mpgemm::TileId
+    int tile;              // mpgemm::TileId for 16-byte-aligned operands
     int vec_ok;            // shapes allow 128-bit loads (pointers checked at run)
-    int64_t tiles_m, tiles_n;
     int group_m;           // tile rows per rasterisation group
     int64_t extent_a, extent_b, extent_c;  // elements spanned by each operand
     char kernel_name[64];

@@ -226,8 +226,73 @@ __device__ inline void tile_coords(const GemmArgs &p, int wg, int &b, int &tm, i
     tn = tw / gsz;
 }
 
+// Epilogue shared by both kernels: C = alpha * acc + beta * C on the wave's
+// FM x FN blocks of 32 x 32, rounded once to fp16 (RNE) or stored as fp32,
+// masked at the M and N edges.  Accumulator register r of lane l in block
+// (i, j) holds C(m, n) with m = l % 32 and n = 8*(r/4) + 4*(l/32) + r%4
+// (block-local), so each lane owns runs of 4 consecutive n of one row.
+template <int FM, int FN, int WTM, int WTN>
+__device__ inline void store_tile(const GemmArgs &p, const floatx16 (&acc)[FM][FN],
+                                  int b, int64_t m0, int64_t n0, int wm, int wn,
+                                  int lane) {
+    const float alpha = p.alpha, beta = p.beta;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int64_t m = m0 + wm * WTM + i * 32 + (lane & 31);
+        if (m >= p.M) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int64_t n = n0 + wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
+                if (n >= p.N) continue;
+                const int64_t off = b * p.sc + m * p.ldc + n;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = alpha * acc[i][j][4 * g + e];
+                const bool full = p.c_vec && (n + 4 <= p.N);
+                if (p.out_f32) {
+                    float *C = (float *)p.C + off;
+                    if (full) {
+                        if (beta != 0.0f) {
+                            const floatx4 c = *(const floatx4 *)C;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) v[e] += beta * c[e];
+                        }
+                        floatx4 o = {v[0], v[1], v[2], v[3]};
+                        *(floatx4 *)C = o;
+                    } else {
+                        for (int e = 0; e < 4 && n + e < p.N; ++e) {
+                            float o = v[e];
+                            if (beta != 0.0f) o += beta * C[e];
+                            C[e] = o;
+                        }
+                    }
+                } else {
+                    _Float16 *C = (_Float16 *)p.C + off;
+                    if (full) {
+                        if (beta != 0.0f) {
+                            const half4 c = *(const half4 *)C;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) v[e] += beta * (float)c[e];
+                        }
+                        half4 o = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+                        *(half4 *)C = o;
+                    } else {
+                        for (int e = 0; e < 4 && n + e < p.N; ++e) {
+                            float o = v[e];
+                            if (beta != 0.0f) o += beta * (float)C[e];
+                            C[e] = (_Float16)o;
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
 template <int BM, int BN, int BK, int WGM, int WGN, bool AK, bool BKC, bool VEC>
-__global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_staged(GemmArgs p) {
     constexpr int NT = 64 * WGM * WGN;
     constexpr int VPR = BK / 8;
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
@@ -323,83 +388,282 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
         __syncthreads();
     }
 
-    // Epilogue.  Accumulator register r of lane l in block (i, j) holds
-    // C(m, n) with m = l % 32 and n = 8*(r/4) + 4*(l/32) + r%4 (block-local).
-    const float alpha = p.alpha, beta = p.beta;
+    store_tile<FM, FN, WTM, WTN>(p, acc, b, m0, n0, wm, wn, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Direct kernel: S-slot LDS ring filled by direct-to-LDS buffer loads.
+//
+// Every wave instruction `buffer_load_dwordx4 ... lds` writes the 16 bytes of
+// lane t at LDS address M0 + 16 t, i.e. one contiguous 1 KiB run per
+// instruction; the swizzled LDS layout is produced by choosing which global
+// 16-byte chunk each lane fetches.  Lanes whose chunk lies outside the matrix
+// are given an offset that fails the buffer range check, which writes zeros.
+//   K-contiguous operand:  LDS rows [r][k], BK/8 chunks per row, chunk
+//                          c stored at c ^ swz(r); fragments by ds_read_b128.
+//   MN-contiguous operand: LDS rows [k][r], R/8 chunks per row, chunk c stored
+//                          at c ^ 4 (k % 4); fragments by two ds_read_b64_tr_b16,
+//                          which transpose 16-bit elements across each group of
+//                          16 lanes (lane j addresses row k0 + j/4 at column
+//                          n0 + 4 (j%4); lane i receives column n0 + i of rows
+//                          k0..k0+3).
+// ---------------------------------------------------------------------------
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+template <int R>
+__device__ __host__ constexpr int mn_swz(int k) {
+    static_assert(R / 8 >= 16, "MN-contiguous rows need at least 16 chunks");
+    return 4 * (k & 3);
+}
+
+// Byte offset of a __shared__ object within the workgroup's LDS allocation.
+__device__ inline uint32_t lds_offset(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// Buffer descriptor as four scalar words, for inline assembly.
+typedef int32_t sgpr4 __attribute__((ext_vector_type(4)));
+
+__device__ inline sgpr4 make_rsrc_words(const void *base, int64_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    const int32_t n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int32_t)bytes);
+    sgpr4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(a >> 32) & 0xffff);  // stride 0
+    r[2] = __builtin_amdgcn_readfirstlane(n);
+    r[3] = kRsrcWord3;
+    return r;
+}
+
+// One 16-byte-per-lane direct-to-LDS load: lane t's data lands at LDS byte
+// address lds_addr + 16 t.  Issued as assembly so that the compiler's
+// wait-count insertion does not treat later LDS reads of other ring slots as
+// dependent on it; the kernel orders it explicitly (vmcnt waits + barriers).
+__device__ inline void lds_dma16(sgpr4 rs, uint32_t lds_addr, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(lds_addr), "s"(rs)
+                 : "m0");
+}
+
+// Waits until at most N vector-memory operations of this wave are pending.
+template <int N>
+__device__ inline void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// Workgroup barrier that is also a compiler memory barrier, without the
+// wait for all outstanding memory operations that a fenced barrier implies.
+__device__ inline void barrier() { asm volatile("s_barrier" : : : "memory"); }
+
+template <int R, int BK, int NW, bool KC>
+struct DirectOperand {
+    static constexpr int VPR = BK / 8;                 // chunks per [r][k] row
+    static constexpr int CPR = R / 8;                  // chunks per [k][r] row
+    static constexpr int CHUNKS = R * BK / 8;          // 16-byte chunks per stage
+    static constexpr int INSTR = CHUNKS / 64;          // 1 KiB instructions per stage
+    static constexpr int PER_WAVE = INSTR / NW;
+    static_assert(CHUNKS % 64 == 0 && INSTR % NW == 0, "stage must split evenly over waves");
+
+    uint32_t off[PER_WAVE];
+    int kin[PER_WAVE];
+    bool ok[PER_WAVE];
+
+    __device__ void init(int wave, int lane, int64_t r0, int64_t rtot, int64_t ld) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int64_t m = m0 + wm * WTM + i * 32 + (lane & 31);
-        if (m >= p.M) continue;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int64_t n = n0 + wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
-                if (n >= p.N) continue;
-                const int64_t off = b * p.sc + m * p.ldc + n;
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = alpha * acc[i][j][4 * g + e];
-                const bool full = p.c_vec && (n + 4 <= p.N);
-                if (p.out_f32) {
-                    float *C = (float *)p.C + off;
-                    if (full) {
-                        if (beta != 0.0f) {
-                            const floatx4 c = *(const floatx4 *)C;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) v[e] += beta * c[e];
-                        }
-                        floatx4 o = {v[0], v[1], v[2], v[3]};
-                        *(floatx4 *)C = o;
-                    } else {
-                        for (int e = 0; e < 4 && n + e < p.N; ++e) {
-                            float o = v[e];
-                            if (beta != 0.0f) o += beta * C[e];
-                            C[e] = o;
-                        }
-                    }
-                } else {
-                    _Float16 *C = (_Float16 *)p.C + off;
-                    if (full) {
-                        if (beta != 0.0f) {
-                            const half4 c = *(const half4 *)C;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) v[e] += beta * (float)c[e];
-                        }
-                        half4 o = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-                        *(half4 *)C = o;
-                    } else {
-                        for (int e = 0; e < 4 && n + e < p.N; ++e) {
-                            float o = v[e];
-                            if (beta != 0.0f) o += beta * (float)C[e];
-                            C[e] = (_Float16)o;
-                        }
-                    }
-                }
+        for (int i = 0; i < PER_WAVE; ++i) {
+            const int p = (i * NW + wave) * 64 + lane;
+            if constexpr (KC) {
+                const int r = p / VPR, c = (p % VPR) ^ swz<VPR>(r);
+                off[i] = (uint32_t)((r * ld + c * 8) * 2);
+                kin[i] = c * 8;
+                ok[i] = r0 + r < rtot;
+            } else {
+                const int k = p / CPR, c = (p % CPR) ^ mn_swz<R>(k);
+                off[i] = (uint32_t)((k * ld + c * 8) * 2);
+                kin[i] = k;
+                ok[i] = r0 + c * 8 < rtot;
             }
         }
     }
+
+    // Issues this wave's share of one stage.  base: element (r0, k0) of the
+    // operand; lds: the operand's region of the ring slot.
+    // Stages at or beyond the end of K fail every range check and write zeros.
+    __device__ void issue(const _Float16 *base, int64_t bytes_left, uint32_t lds_addr,
+                          int wave, int64_t k0, int64_t K) {
+        const sgpr4 rs = make_rsrc_words(base, bytes_left);
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i) {
+            const uint32_t o = (ok[i] && k0 + kin[i] < K) ? off[i] : kOutOfRange;
+            lds_dma16(rs, lds_addr + (uint32_t)((i * NW + wave) * 64 * 16), o);
+        }
+    }
+
+    // MFMA fragment of the 32-row block starting at rb, K sub-step s (16 deep):
+    // lane l receives rows rb + l%32, k = 16 s + 8 (l/32) + 0..7.
+    __device__ half8 frag(const u32x4 *lds, int rb, int s, int lane) const {
+        if constexpr (KC) {
+            const int r = rb + (lane & 31);
+            const int kv = 2 * s + (lane >> 5);
+            return __builtin_bit_cast(half8, lds[r * VPR + (kv ^ swz<VPR>(r))]);
+        } else {
+            const int g4 = lane >> 4, j = lane & 15;
+            const int n = rb + 16 * (g4 & 1) + 4 * (j & 3);
+            const char *bytes = (const char *)lds;
+            v4i16 h[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int k = 16 * s + 8 * (g4 >> 1) + 4 * t + (j >> 2);
+                const int addr = k * R * 2 + (((n >> 3) ^ mn_swz<R>(k)) << 4) + (n & 7) * 2;
+                h[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4i16 *)(bytes + addr));
+            }
+            const v4i16 lo = h[0], hi = h[1];
+            return __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    }
+};
+
+template <int BM, int BN, int BK, int WGM, int WGN, int S, bool AK, bool BKC>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs p) {
+    constexpr int NW = WGM * WGN;
+    constexpr int WTM = BM / WGM, WTN = BN / WGN;
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int NSUB = BK / 16;
+    constexpr int A_CH = BM * BK / 8, B_CH = BN * BK / 8;
+    constexpr int SLOT = A_CH + B_CH;                 // 16-byte chunks per slot
+    using OpA = DirectOperand<BM, BK, NW, AK>;
+    using OpB = DirectOperand<BN, BK, NW, BKC>;
+    constexpr int L = OpA::PER_WAVE + OpB::PER_WAVE;  // loads per lane per stage
+    static_assert(S >= 3, "the ring needs at least three slots");
+    static_assert((S - 2) * L < 64, "vmcnt range");
+    static_assert(NSUB % 2 == 0, "fragment double buffering pairs sub-steps");
+
+    __shared__ u32x4 lds[S * SLOT];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WGN, wn = wave % WGN;
+
+    int b, tm, tn;
+    tile_coords(p, blockIdx.x, b, tm, tn);
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    const _Float16 *Ab = p.A + b * p.sa;
+    const _Float16 *Bb = p.B + b * p.sb;
+    const int64_t a_tile = AK ? m0 * p.lda : m0;
+    const int64_t a_kstep = AK ? BK : BK * p.lda;
+    const int64_t b_tile = BKC ? n0 * p.ldb : n0;
+    const int64_t b_kstep = BKC ? BK : BK * p.ldb;
+
+    OpA opa;
+    OpB opb;
+    opa.init(wave, lane, m0, p.M, p.lda);
+    opb.init(wave, lane, n0, p.N, p.ldb);
+
+    floatx16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int64_t nk = (p.K + BK - 1) / BK;
+
+    const uint32_t lds_base = lds_offset(lds);
+    // Issues stage st into ring slot st % S (zeros when st >= nk).
+    auto issue = [&](int64_t st) {
+        const uint32_t slot = lds_base + (uint32_t)((st % S) * SLOT * 16);
+        const int64_t ao = a_tile + st * a_kstep, bo = b_tile + st * b_kstep;
+        opa.issue(Ab + ao, (p.extent_a - ao) * 2, slot, wave, st * BK, p.K);
+        opb.issue(Bb + bo, (p.extent_b - bo) * 2, slot + A_CH * 16, wave, st * BK, p.K);
+    };
+
+    half8 fa[2][FM], fb[2][FN];
+    auto read_frags = [&](int buf, int64_t st, int s) {
+        const u32x4 *slot = lds + (int)(st % S) * SLOT;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[buf][i] = opa.frag(slot, wm * WTM + i * 32, s, lane);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[buf][j] = opb.frag(slot + A_CH, wn * WTN + j * 32, s, lane);
+    };
+
+    // Every iteration issues exactly L loads per lane (stages past the end are
+    // range-check failures), so the wait counts below are exact.
+#pragma unroll
+    for (int st = 0; st < S - 1; ++st) issue(st);
+    wait_vmcnt<(S - 2) * L>();          // stage 0 resident for this lane
+    barrier();                          // ... and for every lane
+    read_frags(0, 0, 0);
+
+    for (int64_t kt = 0; kt < nk; ++kt) {
+#pragma unroll
+        for (int sub = 0; sub < NSUB; ++sub) {
+            const int cur = sub & 1, nxt = cur ^ 1;
+            if (sub + 1 < NSUB) {
+                read_frags(nxt, kt, sub + 1);
+            } else {
+                // Stage kt+1 resident for every lane; the barrier also certifies
+                // that all waves have finished reading slot (kt-1)%S, refilled
+                // next with stage kt+S-1.  (After the last stage the fragment
+                // reads below fetch a slot that is never used.)
+                wait_vmcnt<(S - 3) * L>();
+                barrier();
+                issue(kt + S - 1);
+                read_frags(nxt, kt + 1, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
+        }
+    }
+    // No direct-to-LDS write may still be in flight when the workgroup's LDS
+    // is released.
+    wait_vmcnt<0>();
+
+    store_tile<FM, FN, WTM, WTN>(p, acc, b, m0, n0, wm, wn, lane);
 }
 
 typedef void (*KernelFn)(GemmArgs);
 
 template <int T, bool AK, bool BKC, bool VEC>
-constexpr KernelFn pick() {
-    return gemm_kernel<kTiles[T].bm, kTiles[T].bn, kTiles[T].bk, kTiles[T].wgm,
+constexpr KernelFn pick_staged() {
+    return gemm_staged<kTiles[T].bm, kTiles[T].bn, kTiles[T].bk, kTiles[T].wgm,
                        kTiles[T].wgn, AK, BKC, VEC>;
 }
 
-// Kernel table indexed [tile][A K-contiguous][B K-contiguous][vec].
+template <int T, bool AK, bool BKC>
+constexpr KernelFn pick_direct() {
+    return gemm_direct<kTiles[T].bm, kTiles[T].bn, kTiles[T].bk, kTiles[T].wgm,
+                       kTiles[T].wgn, kTiles[T].stages, AK, BKC>;
+}
+
+// Kernel table indexed [tile][A K-contiguous][B K-contiguous][vec].  Direct
+// tiles have only the vec entry; staged tiles have both.
 template <int T>
-constexpr void fill_tile(KernelFn (&t)[2][2][2]) {
-    t[0][0][0] = pick<T, false, false, false>();
-    t[0][0][1] = pick<T, false, false, true>();
-    t[0][1][0] = pick<T, false, true, false>();
-    t[0][1][1] = pick<T, false, true, true>();
-    t[1][0][0] = pick<T, true, false, false>();
-    t[1][0][1] = pick<T, true, false, true>();
-    t[1][1][0] = pick<T, true, true, false>();
-    t[1][1][1] = pick<T, true, true, true>();
+void fill_tile(KernelFn (&t)[2][2][2]) {
+    if constexpr (kTiles[T].kind == KIND_DIRECT) {
+        t[0][0][1] = pick_direct<T, false, false>();
+        t[0][1][1] = pick_direct<T, false, true>();
+        t[1][0][1] = pick_direct<T, true, false>();
+        t[1][1][1] = pick_direct<T, true, true>();
+        t[0][0][0] = t[0][1][0] = t[1][0][0] = t[1][1][0] = nullptr;
+    } else {
+        t[0][0][0] = pick_staged<T, false, false, false>();
+        t[0][0][1] = pick_staged<T, false, false, true>();
+        t[0][1][0] = pick_staged<T, false, true, false>();
+        t[0][1][1] = pick_staged<T, false, true, true>();
+        t[1][0][0] = pick_staged<T, true, false, false>();
+        t[1][0][1] = pick_staged<T, true, false, true>();
+        t[1][1][0] = pick_staged<T, true, true, false>();
+        t[1][1][1] = pick_staged<T, true, true, true>();
+    }
 }
 
 struct KernelTable {
@@ -409,6 +673,7 @@ struct KernelTable {
         fill_tile<TILE_128x128>(k[TILE_128x128]);
         fill_tile<TILE_64x64>(k[TILE_64x64]);
         fill_tile<TILE_32x64>(k[TILE_32x64]);
+        fill_tile<TILE_128x128_STAGED>(k[TILE_128x128_STAGED]);
     }
 };
 
@@ -441,6 +706,10 @@ extern "C" int gemm_f16f32_run(gemm_f16f32_plan_t plan, const void *A,
     const int64_t celem = p.out_type == GEMM_OUT_F32 ? 4 : 2;
     const bool c_vec = (p.ldc % 4 == 0) && (p.stride_c % 4 == 0) &&
                        ((uintptr_t)C % (4 * celem) == 0);
+    const int tile = vec ? p.tile : narrow_tile(p.tile);
+    const TileShape &ts = kTiles[tile];
+    const int64_t tiles_m = (p.M + ts.bm - 1) / ts.bm;
+    const int64_t tiles_n = (p.N + ts.bn - 1) / ts.bn;
 
     GemmArgs a;
     a.A = (const _Float16 *)A;
@@ -457,17 +726,17 @@ extern "C" int gemm_f16f32_run(gemm_f16f32_plan_t plan, const void *A,
                                               : (p.N - 1) * p.ldb + p.K;
     a.alpha = alpha;
     a.beta = beta;
-    a.tiles_m = (int)p.tiles_m;
-    a.tiles_n = (int)p.tiles_n;
+    a.tiles_m = (int)tiles_m;
+    a.tiles_n = (int)tiles_n;
     a.group_m = p.group_m;
-    a.total_tiles = (int)(p.tiles_m * p.tiles_n * p.batch);
+    a.total_tiles = (int)(tiles_m * tiles_n * p.batch);
     a.out_f32 = p.out_type == GEMM_OUT_F32;
     a.c_vec = c_vec;
 
-    const TileShape &ts = kTiles[p.tile];
     const int ak = p.layout_a == GEMM_ROW_MAJOR;   // A K-contiguous
     const int bkc = p.layout_b == GEMM_COL_MAJOR;  // B K-contiguous
-    KernelFn fn = kernels().k[p.tile][ak][bkc][vec ? 1 : 0];
+    KernelFn fn = kernels().k[tile][ak][bkc][vec ? 1 : 0];
+    if (!fn) return GEMM_ERR_UNSUPPORTED;
     void *args[] = {&a};
     hipError_t e = hipLaunchKernel((const void *)fn, dim3((unsigned)a.total_tiles),
                                    dim3(64 * ts.wgm * ts.wgn), args, 0,

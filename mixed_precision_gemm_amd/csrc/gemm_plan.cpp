@@ -107,21 +107,21 @@ extern "C" int gemm_f16f32_plan(gemm_f16f32_plan_t *out, int64_t M, int64_t N,
     p->vec_ok = (contig_a % 8 == 0) && (lda % 8 == 0) && (stride_a % 8 == 0) &&
                 (contig_b % 8 == 0) && (ldb % 8 == 0) && (stride_b % 8 == 0);
     p->tile = choose_tile(M, N, batch);
-    // The narrow-load path stages eight 16-bit loads per vector; at the
-    // 256 x 256 tile that exceeds the register budget, so it stops at 128.
-    if (!p->vec_ok && p->tile == TILE_256x256) p->tile = TILE_128x128;
-    const TileShape &ts = kTiles[p->tile];
-    p->tiles_m = ceil_div(M, ts.bm);
-    p->tiles_n = ceil_div(N, ts.bn);
-    if (p->tiles_m * p->tiles_n * batch > 0x7fffffff) {
-        delete p;
-        return GEMM_ERR_UNSUPPORTED;
+    // Unaligned shapes go to the staged kernel, whose largest tile is 128.
+    const int t = p->vec_ok ? p->tile : narrow_tile(p->tile);
+    for (int cand : {p->tile, narrow_tile(p->tile)}) {
+        const TileShape &c = kTiles[cand];
+        if (ceil_div(M, c.bm) * ceil_div(N, c.bn) * batch > 0x7fffffff) {
+            delete p;
+            return GEMM_ERR_UNSUPPORTED;
+        }
     }
     p->group_m = 8;
     snprintf(p->kernel_name, sizeof p->kernel_name, "gemm_%s_%c%c_%s",
-             ts.name, layout_a == GEMM_ROW_MAJOR ? 'n' : 't',
+             kTiles[t].name, layout_a == GEMM_ROW_MAJOR ? 'n' : 't',
              layout_b == GEMM_ROW_MAJOR ? 'n' : 't',
-             p->vec_ok ? "vec16" : "narrow");
+             p->vec_ok ? (kTiles[t].kind == KIND_DIRECT ? "direct" : "vec16")
+                       : "narrow");
     *out = p;
     return GEMM_OK;
 }

@@ -101,7 +101,7 @@ def test_kernel_choice_by_regime():
         p.close()
         return name
     assert kern(8192, 8192, 8192).startswith("gemm_256x256")
-    assert kern(8192, 8192, 8192, layout_b=GEMM_COL_MAJOR).endswith("nt_vec16")
+    assert kern(8192, 8192, 8192, layout_b=GEMM_COL_MAJOR).endswith("nt_direct")
     assert kern(16, 4096, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_32x64")
     assert "narrow" in kern(127, 257, 33)
     assert kern(0, 8, 8) == "none"
