@@ -24,7 +24,9 @@ enum TileId : int {
 //                register staging), for 16-byte-aligned operands;
 //   KIND_STAGED: a two-slot ring filled through registers (global -> VGPR ->
 //                LDS), used for the small tiles and for the narrow-load path.
-enum KernelKind : int { KIND_DIRECT = 0, KIND_STAGED = 1 };
+//   KIND_PINGPONG: the direct ring with 8 waves in two alternating groups
+//                (one computes while the other moves data); 2 x 4 wave grid.
+enum KernelKind : int { KIND_DIRECT = 0, KIND_STAGED = 1, KIND_PINGPONG = 2 };
 
 struct TileShape {
     int bm, bn, bk, wgm, wgn, stages, kind;
@@ -32,8 +34,8 @@ struct TileShape {
 };
 
 constexpr TileShape kTiles[NUM_TILES] = {
-    {256, 256, 32, 2, 2, 4, KIND_DIRECT, "256x256x32s4"},
-    {128, 128, 32, 2, 2, 4, KIND_DIRECT, "128x128x32s4"},
+    {256, 256, 64, 2, 2, 2, KIND_DIRECT, "256x256x64s2"},
+    {128, 128, 64, 2, 2, 2, KIND_DIRECT, "128x128x64s2"},
     {64, 64, 64, 2, 2, 2, KIND_STAGED, "64x64x64"},
     {32, 64, 64, 1, 2, 2, KIND_STAGED, "32x64x64"},
     {128, 128, 64, 2, 2, 2, KIND_STAGED, "128x128x64"},
@@ -42,7 +44,7 @@ constexpr TileShape kTiles[NUM_TILES] = {
 // Tile of the staged kernel that serves operands the direct kernel cannot
 // take (unaligned rows or pointers).
 constexpr int narrow_tile(int t) {
-    return kTiles[t].kind == KIND_DIRECT ? TILE_128x128_STAGED : t;
+    return kTiles[t].kind != KIND_STAGED ? TILE_128x128_STAGED : t;
 }
 
 constexpr int kNumCUs = 256;

@@ -31,6 +31,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gemm_f16f32.h"
 #include "gemm_internal.h"
 
@@ -71,16 +73,20 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t byt
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, kRsrcWord3);
 }
 
-// XOR swizzle of the 16-byte vector index within an LDS row of VPR vectors.
-// For VPR = 8 (BK = 64, rows of 128 B): any 8 consecutive rows read at the same
-// vector column hit 8 distinct 16-byte bank groups of a 128-byte window, and
-// any 16 consecutive rows hit 16 distinct groups of a 256-byte window.
+// XOR swizzle of the 16-byte vector index within an LDS row of VPR vectors,
+// chosen so that the ds_read_b128 fragment reads (32 consecutive rows at one
+// vector column per half-wave) and the row-major stores are free of bank
+// conflicts.  Both forms were checked with the SQ_LDS_BANK_CONFLICT counter on
+// gfx950 against the exact read pattern of the kernels: zero conflict cycles,
+// where an unswizzled layout costs 12 (VPR 4) or 28 (VPR 8) extra cycles per
+// read and other XOR choices for VPR 4 still cost 4.
 template <int VPR>
 __device__ __host__ constexpr int swz(int row) {
+    static_assert(VPR == 4 || VPR == 8, "rows of 64 or 128 bytes");
     if constexpr (VPR == 8) {
         return (row ^ (row >> 3)) & 7;
     } else {
-        return ((row >> 1) ^ (row >> 3)) & (VPR - 1);
+        return (row >> 2) & 3;
     }
 }
 
@@ -411,10 +417,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_staged(GemmArgs p) {
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
+// Chunk XOR of row k of an MN-contiguous tile.  A transpose read touches four
+// consecutive rows (k%4 = 0..3) at the same 32-byte column span per 16 lanes
+// and the same 64-byte span per 32 lanes; XOR values {0, 10, 4, 14} send the
+// four rows to distinct 32-byte windows of every 128 bytes and to distinct
+// 64-byte windows of every 256 bytes (rows are multiples of 256 bytes long),
+// so the read is conflict-free whether the LDS serves 16 or 32 lanes a cycle.
 template <int R>
 __device__ __host__ constexpr int mn_swz(int k) {
     static_assert(R / 8 >= 16, "MN-contiguous rows need at least 16 chunks");
-    return 4 * (k & 3);
+    return (0xE4A0 >> (4 * (k & 3))) & 15;   // k%4 -> 0, 10, 4, 14
 }
 
 // Byte offset of a __shared__ object within the workgroup's LDS allocation.
@@ -492,14 +504,33 @@ struct DirectOperand {
     // Issues this wave's share of one stage.  base: element (r0, k0) of the
     // operand; lds: the operand's region of the ring slot.
     // Stages at or beyond the end of K fail every range check and write zeros.
+    // kin < BK, so the K test is a 32-bit compare with the (uniform) number of
+    // K indices left in this stage, clamped to [0, BK].
     __device__ void issue(const _Float16 *base, int64_t bytes_left, uint32_t lds_addr,
                           int wave, int64_t k0, int64_t K) {
         const sgpr4 rs = make_rsrc_words(base, bytes_left);
+        const int64_t left64 = K - k0;
+        const int left = __builtin_amdgcn_readfirstlane(
+            left64 <= 0 ? 0 : (left64 >= BK ? BK : (int)left64));
 #pragma unroll
         for (int i = 0; i < PER_WAVE; ++i) {
-            const uint32_t o = (ok[i] && k0 + kin[i] < K) ? off[i] : kOutOfRange;
+            const uint32_t o = (ok[i] && kin[i] < left) ? off[i] : kOutOfRange;
             lds_dma16(rs, lds_addr + (uint32_t)((i * NW + wave) * 64 * 16), o);
         }
+    }
+
+    // Split form of issue(): the descriptor and the number of K indices left
+    // in the stage are computed once, then each load is placed by the caller.
+    __device__ sgpr4 stage_rsrc(const _Float16 *base, int64_t bytes_left) const {
+        return make_rsrc_words(base, bytes_left);
+    }
+    __device__ static int stage_left(int64_t k0, int64_t K) {
+        const int64_t left64 = K - k0;
+        return __builtin_amdgcn_readfirstlane(left64 <= 0 ? 0 : (left64 >= BK ? BK : (int)left64));
+    }
+    __device__ void issue_one(int i, sgpr4 rs, uint32_t lds_addr, int wave, int left) const {
+        const uint32_t o = (ok[i] && kin[i] < left) ? off[i] : kOutOfRange;
+        lds_dma16(rs, lds_addr + (uint32_t)((i * NW + wave) * 64 * 16), o);
     }
 
     // MFMA fragment of the 32-row block starting at rb, K sub-step s (16 deep):
@@ -528,7 +559,8 @@ struct DirectOperand {
 };
 
 template <int BM, int BN, int BK, int WGM, int WGN, int S, bool AK, bool BKC>
-__global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs p) {
+__global__ __launch_bounds__(64 * WGM * WGN)
+__attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_direct(GemmArgs p) {
     constexpr int NW = WGM * WGN;
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -538,9 +570,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs p) {
     using OpA = DirectOperand<BM, BK, NW, AK>;
     using OpB = DirectOperand<BN, BK, NW, BKC>;
     constexpr int L = OpA::PER_WAVE + OpB::PER_WAVE;  // loads per lane per stage
-    static_assert(S >= 3, "the ring needs at least three slots");
-    static_assert((S - 2) * L < 64, "vmcnt range");
-    static_assert(NSUB % 2 == 0, "fragment double buffering pairs sub-steps");
+    static_assert(S == 2, "the schedule below is a two-slot ring");
+    static_assert(NSUB >= 2 && NSUB % 2 == 0, "fragment double buffering pairs sub-steps");
+    static_assert(L < 64, "vmcnt range");
 
     __shared__ u32x4 lds[S * SLOT];
 
@@ -573,9 +605,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs p) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     const int64_t nk = (p.K + BK - 1) / BK;
-
     const uint32_t lds_base = lds_offset(lds);
-    // Issues stage st into ring slot st % S (zeros when st >= nk).
+
+    // Issues all of this wave's loads of stage st into ring slot st % 2.
     auto issue = [&](int64_t st) {
         const uint32_t slot = lds_base + (uint32_t)((st % S) * SLOT * 16);
         const int64_t ao = a_tile + st * a_kstep, bo = b_tile + st * b_kstep;
@@ -587,44 +619,231 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs p) {
     auto read_frags = [&](int buf, int64_t st, int s) {
         const u32x4 *slot = lds + (int)(st % S) * SLOT;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) fa[buf][i] = opa.frag(slot, wm * WTM + i * 32, s, lane);
-#pragma unroll
         for (int j = 0; j < FN; ++j) fb[buf][j] = opb.frag(slot + A_CH, wn * WTN + j * 32, s, lane);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[buf][i] = opa.frag(slot, wm * WTM + i * 32, s, lane);
     };
 
-    // Every iteration issues exactly L loads per lane (stages past the end are
-    // range-check failures), so the wait counts below are exact.
+    // One sub-step: the FM*FN MFMAs on fragment buffer `cur`, with the
+    // fragment reads for the next sub-step (stage rst, sub-step rs, into
+    // buffer `nxt`) and `nl` of this wave's direct-to-LDS loads of stage
+    // `dst` (starting at load index l0) spread evenly between them, in a fixed
+    // order the compiler may not change.  Spacing the 1 KiB loads keeps one
+    // wave from stalling on two of them back to back; B fragments are read
+    // first because the next sub-step's first MFMAs need all of them.
+    constexpr int NQ = FM * FN;
+    constexpr int NF = FM + FN;
+    auto substep = [&](int cur, int nxt, int64_t rst, int rs, int64_t dst, auto l0c, auto nlc) {
+        constexpr int l0 = decltype(l0c)::value, nl = decltype(nlc)::value;
+        const u32x4 *rslot = lds + (int)(rst % S) * SLOT;
+        const uint32_t dslot = lds_base + (uint32_t)((dst % S) * SLOT * 16);
+        const int64_t ao = a_tile + dst * a_kstep, bo = b_tile + dst * b_kstep;
+        sgpr4 rsa = {}, rsb = {};
+        int left = 0;
+        if constexpr (nl > 0) {
+            rsa = opa.stage_rsrc(Ab + ao, (p.extent_a - ao) * 2);
+            rsb = opb.stage_rsrc(Bb + bo, (p.extent_b - bo) * 2);
+            left = OpA::stage_left(dst * BK, p.K);
+        }
 #pragma unroll
-    for (int st = 0; st < S - 1; ++st) issue(st);
-    wait_vmcnt<(S - 2) * L>();          // stage 0 resident for this lane
+        for (int q = 0; q < NQ; ++q) {
+            const int i = q / FN, j = q % FN;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
+#pragma unroll
+            for (int l = l0 + q * nl / NQ; l < l0 + (q + 1) * nl / NQ; ++l) {
+                if (l < OpA::PER_WAVE) opa.issue_one(l, rsa, dslot, wave, left);
+                else opb.issue_one(l - OpA::PER_WAVE, rsb, dslot + A_CH * 16, wave, left);
+            }
+#pragma unroll
+            for (int f = q * NF / NQ; f < (q + 1) * NF / NQ; ++f) {
+                if (f < FN) fb[nxt][f] = opb.frag(rslot + A_CH, wn * WTN + f * 32, rs, lane);
+                else fa[nxt][f - FN] = opa.frag(rslot, wm * WTM + (f - FN) * 32, rs, lane);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // Stage kt lives in slot kt % 2.  One barrier per stage, placed before the
+    // last sub-step of stage kt: there every wave has (a) waited for its own
+    // loads of stage kt+1 and (b) drained its LDS reads of stage kt (all of
+    // them were issued during the earlier sub-steps), so after the barrier
+    // stage kt+1 is readable and slot kt % 2 is free: its refill with stage
+    // kt+2 is issued during the last sub-step of stage kt and the first of
+    // stage kt+1, a full stage ahead of the next barrier.  Every stage issues
+    // exactly L loads per lane (stages past the end of K fail the range check
+    // and write zeros), so the wait counts are exact.
+    constexpr int LH = L / 2;
+    using C0 = std::integral_constant<int, 0>;
+    using CLH = std::integral_constant<int, LH>;
+    using CRest = std::integral_constant<int, L - LH>;
+    // Prologue: stage 0 whole, first half of stage 1 (the loop issues the
+    // rest of stage kt+1 in its first sub-step).
+    issue(0);
+    {
+        const uint32_t dslot = lds_base + (uint32_t)(SLOT * 16);
+        const int64_t ao = a_tile + a_kstep, bo = b_tile + b_kstep;
+        const sgpr4 rsa = opa.stage_rsrc(Ab + ao, (p.extent_a - ao) * 2);
+        const sgpr4 rsb = opb.stage_rsrc(Bb + bo, (p.extent_b - bo) * 2);
+        const int left = OpA::stage_left(BK, p.K);
+#pragma unroll
+        for (int l = 0; l < LH; ++l) {
+            if (l < OpA::PER_WAVE) opa.issue_one(l, rsa, dslot, wave, left);
+            else opb.issue_one(l - OpA::PER_WAVE, rsb, dslot + A_CH * 16, wave, left);
+        }
+    }
+    wait_vmcnt<LH>();                   // stage 0 resident for this lane
     barrier();                          // ... and for every lane
     read_frags(0, 0, 0);
 
     for (int64_t kt = 0; kt < nk; ++kt) {
+        substep(0, 1, kt, 1, kt + 1, CLH{}, CRest{});   // rest of stage kt+1
 #pragma unroll
-        for (int sub = 0; sub < NSUB; ++sub) {
-            const int cur = sub & 1, nxt = cur ^ 1;
-            if (sub + 1 < NSUB) {
-                read_frags(nxt, kt, sub + 1);
-            } else {
-                // Stage kt+1 resident for every lane; the barrier also certifies
-                // that all waves have finished reading slot (kt-1)%S, refilled
-                // next with stage kt+S-1.  (After the last stage the fragment
-                // reads below fetch a slot that is never used.)
-                wait_vmcnt<(S - 3) * L>();
-                barrier();
-                issue(kt + S - 1);
-                read_frags(nxt, kt + 1, 0);
-            }
+        for (int sub = 1; sub < NSUB - 1; ++sub)
+            substep(sub & 1, (sub & 1) ^ 1, kt, sub + 1, kt + 1, C0{}, C0{});
+        wait_vmcnt<0>();                // this lane's loads of stage kt+1
+        asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");   // reads of stage kt done
+        barrier();
+        substep((NSUB - 1) & 1, NSUB & 1, kt + 1, 0, kt + 2, C0{}, CLH{});
+    }
+    // No direct-to-LDS write may still be in flight when the workgroup's LDS
+    // is released.
+    wait_vmcnt<0>();
+
+    store_tile<FM, FN, WTM, WTN>(p, acc, b, m0, n0, wm, wn, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Ping-pong kernel: 8 waves, two per SIMD, in two groups of four that take
+// turns.  Phase p: the group p % 2 issues nothing but the MFMAs of one K stage
+// from fragments already in registers, while the other group reads its
+// fragments for its next stage from LDS and issues its share of the
+// direct-to-LDS loads three stages ahead.  One barrier ends every phase, so a
+// SIMD always has one wave feeding its matrix core while the other does the
+// data movement ([GEMM] §4.1 and §5: overlap copy with compute; here the
+// overlap is between the two waves of a SIMD instead of within one).
+//
+// Schedule (stage s = one BK slice, ring slot s % S, S = 4):
+//   group 0: phase 2s   compute(s); wait own loads of s+1; barrier
+//            phase 2s+1 read(s+1); issue loads of s+3; barrier
+//   group 1: phase 2s   read(s); issue loads of s+3; wait own loads of s+1; barrier
+//            phase 2s+1 compute(s); barrier
+// Stage t is first read in phase 2t-1, after the barrier that follows both
+// groups' waits for it; slot (s+3) % 4 held stage s-1, last read in phase
+// 2s-2, before either group refills it.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int BK, int S, bool AK, bool BKC>
+__global__ __launch_bounds__(512)
+__attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_pingpong(GemmArgs p) {
+    constexpr int NW = 8;
+    constexpr int WTM = BM / 2, WTN = BN / 4;          // wave tile
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int NSUB = BK / 16;
+    constexpr int A_CH = BM * BK / 8, B_CH = BN * BK / 8;
+    constexpr int SLOT = A_CH + B_CH;
+    using OpA = DirectOperand<BM, BK, NW, AK>;
+    using OpB = DirectOperand<BN, BK, NW, BKC>;
+    constexpr int L = OpA::PER_WAVE + OpB::PER_WAVE;   // loads per lane per stage
+    static_assert(S == 4, "the schedule above is written for a four-slot ring");
+    static_assert(2 * L < 64, "vmcnt range");
+
+    __shared__ u32x4 lds[S * SLOT];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int group = wave >> 2;                        // waves w and w+4 share a SIMD
+    const int wm = wave >> 2, wn = wave & 3;
+
+    int b, tm, tn;
+    tile_coords(p, blockIdx.x, b, tm, tn);
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    const _Float16 *Ab = p.A + b * p.sa;
+    const _Float16 *Bb = p.B + b * p.sb;
+    const int64_t a_tile = AK ? m0 * p.lda : m0;
+    const int64_t a_kstep = AK ? BK : BK * p.lda;
+    const int64_t b_tile = BKC ? n0 * p.ldb : n0;
+    const int64_t b_kstep = BKC ? BK : BK * p.ldb;
+
+    OpA opa;
+    OpB opb;
+    opa.init(wave, lane, m0, p.M, p.lda);
+    opb.init(wave, lane, n0, p.N, p.ldb);
+
+    floatx16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int64_t nk = (p.K + BK - 1) / BK;
+    const uint32_t lds_base = lds_offset(lds);
+
+    auto issue = [&](int64_t st) {
+        const uint32_t slot = lds_base + (uint32_t)((st % S) * SLOT * 16);
+        const int64_t ao = a_tile + st * a_kstep, bo = b_tile + st * b_kstep;
+        opa.issue(Ab + ao, (p.extent_a - ao) * 2, slot, wave, st * BK, p.K);
+        opb.issue(Bb + bo, (p.extent_b - bo) * 2, slot + A_CH * 16, wave, st * BK, p.K);
+    };
+
+    half8 fa[NSUB][FM], fb[NSUB][FN];
+    auto read_stage = [&](int64_t st) {
+        const u32x4 *slot = lds + (int)(st % S) * SLOT;
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) fa[s][i] = opa.frag(slot, wm * WTM + i * 32, s, lane);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) fb[s][j] = opb.frag(slot + A_CH, wn * WTN + j * 32, s, lane);
+        }
+    };
+    auto compute = [&]() {
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s)
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[s][j], fa[s][i], acc[i][j], 0, 0, 0);
+    };
+    // Phase boundary: no instruction may be moved across it by the compiler.
+    auto phase_end = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Prologue: stages 0..2 in flight (each wave issues exactly L loads per
+    // stage; stages past the end of K are range-check failures).
+    issue(0);
+    issue(1);
+    issue(2);
+    wait_vmcnt<2 * L>();                 // stage 0 landed for this lane
+    phase_end();                         // ... and for every lane
+    if (group == 0) read_stage(0);
+    phase_end();
+
+    if (group == 0) {
+        for (int64_t s = 0; s < nk; ++s) {
+            compute();                                   // phase 2s
+            wait_vmcnt<L>();                             // own loads of stage s+1
+            phase_end();
+            read_stage(s + 1);                           // phase 2s+1
+            issue(s + 3);
+            phase_end();
+        }
+    } else {
+        for (int64_t s = 0; s < nk; ++s) {
+            read_stage(s);                               // phase 2s
+            issue(s + 3);
+            wait_vmcnt<2 * L>();                         // own loads of stage s+1
+            phase_end();
+            compute();                                   // phase 2s+1
+            phase_end();
         }
     }
-    // No direct-to-LDS write may still be in flight when the workgroup's LDS
-    // is released.
+    // No direct-to-LDS write may still be in flight when the LDS is released.
     wait_vmcnt<0>();
 
     store_tile<FM, FN, WTM, WTN>(p, acc, b, m0, n0, wm, wn, lane);
@@ -644,11 +863,22 @@ constexpr KernelFn pick_direct() {
                        kTiles[T].wgn, kTiles[T].stages, AK, BKC>;
 }
 
+template <int T, bool AK, bool BKC>
+constexpr KernelFn pick_pingpong() {
+    return gemm_pingpong<kTiles[T].bm, kTiles[T].bn, kTiles[T].bk, kTiles[T].stages, AK, BKC>;
+}
+
 // Kernel table indexed [tile][A K-contiguous][B K-contiguous][vec].  Direct
 // tiles have only the vec entry; staged tiles have both.
 template <int T>
 void fill_tile(KernelFn (&t)[2][2][2]) {
-    if constexpr (kTiles[T].kind == KIND_DIRECT) {
+    if constexpr (kTiles[T].kind == KIND_PINGPONG) {
+        t[0][0][1] = pick_pingpong<T, false, false>();
+        t[0][1][1] = pick_pingpong<T, false, true>();
+        t[1][0][1] = pick_pingpong<T, true, false>();
+        t[1][1][1] = pick_pingpong<T, true, true>();
+        t[0][0][0] = t[0][1][0] = t[1][0][0] = t[1][1][0] = nullptr;
+    } else if constexpr (kTiles[T].kind == KIND_DIRECT) {
         t[0][0][1] = pick_direct<T, false, false>();
         t[0][1][1] = pick_direct<T, false, true>();
         t[1][0][1] = pick_direct<T, true, false>();

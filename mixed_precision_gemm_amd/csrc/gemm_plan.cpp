@@ -116,11 +116,11 @@ extern "C" int gemm_f16f32_plan(gemm_f16f32_plan_t *out, int64_t M, int64_t N,
             return GEMM_ERR_UNSUPPORTED;
         }
     }
-    p->group_m = 8;
+    p->group_m = 4;
     snprintf(p->kernel_name, sizeof p->kernel_name, "gemm_%s_%c%c_%s",
              kTiles[t].name, layout_a == GEMM_ROW_MAJOR ? 'n' : 't',
              layout_b == GEMM_ROW_MAJOR ? 'n' : 't',
-             p->vec_ok ? (kTiles[t].kind == KIND_DIRECT ? "direct" : "vec16")
+             p->vec_ok ? (kTiles[t].kind == KIND_STAGED ? "vec16" : "direct")
                        : "narrow");
     *out = p;
     return GEMM_OK;
