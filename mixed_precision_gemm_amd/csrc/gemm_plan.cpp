@@ -30,16 +30,24 @@ int64_t operand_extent(int64_t rows, int64_t cols, int64_t ld, int64_t batch,
 
 // Tile choice.  [GEMM] §1.3 rules out autotuning and run-time selection among
 // many kernels; the choice here is a fixed rule on the shape.  [OPS] §4.3
-// asks that the grid fill the device, so the largest tile that still gives at
-// least one workgroup per compute unit is taken; skinny M (token counts of a
-// linear layer) takes the 32-row tile.
+// asks that the grid fill the device.  A tile is taken only if the padding it
+// adds wastes little work (fill = useful outputs / computed outputs) and it
+// yields enough workgroups: the 256 x 256 tile needs a full wave of 256 CUs,
+// the 128 x 128 tile (two workgroups per CU) a quarter of one; otherwise the
+// small staged tiles, the 32-row one for skinny M (token counts of a linear
+// layer).
 int choose_tile(int64_t M, int64_t N, int64_t batch) {
-    if (M <= 32) return TILE_32x64;
     auto count = [&](int t) {
         return ceil_div(M, kTiles[t].bm) * ceil_div(N, kTiles[t].bn) * batch;
     };
-    if (count(TILE_256x256) >= kNumCUs) return TILE_256x256;
-    if (count(TILE_128x128) >= kNumCUs / 2) return TILE_128x128;
+    auto fill = [&](int t) {
+        const double pm = (double)ceil_div(M, kTiles[t].bm) * kTiles[t].bm;
+        const double pn = (double)ceil_div(N, kTiles[t].bn) * kTiles[t].bn;
+        return (double)M * (double)N / (pm * pn);
+    };
+    if (count(TILE_256x256) >= kNumCUs && fill(TILE_256x256) >= 0.8) return TILE_256x256;
+    if (count(TILE_128x128) >= kNumCUs / 4 && fill(TILE_128x128) >= 0.6) return TILE_128x128;
+    if (M <= 32) return TILE_32x64;
     return TILE_64x64;
 }
 
