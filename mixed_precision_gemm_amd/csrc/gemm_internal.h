@@ -16,7 +16,10 @@ enum TileId : int {
     TILE_64x64 = 2,          // small and batched-small products
     TILE_32x64 = 3,          // skinny M (tokens) problems
     TILE_128x128_STAGED = 4, // narrow-load fallback of the two direct tiles
-    NUM_TILES = 5
+    TILE_STREAM16 = 5,       // skinny M <= 16, K-contiguous A and B
+    TILE_STREAM32 = 6,       // skinny M <= 32
+    TILE_STREAM64 = 7,       // skinny M <= 64
+    NUM_TILES = 8
 };
 
 // Two kernel families share the tile table:
@@ -26,7 +29,9 @@ enum TileId : int {
 //                LDS), used for the small tiles and for the narrow-load path.
 //   KIND_PINGPONG: the direct ring with 8 waves in two alternating groups
 //                (one computes while the other moves data); 2 x 4 wave grid.
-enum KernelKind : int { KIND_DIRECT = 0, KIND_STAGED = 1, KIND_PINGPONG = 2 };
+//   KIND_STREAM:  skinny M with K-contiguous A and B: fragments loaded from
+//                global memory straight into registers, K split over 8 waves.
+enum KernelKind : int { KIND_DIRECT = 0, KIND_STAGED = 1, KIND_PINGPONG = 2, KIND_STREAM = 3 };
 
 struct TileShape {
     int bm, bn, bk, wgm, wgn, stages, kind;
@@ -39,12 +44,16 @@ constexpr TileShape kTiles[NUM_TILES] = {
     {64, 64, 64, 2, 2, 2, KIND_STAGED, "64x64x64"},
     {32, 64, 64, 1, 2, 2, KIND_STAGED, "32x64x64"},
     {128, 128, 64, 2, 2, 2, KIND_STAGED, "128x128x64"},
+    {16, 16, 32, 1, 1, 1, KIND_STREAM, "stream16x16"},
+    {32, 16, 32, 1, 1, 1, KIND_STREAM, "stream32x16"},
+    {64, 16, 32, 1, 1, 1, KIND_STREAM, "stream64x16"},
 };
 
 // Tile of the staged kernel that serves operands the direct kernel cannot
 // take (unaligned rows or pointers).
 constexpr int narrow_tile(int t) {
-    return kTiles[t].kind != KIND_STAGED ? TILE_128x128_STAGED : t;
+    return kTiles[t].kind == KIND_STREAM ? (kTiles[t].bm <= 32 ? TILE_32x64 : TILE_64x64)
+           : kTiles[t].kind != KIND_STAGED ? TILE_128x128_STAGED : t;
 }
 
 constexpr int kNumCUs = 256;

@@ -849,6 +849,115 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_pingpong(GemmArgs p) {
     store_tile<FM, FN, WTM, WTN>(p, acc, b, m0, n0, wm, wn, lane);
 }
 
+// ---------------------------------------------------------------------------
+// Streaming kernel for skinny problems (M <= 64) whose A and B are both
+// K-contiguous (row-major A, column-major B: the linear-layer layout, with W
+// stored N x K).  Such a GEMM is bound by reading B once from HBM
+// ([OPS] §1.2 and [GEMM] §2.4: classify by arithmetic intensity first), so
+// the kernel is built to keep many bytes in flight rather than to reuse tiles:
+//   * a workgroup owns 16 columns of C (all M rows, MB blocks of 16) and
+//     splits K over its 8 waves, so even N = 4096 yields 256 workgroups;
+//   * MFMA fragments of v_mfma_f32_16x16x32_f16 are loaded straight from
+//     global memory (lane l holds 8 consecutive k of row/column l % 16 --
+//     16 contiguous bytes of a K-contiguous operand), UNROLL K steps at a
+//     time, with the range check zero-filling rows >= M, columns >= N and
+//     k >= K;
+//   * the 8 partial tiles are summed through LDS and the alpha/beta epilogue
+//     is applied once per output.
+// ---------------------------------------------------------------------------
+typedef float floatx4v __attribute__((ext_vector_type(4)));
+
+template <int MB>
+__global__ __launch_bounds__(512) void gemm_stream(GemmArgs p) {
+    constexpr int NW = 8;
+    constexpr int UNROLL = MB <= 2 ? 8 : 4;
+    __shared__ float red[NW][MB * 16][16];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    int b, tm, tn;
+    tile_coords(p, blockIdx.x, b, tm, tn);
+    const int64_t m0 = (int64_t)tm * (MB * 16), n0 = (int64_t)tn * 16;
+    const _Float16 *Ab = p.A + b * p.sa;
+    const _Float16 *Bb = p.B + b * p.sb;
+
+    // K range of this wave, in steps of 32.
+    const int64_t steps = (p.K + 31) / 32;
+    const int64_t s_lo = steps * wave / NW, s_hi = steps * (wave + 1) / NW;
+
+    const int r16 = lane & 15;            // row of A / column of B this lane loads
+    const int kq = 8 * (lane >> 4);       // first of its 8 consecutive k
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab, p.extent_a * 2);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb, p.extent_b * 2);
+    bool a_ok[MB];
+    uint32_t a_off[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int64_t m = m0 + mb * 16 + r16;
+        a_ok[mb] = m < p.M;
+        a_off[mb] = (uint32_t)((m * p.lda + kq) * 2);
+    }
+    const int64_t n = n0 + r16;
+    const bool b_ok = n < p.N;
+    const uint32_t b_off = (uint32_t)((n * p.ldb + kq) * 2);
+
+    floatx4v acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = floatx4v{0.f, 0.f, 0.f, 0.f};
+
+    for (int64_t s0 = s_lo; s0 < s_hi; s0 += UNROLL) {
+        half8 fa[UNROLL][MB], fb[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int64_t k = (s0 + u) * 32 + kq;
+            const bool kin = (s0 + u < s_hi) && (k < p.K);
+            const uint32_t kb = (uint32_t)((s0 + u) * 64);
+            fb[u] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(
+                rb, (b_ok && kin) ? b_off + kb : kOutOfRange, 0, 0));
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                fa[u][mb] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(
+                    ra, (a_ok[mb] && kin) ? a_off[mb] + kb : kOutOfRange, 0, 0));
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[u][mb], fb[u], acc[mb], 0, 0, 0);
+    }
+
+    // Accumulator register r of lane l holds row 4*(l/16) + r, column l % 16
+    // of each 16 x 16 block.
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave][mb * 16 + 4 * (lane >> 4) + r][r16] = acc[mb][r];
+    __syncthreads();
+
+    const float alpha = p.alpha, beta = p.beta;
+    for (int o = tid; o < MB * 16 * 16; o += NW * 64) {
+        const int i = o >> 4, j = o & 15;
+        const int64_t m = m0 + i, nn = n0 + j;
+        if (m >= p.M || nn >= p.N) continue;
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) v += red[w][i][j];
+        v *= alpha;
+        const int64_t off = b * p.sc + m * p.ldc + nn;
+        if (p.out_f32) {
+            float *C = (float *)p.C + off;
+            if (beta != 0.0f) v += beta * *C;
+            *C = v;
+        } else {
+            _Float16 *C = (_Float16 *)p.C + off;
+            if (beta != 0.0f) v += beta * (float)*C;
+            *C = (_Float16)v;
+        }
+    }
+}
+
 typedef void (*KernelFn)(GemmArgs);
 
 template <int T, bool AK, bool BKC, bool VEC>
@@ -896,6 +1005,14 @@ void fill_tile(KernelFn (&t)[2][2][2]) {
     }
 }
 
+template <int T>
+void fill_stream(KernelFn (&t)[2][2][2]) {
+    // Only the K-contiguous A and B (row-major A, column-major B) 128-bit form.
+    t[0][0][0] = t[0][0][1] = t[0][1][0] = t[0][1][1] = nullptr;
+    t[1][0][0] = t[1][0][1] = t[1][1][0] = nullptr;
+    t[1][1][1] = gemm_stream<kTiles[T].bm / 16>;
+}
+
 struct KernelTable {
     KernelFn k[NUM_TILES][2][2][2];
     KernelTable() {
@@ -904,6 +1021,9 @@ struct KernelTable {
         fill_tile<TILE_64x64>(k[TILE_64x64]);
         fill_tile<TILE_32x64>(k[TILE_32x64]);
         fill_tile<TILE_128x128_STAGED>(k[TILE_128x128_STAGED]);
+        fill_stream<TILE_STREAM16>(k[TILE_STREAM16]);
+        fill_stream<TILE_STREAM32>(k[TILE_STREAM32]);
+        fill_stream<TILE_STREAM64>(k[TILE_STREAM64]);
     }
 };
 
@@ -968,8 +1088,9 @@ extern "C" int gemm_f16f32_run(gemm_f16f32_plan_t plan, const void *A,
     KernelFn fn = kernels().k[tile][ak][bkc][vec ? 1 : 0];
     if (!fn) return GEMM_ERR_UNSUPPORTED;
     void *args[] = {&a};
+    const unsigned threads = ts.kind == KIND_STREAM ? 512u : (unsigned)(64 * ts.wgm * ts.wgn);
     hipError_t e = hipLaunchKernel((const void *)fn, dim3((unsigned)a.total_tiles),
-                                   dim3(64 * ts.wgm * ts.wgn), args, 0,
+                                   dim3(threads), args, 0,
                                    (hipStream_t)stream);
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }

@@ -36,7 +36,10 @@ int64_t operand_extent(int64_t rows, int64_t cols, int64_t ld, int64_t batch,
 // the 128 x 128 tile (two workgroups per CU) a quarter of one; otherwise the
 // small staged tiles, the 32-row one for skinny M (token counts of a linear
 // layer).
-int choose_tile(int64_t M, int64_t N, int64_t batch) {
+int choose_tile(int64_t M, int64_t N, int64_t batch, bool kc_both) {
+    // Skinny M with K-contiguous A and B streams B through registers; at
+    // most 64 rows of A are reused per loaded column of B.
+    if (kc_both && M <= 64) return M <= 16 ? TILE_STREAM16 : M <= 32 ? TILE_STREAM32 : TILE_STREAM64;
     auto count = [&](int t) {
         return ceil_div(M, kTiles[t].bm) * ceil_div(N, kTiles[t].bn) * batch;
     };
@@ -114,7 +117,8 @@ extern "C" int gemm_f16f32_plan(gemm_f16f32_plan_t *out, int64_t M, int64_t N,
     const int64_t contig_b = layout_b == GEMM_ROW_MAJOR ? N : K;
     p->vec_ok = (contig_a % 8 == 0) && (lda % 8 == 0) && (stride_a % 8 == 0) &&
                 (contig_b % 8 == 0) && (ldb % 8 == 0) && (stride_b % 8 == 0);
-    p->tile = choose_tile(M, N, batch);
+    const bool kc_both = layout_a == GEMM_ROW_MAJOR && layout_b == GEMM_COL_MAJOR;
+    p->tile = choose_tile(M, N, batch, kc_both);
     // Unaligned shapes go to the staged kernel, whose largest tile is 128.
     const int t = p->vec_ok ? p->tile : narrow_tile(p->tile);
     for (int cand : {p->tile, narrow_tile(p->tile)}) {
