@@ -102,7 +102,14 @@ def test_kernel_choice_by_regime():
         return name
     assert kern(8192, 8192, 8192).startswith("gemm_256x256")
     assert kern(8192, 8192, 8192, layout_b=GEMM_COL_MAJOR).endswith("nt_direct")
-    assert kern(16, 4096, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_32x64")
+    # skinny, K-contiguous A and B: streaming kernel; other layouts: small tiles
+    assert kern(16, 4096, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_stream16x16")
+    assert kern(40, 4096, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_stream64x16")
+    assert kern(16, 4096, 4096).startswith("gemm_32x64")
+    # batched small products are not put on tiles far larger than themselves
+    assert mpg.Plan(64, 64, 64, batch=512, stride_a=4096, stride_b=4096,
+                    stride_c=4096).kernel.startswith("gemm_64x64")
+    assert kern(1024, 1024, 1024).startswith("gemm_128x128")
     assert "narrow" in kern(127, 257, 33)
     assert kern(0, 8, 8) == "none"
 
