@@ -27,11 +27,9 @@ enum TileId : int {
 //                register staging), for 16-byte-aligned operands;
 //   KIND_STAGED: a two-slot ring filled through registers (global -> VGPR ->
 //                LDS), used for the small tiles and for the narrow-load path.
-//   KIND_PINGPONG: the direct ring with 8 waves in two alternating groups
-//                (one computes while the other moves data); 2 x 4 wave grid.
 //   KIND_STREAM:  skinny M with K-contiguous A and B: fragments loaded from
 //                global memory straight into registers, K split over 8 waves.
-enum KernelKind : int { KIND_DIRECT = 0, KIND_STAGED = 1, KIND_PINGPONG = 2, KIND_STREAM = 3 };
+enum KernelKind : int { KIND_DIRECT = 0, KIND_STAGED = 1, KIND_STREAM = 2 };
 
 struct TileShape {
     int bm, bn, bk, wgm, wgn, stages, kind;

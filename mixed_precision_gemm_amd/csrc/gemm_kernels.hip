@@ -479,58 +479,59 @@ struct DirectOperand {
     static constexpr int PER_WAVE = INSTR / NW;
     static_assert(CHUNKS % 64 == 0 && INSTR % NW == 0, "stage must split evenly over waves");
 
-    uint32_t off[PER_WAVE];
-    int kin[PER_WAVE];
-    bool ok[PER_WAVE];
+    uint32_t off[PER_WAVE];   // byte offset of this lane's chunk, kOutOfRange if past the rows
+    uint32_t kin4[(PER_WAVE + 3) / 4];  // K index (< BK) of each chunk, four per word
 
     __device__ void init(int wave, int lane, int64_t r0, int64_t rtot, int64_t ld) {
 #pragma unroll
+        for (int i = 0; i < (PER_WAVE + 3) / 4; ++i) kin4[i] = 0;
+#pragma unroll
         for (int i = 0; i < PER_WAVE; ++i) {
             const int p = (i * NW + wave) * 64 + lane;
+            bool ok;
+            int kin;
             if constexpr (KC) {
                 const int r = p / VPR, c = (p % VPR) ^ swz<VPR>(r);
                 off[i] = (uint32_t)((r * ld + c * 8) * 2);
-                kin[i] = c * 8;
-                ok[i] = r0 + r < rtot;
+                kin = c * 8;
+                ok = r0 + r < rtot;
             } else {
                 const int k = p / CPR, c = (p % CPR) ^ mn_swz<R>(k);
                 off[i] = (uint32_t)((k * ld + c * 8) * 2);
-                kin[i] = k;
-                ok[i] = r0 + c * 8 < rtot;
+                kin = k;
+                ok = r0 + c * 8 < rtot;
             }
+            if (!ok) off[i] = kOutOfRange;
+            kin4[i / 4] |= (uint32_t)kin << (8 * (i % 4));
         }
     }
 
-    // Issues this wave's share of one stage.  base: element (r0, k0) of the
-    // operand; lds: the operand's region of the ring slot.
-    // Stages at or beyond the end of K fail every range check and write zeros.
-    // kin < BK, so the K test is a 32-bit compare with the (uniform) number of
-    // K indices left in this stage, clamped to [0, BK].
-    __device__ void issue(const _Float16 *base, int64_t bytes_left, uint32_t lds_addr,
-                          int wave, int64_t k0, int64_t K) {
-        const sgpr4 rs = make_rsrc_words(base, bytes_left);
-        const int64_t left64 = K - k0;
-        const int left = __builtin_amdgcn_readfirstlane(
-            left64 <= 0 ? 0 : (left64 >= BK ? BK : (int)left64));
-#pragma unroll
-        for (int i = 0; i < PER_WAVE; ++i) {
-            const uint32_t o = (ok[i] && kin[i] < left) ? off[i] : kOutOfRange;
-            lds_dma16(rs, lds_addr + (uint32_t)((i * NW + wave) * 64 * 16), o);
-        }
-    }
-
-    // Split form of issue(): the descriptor and the number of K indices left
-    // in the stage are computed once, then each load is placed by the caller.
-    __device__ sgpr4 stage_rsrc(const _Float16 *base, int64_t bytes_left) const {
-        return make_rsrc_words(base, bytes_left);
-    }
+    // Number of K indices left in the stage that starts at k0, clamped to
+    // [0, BK] (uniform over the wave).
     __device__ static int stage_left(int64_t k0, int64_t K) {
         const int64_t left64 = K - k0;
         return __builtin_amdgcn_readfirstlane(left64 <= 0 ? 0 : (left64 >= BK ? BK : (int)left64));
     }
+    __device__ sgpr4 stage_rsrc(const _Float16 *base, int64_t bytes_left) const {
+        return make_rsrc_words(base, bytes_left);
+    }
+    // Load i of this wave's share of a stage; chunks at K indices >= left
+    // fail the range check and write zeros.
     __device__ void issue_one(int i, sgpr4 rs, uint32_t lds_addr, int wave, int left) const {
-        const uint32_t o = (ok[i] && kin[i] < left) ? off[i] : kOutOfRange;
+        const int kin = (int)((kin4[i / 4] >> (8 * (i % 4))) & 0xffu);
+        const uint32_t o = kin < left ? off[i] : kOutOfRange;
         lds_dma16(rs, lds_addr + (uint32_t)((i * NW + wave) * 64 * 16), o);
+    }
+
+    // Issues this wave's share of one stage.  base: element (r0, k0) of the
+    // operand; lds: the operand's region of the ring slot.  Stages at or
+    // beyond the end of K fail every range check and write zeros.
+    __device__ void issue(const _Float16 *base, int64_t bytes_left, uint32_t lds_addr,
+                          int wave, int64_t k0, int64_t K) {
+        const sgpr4 rs = make_rsrc_words(base, bytes_left);
+        const int left = stage_left(k0, K);
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i) issue_one(i, rs, lds_addr, wave, left);
     }
 
     // MFMA fragment of the 32-row block starting at rb, K sub-step s (16 deep):
@@ -713,143 +714,6 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_direct(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Ping-pong kernel: 8 waves, two per SIMD, in two groups of four that take
-// turns.  Phase p: the group p % 2 issues nothing but the MFMAs of one K stage
-// from fragments already in registers, while the other group reads its
-// fragments for its next stage from LDS and issues its share of the
-// direct-to-LDS loads three stages ahead.  One barrier ends every phase, so a
-// SIMD always has one wave feeding its matrix core while the other does the
-// data movement ([GEMM] §4.1 and §5: overlap copy with compute; here the
-// overlap is between the two waves of a SIMD instead of within one).
-//
-// Schedule (stage s = one BK slice, ring slot s % S, S = 4):
-//   group 0: phase 2s   compute(s); wait own loads of s+1; barrier
-//            phase 2s+1 read(s+1); issue loads of s+3; barrier
-//   group 1: phase 2s   read(s); issue loads of s+3; wait own loads of s+1; barrier
-//            phase 2s+1 compute(s); barrier
-// Stage t is first read in phase 2t-1, after the barrier that follows both
-// groups' waits for it; slot (s+3) % 4 held stage s-1, last read in phase
-// 2s-2, before either group refills it.
-// ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int S, bool AK, bool BKC>
-__global__ __launch_bounds__(512)
-__attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_pingpong(GemmArgs p) {
-    constexpr int NW = 8;
-    constexpr int WTM = BM / 2, WTN = BN / 4;          // wave tile
-    constexpr int FM = WTM / 32, FN = WTN / 32;
-    constexpr int NSUB = BK / 16;
-    constexpr int A_CH = BM * BK / 8, B_CH = BN * BK / 8;
-    constexpr int SLOT = A_CH + B_CH;
-    using OpA = DirectOperand<BM, BK, NW, AK>;
-    using OpB = DirectOperand<BN, BK, NW, BKC>;
-    constexpr int L = OpA::PER_WAVE + OpB::PER_WAVE;   // loads per lane per stage
-    static_assert(S == 4, "the schedule above is written for a four-slot ring");
-    static_assert(2 * L < 64, "vmcnt range");
-
-    __shared__ u32x4 lds[S * SLOT];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int group = wave >> 2;                        // waves w and w+4 share a SIMD
-    const int wm = wave >> 2, wn = wave & 3;
-
-    int b, tm, tn;
-    tile_coords(p, blockIdx.x, b, tm, tn);
-    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-    const _Float16 *Ab = p.A + b * p.sa;
-    const _Float16 *Bb = p.B + b * p.sb;
-    const int64_t a_tile = AK ? m0 * p.lda : m0;
-    const int64_t a_kstep = AK ? BK : BK * p.lda;
-    const int64_t b_tile = BKC ? n0 * p.ldb : n0;
-    const int64_t b_kstep = BKC ? BK : BK * p.ldb;
-
-    OpA opa;
-    OpB opb;
-    opa.init(wave, lane, m0, p.M, p.lda);
-    opb.init(wave, lane, n0, p.N, p.ldb);
-
-    floatx16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    const int64_t nk = (p.K + BK - 1) / BK;
-    const uint32_t lds_base = lds_offset(lds);
-
-    auto issue = [&](int64_t st) {
-        const uint32_t slot = lds_base + (uint32_t)((st % S) * SLOT * 16);
-        const int64_t ao = a_tile + st * a_kstep, bo = b_tile + st * b_kstep;
-        opa.issue(Ab + ao, (p.extent_a - ao) * 2, slot, wave, st * BK, p.K);
-        opb.issue(Bb + bo, (p.extent_b - bo) * 2, slot + A_CH * 16, wave, st * BK, p.K);
-    };
-
-    half8 fa[NSUB][FM], fb[NSUB][FN];
-    auto read_stage = [&](int64_t st) {
-        const u32x4 *slot = lds + (int)(st % S) * SLOT;
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) {
-#pragma unroll
-            for (int i = 0; i < FM; ++i) fa[s][i] = opa.frag(slot, wm * WTM + i * 32, s, lane);
-#pragma unroll
-            for (int j = 0; j < FN; ++j) fb[s][j] = opb.frag(slot + A_CH, wn * WTN + j * 32, s, lane);
-        }
-    };
-    auto compute = [&]() {
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s)
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[s][j], fa[s][i], acc[i][j], 0, 0, 0);
-    };
-    // Phase boundary: no instruction may be moved across it by the compiler.
-    auto phase_end = [&]() {
-        __builtin_amdgcn_sched_barrier(0);
-        barrier();
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
-    // Prologue: stages 0..2 in flight (each wave issues exactly L loads per
-    // stage; stages past the end of K are range-check failures).
-    issue(0);
-    issue(1);
-    issue(2);
-    wait_vmcnt<2 * L>();                 // stage 0 landed for this lane
-    phase_end();                         // ... and for every lane
-    if (group == 0) read_stage(0);
-    phase_end();
-
-    if (group == 0) {
-        for (int64_t s = 0; s < nk; ++s) {
-            compute();                                   // phase 2s
-            wait_vmcnt<L>();                             // own loads of stage s+1
-            phase_end();
-            read_stage(s + 1);                           // phase 2s+1
-            issue(s + 3);
-            phase_end();
-        }
-    } else {
-        for (int64_t s = 0; s < nk; ++s) {
-            read_stage(s);                               // phase 2s
-            issue(s + 3);
-            wait_vmcnt<2 * L>();                         // own loads of stage s+1
-            phase_end();
-            compute();                                   // phase 2s+1
-            phase_end();
-        }
-    }
-    // No direct-to-LDS write may still be in flight when the LDS is released.
-    wait_vmcnt<0>();
-
-    store_tile<FM, FN, WTM, WTN>(p, acc, b, m0, n0, wm, wn, lane);
-}
-
-// ---------------------------------------------------------------------------
 // Streaming kernel for skinny problems (M <= 64) whose A and B are both
 // K-contiguous (row-major A, column-major B: the linear-layer layout, with W
 // stored N x K).  Such a GEMM is bound by reading B once from HBM
@@ -972,22 +836,11 @@ constexpr KernelFn pick_direct() {
                        kTiles[T].wgn, kTiles[T].stages, AK, BKC>;
 }
 
-template <int T, bool AK, bool BKC>
-constexpr KernelFn pick_pingpong() {
-    return gemm_pingpong<kTiles[T].bm, kTiles[T].bn, kTiles[T].bk, kTiles[T].stages, AK, BKC>;
-}
-
 // Kernel table indexed [tile][A K-contiguous][B K-contiguous][vec].  Direct
 // tiles have only the vec entry; staged tiles have both.
 template <int T>
 void fill_tile(KernelFn (&t)[2][2][2]) {
-    if constexpr (kTiles[T].kind == KIND_PINGPONG) {
-        t[0][0][1] = pick_pingpong<T, false, false>();
-        t[0][1][1] = pick_pingpong<T, false, true>();
-        t[1][0][1] = pick_pingpong<T, true, false>();
-        t[1][1][1] = pick_pingpong<T, true, true>();
-        t[0][0][0] = t[0][1][0] = t[1][0][0] = t[1][1][0] = nullptr;
-    } else if constexpr (kTiles[T].kind == KIND_DIRECT) {
+    if constexpr (kTiles[T].kind == KIND_DIRECT) {
         t[0][0][1] = pick_direct<T, false, false>();
         t[0][1][1] = pick_direct<T, false, true>();
         t[1][0][1] = pick_direct<T, true, false>();

@@ -71,6 +71,24 @@ def test_batched_small(kind):
     parity(case, what=f"batched {kind}")
 
 
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+@pytest.mark.parametrize("shape,tile", [((4000, 4104, 1000), "256x256"),
+                                        ((1000, 1000, 1000), "128x128")])
+def test_large_tiles_ragged_all_layouts(shape, tile, la, lb):
+    """The two large direct tiles with M, N and K all off the tile grid (K
+    tail of 40 in the last 64-deep stage) in every layout, beta != 0; the
+    row lengths stay multiples of 8 so that the direct path is taken."""
+    M, N, K = shape
+    case = gi.make_case(M, N, K, layout_a=la, layout_b=lb, alpha=-0.5, beta=2.0,
+                        seed=21)
+    p = mpg.Plan(M, N, K, la, lb, OUT_F16, case.lda, case.ldb, case.ldc)
+    kernel = p.kernel
+    p.close()
+    assert tile in kernel, kernel
+    rows = sample_rows(M, n_random=64) if M > 1000 else None
+    parity(case, rows=rows, what=f"{kernel} {M}x{N}x{K}")
+
+
 # ----------------------------------------------------- layouts and types
 
 SWEEP = [(1, 1, 1), (2, 3, 5), (8, 8, 8), (31, 33, 17), (32, 64, 64),
