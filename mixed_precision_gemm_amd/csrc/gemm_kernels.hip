@@ -452,10 +452,13 @@ __device__ inline sgpr4 make_rsrc_words(const void *base, int64_t bytes) {
 // address lds_addr + 16 t.  Issued as assembly so that the compiler's
 // wait-count insertion does not treat later LDS reads of other ring slots as
 // dependent on it; the kernel orders it explicitly (vmcnt waits + barriers).
+// lds_addr is the same for every lane (it is read from the first lane so the
+// compiler can keep it in a scalar register).
 __device__ inline void lds_dma16(sgpr4 rs, uint32_t lds_addr, uint32_t voff) {
+    const uint32_t m0v = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr);
     asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
                  :
-                 : "v"(voff), "s"(lds_addr), "s"(rs)
+                 : "v"(voff), "s"(m0v), "s"(rs)
                  : "m0");
 }
 
@@ -469,6 +472,130 @@ __device__ inline void wait_vmcnt() {
 // Workgroup barrier that is also a compiler memory barrier, without the
 // wait for all outstanding memory operations that a fenced barrier implies.
 __device__ inline void barrier() { asm volatile("s_barrier" : : : "memory"); }
+
+// Four consecutive elements of one C row of type T, kept in T: a vector
+// access where the row and alignment allow it (vec), element by element (up
+// to N, zeros beyond) otherwise.
+template <typename T>
+using c4_t = typename std::conditional<sizeof(T) == 4, floatx4, half4>::type;
+
+template <typename T>
+__device__ inline c4_t<T> load_c4(const GemmArgs &p, int64_t off, int64_t n, bool vec) {
+    const T *C = (const T *)p.C + off;
+    if (vec) return *(const c4_t<T> *)C;
+    c4_t<T> c = {};
+    for (int e = 0; e < 4 && n + e < p.N; ++e) c[e] = C[e];
+    return c;
+}
+
+template <typename T>
+__device__ inline void store_c4(const GemmArgs &p, int64_t off, int64_t n, bool vec, floatx4 v) {
+    T *C = (T *)p.C + off;
+    if (vec) {
+        if constexpr (sizeof(T) == 4)
+            *(floatx4 *)C = v;
+        else
+            *(half4 *)C = half4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+        return;
+    }
+    for (int e = 0; e < 4 && n + e < p.N; ++e) C[e] = (T)v[e];
+}
+
+// Epilogue of the direct kernels, C = alpha * acc + beta * C ([GEMM] §4.4:
+// scale, add the old C, round once to the output type), staged through the
+// LDS ring once the main loop has drained it.  In each pass the waves that own
+// a band of PR rows write alpha * acc there in fp32; then every wave reads
+// whole rows back, so that each global load and store instruction covers
+// complete, contiguous row segments of C (the accumulator layout alone would
+// touch 32 rows 16 bytes at a time).  Tiles wholly inside C with vector-
+// aligned rows (FULL) load C in batches of 8 row groups, double-buffered, the
+// first batch of a pass issued before its LDS staging so that its latency
+// overlaps it; edge tiles check every element and load one group at a time.
+// Staged rows are BN fp32 values; 16-byte granule g of row r sits at granule
+// g ^ (r & 15), so neither the column-wise writes nor the row-wise reads
+// conflict on banks.
+template <typename T, bool FULL, int BM, int BN, int WGM, int WGN, int LDS_BYTES, int FM, int FN>
+__device__ inline void store_tile_lds(const GemmArgs &p, const floatx16 (&acc)[FM][FN],
+                                      u32x4 *lds, int b, int64_t m0, int64_t n0,
+                                      int wave, int lane) {
+    constexpr int WTM = BM / WGM, WTN = BN / WGN;
+    constexpr int NW = WGM * WGN;
+    constexpr int GPR = BN / 4;                      // granules per staged row
+    constexpr int PR0 = LDS_BYTES / (BN * 4);
+    constexpr int PR = PR0 < BM ? PR0 : BM;          // rows per pass
+    constexpr int NPASS = BM / PR;
+    constexpr int RPI = 64 / GPR;                    // rows per wave instruction
+    constexpr int IT = PR / (RPI * NW);              // row groups per thread and pass
+    constexpr int CB = FULL ? (IT < 8 ? IT : 8) : 1; // C row groups per load batch
+    constexpr int SW = GPR >= 16 ? 15 : GPR - 1;
+    static_assert(FM * 32 == WTM && FN * 32 == WTN, "accumulator shape");
+    static_assert(GPR <= 64 && 64 % GPR == 0 && GPR >= 8, "row width");
+    static_assert(PR % WTM == 0 && BM % PR == 0 && PR % (RPI * NW) == 0, "pass shape");
+    static_assert(IT % CB == 0, "load batches");
+    const int wm = wave / WGN, wn = wave % WGN;
+    char *base = (char *)lds;
+    const float alpha = p.alpha, beta = p.beta;
+    const int r_in = lane / GPR, g = lane % GPR;
+    const int64_t n = n0 + 4 * g;
+    const bool n_ok = FULL || n < p.N;
+    const bool vec = FULL || (p.c_vec && n + 4 <= p.N);
+    const int64_t cbase = b * p.sc + n;
+    // Two register batches of C: batch k + 1 is in flight while batch k is
+    // combined and stored.
+    c4_t<T> cv[2][CB];
+    auto load_batch = [&](int pass, int it0, int buf) __attribute__((always_inline)) {
+        if (beta == 0.0f) return;
+#pragma unroll
+        for (int t = 0; t < CB; ++t) {
+            const int r = ((it0 + t) * NW + wave) * RPI + r_in;
+            const int64_t m = m0 + pass * PR + r;
+            cv[buf][t] = (FULL || (m < p.M && n_ok)) ? load_c4<T>(p, cbase + m * p.ldc, n, vec)
+                                                     : c4_t<T>{};
+        }
+    };
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
+        load_batch(pass, 0, 0);
+        if ((wm * WTM) / PR == pass) {
+            const int rb = wm * WTM - pass * PR;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int rl = rb + i * 32 + (lane & 31);
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int gr = (wn * WTN + j * 32 + 8 * q) / 4 + (lane >> 5);
+                        const floatx4 v = {alpha * acc[i][j][4 * q], alpha * acc[i][j][4 * q + 1],
+                                           alpha * acc[i][j][4 * q + 2], alpha * acc[i][j][4 * q + 3]};
+                        *(floatx4 *)(base + rl * BN * 4 + ((gr ^ (rl & SW)) << 4)) = v;
+                    }
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+        barrier();
+#pragma unroll
+        for (int it0 = 0; it0 < IT; it0 += CB) {
+            const int buf = (it0 / CB) & 1;
+            if (it0 + CB < IT) load_batch(pass, it0 + CB, buf ^ 1);
+#pragma unroll
+            for (int t = 0; t < CB; ++t) {
+                const int r = ((it0 + t) * NW + wave) * RPI + r_in;
+                const int64_t m = m0 + pass * PR + r;
+                floatx4 v = *(const floatx4 *)(base + r * BN * 4 + ((g ^ (r & SW)) << 4));
+                if (beta != 0.0f) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] += beta * (float)cv[buf][t][e];
+                }
+                if (FULL || (m < p.M && n_ok)) store_c4<T>(p, cbase + m * p.ldc, n, vec, v);
+            }
+        }
+        if (pass + 1 < NPASS) {
+            asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+            barrier();
+        }
+    }
+}
 
 template <int R, int BK, int NW, bool KC>
 struct DirectOperand {
@@ -696,7 +823,8 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_direct(GemmArgs p) {
     barrier();                          // ... and for every lane
     read_frags(0, 0, 0);
 
-    for (int64_t kt = 0; kt < nk; ++kt) {
+    // Sub-steps 0 .. NSUB-2 of stage kt, then the stage barrier.
+    auto stage_head = [&](int64_t kt) __attribute__((always_inline)) {
         substep(0, 1, kt, 1, kt + 1, CLH{}, CRest{});   // rest of stage kt+1
 #pragma unroll
         for (int sub = 1; sub < NSUB - 1; ++sub)
@@ -704,13 +832,38 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_direct(GemmArgs p) {
         wait_vmcnt<0>();                // this lane's loads of stage kt+1
         asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");   // reads of stage kt done
         barrier();
+    };
+    // Last sub-step of stage kt: reads sub-step 0 of stage kt+1 and issues
+    // the first half of stage kt+2.
+    auto stage_tail = [&](int64_t kt) __attribute__((always_inline)) {
         substep((NSUB - 1) & 1, NSUB & 1, kt + 1, 0, kt + 2, C0{}, CLH{});
+    };
+    // The loop is rotated so that its back edge follows the barrier, where no
+    // LDS read is outstanding.
+    stage_head(0);
+    for (int64_t kt = 0; kt + 1 < nk; ++kt) {
+        stage_tail(kt);
+        stage_head(kt + 1);
     }
-    // No direct-to-LDS write may still be in flight when the workgroup's LDS
-    // is released.
+    stage_tail(nk - 1);
+    // Drain the ring: no direct-to-LDS write or fragment read may still be in
+    // flight when the epilogue reuses the LDS.
     wait_vmcnt<0>();
+    asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+    barrier();
 
-    store_tile<FM, FN, WTM, WTN>(p, acc, b, m0, n0, wm, wn, lane);
+    const bool full = p.c_vec && m0 + BM <= p.M && n0 + BN <= p.N;
+    if (p.out_f32) {
+        if (full)
+            store_tile_lds<float, true, BM, BN, WGM, WGN, S * SLOT * 16>(p, acc, lds, b, m0, n0, wave, lane);
+        else
+            store_tile_lds<float, false, BM, BN, WGM, WGN, S * SLOT * 16>(p, acc, lds, b, m0, n0, wave, lane);
+    } else {
+        if (full)
+            store_tile_lds<_Float16, true, BM, BN, WGM, WGN, S * SLOT * 16>(p, acc, lds, b, m0, n0, wave, lane);
+        else
+            store_tile_lds<_Float16, false, BM, BN, WGM, WGN, S * SLOT * 16>(p, acc, lds, b, m0, n0, wave, lane);
+    }
 }
 
 // ---------------------------------------------------------------------------
