@@ -27,9 +27,10 @@ enum TileId : int {
 //                register staging), for 16-byte-aligned operands;
 //   KIND_STAGED: a two-slot ring filled through registers (global -> VGPR ->
 //                LDS), used for the small tiles and for the narrow-load path.
+//   KIND_DIRECT16: the direct ring computed with 16 x 16 x 32 MFMAs.
 //   KIND_STREAM:  skinny M with K-contiguous A and B: fragments loaded from
 //                global memory straight into registers, K split over 8 waves.
-enum KernelKind : int { KIND_DIRECT = 0, KIND_STAGED = 1, KIND_STREAM = 2 };
+enum KernelKind : int { KIND_DIRECT = 0, KIND_STAGED = 1, KIND_STREAM = 2, KIND_DIRECT16 = 3 };
 
 struct TileShape {
     int bm, bn, bk, wgm, wgn, stages, kind;
@@ -37,7 +38,7 @@ struct TileShape {
 };
 
 constexpr TileShape kTiles[NUM_TILES] = {
-    {256, 256, 64, 2, 2, 2, KIND_DIRECT, "256x256x64s2"},
+    {256, 256, 64, 2, 2, 2, KIND_DIRECT16, "256x256x64m16"},
     {128, 128, 64, 2, 2, 2, KIND_DIRECT, "128x128x64s2"},
     {64, 64, 64, 2, 2, 2, KIND_STAGED, "64x64x64"},
     {32, 64, 64, 1, 2, 2, KIND_STAGED, "32x64x64"},

@@ -417,16 +417,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_staged(GemmArgs p) {
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-// Chunk XOR of row k of an MN-contiguous tile.  A transpose read touches four
-// consecutive rows (k%4 = 0..3) at the same 32-byte column span per 16 lanes
-// and the same 64-byte span per 32 lanes; XOR values {0, 10, 4, 14} send the
-// four rows to distinct 32-byte windows of every 128 bytes and to distinct
-// 64-byte windows of every 256 bytes (rows are multiples of 256 bytes long),
-// so the read is conflict-free whether the LDS serves 16 or 32 lanes a cycle.
+// Chunk XOR of row k of an MN-contiguous tile (rows are multiples of 256
+// bytes long, so only the chunk index picks the bank).  A transpose read
+// touches four consecutive rows (k%4 = 0..3) per 16 lanes.  For a 32 x 32
+// fragment a 32-lane pass covers those four rows over a 64-byte column span;
+// for a 16 x 16 fragment it covers rows k..k+3 and k+8..k+11 over a 32-byte
+// span.  XOR values {0, 10, 4, 14} by k%4, with chunk bit 1 flipped by bit 3
+// of k, give every 8-byte piece of either pass its own bank (checked against
+// a 64-bank, 4-byte model for 16- and 32-lane passes).
 template <int R>
 __device__ __host__ constexpr int mn_swz(int k) {
     static_assert(R / 8 >= 16, "MN-contiguous rows need at least 16 chunks");
-    return (0xE4A0 >> (4 * (k & 3))) & 15;   // k%4 -> 0, 10, 4, 14
+    // k%4 -> 0, 10, 4, 14, and bit 3 of k flips chunk bit 1: rows k and k+8
+    // are read by the two halves of one 32-lane pass of the 16 x 16 fragment
+    // read, rows k..k+3 by one 16-lane group of either fragment read.
+    return ((0xE4A0 >> (4 * (k & 3))) & 15) ^ (((k >> 3) & 1) << 1);
 }
 
 // Byte offset of a __shared__ object within the workgroup's LDS allocation.
@@ -514,8 +519,9 @@ __device__ inline void store_c4(const GemmArgs &p, int64_t off, int64_t n, bool 
 // Staged rows are BN fp32 values; 16-byte granule g of row r sits at granule
 // g ^ (r & 15), so neither the column-wise writes nor the row-wise reads
 // conflict on banks.
-template <typename T, bool FULL, int BM, int BN, int WGM, int WGN, int LDS_BYTES, int FM, int FN>
-__device__ inline void store_tile_lds(const GemmArgs &p, const floatx16 (&acc)[FM][FN],
+template <typename T, bool FULL, int BM, int BN, int WGM, int WGN, int LDS_BYTES, int MB,
+          typename AccT, int FM, int FN>
+__device__ inline void store_tile_lds(const GemmArgs &p, const AccT (&acc)[FM][FN],
                                       u32x4 *lds, int b, int64_t m0, int64_t n0,
                                       int wave, int lane) {
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
@@ -528,7 +534,8 @@ __device__ inline void store_tile_lds(const GemmArgs &p, const floatx16 (&acc)[F
     constexpr int IT = PR / (RPI * NW);              // row groups per thread and pass
     constexpr int CB = FULL ? (IT < 8 ? IT : 8) : 1; // C row groups per load batch
     constexpr int SW = GPR >= 16 ? 15 : GPR - 1;
-    static_assert(FM * 32 == WTM && FN * 32 == WTN, "accumulator shape");
+    static_assert(FM * MB == WTM && FN * MB == WTN, "accumulator shape");
+    static_assert(sizeof(AccT) == MB * MB / 64 * 4, "MFMA block");
     static_assert(GPR <= 64 && 64 % GPR == 0 && GPR >= 8, "row width");
     static_assert(PR % WTM == 0 && BM % PR == 0 && PR % (RPI * NW) == 0, "pass shape");
     static_assert(IT % CB == 0, "load batches");
@@ -558,14 +565,18 @@ __device__ inline void store_tile_lds(const GemmArgs &p, const floatx16 (&acc)[F
         load_batch(pass, 0, 0);
         if ((wm * WTM) / PR == pass) {
             const int rb = wm * WTM - pass * PR;
+            // MFMA block layout (operands swapped so that C is not
+            // transposed): in a 32 x 32 block lane l holds row l%32, columns
+            // 8q + 4(l/32) + 0..3 in registers 4q..4q+3; in a 16 x 16 block
+            // lane l holds row l%16, columns 4(l/16) + 0..3.
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
-                const int rl = rb + i * 32 + (lane & 31);
+                const int rl = rb + i * MB + (lane % MB);
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int gr = (wn * WTN + j * 32 + 8 * q) / 4 + (lane >> 5);
+                    for (int q = 0; q < MB * MB / 256; ++q) {
+                        const int gr = (wn * WTN + j * MB) / 4 + (MB == 32 ? 2 * q + (lane >> 5) : (lane >> 4));
                         const floatx4 v = {alpha * acc[i][j][4 * q], alpha * acc[i][j][4 * q + 1],
                                            alpha * acc[i][j][4 * q + 2], alpha * acc[i][j][4 * q + 3]};
                         *(floatx4 *)(base + rl * BN * 4 + ((gr ^ (rl & SW)) << 4)) = v;
@@ -642,6 +653,10 @@ struct DirectOperand {
     __device__ sgpr4 stage_rsrc(const _Float16 *base, int64_t bytes_left) const {
         return make_rsrc_words(base, bytes_left);
     }
+    // Load i of a stage that lies wholly inside K: no K test.
+    __device__ void issue_one_full(int i, sgpr4 rs, uint32_t lds_addr, int wave) const {
+        lds_dma16(rs, lds_addr + (uint32_t)((i * NW + wave) * 64 * 16), off[i]);
+    }
     // Load i of this wave's share of a stage; chunks at K indices >= left
     // fail the range check and write zeros.
     __device__ void issue_one(int i, sgpr4 rs, uint32_t lds_addr, int wave, int left) const {
@@ -676,6 +691,31 @@ struct DirectOperand {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const int k = 16 * s + 8 * (g4 >> 1) + 4 * t + (j >> 2);
+                const int addr = k * R * 2 + (((n >> 3) ^ mn_swz<R>(k)) << 4) + (n & 7) * 2;
+                h[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4i16 *)(bytes + addr));
+            }
+            const v4i16 lo = h[0], hi = h[1];
+            return __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    }
+
+    // Fragment of the 16 x 16 x 32 MFMA for the 16-row block starting at rb,
+    // K step s (32 deep): lane l receives row rb + l%16,
+    // k = 32 s + 8 (l/16) + 0..7.
+    __device__ half8 frag16(const u32x4 *lds, int rb, int s, int lane) const {
+        if constexpr (KC) {
+            const int r = rb + (lane & 15);
+            const int kv = 4 * s + (lane >> 4);
+            return __builtin_bit_cast(half8, lds[r * VPR + (kv ^ swz<VPR>(r))]);
+        } else {
+            const int g4 = lane >> 4, j = lane & 15;
+            const int n = rb + 4 * (j & 3);
+            const char *bytes = (const char *)lds;
+            v4i16 h[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int k = 32 * s + 8 * g4 + 4 * t + (j >> 2);
                 const int addr = k * R * 2 + (((n >> 3) ^ mn_swz<R>(k)) << 4) + (n & 7) * 2;
                 h[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (__attribute__((address_space(3))) v4i16 *)(bytes + addr));
@@ -855,14 +895,266 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_direct(GemmArgs p) {
     const bool full = p.c_vec && m0 + BM <= p.M && n0 + BN <= p.N;
     if (p.out_f32) {
         if (full)
-            store_tile_lds<float, true, BM, BN, WGM, WGN, S * SLOT * 16>(p, acc, lds, b, m0, n0, wave, lane);
+            store_tile_lds<float, true, BM, BN, WGM, WGN, S * SLOT * 16, 32>(p, acc, lds, b, m0, n0, wave, lane);
         else
-            store_tile_lds<float, false, BM, BN, WGM, WGN, S * SLOT * 16>(p, acc, lds, b, m0, n0, wave, lane);
+            store_tile_lds<float, false, BM, BN, WGM, WGN, S * SLOT * 16, 32>(p, acc, lds, b, m0, n0, wave, lane);
     } else {
         if (full)
-            store_tile_lds<_Float16, true, BM, BN, WGM, WGN, S * SLOT * 16>(p, acc, lds, b, m0, n0, wave, lane);
+            store_tile_lds<_Float16, true, BM, BN, WGM, WGN, S * SLOT * 16, 32>(p, acc, lds, b, m0, n0, wave, lane);
         else
-            store_tile_lds<_Float16, false, BM, BN, WGM, WGN, S * SLOT * 16>(p, acc, lds, b, m0, n0, wave, lane);
+            store_tile_lds<_Float16, false, BM, BN, WGM, WGN, S * SLOT * 16, 32>(p, acc, lds, b, m0, n0, wave, lane);
+    }
+}
+
+// Per-lane LDS byte offsets of one operand's 16 x 16 x 32 fragments for one
+// wave (rows or columns wb .. wb + 16 NBLK - 1 of a BK = 64 ring slot), so
+// that every fragment read is a base register plus an immediate offset.  Two
+// sets: `cur` addresses the slot of the stage being computed, `nxt` the slot
+// of the next one; the two slots are 64 KiB apart, so advancing a stage is one
+// XOR per register (advance()) and no other address arithmetic is left in
+// the K loop.
+//   K-contiguous: row r = wb + 16 i + l%16 keeps its K chunk kv = 4 s + l/16
+//     at kv ^ swz(r).  With wb a multiple of 64 that is X ^ (4 s ^ (2 i & 6)),
+//     X = (l/16) ^ (l%16 & 7) ^ (l%16 >> 3): four bases, by (2 i & 6) ^ 4 s.
+//   MN-contiguous: column n = wb + 16 i + 4 (l%4) of row
+//     k = 32 s + 4 t + 8 (l/16) + (l%16)/4 sits in chunk (n >> 3) ^ mn_swz(k),
+//     and mn_swz(k) depends only on k%4 and bit 3 of k, both fixed by the
+//     lane: one base per block i, rows 32 s + 4 t as immediates.
+template <int R, int BK, bool KC, int NBLK, int SLOT_BYTES>
+struct Frag16 {
+    static_assert(BK == 64, "128-byte K rows");
+    static_assert(SLOT_BYTES == 65536, "slots 64 KiB apart: advance() flips bit 16");
+    static constexpr int NCLS = KC ? 4 : NBLK;
+    uint32_t cur[NCLS], nxt[NCLS];
+
+    // Bases for stage 0 (slot 0) in cur and stage 1 (slot 1) in nxt.
+    __device__ void setup(int lane, int wb, uint32_t region) {
+        const int lr = lane & 15, lg = lane >> 4;
+        if constexpr (KC) {
+            const int X = lg ^ (lr & 7) ^ (lr >> 3);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                cur[c] = region + (uint32_t)((wb + lr) * BK * 2 + 16 * (X ^ (2 * c)));
+        } else {
+            const int W = ((lr & 3) >> 1) ^ mn_swz<R>(8 * lg + (lr >> 2));
+#pragma unroll
+            for (int i = 0; i < NBLK; ++i)
+                cur[i] = region + (uint32_t)((8 * lg + (lr >> 2)) * R * 2 +
+                                             16 * ((wb / 8 + 2 * i) ^ W) + 8 * (lr & 1));
+        }
+#pragma unroll
+        for (int c = 0; c < NCLS; ++c) nxt[c] = cur[c] + SLOT_BYTES;
+    }
+
+    __device__ void advance() {
+#pragma unroll
+        for (int c = 0; c < NCLS; ++c) {
+            cur[c] ^= (uint32_t)SLOT_BYTES;
+            nxt[c] ^= (uint32_t)SLOT_BYTES;
+        }
+    }
+
+    // Fragment of block i, K step s (32 deep) of the current (NEXT = false)
+    // or next stage: lane l receives row (or column) wb + 16 i + l%16,
+    // k = 32 s + 8 (l/16) + 0..7.
+    template <bool NEXT>
+    __device__ half8 read(const u32x4 *lds, int i, int s) const {
+        const char *bytes = (const char *)lds;
+        const uint32_t *b = NEXT ? nxt : cur;
+        if constexpr (KC) {
+            const int c = (((2 * i) & 6) ^ (4 * s)) >> 1;
+            return __builtin_bit_cast(half8, *(const u32x4 *)(bytes + b[c] + 16 * BK * 2 * i));
+        } else {
+            v4i16 h[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                h[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4i16 *)(bytes + b[i] + (32 * s + 4 * t) * R * 2));
+            const v4i16 lo = h[0], hi = h[1];
+            return __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Direct kernel on 16 x 16 x 32 MFMAs.  Same ring, loads and epilogue as
+// gemm_direct; each wave owns (BM/WGM) x (BN/WGN) outputs as 16 x 16
+// accumulator blocks.  With a 128 x 128 wave tile a 32-deep K step is 64
+// MFMAs of 16 cycles fed by 16 one-KiB fragment reads -- the same LDS traffic
+// per flop as 32 x 32 blocks -- and back-to-back 16 x 16 x 32 MFMAs on
+// independent accumulators keep the matrix core busier than 32 x 32 x 16
+// ones do on gfx950 (measured: 97 % against 75 % of peak for the same 128 x
+// 128 register tile with no memory traffic at all).
+//
+// Stage kt (BK = 64: two K steps) lives in ring slot kt % 2.  The K loop is
+// rotated so that its back edge follows the stage barrier:
+//   head(kt): K step 0 of stage kt, reading the fragments of K step 1; wait
+//             for this lane's loads of stage kt+1 and for all LDS reads;
+//             barrier -- stage kt+1 is readable and slot kt % 2 is free;
+//   tail(kt): K step 1 of stage kt, reading the fragments of stage kt+1 K
+//             step 0 and issuing all loads of stage kt+2 into slot kt % 2.
+// Every load thus has the next two K steps to land.  Each stage issues
+// exactly L loads per lane (stages past the end of K fail the range check
+// and write zeros), so the wait counts are exact.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int BK, int WGM, int WGN, int S, bool AK, bool BKC>
+__global__ __launch_bounds__(64 * WGM * WGN)
+__attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_direct16(GemmArgs p) {
+    constexpr int NW = WGM * WGN;
+    constexpr int WTM = BM / WGM, WTN = BN / WGN;
+    constexpr int FM = WTM / 16, FN = WTN / 16;
+    constexpr int NKS = BK / 32;
+    constexpr int A_CH = BM * BK / 8, B_CH = BN * BK / 8;
+    constexpr int SLOT = A_CH + B_CH;                 // 16-byte chunks per slot
+    using OpA = DirectOperand<BM, BK, NW, AK>;
+    using OpB = DirectOperand<BN, BK, NW, BKC>;
+    constexpr int L = OpA::PER_WAVE + OpB::PER_WAVE;  // loads per lane per stage
+    static_assert(S == 2, "the schedule is a two-slot ring");
+    static_assert(NKS == 2, "head and tail are one K step each");
+    static_assert(L < 64, "vmcnt range");
+
+    __shared__ u32x4 lds[S * SLOT];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WGN, wn = wave % WGN;
+
+    int b, tm, tn;
+    tile_coords(p, blockIdx.x, b, tm, tn);
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    const _Float16 *Ab = p.A + b * p.sa;
+    const _Float16 *Bb = p.B + b * p.sb;
+    const int64_t a_tile = AK ? m0 * p.lda : m0;
+    const int64_t a_kstep = AK ? BK : BK * p.lda;
+    const int64_t b_tile = BKC ? n0 * p.ldb : n0;
+    const int64_t b_kstep = BKC ? BK : BK * p.ldb;
+
+    OpA opa;
+    OpB opb;
+    opa.init(wave, lane, m0, p.M, p.lda);
+    opb.init(wave, lane, n0, p.N, p.ldb);
+
+    floatx4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int64_t nk = (p.K + BK - 1) / BK;
+    const uint32_t lds_base = lds_offset(lds);
+
+    auto issue = [&](int64_t st) __attribute__((always_inline)) {
+        const uint32_t slot = lds_base + (uint32_t)((st % S) * SLOT * 16);
+        const int64_t ao = a_tile + st * a_kstep, bo = b_tile + st * b_kstep;
+        opa.issue(Ab + ao, (p.extent_a - ao) * 2, slot, wave, st * BK, p.K);
+        opb.issue(Bb + bo, (p.extent_b - bo) * 2, slot + A_CH * 16, wave, st * BK, p.K);
+    };
+
+    static_assert(WTM % 64 == 0 && WTN % 64 == 0, "fragment base classes need 64-aligned wave tiles");
+    Frag16<BM, BK, AK, FM, SLOT * 16> fra;
+    Frag16<BN, BK, BKC, FN, SLOT * 16> frb;
+    fra.setup(lane, wm * WTM, 0);
+    frb.setup(lane, wn * WTN, A_CH * 16);
+
+    half8 fa[2][FM], fb[2][FN];
+    using Z = std::integral_constant<int, 0>;
+    using O = std::integral_constant<int, 1>;
+
+    // One K step: the FM*FN MFMAs on fragment buffer CUR, with the reads of
+    // the next K step's fragments (ring slot RSL, step RKS, into buffer
+    // CUR ^ 1) and, if LOADS, this wave's L direct-to-LDS loads of stage dst
+    // (into slot DSL) spread evenly between them in a fixed order.  B
+    // fragments are read first: the next step's first FN MFMAs need all of
+    // them.  Only K-contiguous operands test K: rows k >= K of an
+    // MN-contiguous operand start past its extent and fail the range check.
+    constexpr int NQ = FM * FN;
+    constexpr int NF = FM + FN;
+    auto kstep = [&](auto curc, auto nextc, auto rksc, auto loadsc, int64_t dst)
+                     __attribute__((always_inline)) {
+        constexpr int CUR = decltype(curc)::value, RKS = decltype(rksc)::value;
+        constexpr bool NEXT = decltype(nextc)::value, LOADS = decltype(loadsc)::value;
+        constexpr int nl = LOADS ? L : 0;
+        const uint32_t dslot = lds_base + (uint32_t)((dst & 1) * SLOT * 16);
+        sgpr4 rsa = {}, rsb = {};
+        int left = BK;
+        if constexpr (LOADS) {
+            const int64_t ao = a_tile + dst * a_kstep, bo = b_tile + dst * b_kstep;
+            rsa = opa.stage_rsrc(Ab + ao, (p.extent_a - ao) * 2);
+            rsb = opb.stage_rsrc(Bb + bo, (p.extent_b - bo) * 2);
+            if constexpr (AK || BKC) left = OpA::stage_left(dst * BK, p.K);
+        }
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int i = q / FN, j = q % FN;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[CUR][j], fa[CUR][i], acc[i][j], 0, 0, 0);
+#pragma unroll
+            for (int l = q * nl / NQ; l < (q + 1) * nl / NQ; ++l) {
+                if (l < OpA::PER_WAVE) {
+                    if constexpr (AK) opa.issue_one(l, rsa, dslot, wave, left);
+                    else opa.issue_one_full(l, rsa, dslot, wave);
+                } else {
+                    if constexpr (BKC) opb.issue_one(l - OpA::PER_WAVE, rsb, dslot + A_CH * 16, wave, left);
+                    else opb.issue_one_full(l - OpA::PER_WAVE, rsb, dslot + A_CH * 16, wave);
+                }
+            }
+#pragma unroll
+            for (int f = q * NF / NQ; f < (q + 1) * NF / NQ; ++f) {
+                if (f < FN) fb[CUR ^ 1][f] = frb.template read<NEXT>(lds, f, RKS);
+                else fa[CUR ^ 1][f - FN] = fra.template read<NEXT>(lds, f - FN, RKS);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // head(): K step 0 of stage kt, reading its K step 1; then the stage
+    // barrier.  tail(kt): K step 1 of stage kt, reading K step 0 of stage
+    // kt+1 and loading stage kt+2 into the slot stage kt used.
+    auto head = [&]() __attribute__((always_inline)) {
+        kstep(Z{}, std::false_type{}, O{}, std::false_type{}, 0);
+        wait_vmcnt<0>();                // this lane's loads of stage kt+1
+        asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");   // reads of stage kt done
+        barrier();
+    };
+    auto tail = [&](int64_t kt) __attribute__((always_inline)) {
+        kstep(O{}, std::true_type{}, Z{}, std::true_type{}, kt + 2);
+    };
+
+    // Prologue: stages 0 and 1 whole.
+    issue(0);
+    issue(1);
+    wait_vmcnt<L>();                    // stage 0 resident for this lane
+    barrier();                          // ... and for every lane
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[0][j] = frb.template read<false>(lds, j, 0);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[0][i] = fra.template read<false>(lds, i, 0);
+
+    head();
+    for (int64_t kt = 0; kt + 1 < nk; ++kt) {
+        tail(kt);
+        fra.advance();
+        frb.advance();
+        head();
+    }
+    tail(nk - 1);
+
+    // Drain the ring before the epilogue reuses the LDS.
+    wait_vmcnt<0>();
+    asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+    barrier();
+
+    const bool full = p.c_vec && m0 + BM <= p.M && n0 + BN <= p.N;
+    if (p.out_f32) {
+        if (full)
+            store_tile_lds<float, true, BM, BN, WGM, WGN, S * SLOT * 16, 16>(p, acc, lds, b, m0, n0, wave, lane);
+        else
+            store_tile_lds<float, false, BM, BN, WGM, WGN, S * SLOT * 16, 16>(p, acc, lds, b, m0, n0, wave, lane);
+    } else {
+        if (full)
+            store_tile_lds<_Float16, true, BM, BN, WGM, WGN, S * SLOT * 16, 16>(p, acc, lds, b, m0, n0, wave, lane);
+        else
+            store_tile_lds<_Float16, false, BM, BN, WGM, WGN, S * SLOT * 16, 16>(p, acc, lds, b, m0, n0, wave, lane);
     }
 }
 
@@ -984,6 +1276,12 @@ constexpr KernelFn pick_staged() {
 }
 
 template <int T, bool AK, bool BKC>
+constexpr KernelFn pick_direct16() {
+    return gemm_direct16<kTiles[T].bm, kTiles[T].bn, kTiles[T].bk, kTiles[T].wgm,
+                         kTiles[T].wgn, kTiles[T].stages, AK, BKC>;
+}
+
+template <int T, bool AK, bool BKC>
 constexpr KernelFn pick_direct() {
     return gemm_direct<kTiles[T].bm, kTiles[T].bn, kTiles[T].bk, kTiles[T].wgm,
                        kTiles[T].wgn, kTiles[T].stages, AK, BKC>;
@@ -993,7 +1291,13 @@ constexpr KernelFn pick_direct() {
 // tiles have only the vec entry; staged tiles have both.
 template <int T>
 void fill_tile(KernelFn (&t)[2][2][2]) {
-    if constexpr (kTiles[T].kind == KIND_DIRECT) {
+    if constexpr (kTiles[T].kind == KIND_DIRECT16) {
+        t[0][0][1] = pick_direct16<T, false, false>();
+        t[0][1][1] = pick_direct16<T, false, true>();
+        t[1][0][1] = pick_direct16<T, true, false>();
+        t[1][1][1] = pick_direct16<T, true, true>();
+        t[0][0][0] = t[0][1][0] = t[1][0][0] = t[1][1][0] = nullptr;
+    } else if constexpr (kTiles[T].kind == KIND_DIRECT) {
         t[0][0][1] = pick_direct<T, false, false>();
         t[0][1][1] = pick_direct<T, false, true>();
         t[1][0][1] = pick_direct<T, true, false>();
