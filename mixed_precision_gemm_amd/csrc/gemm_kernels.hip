@@ -653,6 +653,23 @@ struct DirectOperand {
     __device__ sgpr4 stage_rsrc(const _Float16 *base, int64_t bytes_left) const {
         return make_rsrc_words(base, bytes_left);
     }
+    // For K-contiguous 128-byte rows the K index of load i depends on i only
+    // through (i NW + wave) % 8, i.e. on i % KCL: the K test of a stage needs
+    // KCL compares (kmask) and one select per load (issue_one_masked).
+    static constexpr int KCL = NW % 8 == 0 ? 1 : NW % 4 == 0 ? 2 : NW % 2 == 0 ? 4 : 8;
+    struct KMask { bool ok[KCL]; };
+    __device__ KMask kmask(int left) const {
+        static_assert(KC && VPR == 8, "classes derived for K-contiguous 128-byte rows");
+        KMask m;
+#pragma unroll
+        for (int c = 0; c < KCL; ++c)
+            m.ok[c] = (int)((kin4[c / 4] >> (8 * (c % 4))) & 0xffu) < left;
+        return m;
+    }
+    __device__ void issue_one_masked(int i, sgpr4 rs, uint32_t lds_addr, int wave, const KMask &m) const {
+        lds_dma16(rs, lds_addr + (uint32_t)((i * NW + wave) * 64 * 16), m.ok[i % KCL] ? off[i] : kOutOfRange);
+    }
+
     // Load i of a stage that lies wholly inside K: no K test.
     __device__ void issue_one_full(int i, sgpr4 rs, uint32_t lds_addr, int wave) const {
         lds_dma16(rs, lds_addr + (uint32_t)((i * NW + wave) * 64 * 16), off[i]);
@@ -997,7 +1014,7 @@ struct Frag16 {
 // exactly L loads per lane (stages past the end of K fail the range check
 // and write zeros), so the wait counts are exact.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int WGM, int WGN, int S, bool AK, bool BKC>
+template <int BM, int BN, int BK, int WGM, int WGN, int S, bool AK, bool BKC, bool KFULL>
 __global__ __launch_bounds__(64 * WGM * WGN)
 __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_direct16(GemmArgs p) {
     constexpr int NW = WGM * WGN;
@@ -1068,6 +1085,9 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_direct16(GemmArgs p) {
     // fragments are read first: the next step's first FN MFMAs need all of
     // them.  Only K-contiguous operands test K: rows k >= K of an
     // MN-contiguous operand start past its extent and fail the range check.
+    // KFULL (K a multiple of BK) tests nothing: every stage inside K is full,
+    // and the loads of the one or two stages past the end (issued by the last
+    // tails) are range-checked reads that land in slots no MFMA reads again.
     constexpr int NQ = FM * FN;
     constexpr int NF = FM + FN;
     auto kstep = [&](auto curc, auto nextc, auto rksc, auto loadsc, int64_t dst)
@@ -1077,12 +1097,17 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_direct16(GemmArgs p) {
         constexpr int nl = LOADS ? L : 0;
         const uint32_t dslot = lds_base + (uint32_t)((dst & 1) * SLOT * 16);
         sgpr4 rsa = {}, rsb = {};
-        int left = BK;
+        typename OpA::KMask ma = {};
+        typename OpB::KMask mb = {};
         if constexpr (LOADS) {
             const int64_t ao = a_tile + dst * a_kstep, bo = b_tile + dst * b_kstep;
             rsa = opa.stage_rsrc(Ab + ao, (p.extent_a - ao) * 2);
             rsb = opb.stage_rsrc(Bb + bo, (p.extent_b - bo) * 2);
-            if constexpr (AK || BKC) left = OpA::stage_left(dst * BK, p.K);
+            if constexpr (!KFULL && (AK || BKC)) {
+                const int left = OpA::stage_left(dst * BK, p.K);
+                if constexpr (AK) ma = opa.kmask(left);
+                if constexpr (BKC) mb = opb.kmask(left);
+            }
         }
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
@@ -1091,10 +1116,10 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_direct16(GemmArgs p) {
 #pragma unroll
             for (int l = q * nl / NQ; l < (q + 1) * nl / NQ; ++l) {
                 if (l < OpA::PER_WAVE) {
-                    if constexpr (AK) opa.issue_one(l, rsa, dslot, wave, left);
+                    if constexpr (AK && !KFULL) opa.issue_one_masked(l, rsa, dslot, wave, ma);
                     else opa.issue_one_full(l, rsa, dslot, wave);
                 } else {
-                    if constexpr (BKC) opb.issue_one(l - OpA::PER_WAVE, rsb, dslot + A_CH * 16, wave, left);
+                    if constexpr (BKC && !KFULL) opb.issue_one_masked(l - OpA::PER_WAVE, rsb, dslot + A_CH * 16, wave, mb);
                     else opb.issue_one_full(l - OpA::PER_WAVE, rsb, dslot + A_CH * 16, wave);
                 }
             }
@@ -1275,10 +1300,10 @@ constexpr KernelFn pick_staged() {
                        kTiles[T].wgn, AK, BKC, VEC>;
 }
 
-template <int T, bool AK, bool BKC>
+template <int T, bool AK, bool BKC, bool KFULL = false>
 constexpr KernelFn pick_direct16() {
     return gemm_direct16<kTiles[T].bm, kTiles[T].bn, kTiles[T].bk, kTiles[T].wgm,
-                         kTiles[T].wgn, kTiles[T].stages, AK, BKC>;
+                         kTiles[T].wgn, kTiles[T].stages, AK, BKC, KFULL>;
 }
 
 template <int T, bool AK, bool BKC>
@@ -1325,7 +1350,13 @@ void fill_stream(KernelFn (&t)[2][2][2]) {
 
 struct KernelTable {
     KernelFn k[NUM_TILES][2][2][2];
+    KernelFn kfull[2][2];   // TILE_256x256 when K is a multiple of its BK
     KernelTable() {
+        static_assert(kTiles[TILE_256x256].kind == KIND_DIRECT16, "K-full variants are direct16");
+        kfull[0][0] = pick_direct16<TILE_256x256, false, false, true>();
+        kfull[0][1] = pick_direct16<TILE_256x256, false, true, true>();
+        kfull[1][0] = pick_direct16<TILE_256x256, true, false, true>();
+        kfull[1][1] = pick_direct16<TILE_256x256, true, true, true>();
         fill_tile<TILE_256x256>(k[TILE_256x256]);
         fill_tile<TILE_128x128>(k[TILE_128x128]);
         fill_tile<TILE_64x64>(k[TILE_64x64]);
@@ -1396,6 +1427,7 @@ extern "C" int gemm_f16f32_run(gemm_f16f32_plan_t plan, const void *A,
     const int ak = p.layout_a == GEMM_ROW_MAJOR;   // A K-contiguous
     const int bkc = p.layout_b == GEMM_COL_MAJOR;  // B K-contiguous
     KernelFn fn = kernels().k[tile][ak][bkc][vec ? 1 : 0];
+    if (tile == TILE_256x256 && p.K % kTiles[tile].bk == 0) fn = kernels().kfull[ak][bkc];
     if (!fn) return GEMM_ERR_UNSUPPORTED;
     void *args[] = {&a};
     const unsigned threads = ts.kind == KIND_STREAM ? 512u : (unsigned)(64 * ts.wgm * ts.wgn);
