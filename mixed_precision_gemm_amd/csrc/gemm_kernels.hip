@@ -90,6 +90,19 @@ __device__ __host__ constexpr int swz(int row) {
     }
 }
 
+// Chunk XOR for 128-byte K rows read as 16 x 16 x 32 fragments (16 rows at
+// four K chunks per instruction).  ds_read_b128 serves 16 lanes a pass,
+// lanes i..i+7 together with i+32..i+39: eight rows at two chunks two apart.
+// Row bits (1, 3, 2) become chunk bits (0, 1, 2): within every 8-row group
+// the even (and the odd) rows take one XOR from each class {c, c^2}, and
+// across 16 rows all eight values, so each pass touches 64 distinct banks.
+// A 64-bank model fitted to the counter (zero for the 32-row reads above,
+// two-way for this read pattern under swz<8>) gives zero conflicts for this
+// form.  It depends on row % 16 only.
+__device__ __host__ constexpr int swz16(int row) {
+    return ((row >> 1) & 1) | (((row >> 3) & 1) << 1) | (((row >> 2) & 1) << 2);
+}
+
 // Transposes an 8 x 8 block of fp16: in[c] holds row c (8 elements along the
 // contiguous dimension), out[e] receives column e (8 elements, one per row).
 __device__ inline void transpose8x8(const u32x4 in[8], u32x4 out[8]) {
@@ -608,7 +621,7 @@ __device__ inline void store_tile_lds(const GemmArgs &p, const AccT (&acc)[FM][F
     }
 }
 
-template <int R, int BK, int NW, bool KC>
+template <int R, int BK, int NW, bool KC, bool S16 = false>
 struct DirectOperand {
     static constexpr int VPR = BK / 8;                 // chunks per [r][k] row
     static constexpr int CPR = R / 8;                  // chunks per [k][r] row
@@ -629,7 +642,7 @@ struct DirectOperand {
             bool ok;
             int kin;
             if constexpr (KC) {
-                const int r = p / VPR, c = (p % VPR) ^ swz<VPR>(r);
+                const int r = p / VPR, c = (p % VPR) ^ (S16 ? swz16(r) : swz<VPR>(r));
                 off[i] = (uint32_t)((r * ld + c * 8) * 2);
                 kin = c * 8;
                 ok = r0 + r < rtot;
@@ -654,20 +667,19 @@ struct DirectOperand {
         return make_rsrc_words(base, bytes_left);
     }
     // For K-contiguous 128-byte rows the K index of load i depends on i only
-    // through (i NW + wave) % 8, i.e. on i % KCL: the K test of a stage needs
-    // KCL compares (kmask) and one select per load (issue_one_masked).
-    static constexpr int KCL = NW % 8 == 0 ? 1 : NW % 4 == 0 ? 2 : NW % 2 == 0 ? 4 : 8;
-    struct KMask { bool ok[KCL]; };
-    __device__ KMask kmask(int left) const {
-        static_assert(KC && VPR == 8, "classes derived for K-contiguous 128-byte rows");
-        KMask m;
-#pragma unroll
-        for (int c = 0; c < KCL; ++c)
-            m.ok[c] = (int)((kin4[c / 4] >> (8 * (c % 4))) & 0xffu) < left;
-        return m;
+    // through (i NW + wave) % 8 (swz<8>) or (i NW + wave) % 2 (swz16), i.e.
+    // on i % KCL: the K test of a stage needs KCL compares (kmask) and one
+    // select per load (issue_one_masked).
+    static constexpr int KCL = S16 ? (NW % 2 == 0 ? 1 : 2)
+                                   : (NW % 8 == 0 ? 1 : NW % 4 == 0 ? 2 : NW % 2 == 0 ? 4 : 8);
+    // With one class (swz16 and an even number of loading waves) the test is
+    // a single compare per stage.
+    __device__ bool kmask(int left) const {
+        static_assert(KC && VPR == 8 && KCL == 1, "one K class");
+        return (int)(kin4[0] & 0xffu) < left;
     }
-    __device__ void issue_one_masked(int i, sgpr4 rs, uint32_t lds_addr, int wave, const KMask &m) const {
-        lds_dma16(rs, lds_addr + (uint32_t)((i * NW + wave) * 64 * 16), m.ok[i % KCL] ? off[i] : kOutOfRange);
+    __device__ void issue_one_masked(int i, sgpr4 rs, uint32_t lds_addr, int wave, bool ok) const {
+        lds_dma16(rs, lds_addr + (uint32_t)((i * NW + wave) * 64 * 16), ok ? off[i] : kOutOfRange);
     }
 
     // Load i of a stage that lies wholly inside K: no K test.
@@ -708,31 +720,6 @@ struct DirectOperand {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const int k = 16 * s + 8 * (g4 >> 1) + 4 * t + (j >> 2);
-                const int addr = k * R * 2 + (((n >> 3) ^ mn_swz<R>(k)) << 4) + (n & 7) * 2;
-                h[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) v4i16 *)(bytes + addr));
-            }
-            const v4i16 lo = h[0], hi = h[1];
-            return __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-    }
-
-    // Fragment of the 16 x 16 x 32 MFMA for the 16-row block starting at rb,
-    // K step s (32 deep): lane l receives row rb + l%16,
-    // k = 32 s + 8 (l/16) + 0..7.
-    __device__ half8 frag16(const u32x4 *lds, int rb, int s, int lane) const {
-        if constexpr (KC) {
-            const int r = rb + (lane & 15);
-            const int kv = 4 * s + (lane >> 4);
-            return __builtin_bit_cast(half8, lds[r * VPR + (kv ^ swz<VPR>(r))]);
-        } else {
-            const int g4 = lane >> 4, j = lane & 15;
-            const int n = rb + 4 * (j & 3);
-            const char *bytes = (const char *)lds;
-            v4i16 h[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int k = 32 * s + 8 * g4 + 4 * t + (j >> 2);
                 const int addr = k * R * 2 + (((n >> 3) ^ mn_swz<R>(k)) << 4) + (n & 7) * 2;
                 h[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (__attribute__((address_space(3))) v4i16 *)(bytes + addr));
@@ -931,8 +918,8 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_direct(GemmArgs p) {
 // XOR per register (advance()) and no other address arithmetic is left in
 // the K loop.
 //   K-contiguous: row r = wb + 16 i + l%16 keeps its K chunk kv = 4 s + l/16
-//     at kv ^ swz(r).  With wb a multiple of 64 that is X ^ (4 s ^ (2 i & 6)),
-//     X = (l/16) ^ (l%16 & 7) ^ (l%16 >> 3): four bases, by (2 i & 6) ^ 4 s.
+//     at kv ^ swz16(r) = (l/16 ^ swz16(l%16)) ^ 4 s (swz16 depends on r % 16
+//     only): two bases, by s, and 16 rows per block as immediates.
 //   MN-contiguous: column n = wb + 16 i + 4 (l%4) of row
 //     k = 32 s + 4 t + 8 (l/16) + (l%16)/4 sits in chunk (n >> 3) ^ mn_swz(k),
 //     and mn_swz(k) depends only on k%4 and bit 3 of k, both fixed by the
@@ -941,17 +928,17 @@ template <int R, int BK, bool KC, int NBLK, int SLOT_BYTES>
 struct Frag16 {
     static_assert(BK == 64, "128-byte K rows");
     static_assert(SLOT_BYTES == 65536, "slots 64 KiB apart: advance() flips bit 16");
-    static constexpr int NCLS = KC ? 4 : NBLK;
+    static constexpr int NCLS = KC ? 2 : NBLK;
     uint32_t cur[NCLS], nxt[NCLS];
 
     // Bases for stage 0 (slot 0) in cur and stage 1 (slot 1) in nxt.
     __device__ void setup(int lane, int wb, uint32_t region) {
         const int lr = lane & 15, lg = lane >> 4;
         if constexpr (KC) {
-            const int X = lg ^ (lr & 7) ^ (lr >> 3);
+            const int X = lg ^ swz16(lr);
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                cur[c] = region + (uint32_t)((wb + lr) * BK * 2 + 16 * (X ^ (2 * c)));
+            for (int c = 0; c < 2; ++c)
+                cur[c] = region + (uint32_t)((wb + lr) * BK * 2 + 16 * (X ^ (4 * c)));
         } else {
             const int W = ((lr & 3) >> 1) ^ mn_swz<R>(8 * lg + (lr >> 2));
 #pragma unroll
@@ -979,8 +966,7 @@ struct Frag16 {
         const char *bytes = (const char *)lds;
         const uint32_t *b = NEXT ? nxt : cur;
         if constexpr (KC) {
-            const int c = (((2 * i) & 6) ^ (4 * s)) >> 1;
-            return __builtin_bit_cast(half8, *(const u32x4 *)(bytes + b[c] + 16 * BK * 2 * i));
+            return __builtin_bit_cast(half8, *(const u32x4 *)(bytes + b[s] + 16 * BK * 2 * i));
         } else {
             v4i16 h[2];
 #pragma unroll
@@ -1023,8 +1009,8 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_direct16(GemmArgs p) {
     constexpr int NKS = BK / 32;
     constexpr int A_CH = BM * BK / 8, B_CH = BN * BK / 8;
     constexpr int SLOT = A_CH + B_CH;                 // 16-byte chunks per slot
-    using OpA = DirectOperand<BM, BK, NW, AK>;
-    using OpB = DirectOperand<BN, BK, NW, BKC>;
+    using OpA = DirectOperand<BM, BK, NW, AK, true>;
+    using OpB = DirectOperand<BN, BK, NW, BKC, true>;
     constexpr int L = OpA::PER_WAVE + OpB::PER_WAVE;  // loads per lane per stage
     static_assert(S == 2, "the schedule is a two-slot ring");
     static_assert(NKS == 2, "head and tail are one K step each");
@@ -1068,7 +1054,7 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_direct16(GemmArgs p) {
         opb.issue(Bb + bo, (p.extent_b - bo) * 2, slot + A_CH * 16, wave, st * BK, p.K);
     };
 
-    static_assert(WTM % 64 == 0 && WTN % 64 == 0, "fragment base classes need 64-aligned wave tiles");
+    static_assert(WTM % 16 == 0 && WTN % 16 == 0, "16-row fragment blocks");
     Frag16<BM, BK, AK, FM, SLOT * 16> fra;
     Frag16<BN, BK, BKC, FN, SLOT * 16> frb;
     fra.setup(lane, wm * WTM, 0);
@@ -1097,8 +1083,7 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_direct16(GemmArgs p) {
         constexpr int nl = LOADS ? L : 0;
         const uint32_t dslot = lds_base + (uint32_t)((dst & 1) * SLOT * 16);
         sgpr4 rsa = {}, rsb = {};
-        typename OpA::KMask ma = {};
-        typename OpB::KMask mb = {};
+        bool ma = true, mb = true;
         if constexpr (LOADS) {
             const int64_t ao = a_tile + dst * a_kstep, bo = b_tile + dst * b_kstep;
             rsa = opa.stage_rsrc(Ab + ao, (p.extent_a - ao) * 2);
