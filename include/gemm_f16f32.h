@@ -36,12 +36,18 @@
  * A column-major C is obtained by the caller by swapping operands
  * (C^T = B^T A^T).
  *
- * Ownership: the caller owns A, B, C and the stream.  A plan owns host
- * memory only (no device memory, no scratch), is immutable after creation,
- * and may be run concurrently on several streams.  gemm_f16f32_run is
+ * Ownership: the caller owns A, B, C and the stream.  A plan owns its host
+ * memory and, if it cuts K into slices (split-K: its kernel name ends in
+ * "_sk<slices>"), a device workspace of fp32 partial tiles (slices x tiles x
+ * 64 KiB, plus 4 bytes per tile), allocated and cleared on the current device
+ * by the plan's first run and freed by gemm_f16f32_destroy.  Runs of one
+ * split-K plan share that workspace: they may follow each other on a stream
+ * but must not execute concurrently (on two streams at once); any other plan
+ * may be run concurrently on several streams.  gemm_f16f32_run is
  * asynchronous on the given stream: A, B, C must stay valid until the stream
- * has passed the launched kernel.  The launch copies what it needs from the
- * plan, so a plan may be destroyed as soon as gemm_f16f32_run returns.
+ * has passed the launched kernel.  A plan may be destroyed as soon as
+ * gemm_f16f32_run returns; destroying a plan that holds a workspace first
+ * waits for the device to finish its work.
  *
  * Errors: every function returns a status code (GEMM_OK == 0 or a negative
  * GEMM_ERR_*); no exception crosses this boundary and there is no global
@@ -67,7 +73,7 @@ enum {
     GEMM_ERR_INVALID_ARG = -1,  /* argument violates a rule stated below    */
     GEMM_ERR_UNSUPPORTED = -2,  /* valid but outside what the kernels cover */
     GEMM_ERR_HIP = -3,          /* the HIP runtime refused the launch       */
-    GEMM_ERR_NOMEM = -4         /* host allocation for the plan failed      */
+    GEMM_ERR_NOMEM = -4         /* host or workspace allocation failed      */
 };
 
 /*
@@ -109,13 +115,17 @@ int gemm_f16f32_plan(gemm_f16f32_plan_t *out,
  * of C must not overlap those of A or B -> INVALID_ARG.  Pointer alignment is
  * never an error: 16-byte-aligned operands whose leading dimensions are
  * multiples of 8 take the 128-bit load path, others a narrow-load path with
- * the same results up to summation order.  A failed launch -> GEMM_ERR_HIP.
+ * the same results up to summation order (the narrow path does not split
+ * K).  A split-K plan's first run allocates its workspace (failure -> NOMEM)
+ * and synchronises the device once; running it later on another device than
+ * that first run's -> INVALID_ARG.  A failed launch -> GEMM_ERR_HIP.
  */
 int gemm_f16f32_run(gemm_f16f32_plan_t plan,
                     const void *A, const void *B, void *C,
                     float alpha, float beta, void *stream);
 
-/* Frees a plan.  NULL is a no-op.  Returns GEMM_OK. */
+/* Frees a plan (and its workspace, after waiting for the device to finish
+ * its work).  NULL is a no-op.  Returns GEMM_OK. */
 int gemm_f16f32_destroy(gemm_f16f32_plan_t plan);
 
 /* A static, NUL-terminated description of a status code (never NULL). */

@@ -19,7 +19,8 @@ enum TileId : int {
     TILE_STREAM16 = 5,       // skinny M <= 16, K-contiguous A and B
     TILE_STREAM32 = 6,       // skinny M <= 32
     TILE_STREAM64 = 7,       // skinny M <= 64
-    NUM_TILES = 8
+    TILE_STREAM128 = 8,      // skinny M <= 128
+    NUM_TILES = 9
 };
 
 // Two kernel families share the tile table:
@@ -46,6 +47,7 @@ constexpr TileShape kTiles[NUM_TILES] = {
     {16, 16, 32, 1, 1, 1, KIND_STREAM, "stream16x16"},
     {32, 16, 32, 1, 1, 1, KIND_STREAM, "stream32x16"},
     {64, 16, 32, 1, 1, 1, KIND_STREAM, "stream64x16"},
+    {128, 16, 32, 1, 1, 1, KIND_STREAM, "stream128x16"},
 };
 
 // Tile of the staged kernel that serves operands the direct kernel cannot
@@ -68,5 +70,10 @@ struct gemm_f16f32_plan_s {
     int vec_ok;            // shapes allow 128-bit loads (pointers checked at run)
     int group_m;           // tile rows per rasterisation group
     int64_t extent_a, extent_b, extent_c;  // elements spanned by each operand
+    int ksplit;            // K slices per output tile (split-K when > 1)
+    int64_t kchunk;        // K indices per slice, a multiple of 64
+    int64_t ws_bytes;      // workspace: ksplit * tiles fp32 partial tiles + tile counters
+    void *ws;              // device workspace, allocated by the first split-K run
+    int ws_device;         // device that holds ws
     char kernel_name[64];
 };

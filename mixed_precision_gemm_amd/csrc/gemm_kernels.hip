@@ -66,7 +66,26 @@ struct GemmArgs {
     int total_tiles;
     int out_f32;
     int c_vec;                    // C rows allow 4-element vector access
+    // Split-K (direct 128 x 128 tile only): K is cut into ksplit slices of
+    // kchunk indices; grid = total_tiles * ksplit, block id = slice *
+    // total_tiles + tile.  ws holds one fp32 partial tile per (slice, tile),
+    // ws_count one arrival counter per tile (zero between launches).
+    int ksplit;
+    int64_t kchunk;
+    float *ws;
+    int *ws_count;
 };
+
+// Restricts the arguments to K slice `slice` (split-K): operands advance by
+// the slice's first K index, K shrinks to the slice.
+__device__ inline void apply_k_slice(GemmArgs &p, int slice, bool a_kc, bool b_kc) {
+    const int64_t k0 = (int64_t)slice * p.kchunk;
+    const int64_t kc = p.K - k0 < p.kchunk ? p.K - k0 : p.kchunk;
+    const int64_t da = a_kc ? k0 : k0 * p.lda, db = b_kc ? k0 : k0 * p.ldb;
+    p.A += da; p.extent_a -= da;
+    p.B += db; p.extent_b -= db;
+    p.K = kc;
+}
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
     const int32_t n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int32_t)bytes);
@@ -621,6 +640,115 @@ __device__ inline void store_tile_lds(const GemmArgs &p, const AccT (&acc)[FM][F
     }
 }
 
+// Split-K epilogue ([GEMM] §4.4's epilogue, applied once per output after
+// the K slices are summed).  Every workgroup stages its raw fp32 accumulators
+// through the drained LDS ring and writes them, row by row, as the partial
+// tile (slice, tile) of the workspace; then it fences and counts itself on
+// the tile's counter.  The last to arrive sums the slices in slice order
+// 0..ksplit-1 -- a fixed order, so results do not depend on which slice
+// finished last -- applies alpha * sum + beta * C, rounds once, stores C, and
+// resets the counter for the next launch.
+template <typename T, int BM, int BN, int WGM, int WGN, int LDS_BYTES, int MB,
+          typename AccT, int FM, int FN>
+__device__ inline void store_tile_splitk(const GemmArgs &p, const AccT (&acc)[FM][FN],
+                                         u32x4 *lds, int tile, int slice, int b,
+                                         int64_t m0, int64_t n0, int wave, int lane) {
+    constexpr int WTM = BM / WGM, WTN = BN / WGN;
+    constexpr int NW = WGM * WGN;
+    constexpr int GPR = BN / 4;
+    constexpr int RPI = 64 / GPR;
+    constexpr int IT = BM / (RPI * NW);
+    constexpr int SW = GPR >= 16 ? 15 : GPR - 1;
+    static_assert(BM * BN * 4 <= LDS_BYTES, "one staging pass");
+    static_assert(FM * MB == WTM && FN * MB == WTN, "accumulator shape");
+    static_assert(GPR <= 64 && 64 % GPR == 0 && BM % (RPI * NW) == 0, "row mapping");
+    const int wm = wave / WGN, wn = wave % WGN;
+    char *base = (char *)lds;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int rl = wm * WTM + i * MB + (lane % MB);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < MB * MB / 256; ++q) {
+                const int gr = (wn * WTN + j * MB) / 4 + (MB == 32 ? 2 * q + (lane >> 5) : (lane >> 4));
+                const floatx4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                *(floatx4 *)(base + rl * BN * 4 + ((gr ^ (rl & SW)) << 4)) = v;
+            }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+    barrier();
+    const int r_in = lane / GPR, g = lane % GPR;
+    const int64_t tile_elems = (int64_t)BM * BN;
+    // Partials bypass the per-XCD L2 (cache policy sc0 sc1: written through
+    // to memory and read from there), so the slices of a tile may run on
+    // different XCDs without an L2-wide write-back or invalidate.
+    constexpr int kCoherent = 1 | 16;
+    const __amdgpu_buffer_rsrc_t rws = make_rsrc(p.ws, (int64_t)p.ksplit * p.total_tiles * tile_elems * 4);
+    const uint32_t mine = (uint32_t)(((int64_t)slice * p.total_tiles + tile) * tile_elems * 4);
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int r = (it * NW + wave) * RPI + r_in;
+        const u32x4 v = *(const u32x4 *)(base + r * BN * 4 + ((g ^ (r & SW)) << 4));
+        __builtin_amdgcn_raw_buffer_store_b128(v, rws, mine + (uint32_t)((r * BN + 4 * g) * 4), 0, kCoherent);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");   // this lane's partial is in memory
+    __syncthreads();
+    __shared__ int last_flag;
+    if (threadIdx.x == 0)
+        last_flag = __hip_atomic_fetch_add(&p.ws_count[tile], 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT) == p.ksplit - 1;
+    __syncthreads();
+    if (!last_flag) return;
+    const float alpha = p.alpha, beta = p.beta;
+    const int64_t n = n0 + 4 * g;
+    const bool n_ok = n < p.N;
+    const bool vec = p.c_vec && n + 4 <= p.N;
+    const uint32_t tile0 = (uint32_t)((int64_t)tile * tile_elems * 4);
+    const uint32_t slice_stride = (uint32_t)((int64_t)p.total_tiles * tile_elems * 4);
+    // All slices of RB row groups (and their C) are requested before any is
+    // summed: the partials come from memory, so the reduction is latency
+    // bound unless many loads are in flight.  Slices are summed in order.
+    constexpr int KSMAX = 8, RB = 2;
+    static_assert(IT % RB == 0, "row batches");
+#pragma unroll 1
+    for (int it0 = 0; it0 < IT; it0 += RB) {
+        floatx4 part[RB][KSMAX];
+        c4_t<T> cv[RB];
+#pragma unroll
+        for (int u = 0; u < RB; ++u) {
+            const int r = ((it0 + u) * NW + wave) * RPI + r_in;
+            const int64_t m = m0 + r;
+#pragma unroll
+            for (int sl = 0; sl < KSMAX; ++sl)
+                part[u][sl] = sl < p.ksplit
+                    ? __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+                          rws, tile0 + (uint32_t)sl * slice_stride + (uint32_t)((r * BN + 4 * g) * 4), 0, kCoherent))
+                    : floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+            cv[u] = (beta != 0.0f && m < p.M && n_ok) ? load_c4<T>(p, b * p.sc + m * p.ldc + n, n, vec) : c4_t<T>{};
+        }
+#pragma unroll
+        for (int u = 0; u < RB; ++u) {
+            const int r = ((it0 + u) * NW + wave) * RPI + r_in;
+            const int64_t m = m0 + r;
+            floatx4 sum = part[u][0];
+#pragma unroll
+            for (int sl = 1; sl < KSMAX; ++sl)
+                if (sl < p.ksplit) sum += part[u][sl];
+            if (m < p.M && n_ok) {
+                floatx4 v = alpha * sum;
+                if (beta != 0.0f) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] += beta * (float)cv[u][e];
+                }
+                store_c4<T>(p, b * p.sc + m * p.ldc + n, n, vec, v);
+            }
+        }
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&p.ws_count[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int R, int BK, int NW, bool KC, bool S16 = false>
 struct DirectOperand {
     static constexpr int VPR = BK / 8;                 // chunks per [r][k] row
@@ -732,7 +860,8 @@ struct DirectOperand {
 
 template <int BM, int BN, int BK, int WGM, int WGN, int S, bool AK, bool BKC>
 __global__ __launch_bounds__(64 * WGM * WGN)
-__attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_direct(GemmArgs p) {
+__attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_direct(GemmArgs pin) {
+    GemmArgs p = pin;
     constexpr int NW = WGM * WGN;
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -753,8 +882,11 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_direct(GemmArgs p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WGN, wn = wave % WGN;
 
+    const int slice = (int)(blockIdx.x / (unsigned)p.total_tiles);
+    const int tile = (int)(blockIdx.x - (unsigned)slice * (unsigned)p.total_tiles);
+    if (p.ksplit > 1) apply_k_slice(p, slice, AK, BKC);
     int b, tm, tn;
-    tile_coords(p, blockIdx.x, b, tm, tn);
+    tile_coords(p, tile, b, tm, tn);
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const _Float16 *Ab = p.A + b * p.sa;
     const _Float16 *Bb = p.B + b * p.sb;
@@ -896,6 +1028,13 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_direct(GemmArgs p) {
     asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
     barrier();
 
+    if (p.ksplit > 1) {
+        if (p.out_f32)
+            store_tile_splitk<float, BM, BN, WGM, WGN, S * SLOT * 16, 32>(p, acc, lds, tile, slice, b, m0, n0, wave, lane);
+        else
+            store_tile_splitk<_Float16, BM, BN, WGM, WGN, S * SLOT * 16, 32>(p, acc, lds, tile, slice, b, m0, n0, wave, lane);
+        return;
+    }
     const bool full = p.c_vec && m0 + BM <= p.M && n0 + BN <= p.N;
     if (p.out_f32) {
         if (full)
@@ -1350,6 +1489,7 @@ struct KernelTable {
         fill_stream<TILE_STREAM16>(k[TILE_STREAM16]);
         fill_stream<TILE_STREAM32>(k[TILE_STREAM32]);
         fill_stream<TILE_STREAM64>(k[TILE_STREAM64]);
+        fill_stream<TILE_STREAM128>(k[TILE_STREAM128]);
     }
 };
 
@@ -1408,6 +1548,34 @@ extern "C" int gemm_f16f32_run(gemm_f16f32_plan_t plan, const void *A,
     a.total_tiles = (int)(tiles_m * tiles_n * p.batch);
     a.out_f32 = p.out_type == GEMM_OUT_F32;
     a.c_vec = c_vec;
+    a.ksplit = 1;
+    a.kchunk = p.K;
+    a.ws = nullptr;
+    a.ws_count = nullptr;
+    if (tile == p.tile && p.ksplit > 1) {
+        // The workspace is allocated and its counters cleared on the plan's
+        // first split-K run; they return to zero at the end of every launch.
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
+        if (plan->ws && plan->ws_device != dev) return GEMM_ERR_INVALID_ARG;
+        if (!plan->ws) {
+            void *ws = nullptr;
+            if (hipMalloc(&ws, (size_t)p.ws_bytes) != hipSuccess) return GEMM_ERR_NOMEM;
+            const int64_t partial = p.ws_bytes - a.total_tiles * 4;
+            // Cleared before any stream can use it (a one-time synchronisation).
+            if (hipMemset((char *)ws + partial, 0, (size_t)a.total_tiles * 4) != hipSuccess ||
+                hipDeviceSynchronize() != hipSuccess) {
+                (void)hipFree(ws);
+                return GEMM_ERR_HIP;
+            }
+            plan->ws = ws;
+            plan->ws_device = dev;
+        }
+        a.ksplit = p.ksplit;
+        a.kchunk = p.kchunk;
+        a.ws = (float *)plan->ws;
+        a.ws_count = (int *)((char *)plan->ws + (p.ws_bytes - a.total_tiles * 4));
+    }
 
     const int ak = p.layout_a == GEMM_ROW_MAJOR;   // A K-contiguous
     const int bkc = p.layout_b == GEMM_COL_MAJOR;  // B K-contiguous
@@ -1416,7 +1584,7 @@ extern "C" int gemm_f16f32_run(gemm_f16f32_plan_t plan, const void *A,
     if (!fn) return GEMM_ERR_UNSUPPORTED;
     void *args[] = {&a};
     const unsigned threads = ts.kind == KIND_STREAM ? 512u : (unsigned)(64 * ts.wgm * ts.wgn);
-    hipError_t e = hipLaunchKernel((const void *)fn, dim3((unsigned)a.total_tiles),
+    hipError_t e = hipLaunchKernel((const void *)fn, dim3((unsigned)a.total_tiles * (unsigned)a.ksplit),
                                    dim3(threads), args, 0,
                                    (hipStream_t)stream);
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;

@@ -10,6 +10,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
+#include <hip/hip_runtime.h>
 #include <new>
 
 #include "gemm_f16f32.h"
@@ -36,7 +38,7 @@ int64_t operand_extent(int64_t rows, int64_t cols, int64_t ld, int64_t batch,
 // the 128 x 128 tile (two workgroups per CU) a quarter of one; otherwise the
 // small staged tiles, the 32-row one for skinny M (token counts of a linear
 // layer).
-int choose_tile(int64_t M, int64_t N, int64_t batch, bool kc_both) {
+int choose_tile(int64_t M, int64_t N, int64_t K, int64_t batch, bool kc_both, bool vec_ok) {
     // Skinny M with K-contiguous A and B streams B through registers; at
     // most 64 rows of A are reused per loaded column of B.
     if (kc_both && M <= 64) return M <= 16 ? TILE_STREAM16 : M <= 32 ? TILE_STREAM32 : TILE_STREAM64;
@@ -50,8 +52,33 @@ int choose_tile(int64_t M, int64_t N, int64_t batch, bool kc_both) {
     };
     if (count(TILE_256x256) >= kNumCUs && fill(TILE_256x256) >= 0.8) return TILE_256x256;
     if (count(TILE_128x128) >= kNumCUs / 4 && fill(TILE_128x128) >= 0.6) return TILE_128x128;
+    // Too few tiles to fill the CUs but enough K to cut: the 128 tile with
+    // split-K (choose_ksplit) moves each operand byte once with 256+ workgroups.
+    if (vec_ok && batch == 1 && K >= 1024 && count(TILE_128x128) < kNumCUs) return TILE_128x128;
     if (M <= 32) return TILE_32x64;
     return TILE_64x64;
+}
+
+// K slices for the direct 128 tile: enough workgroups to cover the CUs, each
+// slice at least 512 deep and a multiple of the 64-deep stage, at most 8
+// slices and 1024 workgroups.  Tiles that already fill a quarter of the CUs
+// (two workgroups per CU) are cut only when K is deep: the partial tiles and
+// their reduction cost more than they gain at K ~ 1024 (measured at 1024^3).
+void choose_ksplit(gemm_f16f32_plan_s *p, int64_t tiles) {
+    p->ksplit = 1;
+    p->kchunk = p->K;
+    if (p->tile != TILE_128x128 || !p->vec_ok || p->batch != 1 || tiles >= kNumCUs) return;
+    if (tiles >= kNumCUs / 4 && p->K < 2048) return;
+    int64_t ks = ceil_div(kNumCUs, tiles);
+    ks = std::min<int64_t>(ks, p->K / 512);
+    ks = std::min<int64_t>(ks, 8);
+    ks = std::min<int64_t>(ks, 1024 / tiles);
+    if (ks < 2) return;
+    const int64_t chunk = ceil_div(ceil_div(p->K, ks), 64) * 64;
+    p->kchunk = chunk;
+    p->ksplit = (int)ceil_div(p->K, chunk);
+    if (p->ksplit < 2) { p->ksplit = 1; p->kchunk = p->K; return; }
+    p->ws_bytes = (int64_t)p->ksplit * tiles * 128 * 128 * 4 + tiles * 4;
 }
 
 }  // namespace
@@ -118,7 +145,7 @@ extern "C" int gemm_f16f32_plan(gemm_f16f32_plan_t *out, int64_t M, int64_t N,
     p->vec_ok = (contig_a % 8 == 0) && (lda % 8 == 0) && (stride_a % 8 == 0) &&
                 (contig_b % 8 == 0) && (ldb % 8 == 0) && (stride_b % 8 == 0);
     const bool kc_both = layout_a == GEMM_ROW_MAJOR && layout_b == GEMM_COL_MAJOR;
-    p->tile = choose_tile(M, N, batch, kc_both);
+    p->tile = choose_tile(M, N, K, batch, kc_both, p->vec_ok);
     // Unaligned shapes go to the staged kernel, whose largest tile is 128.
     const int t = p->vec_ok ? p->tile : narrow_tile(p->tile);
     for (int cand : {p->tile, narrow_tile(p->tile)}) {
@@ -129,16 +156,27 @@ extern "C" int gemm_f16f32_plan(gemm_f16f32_plan_t *out, int64_t M, int64_t N,
         }
     }
     p->group_m = 4;
-    snprintf(p->kernel_name, sizeof p->kernel_name, "gemm_%s_%c%c_%s",
+    choose_ksplit(p, ceil_div(M, kTiles[p->tile].bm) * ceil_div(N, kTiles[p->tile].bn) * batch);
+    char split[16] = "";
+    if (p->ksplit > 1) snprintf(split, sizeof split, "_sk%d", p->ksplit);
+    snprintf(p->kernel_name, sizeof p->kernel_name, "gemm_%s_%c%c_%s%s",
              kTiles[t].name, layout_a == GEMM_ROW_MAJOR ? 'n' : 't',
              layout_b == GEMM_ROW_MAJOR ? 'n' : 't',
              p->vec_ok ? (kTiles[t].kind == KIND_STAGED ? "vec16" : "direct")
-                       : "narrow");
+                       : "narrow", split);
     *out = p;
     return GEMM_OK;
 }
 
 extern "C" int gemm_f16f32_destroy(gemm_f16f32_plan_t plan) {
+    if (plan && plan->ws) {
+        int cur = 0;
+        const bool swap = hipGetDevice(&cur) == hipSuccess && cur != plan->ws_device;
+        if (swap) (void)hipSetDevice(plan->ws_device);
+        (void)hipDeviceSynchronize();   // no launch of this plan may still use it
+        (void)hipFree(plan->ws);
+        if (swap) (void)hipSetDevice(cur);
+    }
     delete plan;
     return GEMM_OK;
 }

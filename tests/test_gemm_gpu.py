@@ -296,3 +296,70 @@ def test_run_to_run_bitwise_determinism():
         torch.cuda.synchronize()
         outs.append(dC.cpu())
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+# ------------------------------------------------------------- split-K
+
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+def test_split_k_all_layouts(la, lb):
+    """Skinny-M shapes whose 128 tiles cannot fill the CUs take split-K."""
+    M, N, K = 64, 2048, 4096
+    case = gi.make_case(M, N, K, layout_a=la, layout_b=lb, alpha=1.0, beta=1.0, seed=31)
+    p = mpg.Plan(M, N, K, la, lb, OUT_F16, case.lda, case.ldb, case.ldc)
+    kernel = p.kernel
+    p.close()
+    if (la, lb) != (ROW_MAJOR, COL_MAJOR):       # NT with M <= 64 streams instead
+        assert "_sk" in kernel, kernel
+    parity(case, what=f"{kernel} {M}x{N}x{K}")
+
+
+def test_split_k_fp32_ragged_alpha_beta():
+    """Ragged N and a short last K slice (K = 3000 in slices of 384), fp32 C,
+    alpha = 2, beta = -0.5."""
+    M, N, K = 100, 1000, 3000
+    case = gi.make_case(M, N, K, out_type=OUT_F32, alpha=2.0, beta=-0.5, seed=32)
+    p = mpg.Plan(M, N, K, ROW_MAJOR, ROW_MAJOR, OUT_F32, case.lda, case.ldb, case.ldc)
+    assert "_sk" in p.kernel, p.kernel
+    p.close()
+    parity(case, what="split-K fp32 ragged")
+
+
+def test_split_k_repeatable_and_interleaved():
+    """The arrival counters return to zero after every launch: a split-K plan
+    run twice gives the same bits, also with another split-K plan launched in
+    between on the same stream."""
+    c1 = gi.linear_case(128, 4096)
+    c2 = gi.make_case(16, 4096, 4096, seed=33)
+    p1 = mpg.Plan(c1.M, c1.N, c1.K, c1.layout_a, c1.layout_b, c1.out_type, c1.lda, c1.ldb, c1.ldc)
+    p2 = mpg.Plan(c2.M, c2.N, c2.K, c2.layout_a, c2.layout_b, c2.out_type, c2.lda, c2.ldb, c2.ldc)
+    assert "_sk" in p1.kernel and "_sk" in p2.kernel, (p1.kernel, p2.kernel)
+    A1, B1, C1 = to_device(c1)
+    A2, B2, C2 = to_device(c2)
+    outs = []
+    for _ in range(3):
+        C1.zero_()
+        p1.run(A1, B1, C1, c1.alpha, c1.beta)
+        p2.run(A2, B2, C2, c2.alpha, c2.beta)
+        torch.cuda.synchronize()
+        outs.append(C1.clone())
+    p1.close()
+    p2.close()
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+    ref, scale = oracle_for(c1)
+    check_bound(c_logical(c1, outs[0].cpu()), ref, scale, c1.out_type, "split-K repeat")
+    ref2, scale2 = oracle_for(c2)
+    check_bound(c_logical(c2, C2.cpu()), ref2, scale2, c2.out_type, "split-K interleaved")
+
+
+def test_split_k_plan_with_misaligned_pointers_runs_unsplit():
+    M, N, K = 16, 1024, 2048
+    case = gi.make_case(M, N, K, beta=1.0, seed=34)
+    p = mpg.Plan(M, N, K)
+    assert "_sk" in p.kernel, p.kernel
+    p.close()
+    A = torch.zeros(case.A.numel() + 1, dtype=torch.float16, device="cuda")
+    A[1:] = case.A.cuda()
+    B, C = case.B.cuda(), case.C.cuda()
+    run_case(case, A[1:], B, C)
+    ref, scale = oracle_for(case)
+    check_bound(c_logical(case, C.cpu()), ref, scale, OUT_F16, "split-K plan, narrow run")
