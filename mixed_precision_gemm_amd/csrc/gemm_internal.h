@@ -8,8 +8,8 @@ namespace mpgemm {
 
 // Workgroup tile shapes.  BM x BN is the output tile of one workgroup, BK the
 // K depth of one LDS stage, WGM x WGN the grid of 64-lane waves that split the
-// output tile.  Each wave owns (BM/WGM) x (BN/WGN) outputs as 32 x 32 MFMA
-// accumulator blocks.
+// output tile.  Each wave owns (BM/WGM) x (BN/WGN) outputs as MFMA accumulator
+// blocks (16 x 16 in the direct kernels, 32 x 32 in the staged one).
 enum TileId : int {
     TILE_256x256 = 0,        // compute-bound square-ish problems
     TILE_128x128 = 1,        // medium problems: more workgroups to fill 256 CUs
@@ -23,15 +23,15 @@ enum TileId : int {
     NUM_TILES = 9
 };
 
-// Two kernel families share the tile table:
-//   KIND_DIRECT: an S-slot LDS ring filled by direct-to-LDS buffer loads (no
-//                register staging), for 16-byte-aligned operands;
+// Three kernel families share the tile table:
+//   KIND_DIRECT16: a two-slot LDS ring filled by direct-to-LDS buffer loads
+//                (no register staging) and computed with 16 x 16 x 32 MFMAs,
+//                for 16-byte-aligned operands; split-K capable;
 //   KIND_STAGED: a two-slot ring filled through registers (global -> VGPR ->
-//                LDS), used for the small tiles and for the narrow-load path.
-//   KIND_DIRECT16: the direct ring computed with 16 x 16 x 32 MFMAs.
+//                LDS), used for the small tiles and for the narrow-load path;
 //   KIND_STREAM:  skinny M with K-contiguous A and B: fragments loaded from
 //                global memory straight into registers, K split over 8 waves.
-enum KernelKind : int { KIND_DIRECT = 0, KIND_STAGED = 1, KIND_STREAM = 2, KIND_DIRECT16 = 3 };
+enum KernelKind : int { KIND_STAGED = 1, KIND_STREAM = 2, KIND_DIRECT16 = 3 };
 
 struct TileShape {
     int bm, bn, bk, wgm, wgn, stages, kind;
@@ -40,7 +40,7 @@ struct TileShape {
 
 constexpr TileShape kTiles[NUM_TILES] = {
     {256, 256, 64, 2, 2, 2, KIND_DIRECT16, "256x256x64m16"},
-    {128, 128, 64, 2, 2, 2, KIND_DIRECT, "128x128x64s2"},
+    {128, 128, 64, 2, 2, 2, KIND_DIRECT16, "128x128x64m16"},
     {64, 64, 64, 2, 2, 2, KIND_STAGED, "64x64x64"},
     {32, 64, 64, 1, 2, 2, KIND_STAGED, "32x64x64"},
     {128, 128, 64, 2, 2, 2, KIND_STAGED, "128x128x64"},

@@ -8,24 +8,27 @@
 //
 // Structure of one workgroup (the pages' three-level data flow, [CATLASS] §2.2
 // and [GEMM] §3, rebuilt for CDNA4):
-//   * it owns one BM x BN tile of C ([GEMM] §3.1, [CATLASS] §2.1) and walks K in
-//     steps of BK, keeping the fp32 accumulators in registers for the whole K
-//     loop ([GEMM] §3.2, §6.2);
+//   * it owns one BM x BN tile of C ([GEMM] §3.1, [CATLASS] §2.1) -- or, with
+//     split-K, one K slice of it -- and walks K in steps of BK, keeping the
+//     fp32 accumulators in registers for the whole K loop ([GEMM] §3.2, §6.2);
 //   * each K step stages an A tile (BM x BK) and a B tile (BK x BN) from global
-//     memory into one slot of a two-slot LDS ring with 128-bit buffer loads
-//     ([OPS] §3.5, [GEMM] §4.1); the loads for step k+1 are issued before the
-//     MFMAs of step k and written to the other slot after them ([GEMM] §5.1,
-//     §5.4: issue the future, wait for the past);
+//     memory into one slot of a two-slot LDS ring ([OPS] §3.5, [GEMM] §4.1):
+//     the direct kernels (gemm_direct16) use buffer loads that write LDS
+//     without passing through registers, the staged kernel (gemm_staged)
+//     128-bit loads through registers; the loads for a later step are issued
+//     among the MFMAs of the current one ([GEMM] §5.1, §5.4: issue the
+//     future, wait for the past);
 //   * out-of-range elements (rows >= M or N, the K remainder) are loaded as
 //     zeros through the buffer descriptor's range check, so the main loop has
 //     no data-dependent branch ([GEMM] §3.4: zero padding, not predication);
-//   * both operands are stored K-contiguous in LDS -- an MN-contiguous operand
-//     is transposed in registers on its way in -- with the 16-byte vectors of a
-//     row XOR-swizzled by the row index so that ds_read_b128 of MFMA fragments
-//     and ds_write_b128 are free of bank conflicts ([OPS] §3.3 and [GEMM] §4.3
-//     pad rows instead; the swizzle costs no LDS);
-//   * 64-lane waves read their fragments with ds_read_b128 and accumulate with
-//     v_mfma_f32_32x32x16_f16 (fp16 products, fp32 sums; [GEMM] §2.3, §6.2);
+//   * LDS rows are XOR-swizzled by the row index so that the fragment reads
+//     are free of bank conflicts ([OPS] §3.3 and [GEMM] §4.3 pad rows
+//     instead; the swizzle costs no LDS).  The direct kernels keep each
+//     operand in its global orientation and read MN-contiguous fragments with
+//     transposing LDS reads; the staged kernel transposes in registers;
+//   * 64-lane waves accumulate with v_mfma_f32_16x16x32_f16 (direct and
+//     streaming kernels) or v_mfma_f32_32x32x16_f16 (staged kernel): fp16
+//     products, fp32 sums ([GEMM] §2.3, §6.2);
 //   * the epilogue forms alpha*acc + beta*C in fp32, rounds once to fp16 (RNE)
 //     or stores fp32, and masks the tile edges ([CATLASS] §2.1, [OPS] §3.2).
 #include <hip/hip_runtime.h>
@@ -438,9 +441,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_staged(GemmArgs p) {
 // 16-byte chunk each lane fetches.  Lanes whose chunk lies outside the matrix
 // are given an offset that fails the buffer range check, which writes zeros.
 //   K-contiguous operand:  LDS rows [r][k], BK/8 chunks per row, chunk
-//                          c stored at c ^ swz(r); fragments by ds_read_b128.
+//                          c stored at c ^ swz16(r); fragments by ds_read_b128.
 //   MN-contiguous operand: LDS rows [k][r], R/8 chunks per row, chunk c stored
-//                          at c ^ 4 (k % 4); fragments by two ds_read_b64_tr_b16,
+//                          at c ^ mn_swz(k); fragments by two ds_read_b64_tr_b16,
 //                          which transpose 16-bit elements across each group of
 //                          16 lanes (lane j addresses row k0 + j/4 at column
 //                          n0 + 4 (j%4); lane i receives column n0 + i of rows
@@ -749,7 +752,7 @@ __device__ inline void store_tile_splitk(const GemmArgs &p, const AccT (&acc)[FM
         __hip_atomic_store(&p.ws_count[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int R, int BK, int NW, bool KC, bool S16 = false>
+template <int R, int BK, int NW, bool KC>
 struct DirectOperand {
     static constexpr int VPR = BK / 8;                 // chunks per [r][k] row
     static constexpr int CPR = R / 8;                  // chunks per [k][r] row
@@ -770,7 +773,7 @@ struct DirectOperand {
             bool ok;
             int kin;
             if constexpr (KC) {
-                const int r = p / VPR, c = (p % VPR) ^ (S16 ? swz16(r) : swz<VPR>(r));
+                const int r = p / VPR, c = (p % VPR) ^ swz16(r);
                 off[i] = (uint32_t)((r * ld + c * 8) * 2);
                 kin = c * 8;
                 ok = r0 + r < rtot;
@@ -795,13 +798,12 @@ struct DirectOperand {
         return make_rsrc_words(base, bytes_left);
     }
     // For K-contiguous 128-byte rows the K index of load i depends on i only
-    // through (i NW + wave) % 8 (swz<8>) or (i NW + wave) % 2 (swz16), i.e.
-    // on i % KCL: the K test of a stage needs KCL compares (kmask) and one
-    // select per load (issue_one_masked).
-    static constexpr int KCL = S16 ? (NW % 2 == 0 ? 1 : 2)
-                                   : (NW % 8 == 0 ? 1 : NW % 4 == 0 ? 2 : NW % 2 == 0 ? 4 : 8);
-    // With one class (swz16 and an even number of loading waves) the test is
-    // a single compare per stage.
+    // through (i NW + wave) % 2 (load i covers rows 8 (i NW + wave) .. + 7,
+    // and of their row bits swz16 takes bit 3 from that index): with an even
+    // number of loading waves, one K class per wave, and the K test of a
+    // stage is a single compare (kmask) and one select per load
+    // (issue_one_masked).
+    static constexpr int KCL = NW % 2 == 0 ? 1 : 2;
     __device__ bool kmask(int left) const {
         static_assert(KC && VPR == 8 && KCL == 1, "one K class");
         return (int)(kin4[0] & 0xffu) < left;
@@ -833,229 +835,16 @@ struct DirectOperand {
         for (int i = 0; i < PER_WAVE; ++i) issue_one(i, rs, lds_addr, wave, left);
     }
 
-    // MFMA fragment of the 32-row block starting at rb, K sub-step s (16 deep):
-    // lane l receives rows rb + l%32, k = 16 s + 8 (l/32) + 0..7.
-    __device__ half8 frag(const u32x4 *lds, int rb, int s, int lane) const {
-        if constexpr (KC) {
-            const int r = rb + (lane & 31);
-            const int kv = 2 * s + (lane >> 5);
-            return __builtin_bit_cast(half8, lds[r * VPR + (kv ^ swz<VPR>(r))]);
-        } else {
-            const int g4 = lane >> 4, j = lane & 15;
-            const int n = rb + 16 * (g4 & 1) + 4 * (j & 3);
-            const char *bytes = (const char *)lds;
-            v4i16 h[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int k = 16 * s + 8 * (g4 >> 1) + 4 * t + (j >> 2);
-                const int addr = k * R * 2 + (((n >> 3) ^ mn_swz<R>(k)) << 4) + (n & 7) * 2;
-                h[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) v4i16 *)(bytes + addr));
-            }
-            const v4i16 lo = h[0], hi = h[1];
-            return __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-    }
 };
-
-template <int BM, int BN, int BK, int WGM, int WGN, int S, bool AK, bool BKC>
-__global__ __launch_bounds__(64 * WGM * WGN)
-__attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_direct(GemmArgs pin) {
-    GemmArgs p = pin;
-    constexpr int NW = WGM * WGN;
-    constexpr int WTM = BM / WGM, WTN = BN / WGN;
-    constexpr int FM = WTM / 32, FN = WTN / 32;
-    constexpr int NSUB = BK / 16;
-    constexpr int A_CH = BM * BK / 8, B_CH = BN * BK / 8;
-    constexpr int SLOT = A_CH + B_CH;                 // 16-byte chunks per slot
-    using OpA = DirectOperand<BM, BK, NW, AK>;
-    using OpB = DirectOperand<BN, BK, NW, BKC>;
-    constexpr int L = OpA::PER_WAVE + OpB::PER_WAVE;  // loads per lane per stage
-    static_assert(S == 2, "the schedule below is a two-slot ring");
-    static_assert(NSUB >= 2 && NSUB % 2 == 0, "fragment double buffering pairs sub-steps");
-    static_assert(L < 64, "vmcnt range");
-
-    __shared__ u32x4 lds[S * SLOT];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / WGN, wn = wave % WGN;
-
-    const int slice = (int)(blockIdx.x / (unsigned)p.total_tiles);
-    const int tile = (int)(blockIdx.x - (unsigned)slice * (unsigned)p.total_tiles);
-    if (p.ksplit > 1) apply_k_slice(p, slice, AK, BKC);
-    int b, tm, tn;
-    tile_coords(p, tile, b, tm, tn);
-    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-    const _Float16 *Ab = p.A + b * p.sa;
-    const _Float16 *Bb = p.B + b * p.sb;
-    const int64_t a_tile = AK ? m0 * p.lda : m0;
-    const int64_t a_kstep = AK ? BK : BK * p.lda;
-    const int64_t b_tile = BKC ? n0 * p.ldb : n0;
-    const int64_t b_kstep = BKC ? BK : BK * p.ldb;
-
-    OpA opa;
-    OpB opb;
-    opa.init(wave, lane, m0, p.M, p.lda);
-    opb.init(wave, lane, n0, p.N, p.ldb);
-
-    floatx16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    const int64_t nk = (p.K + BK - 1) / BK;
-    const uint32_t lds_base = lds_offset(lds);
-
-    // Issues all of this wave's loads of stage st into ring slot st % 2.
-    auto issue = [&](int64_t st) {
-        const uint32_t slot = lds_base + (uint32_t)((st % S) * SLOT * 16);
-        const int64_t ao = a_tile + st * a_kstep, bo = b_tile + st * b_kstep;
-        opa.issue(Ab + ao, (p.extent_a - ao) * 2, slot, wave, st * BK, p.K);
-        opb.issue(Bb + bo, (p.extent_b - bo) * 2, slot + A_CH * 16, wave, st * BK, p.K);
-    };
-
-    half8 fa[2][FM], fb[2][FN];
-    auto read_frags = [&](int buf, int64_t st, int s) {
-        const u32x4 *slot = lds + (int)(st % S) * SLOT;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) fb[buf][j] = opb.frag(slot + A_CH, wn * WTN + j * 32, s, lane);
-#pragma unroll
-        for (int i = 0; i < FM; ++i) fa[buf][i] = opa.frag(slot, wm * WTM + i * 32, s, lane);
-    };
-
-    // One sub-step: the FM*FN MFMAs on fragment buffer `cur`, with the
-    // fragment reads for the next sub-step (stage rst, sub-step rs, into
-    // buffer `nxt`) and `nl` of this wave's direct-to-LDS loads of stage
-    // `dst` (starting at load index l0) spread evenly between them, in a fixed
-    // order the compiler may not change.  Spacing the 1 KiB loads keeps one
-    // wave from stalling on two of them back to back; B fragments are read
-    // first because the next sub-step's first MFMAs need all of them.
-    constexpr int NQ = FM * FN;
-    constexpr int NF = FM + FN;
-    auto substep = [&](int cur, int nxt, int64_t rst, int rs, int64_t dst, auto l0c, auto nlc) {
-        constexpr int l0 = decltype(l0c)::value, nl = decltype(nlc)::value;
-        const u32x4 *rslot = lds + (int)(rst % S) * SLOT;
-        const uint32_t dslot = lds_base + (uint32_t)((dst % S) * SLOT * 16);
-        const int64_t ao = a_tile + dst * a_kstep, bo = b_tile + dst * b_kstep;
-        sgpr4 rsa = {}, rsb = {};
-        int left = 0;
-        if constexpr (nl > 0) {
-            rsa = opa.stage_rsrc(Ab + ao, (p.extent_a - ao) * 2);
-            rsb = opb.stage_rsrc(Bb + bo, (p.extent_b - bo) * 2);
-            left = OpA::stage_left(dst * BK, p.K);
-        }
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            const int i = q / FN, j = q % FN;
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
-#pragma unroll
-            for (int l = l0 + q * nl / NQ; l < l0 + (q + 1) * nl / NQ; ++l) {
-                if (l < OpA::PER_WAVE) opa.issue_one(l, rsa, dslot, wave, left);
-                else opb.issue_one(l - OpA::PER_WAVE, rsb, dslot + A_CH * 16, wave, left);
-            }
-#pragma unroll
-            for (int f = q * NF / NQ; f < (q + 1) * NF / NQ; ++f) {
-                if (f < FN) fb[nxt][f] = opb.frag(rslot + A_CH, wn * WTN + f * 32, rs, lane);
-                else fa[nxt][f - FN] = opa.frag(rslot, wm * WTM + (f - FN) * 32, rs, lane);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-
-    // Stage kt lives in slot kt % 2.  One barrier per stage, placed before the
-    // last sub-step of stage kt: there every wave has (a) waited for its own
-    // loads of stage kt+1 and (b) drained its LDS reads of stage kt (all of
-    // them were issued during the earlier sub-steps), so after the barrier
-    // stage kt+1 is readable and slot kt % 2 is free: its refill with stage
-    // kt+2 is issued during the last sub-step of stage kt and the first of
-    // stage kt+1, a full stage ahead of the next barrier.  Every stage issues
-    // exactly L loads per lane (stages past the end of K fail the range check
-    // and write zeros), so the wait counts are exact.
-    constexpr int LH = L / 2;
-    using C0 = std::integral_constant<int, 0>;
-    using CLH = std::integral_constant<int, LH>;
-    using CRest = std::integral_constant<int, L - LH>;
-    // Prologue: stage 0 whole, first half of stage 1 (the loop issues the
-    // rest of stage kt+1 in its first sub-step).
-    issue(0);
-    {
-        const uint32_t dslot = lds_base + (uint32_t)(SLOT * 16);
-        const int64_t ao = a_tile + a_kstep, bo = b_tile + b_kstep;
-        const sgpr4 rsa = opa.stage_rsrc(Ab + ao, (p.extent_a - ao) * 2);
-        const sgpr4 rsb = opb.stage_rsrc(Bb + bo, (p.extent_b - bo) * 2);
-        const int left = OpA::stage_left(BK, p.K);
-#pragma unroll
-        for (int l = 0; l < LH; ++l) {
-            if (l < OpA::PER_WAVE) opa.issue_one(l, rsa, dslot, wave, left);
-            else opb.issue_one(l - OpA::PER_WAVE, rsb, dslot + A_CH * 16, wave, left);
-        }
-    }
-    wait_vmcnt<LH>();                   // stage 0 resident for this lane
-    barrier();                          // ... and for every lane
-    read_frags(0, 0, 0);
-
-    // Sub-steps 0 .. NSUB-2 of stage kt, then the stage barrier.
-    auto stage_head = [&](int64_t kt) __attribute__((always_inline)) {
-        substep(0, 1, kt, 1, kt + 1, CLH{}, CRest{});   // rest of stage kt+1
-#pragma unroll
-        for (int sub = 1; sub < NSUB - 1; ++sub)
-            substep(sub & 1, (sub & 1) ^ 1, kt, sub + 1, kt + 1, C0{}, C0{});
-        wait_vmcnt<0>();                // this lane's loads of stage kt+1
-        asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");   // reads of stage kt done
-        barrier();
-    };
-    // Last sub-step of stage kt: reads sub-step 0 of stage kt+1 and issues
-    // the first half of stage kt+2.
-    auto stage_tail = [&](int64_t kt) __attribute__((always_inline)) {
-        substep((NSUB - 1) & 1, NSUB & 1, kt + 1, 0, kt + 2, C0{}, CLH{});
-    };
-    // The loop is rotated so that its back edge follows the barrier, where no
-    // LDS read is outstanding.
-    stage_head(0);
-    for (int64_t kt = 0; kt + 1 < nk; ++kt) {
-        stage_tail(kt);
-        stage_head(kt + 1);
-    }
-    stage_tail(nk - 1);
-    // Drain the ring: no direct-to-LDS write or fragment read may still be in
-    // flight when the epilogue reuses the LDS.
-    wait_vmcnt<0>();
-    asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
-    barrier();
-
-    if (p.ksplit > 1) {
-        if (p.out_f32)
-            store_tile_splitk<float, BM, BN, WGM, WGN, S * SLOT * 16, 32>(p, acc, lds, tile, slice, b, m0, n0, wave, lane);
-        else
-            store_tile_splitk<_Float16, BM, BN, WGM, WGN, S * SLOT * 16, 32>(p, acc, lds, tile, slice, b, m0, n0, wave, lane);
-        return;
-    }
-    const bool full = p.c_vec && m0 + BM <= p.M && n0 + BN <= p.N;
-    if (p.out_f32) {
-        if (full)
-            store_tile_lds<float, true, BM, BN, WGM, WGN, S * SLOT * 16, 32>(p, acc, lds, b, m0, n0, wave, lane);
-        else
-            store_tile_lds<float, false, BM, BN, WGM, WGN, S * SLOT * 16, 32>(p, acc, lds, b, m0, n0, wave, lane);
-    } else {
-        if (full)
-            store_tile_lds<_Float16, true, BM, BN, WGM, WGN, S * SLOT * 16, 32>(p, acc, lds, b, m0, n0, wave, lane);
-        else
-            store_tile_lds<_Float16, false, BM, BN, WGM, WGN, S * SLOT * 16, 32>(p, acc, lds, b, m0, n0, wave, lane);
-    }
-}
 
 // Per-lane LDS byte offsets of one operand's 16 x 16 x 32 fragments for one
 // wave (rows or columns wb .. wb + 16 NBLK - 1 of a BK = 64 ring slot), so
 // that every fragment read is a base register plus an immediate offset.  Two
 // sets: `cur` addresses the slot of the stage being computed, `nxt` the slot
-// of the next one; the two slots are 64 KiB apart, so advancing a stage is one
-// XOR per register (advance()) and no other address arithmetic is left in
-// the K loop.
+// of the next one.  Slot 0 starts at 0 and slot 1 one slot size (a power of
+// two) above it, and every slot-0 address is below the slot size, so
+// advancing a stage is one XOR per register (advance()) and no other address
+// arithmetic is left in the K loop.
 //   K-contiguous: row r = wb + 16 i + l%16 keeps its K chunk kv = 4 s + l/16
 //     at kv ^ swz16(r) = (l/16 ^ swz16(l%16)) ^ 4 s (swz16 depends on r % 16
 //     only): two bases, by s, and 16 rows per block as immediates.
@@ -1066,7 +855,8 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_direct(GemmArgs pin) {
 template <int R, int BK, bool KC, int NBLK, int SLOT_BYTES>
 struct Frag16 {
     static_assert(BK == 64, "128-byte K rows");
-    static_assert(SLOT_BYTES == 65536, "slots 64 KiB apart: advance() flips bit 16");
+    static_assert((SLOT_BYTES & (SLOT_BYTES - 1)) == 0 && SLOT_BYTES <= 65536,
+                  "slot size a power of two: advance() flips one address bit");
     static constexpr int NCLS = KC ? 2 : NBLK;
     uint32_t cur[NCLS], nxt[NCLS];
 
@@ -1119,8 +909,8 @@ struct Frag16 {
 };
 
 // ---------------------------------------------------------------------------
-// Direct kernel on 16 x 16 x 32 MFMAs.  Same ring, loads and epilogue as
-// gemm_direct; each wave owns (BM/WGM) x (BN/WGN) outputs as 16 x 16
+// Direct kernel on 16 x 16 x 32 MFMAs (256 x 256 and 128 x 128 tiles): the
+// ring, loads and swizzles above; each wave owns (BM/WGM) x (BN/WGN) outputs as 16 x 16
 // accumulator blocks.  With a 128 x 128 wave tile a 32-deep K step is 64
 // MFMAs of 16 cycles fed by 16 one-KiB fragment reads -- the same LDS traffic
 // per flop as 32 x 32 blocks -- and back-to-back 16 x 16 x 32 MFMAs on
@@ -1141,15 +931,17 @@ struct Frag16 {
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int BK, int WGM, int WGN, int S, bool AK, bool BKC, bool KFULL>
 __global__ __launch_bounds__(64 * WGM * WGN)
-__attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_direct16(GemmArgs p) {
+__attribute__((amdgpu_waves_per_eu(BM * BN >= 65536 ? 1 : 2, BM * BN >= 65536 ? 1 : 2)))
+void gemm_direct16(GemmArgs pin) {
+    GemmArgs p = pin;
     constexpr int NW = WGM * WGN;
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
     constexpr int FM = WTM / 16, FN = WTN / 16;
     constexpr int NKS = BK / 32;
     constexpr int A_CH = BM * BK / 8, B_CH = BN * BK / 8;
     constexpr int SLOT = A_CH + B_CH;                 // 16-byte chunks per slot
-    using OpA = DirectOperand<BM, BK, NW, AK, true>;
-    using OpB = DirectOperand<BN, BK, NW, BKC, true>;
+    using OpA = DirectOperand<BM, BK, NW, AK>;
+    using OpB = DirectOperand<BN, BK, NW, BKC>;
     constexpr int L = OpA::PER_WAVE + OpB::PER_WAVE;  // loads per lane per stage
     static_assert(S == 2, "the schedule is a two-slot ring");
     static_assert(NKS == 2, "head and tail are one K step each");
@@ -1162,8 +954,11 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_direct16(GemmArgs p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WGN, wn = wave % WGN;
 
+    const int slice = (int)(blockIdx.x / (unsigned)p.total_tiles);
+    const int tile = (int)(blockIdx.x - (unsigned)slice * (unsigned)p.total_tiles);
+    if (p.ksplit > 1) apply_k_slice(p, slice, AK, BKC);
     int b, tm, tn;
-    tile_coords(p, blockIdx.x, b, tm, tn);
+    tile_coords(p, tile, b, tm, tn);
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const _Float16 *Ab = p.A + b * p.sa;
     const _Float16 *Bb = p.B + b * p.sb;
@@ -1293,6 +1088,17 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_direct16(GemmArgs p) {
     asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
     barrier();
 
+    // Split-K stages a whole fp32 tile in the ring, so only tiles that fit
+    // take it (the planner splits no other).
+    if constexpr (BM * BN * 4 <= S * SLOT * 16) {
+        if (p.ksplit > 1) {
+            if (p.out_f32)
+                store_tile_splitk<float, BM, BN, WGM, WGN, S * SLOT * 16, 16>(p, acc, lds, tile, slice, b, m0, n0, wave, lane);
+            else
+                store_tile_splitk<_Float16, BM, BN, WGM, WGN, S * SLOT * 16, 16>(p, acc, lds, tile, slice, b, m0, n0, wave, lane);
+            return;
+        }
+    }
     const bool full = p.c_vec && m0 + BM <= p.M && n0 + BN <= p.N;
     if (p.out_f32) {
         if (full)
@@ -1430,12 +1236,6 @@ constexpr KernelFn pick_direct16() {
                          kTiles[T].wgn, kTiles[T].stages, AK, BKC, KFULL>;
 }
 
-template <int T, bool AK, bool BKC>
-constexpr KernelFn pick_direct() {
-    return gemm_direct<kTiles[T].bm, kTiles[T].bn, kTiles[T].bk, kTiles[T].wgm,
-                       kTiles[T].wgn, kTiles[T].stages, AK, BKC>;
-}
-
 // Kernel table indexed [tile][A K-contiguous][B K-contiguous][vec].  Direct
 // tiles have only the vec entry; staged tiles have both.
 template <int T>
@@ -1445,12 +1245,6 @@ void fill_tile(KernelFn (&t)[2][2][2]) {
         t[0][1][1] = pick_direct16<T, false, true>();
         t[1][0][1] = pick_direct16<T, true, false>();
         t[1][1][1] = pick_direct16<T, true, true>();
-        t[0][0][0] = t[0][1][0] = t[1][0][0] = t[1][1][0] = nullptr;
-    } else if constexpr (kTiles[T].kind == KIND_DIRECT) {
-        t[0][0][1] = pick_direct<T, false, false>();
-        t[0][1][1] = pick_direct<T, false, true>();
-        t[1][0][1] = pick_direct<T, true, false>();
-        t[1][1][1] = pick_direct<T, true, true>();
         t[0][0][0] = t[0][1][0] = t[1][0][0] = t[1][1][0] = nullptr;
     } else {
         t[0][0][0] = pick_staged<T, false, false, false>();
@@ -1474,13 +1268,18 @@ void fill_stream(KernelFn (&t)[2][2][2]) {
 
 struct KernelTable {
     KernelFn k[NUM_TILES][2][2][2];
-    KernelFn kfull[2][2];   // TILE_256x256 when K is a multiple of its BK
+    KernelFn kfull[2][2][2];   // [tile is 256x256][A K-contiguous][B K-contiguous]: K a multiple of BK
     KernelTable() {
-        static_assert(kTiles[TILE_256x256].kind == KIND_DIRECT16, "K-full variants are direct16");
-        kfull[0][0] = pick_direct16<TILE_256x256, false, false, true>();
-        kfull[0][1] = pick_direct16<TILE_256x256, false, true, true>();
-        kfull[1][0] = pick_direct16<TILE_256x256, true, false, true>();
-        kfull[1][1] = pick_direct16<TILE_256x256, true, true, true>();
+        static_assert(kTiles[TILE_256x256].kind == KIND_DIRECT16 &&
+                      kTiles[TILE_128x128].kind == KIND_DIRECT16, "K-full variants are direct16");
+        kfull[1][0][0] = pick_direct16<TILE_256x256, false, false, true>();
+        kfull[1][0][1] = pick_direct16<TILE_256x256, false, true, true>();
+        kfull[1][1][0] = pick_direct16<TILE_256x256, true, false, true>();
+        kfull[1][1][1] = pick_direct16<TILE_256x256, true, true, true>();
+        kfull[0][0][0] = pick_direct16<TILE_128x128, false, false, true>();
+        kfull[0][0][1] = pick_direct16<TILE_128x128, false, true, true>();
+        kfull[0][1][0] = pick_direct16<TILE_128x128, true, false, true>();
+        kfull[0][1][1] = pick_direct16<TILE_128x128, true, true, true>();
         fill_tile<TILE_256x256>(k[TILE_256x256]);
         fill_tile<TILE_128x128>(k[TILE_128x128]);
         fill_tile<TILE_64x64>(k[TILE_64x64]);
@@ -1580,7 +1379,10 @@ extern "C" int gemm_f16f32_run(gemm_f16f32_plan_t plan, const void *A,
     const int ak = p.layout_a == GEMM_ROW_MAJOR;   // A K-contiguous
     const int bkc = p.layout_b == GEMM_COL_MAJOR;  // B K-contiguous
     KernelFn fn = kernels().k[tile][ak][bkc][vec ? 1 : 0];
-    if (tile == TILE_256x256 && p.K % kTiles[tile].bk == 0) fn = kernels().kfull[ak][bkc];
+    // K-full variants: every stage inside K (for split-K, every slice: kchunk
+    // is a multiple of BK, so K must be too).
+    if ((tile == TILE_256x256 || tile == TILE_128x128) && p.K % kTiles[tile].bk == 0)
+        fn = kernels().kfull[tile == TILE_256x256 ? 1 : 0][ak][bkc];
     if (!fn) return GEMM_ERR_UNSUPPORTED;
     void *args[] = {&a};
     const unsigned threads = ts.kind == KIND_STREAM ? 512u : (unsigned)(64 * ts.wgm * ts.wgn);

@@ -107,7 +107,7 @@ def test_kernel_choice_by_regime():
     assert kern(40, 4096, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_stream64x16")
     # skinny with row-major B: too few tiles for the CUs, so the 128 tile with
     # its K cut into slices (split-K, suffix _sk<slices>)
-    assert kern(16, 4096, 4096) == "gemm_128x128x64s2_nn_direct_sk8"
+    assert kern(16, 4096, 4096) == "gemm_128x128x64m16_nn_direct_sk8"
     assert kern(128, 11008, 4096, layout_b=GEMM_COL_MAJOR).endswith("nt_direct_sk3")
     # 2048^2 already fills the CUs with 128 tiles; short K is not cut
     assert not kern(2048, 2048, 2048).endswith(tuple(f"_sk{k}" for k in range(2, 9)))
