@@ -75,5 +75,15 @@ struct gemm_f16f32_plan_s {
     int64_t ws_bytes;      // workspace: ksplit * tiles fp32 partial tiles + tile counters
     void *ws;              // device workspace, allocated by the first split-K run
     int ws_device;         // device that holds ws
+    // Repacking: an operand whose rows do not allow 128-bit loads (leading
+    // dimension, contiguous extent or batch stride not a multiple of 8) is
+    // copied, before a direct or streaming kernel runs, into a dense buffer
+    // with rows padded to a multiple of 8 elements (zeros in the padding).
+    int pack;              // operands repacked because of their shape: bit 0 A, bit 1 B
+    int64_t ld8_a, ld8_b;  // leading dimensions of the packed copies
+    int64_t pack_off_b;    // byte offset of B's copy in pack_ws
+    int64_t pack_bytes;    // bytes of both copies
+    void *pack_ws;         // device buffer of the copies, allocated by the first run that packs
+    int pack_device;       // device that holds pack_ws
     char kernel_name[64];
 };

@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "gemm_f16f32.h"
@@ -1119,23 +1120,25 @@ void gemm_direct16(GemmArgs pin) {
 // stored N x K).  Such a GEMM is bound by reading B once from HBM
 // ([OPS] §1.2 and [GEMM] §2.4: classify by arithmetic intensity first), so
 // the kernel is built to keep many bytes in flight rather than to reuse tiles:
-//   * a workgroup owns 16 columns of C (all M rows, MB blocks of 16) and
+//   * a workgroup owns NB x 16 columns of C (all M rows, MB blocks of 16) and
 //     splits K over its 8 waves, so even N = 4096 yields 256 workgroups;
 //   * MFMA fragments of v_mfma_f32_16x16x32_f16 are loaded straight from
 //     global memory (lane l holds 8 consecutive k of row/column l % 16 --
 //     16 contiguous bytes of a K-contiguous operand), UNROLL K steps at a
 //     time, with the range check zero-filling rows >= M, columns >= N and
-//     k >= K;
+//     k >= K; each A fragment feeds NB MFMAs, so A (re-read by every
+//     workgroup from L2) costs 1/NB of the load instructions it would;
 //   * the 8 partial tiles are summed through LDS and the alpha/beta epilogue
 //     is applied once per output.
 // ---------------------------------------------------------------------------
 typedef float floatx4v __attribute__((ext_vector_type(4)));
 
-template <int MB>
+template <int MB, int NB>
 __global__ __launch_bounds__(512) void gemm_stream(GemmArgs p) {
     constexpr int NW = 8;
-    constexpr int UNROLL = MB <= 2 ? 8 : 4;
-    __shared__ float red[NW][MB * 16][16];
+    constexpr int UNROLL = MB + NB <= 3 ? 8 : 4;
+    static_assert(MB * NB <= 8, "reduction buffer within 64 KiB");
+    __shared__ float red[NW][MB * 16][NB * 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1143,7 +1146,7 @@ __global__ __launch_bounds__(512) void gemm_stream(GemmArgs p) {
 
     int b, tm, tn;
     tile_coords(p, blockIdx.x, b, tm, tn);
-    const int64_t m0 = (int64_t)tm * (MB * 16), n0 = (int64_t)tn * 16;
+    const int64_t m0 = (int64_t)tm * (MB * 16), n0 = (int64_t)tn * (NB * 16);
     const _Float16 *Ab = p.A + b * p.sa;
     const _Float16 *Bb = p.B + b * p.sb;
 
@@ -1155,31 +1158,38 @@ __global__ __launch_bounds__(512) void gemm_stream(GemmArgs p) {
     const int kq = 8 * (lane >> 4);       // first of its 8 consecutive k
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab, p.extent_a * 2);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb, p.extent_b * 2);
-    bool a_ok[MB];
-    uint32_t a_off[MB];
+    bool a_ok[MB], b_ok[NB];
+    uint32_t a_off[MB], b_off[NB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
         const int64_t m = m0 + mb * 16 + r16;
         a_ok[mb] = m < p.M;
         a_off[mb] = (uint32_t)((m * p.lda + kq) * 2);
     }
-    const int64_t n = n0 + r16;
-    const bool b_ok = n < p.N;
-    const uint32_t b_off = (uint32_t)((n * p.ldb + kq) * 2);
-
-    floatx4v acc[MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[mb] = floatx4v{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < NB; ++nb) {
+        const int64_t n = n0 + nb * 16 + r16;
+        b_ok[nb] = n < p.N;
+        b_off[nb] = (uint32_t)((n * p.ldb + kq) * 2);
+    }
+
+    floatx4v acc[MB][NB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = floatx4v{0.f, 0.f, 0.f, 0.f};
 
     for (int64_t s0 = s_lo; s0 < s_hi; s0 += UNROLL) {
-        half8 fa[UNROLL][MB], fb[UNROLL];
+        half8 fa[UNROLL][MB], fb[UNROLL][NB];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int64_t k = (s0 + u) * 32 + kq;
             const bool kin = (s0 + u < s_hi) && (k < p.K);
             const uint32_t kb = (uint32_t)((s0 + u) * 64);
-            fb[u] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(
-                rb, (b_ok && kin) ? b_off + kb : kOutOfRange, 0, 0));
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                fb[u][nb] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(
+                    rb, (b_ok[nb] && kin) ? b_off[nb] + kb : kOutOfRange, 0, 0));
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
                 fa[u][mb] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(
@@ -1189,7 +1199,9 @@ __global__ __launch_bounds__(512) void gemm_stream(GemmArgs p) {
         for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
-                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[u][mb], fb[u], acc[mb], 0, 0, 0);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[u][mb], fb[u][nb], acc[mb][nb], 0, 0, 0);
     }
 
     // Accumulator register r of lane l holds row 4*(l/16) + r, column l % 16
@@ -1197,12 +1209,15 @@ __global__ __launch_bounds__(512) void gemm_stream(GemmArgs p) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[wave][mb * 16 + 4 * (lane >> 4) + r][r16] = acc[mb][r];
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                red[wave][mb * 16 + 4 * (lane >> 4) + r][nb * 16 + r16] = acc[mb][nb][r];
     __syncthreads();
 
     const float alpha = p.alpha, beta = p.beta;
-    for (int o = tid; o < MB * 16 * 16; o += NW * 64) {
-        const int i = o >> 4, j = o & 15;
+    for (int o = tid; o < MB * 16 * NB * 16; o += NW * 64) {
+        const int i = o / (NB * 16), j = o % (NB * 16);
         const int64_t m = m0 + i, nn = n0 + j;
         if (m >= p.M || nn >= p.N) continue;
         float v = 0.f;
@@ -1219,6 +1234,63 @@ __global__ __launch_bounds__(512) void gemm_stream(GemmArgs p) {
             if (beta != 0.0f) v += beta * (float)*C;
             *C = (_Float16)v;
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Repacking of an operand whose rows are not 16-byte aligned ([GEMM] §3.4:
+// edges are handled by zero padding).  Copies `outer` rows of `cols`
+// elements (leading dimension ld, batch stride `stride`, any 2-byte
+// alignment) into a dense buffer of rows ld8 = cols rounded up to 8, zeros in
+// columns cols..ld8-1, so that the direct and streaming kernels can read
+// every row as whole 16-byte chunks.  One thread writes one 16-byte chunk: it
+// reads the one or two 16-byte-aligned source blocks that hold the chunk's
+// valid elements (never a block without one, so every read stays inside the
+// pages of the operand) and shifts them into place.  HBM bound: the operand
+// is read once and written once.
+// ---------------------------------------------------------------------------
+struct PackArgs {
+    const _Float16 *src;
+    _Float16 *dst;
+    int64_t ld, stride, outer, cols, ld8, batch;
+};
+
+// Chunk counts below 2^31 (checked by the planner and the launcher): 32-bit
+// index math, and c + grid stride stays below 2^32.
+__global__ __launch_bounds__(256) void gemm_pack16(PackArgs a) {
+    const uint32_t cpr = (uint32_t)(a.ld8 / 8);     // chunks per packed row
+    const uint32_t outer = (uint32_t)a.outer;
+    const uint32_t total = (uint32_t)(a.batch * a.outer) * cpr;
+    for (uint32_t c = blockIdx.x * 256u + threadIdx.x; c < total; c += gridDim.x * 256u) {
+        const uint32_t j = c % cpr, row = c / cpr;  // row over all batch items
+        const uint32_t b = row / outer, r = row - b * outer;
+        const int64_t left = a.cols - 8 * (int64_t)j;
+        const int nvalid = left >= 8 ? 8 : (int)left;   // >= 1: j < ceil(cols / 8)
+        const uintptr_t first = (uintptr_t)(a.src + (int64_t)b * a.stride + (int64_t)r * a.ld + 8 * (int64_t)j);
+        const uintptr_t blk = first & ~(uintptr_t)15;
+        const int sh = (int)(first & 15);            // even: fp16 elements
+        const u32x4 w0 = *(const u32x4 *)blk;
+        // The second block holds a valid element only if the chunk's valid
+        // bytes run past the first.
+        const u32x4 w1 = sh + 2 * nvalid > 16 ? *(const u32x4 *)(blk + 16) : u32x4{0, 0, 0, 0};
+        const int s4 = sh >> 2, sb = sh & 3;
+        uint32_t e[5];
+        // e[i] = dword s4 + i of the 8-dword window w0:w1.
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            const int k = s4 + i;
+            e[i] = k == 0 ? w0[0] : k == 1 ? w0[1] : k == 2 ? w0[2] : k == 3 ? w0[3]
+                 : k == 4 ? w1[0] : k == 5 ? w1[1] : k == 6 ? w1[2] : w1[3];
+        }
+        u32x4 out;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t v = __builtin_amdgcn_alignbyte(e[i + 1], e[i], (uint32_t)sb);
+            if (2 * i >= nvalid) v = 0;
+            else if (2 * i + 1 >= nvalid) v &= 0xffffu;
+            out[i] = v;
+        }
+        *(u32x4 *)(a.dst + (int64_t)row * a.ld8 + 8 * (int64_t)j) = out;
     }
 }
 
@@ -1263,7 +1335,7 @@ void fill_stream(KernelFn (&t)[2][2][2]) {
     // Only the K-contiguous A and B (row-major A, column-major B) 128-bit form.
     t[0][0][0] = t[0][0][1] = t[0][1][0] = t[0][1][1] = nullptr;
     t[1][0][0] = t[1][0][1] = t[1][1][0] = nullptr;
-    t[1][1][1] = gemm_stream<kTiles[T].bm / 16>;
+    t[1][1][1] = gemm_stream<kTiles[T].bm / 16, kTiles[T].bn / 16>;
 }
 
 struct KernelTable {
@@ -1302,6 +1374,16 @@ bool ranges_overlap(uintptr_t a, int64_t a_bytes, uintptr_t b, int64_t b_bytes) 
     return a < b + (uintptr_t)b_bytes && b < a + (uintptr_t)a_bytes;
 }
 
+// Whether the packed copy of operand 0 (A) or 1 (B) has fewer than 2^31
+// 16-byte chunks: the pack kernel's 32-bit index plus its grid stride (at
+// most 2^21) then never wraps.
+bool packable(const gemm_f16f32_plan_s &p, int which) {
+    const bool rm = (which == 0 ? p.layout_a : p.layout_b) == GEMM_ROW_MAJOR;
+    const int64_t outer = which == 0 ? (rm ? p.M : p.K) : (rm ? p.K : p.N);
+    const int64_t ld8 = which == 0 ? p.ld8_a : p.ld8_b;
+    return p.batch * outer * (ld8 / 8) < (int64_t(1) << 31);
+}
+
 }  // namespace
 
 extern "C" int gemm_f16f32_run(gemm_f16f32_plan_t plan, const void *A,
@@ -1317,7 +1399,14 @@ extern "C" int gemm_f16f32_run(gemm_f16f32_plan_t plan, const void *A,
                     ranges_overlap((uintptr_t)C, cbytes, (uintptr_t)B, p.extent_b * 2)))
         return GEMM_ERR_INVALID_ARG;
 
-    const bool vec = p.vec_ok && ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0);
+    // Operands copied into the plan's padded buffers first: those whose shape
+    // needs it, and, for the direct and streaming kernels, any whose pointer
+    // is not 16-byte aligned.  The staged tiles take a misaligned pointer
+    // with element-wide loads instead.
+    const bool fast = p.vec_ok && kTiles[p.tile].kind != KIND_STAGED;
+    const bool pack_a = p.K > 0 && ((p.pack & 1) || (fast && packable(p, 0) && (uintptr_t)A % 16 != 0));
+    const bool pack_b = p.K > 0 && ((p.pack & 2) || (fast && packable(p, 1) && (uintptr_t)B % 16 != 0));
+    const bool vec = p.vec_ok && (pack_a || (uintptr_t)A % 16 == 0) && (pack_b || (uintptr_t)B % 16 == 0);
     const int64_t celem = p.out_type == GEMM_OUT_F32 ? 4 : 2;
     const bool c_vec = (p.ldc % 4 == 0) && (p.stride_c % 4 == 0) &&
                        ((uintptr_t)C % (4 * celem) == 0);
@@ -1374,6 +1463,55 @@ extern "C" int gemm_f16f32_run(gemm_f16f32_plan_t plan, const void *A,
         a.kchunk = p.kchunk;
         a.ws = (float *)plan->ws;
         a.ws_count = (int *)((char *)plan->ws + (p.ws_bytes - a.total_tiles * 4));
+    }
+
+    if (pack_a || pack_b) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
+        if (plan->pack_ws && plan->pack_device != dev) return GEMM_ERR_INVALID_ARG;
+        if (!plan->pack_ws) {
+            void *buf = nullptr;
+            if (hipMalloc(&buf, (size_t)p.pack_bytes) != hipSuccess) return GEMM_ERR_NOMEM;
+            plan->pack_ws = buf;
+            plan->pack_device = dev;
+        }
+        auto pack = [&](const void *src, int layout, int64_t rows_rm, int64_t cols_rm, int64_t ld,
+                        int64_t stride, int64_t ld8, _Float16 *dst) {
+            PackArgs pa;
+            pa.src = (const _Float16 *)src;
+            pa.dst = dst;
+            pa.ld = ld;
+            pa.stride = stride;
+            pa.outer = layout == GEMM_ROW_MAJOR ? rows_rm : cols_rm;
+            pa.cols = layout == GEMM_ROW_MAJOR ? cols_rm : rows_rm;
+            pa.ld8 = ld8;
+            pa.batch = p.batch;
+            const int64_t chunks = pa.batch * pa.outer * (ld8 / 8);
+            const int64_t blocks = std::min<int64_t>((chunks + 255) / 256, 8192);
+            void *pargs[] = {&pa};
+            return hipLaunchKernel((const void *)gemm_pack16, dim3((unsigned)blocks), dim3(256),
+                                   pargs, 0, (hipStream_t)stream);
+        };
+        _Float16 *pa_dst = (_Float16 *)plan->pack_ws;
+        _Float16 *pb_dst = (_Float16 *)((char *)plan->pack_ws + p.pack_off_b);
+        if (pack_a) {
+            if (pack(A, p.layout_a, p.M, p.K, p.lda, p.stride_a, p.ld8_a, pa_dst) != hipSuccess)
+                return GEMM_ERR_HIP;
+            const int64_t outer = p.layout_a == GEMM_ROW_MAJOR ? p.M : p.K;
+            a.A = pa_dst;
+            a.lda = p.ld8_a;
+            a.sa = outer * p.ld8_a;
+            a.extent_a = outer * p.ld8_a;
+        }
+        if (pack_b) {
+            if (pack(B, p.layout_b, p.K, p.N, p.ldb, p.stride_b, p.ld8_b, pb_dst) != hipSuccess)
+                return GEMM_ERR_HIP;
+            const int64_t outer = p.layout_b == GEMM_ROW_MAJOR ? p.K : p.N;
+            a.B = pb_dst;
+            a.ldb = p.ld8_b;
+            a.sb = outer * p.ld8_b;
+            a.extent_b = outer * p.ld8_b;
+        }
     }
 
     const int ak = p.layout_a == GEMM_ROW_MAJOR;   // A K-contiguous

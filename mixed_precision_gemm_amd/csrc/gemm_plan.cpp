@@ -138,15 +138,39 @@ extern "C" int gemm_f16f32_plan(gemm_f16f32_plan_t *out, int64_t M, int64_t N,
         return GEMM_OK;
     }
     // 128-bit loads need every 8-element vector along an operand's contiguous
-    // dimension to be either wholly inside or wholly outside the matrix, and
-    // every row (and batch item) to start on a 16-byte boundary.
+    // dimension to be either wholly inside the matrix or zero, and every row
+    // (and batch item) to start on a 16-byte boundary.
     const int64_t contig_a = layout_a == GEMM_ROW_MAJOR ? K : M;
     const int64_t contig_b = layout_b == GEMM_ROW_MAJOR ? N : K;
-    p->vec_ok = (contig_a % 8 == 0) && (lda % 8 == 0) && (stride_a % 8 == 0) &&
-                (contig_b % 8 == 0) && (ldb % 8 == 0) && (stride_b % 8 == 0);
+    const int64_t outer_a = layout_a == GEMM_ROW_MAJOR ? M : K;
+    const int64_t outer_b = layout_b == GEMM_ROW_MAJOR ? K : N;
+    const bool a_ok = (contig_a % 8 == 0) && (lda % 8 == 0) && (stride_a % 8 == 0);
+    const bool b_ok = (contig_b % 8 == 0) && (ldb % 8 == 0) && (stride_b % 8 == 0);
     const bool kc_both = layout_a == GEMM_ROW_MAJOR && layout_b == GEMM_COL_MAJOR;
-    p->tile = choose_tile(M, N, K, batch, kc_both, p->vec_ok);
-    // Unaligned shapes go to the staged kernel, whose largest tile is 128.
+    // Copies padded to 8-element rows; sized here, allocated only by a run
+    // that packs (an operand of this shape, or a misaligned pointer).
+    p->ld8_a = ceil_div(contig_a, 8) * 8;
+    p->ld8_b = ceil_div(contig_b, 8) * 8;
+    const int64_t bytes_a = ceil_div(batch * outer_a * p->ld8_a * 2, 256) * 256;
+    p->pack_off_b = bytes_a;
+    p->pack_bytes = bytes_a + batch * outer_b * p->ld8_b * 2;
+    p->tile = choose_tile(M, N, K, batch, kc_both, true);
+    if (a_ok && b_ok) {
+        p->vec_ok = 1;
+    } else if (kTiles[p->tile].kind != KIND_STAGED && K > 0 &&
+               (a_ok || batch * outer_a * (p->ld8_a / 8) < (int64_t(1) << 31)) &&
+               (b_ok || batch * outer_b * (p->ld8_b / 8) < (int64_t(1) << 31))) {
+        // Shapes for the direct or streaming kernels repack the unaligned
+        // operands: one extra pass over them instead of element-wide loads
+        // for the whole K loop (copies of fewer than 2^31 16-byte chunks).
+        p->vec_ok = 1;
+        p->pack = (a_ok ? 0 : 1) | (b_ok ? 0 : 2);
+    } else {
+        // Small products keep the operands in place: the staged kernel with
+        // element-wide loads, whose largest tile is 128.
+        p->vec_ok = 0;
+        p->tile = choose_tile(M, N, K, batch, kc_both, false);
+    }
     const int t = p->vec_ok ? p->tile : narrow_tile(p->tile);
     for (int cand : {p->tile, narrow_tile(p->tile)}) {
         const TileShape &c = kTiles[cand];
@@ -159,23 +183,35 @@ extern "C" int gemm_f16f32_plan(gemm_f16f32_plan_t *out, int64_t M, int64_t N,
     choose_ksplit(p, ceil_div(M, kTiles[p->tile].bm) * ceil_div(N, kTiles[p->tile].bn) * batch);
     char split[16] = "";
     if (p->ksplit > 1) snprintf(split, sizeof split, "_sk%d", p->ksplit);
-    snprintf(p->kernel_name, sizeof p->kernel_name, "gemm_%s_%c%c_%s%s",
+    static const char *const kPackSuffix[4] = {"", "_pka", "_pkb", "_pkab"};
+    snprintf(p->kernel_name, sizeof p->kernel_name, "gemm_%s_%c%c_%s%s%s",
              kTiles[t].name, layout_a == GEMM_ROW_MAJOR ? 'n' : 't',
              layout_b == GEMM_ROW_MAJOR ? 'n' : 't',
              p->vec_ok ? (kTiles[t].kind == KIND_STAGED ? "vec16" : "direct")
-                       : "narrow", split);
+                       : "narrow", split, kPackSuffix[p->pack]);
     *out = p;
     return GEMM_OK;
 }
 
+namespace {
+
+// Frees a device buffer of the plan once no launch can still use it.
+void free_plan_buffer(void *buf, int device) {
+    if (!buf) return;
+    int cur = 0;
+    const bool swap = hipGetDevice(&cur) == hipSuccess && cur != device;
+    if (swap) (void)hipSetDevice(device);
+    (void)hipDeviceSynchronize();
+    (void)hipFree(buf);
+    if (swap) (void)hipSetDevice(cur);
+}
+
+}  // namespace
+
 extern "C" int gemm_f16f32_destroy(gemm_f16f32_plan_t plan) {
-    if (plan && plan->ws) {
-        int cur = 0;
-        const bool swap = hipGetDevice(&cur) == hipSuccess && cur != plan->ws_device;
-        if (swap) (void)hipSetDevice(plan->ws_device);
-        (void)hipDeviceSynchronize();   // no launch of this plan may still use it
-        (void)hipFree(plan->ws);
-        if (swap) (void)hipSetDevice(cur);
+    if (plan) {
+        free_plan_buffer(plan->ws, plan->ws_device);
+        free_plan_buffer(plan->pack_ws, plan->pack_device);
     }
     delete plan;
     return GEMM_OK;
@@ -187,7 +223,7 @@ extern "C" const char *gemm_f16f32_status_string(int status) {
     case GEMM_ERR_INVALID_ARG: return "GEMM_ERR_INVALID_ARG: an argument violates the documented rules";
     case GEMM_ERR_UNSUPPORTED: return "GEMM_ERR_UNSUPPORTED: valid, but outside what the kernels cover";
     case GEMM_ERR_HIP: return "GEMM_ERR_HIP: the HIP runtime refused the launch";
-    case GEMM_ERR_NOMEM: return "GEMM_ERR_NOMEM: host allocation failed";
+    case GEMM_ERR_NOMEM: return "GEMM_ERR_NOMEM: allocation failed (plan, or device workspace at run)";
     default: return "unknown status";
     }
 }

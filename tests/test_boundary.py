@@ -120,6 +120,33 @@ def test_kernel_choice_by_regime():
     assert kern(0, 8, 8) == "none"
 
 
+def test_repacking_choice():
+    """Rows that are not multiples of 8 elements: shapes for the direct or
+    streaming kernels repack the offending operands (suffix _pka/_pkb/_pkab);
+    small products use the staged kernel's element-wide loads instead."""
+    def kern(*a, **k):
+        with mpg.Plan(*a, **k) as p:
+            return p.kernel
+    assert kern(4095, 4095, 4095) == "gemm_256x256x64m16_nn_direct_pkab"
+    # K odd: only K-contiguous operands are affected
+    assert kern(1000, 1000, 999).endswith("nn_direct_pka")
+    assert kern(1000, 1000, 999, layout_b=GEMM_COL_MAJOR).endswith("nt_direct_pkab")
+    assert kern(1000, 1000, 999, layout_a=GEMM_COL_MAJOR).endswith("tn_direct")
+    # odd leading dimension with aligned extents
+    assert kern(1024, 1024, 1024, lda=1025).endswith("nn_direct_pka")
+    assert kern(1024, 1024, 1024, ldb=1028).endswith("nn_direct_pkb")
+    # deep K with few tiles: repacked and split
+    assert kern(50, 333, 4100) == "gemm_128x128x64m16_nn_direct_sk8_pkab"
+    # skinny NT: streaming kernel on repacked operands
+    assert kern(7, 4097, 4099, layout_b=GEMM_COL_MAJOR) == "gemm_stream16x16_nt_direct_pkab"
+    # small or batched-small: no copies
+    assert kern(127, 257, 33) == "gemm_64x64x64_nn_narrow"
+    assert kern(33, 33, 33, batch=1000, stride_a=33 * 33, stride_b=33 * 33,
+                stride_c=33 * 33).endswith("narrow")
+    # K = 0 reads no operand
+    assert "_pk" not in kern(1000, 1000, 0, lda=1)
+
+
 def test_run_rejects_bad_arguments_before_launch():
     with mpg.Plan(64, 64, 64) as p:
         h = p.handle

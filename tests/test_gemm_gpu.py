@@ -351,7 +351,9 @@ def test_split_k_repeatable_and_interleaved():
     check_bound(c_logical(c2, C2.cpu()), ref2, scale2, c2.out_type, "split-K interleaved")
 
 
-def test_split_k_plan_with_misaligned_pointers_runs_unsplit():
+def test_split_k_plan_with_misaligned_pointer_repacks():
+    """A split-K plan run with a misaligned A: A is copied into the plan's
+    padded buffer and the split kernel runs on the copy."""
     M, N, K = 16, 1024, 2048
     case = gi.make_case(M, N, K, beta=1.0, seed=34)
     p = mpg.Plan(M, N, K)
@@ -362,4 +364,112 @@ def test_split_k_plan_with_misaligned_pointers_runs_unsplit():
     B, C = case.B.cuda(), case.C.cuda()
     run_case(case, A[1:], B, C)
     ref, scale = oracle_for(case)
-    check_bound(c_logical(case, C.cpu()), ref, scale, OUT_F16, "split-K plan, narrow run")
+    check_bound(c_logical(case, C.cpu()), ref, scale, OUT_F16, "split-K plan, misaligned A")
+
+
+# ------------------------------------------------------------ repacking
+
+def plan_kernel(case):
+    with mpg.Plan(case.M, case.N, case.K, case.layout_a, case.layout_b, case.out_type,
+                  case.lda, case.ldb, case.ldc, case.batch, case.stride_a,
+                  case.stride_b, case.stride_c) as p:
+        return p.kernel
+
+
+def expected_pack_suffix(case):
+    """Operands whose rows do not allow 16-byte loads: _pka, _pkb, _pkab."""
+    ca = case.K if case.layout_a == ROW_MAJOR else case.M
+    cb = case.N if case.layout_b == ROW_MAJOR else case.K
+    sa = case.stride_a if case.batch > 1 else 0
+    sb = case.stride_b if case.batch > 1 else 0
+    pa = any(v % 8 for v in (ca, case.lda, sa))
+    pb = any(v % 8 for v in (cb, case.ldb, sb))
+    return "_pk" + ("a" if pa else "") + ("b" if pb else "") if (pa or pb) else ""
+
+
+def nan_padding(case):
+    """NaN in every element of A and B beyond the logical rows' ends (the
+    repacking copies only the logical elements and zero-fills the rest)."""
+    ca = case.K if case.layout_a == ROW_MAJOR else case.M
+    cb = case.N if case.layout_b == ROW_MAJOR else case.K
+    A = case.A.reshape(-1, case.lda).clone()
+    A[:, ca:] = float("nan")
+    B = case.B.reshape(-1, case.ldb).clone()
+    B[:, cb:] = float("nan")
+    case.A, case.B = A.reshape(-1), B.reshape(-1)
+
+
+@pytest.mark.parametrize("out_type", [OUT_F16, OUT_F32])
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+def test_repacked_operands_all_layouts(la, lb, out_type):
+    """Shapes for the direct kernels (128 tile, split-K) whose row lengths
+    are not multiples of 8: odd M, N and K (so the K tail ends inside an
+    8-element chunk of a K-contiguous row), leading dimensions with
+    NaN-filled padding, beta on and off."""
+    shapes = [(300, 260, 1500, 3), (1000, 1000, 999, 0), (50, 333, 4100, 5),
+              (4097, 63, 1025, 1)]
+    for i, (M, N, K, extra) in enumerate(shapes):
+        lda = (K if la == ROW_MAJOR else M) + extra
+        ldb = (N if lb == ROW_MAJOR else K) + extra
+        case = gi.make_case(M, N, K, layout_a=la, layout_b=lb, out_type=out_type,
+                            lda=lda, ldb=ldb, alpha=-0.5, beta=0.0 if i == 1 else 2.0,
+                            seed=40 + i)
+        nan_padding(case)
+        kernel = plan_kernel(case)
+        suffix = expected_pack_suffix(case)
+        assert "direct" in kernel and kernel.endswith(suffix), (kernel, suffix)
+        rows = sample_rows(M, n_random=32) if M >= 1000 else None
+        parity(case, rows=rows, what=f"{kernel} {M}x{N}x{K} lda={lda} ldb={ldb}")
+
+
+def test_repacked_batched_odd_strides():
+    """Strided batch on the 128 tile with odd leading dimensions and hence
+    odd batch strides for A and B."""
+    M, N, K, batch = 520, 520, 200, 4
+    case = gi.make_case(M, N, K, lda=K + 1, ldb=N + 1, batch=batch, beta=1.0, seed=50)
+    kernel = plan_kernel(case)
+    assert "128x128" in kernel and kernel.endswith("_pkab"), kernel
+    parity(case, what=f"{kernel} batch {batch}")
+
+
+@pytest.mark.parametrize("M", [7, 40])
+def test_repacked_streaming(M):
+    """Skinny NT (streaming kernel) with K odd: both operands repacked."""
+    N, K = 4097, 4099
+    case = gi.linear_case(M, N, K, seed=51)
+    kernel = plan_kernel(case)
+    assert "stream" in kernel and kernel.endswith("_pkab"), kernel
+    parity(case, what=f"{kernel} {M}x{N}x{K}")
+
+
+def test_repacked_full_tile_sampled():
+    """The 256 tile on 4095^3 (every operand repacked), sampled rows."""
+    n = 4095
+    case = gi.make_case(n, n, n, layout_b=COL_MAJOR, beta=1.0, seed=52)
+    kernel = plan_kernel(case)
+    assert "256x256" in kernel and kernel.endswith("_pkab"), kernel
+    parity(case, rows=sample_rows(n, n_random=48), what=kernel)
+
+
+def test_misaligned_pointers_repack_on_direct_tile_and_reuse_buffer():
+    """A direct-tile plan given misaligned A and B pointers copies both; a
+    second run of the same plan with other data reuses the copies."""
+    M, N, K = 1000, 1000, 1000
+    p = mpg.Plan(M, N, K, ROW_MAJOR, COL_MAJOR)
+    assert "direct" in p.kernel and "_pk" not in p.kernel, p.kernel
+    try:
+        for seed, (oa, ob) in ((60, (1, 3)), (61, (5, 2))):
+            case = gi.make_case(M, N, K, layout_b=COL_MAJOR, beta=1.0, seed=seed)
+            A = torch.zeros(case.A.numel() + oa, dtype=torch.float16, device="cuda")
+            B = torch.zeros(case.B.numel() + ob, dtype=torch.float16, device="cuda")
+            A[oa:] = case.A.cuda()
+            B[ob:] = case.B.cuda()
+            C = case.C.cuda()
+            p.run(A[oa:], B[ob:], C, case.alpha, case.beta)
+            torch.cuda.synchronize()
+            rows = sample_rows(M, n_random=32)
+            ref, scale = oracle_for(case, rows)
+            check_bound(c_logical(case, C.cpu(), rows), ref, scale, OUT_F16,
+                        f"misaligned run seed {seed}")
+    finally:
+        p.close()
