@@ -37,17 +37,23 @@
  * (C^T = B^T A^T).
  *
  * Ownership: the caller owns A, B, C and the stream.  A plan owns its host
- * memory and, if it cuts K into slices (split-K: its kernel name ends in
- * "_sk<slices>"), a device workspace of fp32 partial tiles (slices x tiles x
- * 64 KiB, plus 4 bytes per tile), allocated and cleared on the current device
- * by the plan's first run and freed by gemm_f16f32_destroy.  Runs of one
- * split-K plan share that workspace: they may follow each other on a stream
- * but must not execute concurrently (on two streams at once); any other plan
- * may be run concurrently on several streams.  gemm_f16f32_run is
- * asynchronous on the given stream: A, B, C must stay valid until the stream
- * has passed the launched kernel.  A plan may be destroyed as soon as
- * gemm_f16f32_run returns; destroying a plan that holds a workspace first
- * waits for the device to finish its work.
+ * memory and up to two device buffers, each allocated on the current device
+ * by the first run that needs it and freed by gemm_f16f32_destroy:
+ *   - split-K (kernel name contains "_sk<slices>"): fp32 partial tiles
+ *     (slices x tiles x 64 KiB, plus 4 bytes per tile), cleared when
+ *     allocated;
+ *   - repacking (kernel name ends in "_pka", "_pkb" or "_pkab", or a run of a
+ *     direct or streaming plan given an A or B pointer that is not 16-byte
+ *     aligned): dense copies of A and B with rows padded to a multiple of 8
+ *     elements (2 x batch x rows x padded row length bytes for A and B
+ *     together, at most).
+ * Runs of one plan that holds such a buffer share it: they may follow each
+ * other on a stream but must not execute concurrently (on two streams at
+ * once); a plan with neither may be run concurrently on several streams.
+ * gemm_f16f32_run is asynchronous on the given stream: A, B, C must stay
+ * valid until the stream has passed the launched kernels.  A plan may be
+ * destroyed as soon as gemm_f16f32_run returns; destroying a plan that holds
+ * a device buffer first waits for the device to finish its work.
  *
  * Errors: every function returns a status code (GEMM_OK == 0 or a negative
  * GEMM_ERR_*); no exception crosses this boundary and there is no global
@@ -104,7 +110,8 @@ int gemm_f16f32_plan(gemm_f16f32_plan_t *out,
                      int64_t stride_c);
 
 /*
- * Runs a plan: launches one kernel on `stream` and returns without waiting.
+ * Runs a plan: launches its kernels on `stream` (the GEMM, preceded by one
+ * copy kernel per repacked operand) and returns without waiting.
  *   A, B   device pointers to binary16 storage (const), described by the plan.
  *   C      device pointer to binary16 or fp32 storage, read (beta != 0) and
  *          written.
@@ -113,29 +120,37 @@ int gemm_f16f32_plan(gemm_f16f32_plan_t *out,
  * Rules: plan != NULL; A, B, C non-NULL unless the plan's M*N == 0 (then the
  * call is a no-op and returns GEMM_OK) -- else INVALID_ARG.  The address range
  * of C must not overlap those of A or B -> INVALID_ARG.  Pointer alignment is
- * never an error: 16-byte-aligned operands whose leading dimensions are
- * multiples of 8 take the 128-bit load path, others a narrow-load path with
- * the same results up to summation order (the narrow path does not split
- * K).  A split-K plan's first run allocates its workspace (failure -> NOMEM)
- * and synchronises the device once; running it later on another device than
- * that first run's -> INVALID_ARG.  A failed launch -> GEMM_ERR_HIP.
+ * never an error: 16-byte-aligned operands whose leading dimensions,
+ * contiguous extents and batch strides are multiples of 8 are read in place
+ * with 128-bit loads; other operands are either copied first into the
+ * plan's padded buffer (direct and streaming kernels) or read with
+ * element-wide loads (the small staged tiles, which do not split K), with
+ * the same results up to summation order.  The first run that needs a
+ * device buffer allocates it (failure -> NOMEM; the split-K buffer's first
+ * run also synchronises the device once); running the plan later on another
+ * device than the one holding the buffer -> INVALID_ARG.  A failed launch ->
+ * GEMM_ERR_HIP.
  */
 int gemm_f16f32_run(gemm_f16f32_plan_t plan,
                     const void *A, const void *B, void *C,
                     float alpha, float beta, void *stream);
 
-/* Frees a plan (and its workspace, after waiting for the device to finish
- * its work).  NULL is a no-op.  Returns GEMM_OK. */
+/* Frees a plan (and its device buffers, after waiting for the device to
+ * finish its work).  NULL is a no-op.  Returns GEMM_OK. */
 int gemm_f16f32_destroy(gemm_f16f32_plan_t plan);
 
 /* A static, NUL-terminated description of a status code (never NULL). */
 const char *gemm_f16f32_status_string(int status);
 
 /*
- * Name of the kernel configuration the plan chose (tile sizes, layout path,
- * "vec16" when the shapes allow 128-bit loads, else "narrow"), as a
- * NUL-terminated string owned by the plan (valid until it is destroyed), or
- * "none" for a no-op plan and "invalid" for NULL.  Diagnostic only.
+ * Name of the kernel configuration the plan chose, as a NUL-terminated
+ * string owned by the plan (valid until it is destroyed), or "none" for a
+ * no-op plan and "invalid" for NULL.  Diagnostic only.  Form:
+ * gemm_<tile>_<nn|nt|tn|tt>_<path>[_sk<slices>][_pka|_pkb|_pkab], where path
+ * is "direct" (direct or streaming kernel), "vec16" (staged tile, 128-bit
+ * loads) or "narrow" (staged tile, element-wide loads), _sk gives the K
+ * slices of a split-K plan and _pk the operands repacked because of their
+ * shape.
  */
 const char *gemm_f16f32_plan_kernel(gemm_f16f32_plan_t plan);
 

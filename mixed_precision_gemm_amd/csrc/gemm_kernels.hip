@@ -1249,48 +1249,59 @@ __global__ __launch_bounds__(512) void gemm_stream(GemmArgs p) {
 // pages of the operand) and shifts them into place.  HBM bound: the operand
 // is read once and written once.
 // ---------------------------------------------------------------------------
-struct PackArgs {
+struct PackOperand {
     const _Float16 *src;
     _Float16 *dst;
-    int64_t ld, stride, outer, cols, ld8, batch;
+    int64_t ld, stride, outer, cols, ld8;
+    uint32_t chunks;   // batch * outer * ld8 / 8
+};
+struct PackArgs {
+    PackOperand op[2];   // op[1].chunks == 0 when only one operand is copied
 };
 
-// Chunk counts below 2^31 (checked by the planner and the launcher): 32-bit
-// index math, and c + grid stride stays below 2^32.
-__global__ __launch_bounds__(256) void gemm_pack16(PackArgs a) {
+// Copies chunk c of one operand (see above).
+__device__ inline void pack_chunk(const PackOperand &a, uint32_t c) {
     const uint32_t cpr = (uint32_t)(a.ld8 / 8);     // chunks per packed row
     const uint32_t outer = (uint32_t)a.outer;
-    const uint32_t total = (uint32_t)(a.batch * a.outer) * cpr;
+    const uint32_t j = c % cpr, row = c / cpr;      // row over all batch items
+    const uint32_t b = row / outer, r = row - b * outer;
+    const int64_t left = a.cols - 8 * (int64_t)j;
+    const int nvalid = left >= 8 ? 8 : (int)left;   // >= 1: j < ceil(cols / 8)
+    const uintptr_t first = (uintptr_t)(a.src + (int64_t)b * a.stride + (int64_t)r * a.ld + 8 * (int64_t)j);
+    const uintptr_t blk = first & ~(uintptr_t)15;
+    const int sh = (int)(first & 15);                // even: fp16 elements
+    const u32x4 w0 = *(const u32x4 *)blk;
+    // The second block holds a valid element only if the chunk's valid bytes
+    // run past the first.
+    const u32x4 w1 = sh + 2 * nvalid > 16 ? *(const u32x4 *)(blk + 16) : u32x4{0, 0, 0, 0};
+    const int s4 = sh >> 2, sb = sh & 3;
+    uint32_t e[5];
+    // e[i] = dword s4 + i of the 8-dword window w0:w1.
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        const int k = s4 + i;
+        e[i] = k == 0 ? w0[0] : k == 1 ? w0[1] : k == 2 ? w0[2] : k == 3 ? w0[3]
+             : k == 4 ? w1[0] : k == 5 ? w1[1] : k == 6 ? w1[2] : w1[3];
+    }
+    u32x4 out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t v = __builtin_amdgcn_alignbyte(e[i + 1], e[i], (uint32_t)sb);
+        if (2 * i >= nvalid) v = 0;
+        else if (2 * i + 1 >= nvalid) v &= 0xffffu;
+        out[i] = v;
+    }
+    *(u32x4 *)(a.dst + (int64_t)row * a.ld8 + 8 * (int64_t)j) = out;
+}
+
+// One launch copies one or both operands: chunks [0, op[0].chunks) of A (or
+// B), then op[1]'s.  Chunk counts sum below 2^31 (checked by the planner and
+// the launcher): 32-bit index math, and c + grid stride stays below 2^32.
+__global__ __launch_bounds__(256) void gemm_pack16(PackArgs a) {
+    const uint32_t n0 = a.op[0].chunks, total = n0 + a.op[1].chunks;
     for (uint32_t c = blockIdx.x * 256u + threadIdx.x; c < total; c += gridDim.x * 256u) {
-        const uint32_t j = c % cpr, row = c / cpr;  // row over all batch items
-        const uint32_t b = row / outer, r = row - b * outer;
-        const int64_t left = a.cols - 8 * (int64_t)j;
-        const int nvalid = left >= 8 ? 8 : (int)left;   // >= 1: j < ceil(cols / 8)
-        const uintptr_t first = (uintptr_t)(a.src + (int64_t)b * a.stride + (int64_t)r * a.ld + 8 * (int64_t)j);
-        const uintptr_t blk = first & ~(uintptr_t)15;
-        const int sh = (int)(first & 15);            // even: fp16 elements
-        const u32x4 w0 = *(const u32x4 *)blk;
-        // The second block holds a valid element only if the chunk's valid
-        // bytes run past the first.
-        const u32x4 w1 = sh + 2 * nvalid > 16 ? *(const u32x4 *)(blk + 16) : u32x4{0, 0, 0, 0};
-        const int s4 = sh >> 2, sb = sh & 3;
-        uint32_t e[5];
-        // e[i] = dword s4 + i of the 8-dword window w0:w1.
-#pragma unroll
-        for (int i = 0; i < 5; ++i) {
-            const int k = s4 + i;
-            e[i] = k == 0 ? w0[0] : k == 1 ? w0[1] : k == 2 ? w0[2] : k == 3 ? w0[3]
-                 : k == 4 ? w1[0] : k == 5 ? w1[1] : k == 6 ? w1[2] : w1[3];
-        }
-        u32x4 out;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t v = __builtin_amdgcn_alignbyte(e[i + 1], e[i], (uint32_t)sb);
-            if (2 * i >= nvalid) v = 0;
-            else if (2 * i + 1 >= nvalid) v &= 0xffffu;
-            out[i] = v;
-        }
-        *(u32x4 *)(a.dst + (int64_t)row * a.ld8 + 8 * (int64_t)j) = out;
+        if (c < n0) pack_chunk(a.op[0], c);
+        else pack_chunk(a.op[1], c - n0);
     }
 }
 
@@ -1374,14 +1385,14 @@ bool ranges_overlap(uintptr_t a, int64_t a_bytes, uintptr_t b, int64_t b_bytes) 
     return a < b + (uintptr_t)b_bytes && b < a + (uintptr_t)a_bytes;
 }
 
-// Whether the packed copy of operand 0 (A) or 1 (B) has fewer than 2^31
-// 16-byte chunks: the pack kernel's 32-bit index plus its grid stride (at
-// most 2^21) then never wraps.
-bool packable(const gemm_f16f32_plan_s &p, int which) {
-    const bool rm = (which == 0 ? p.layout_a : p.layout_b) == GEMM_ROW_MAJOR;
-    const int64_t outer = which == 0 ? (rm ? p.M : p.K) : (rm ? p.K : p.N);
-    const int64_t ld8 = which == 0 ? p.ld8_a : p.ld8_b;
-    return p.batch * outer * (ld8 / 8) < (int64_t(1) << 31);
+// Whether the packed copies of A and B together have fewer than 2^31 16-byte
+// chunks: the pack kernel's 32-bit index plus its grid stride (at most 2^21)
+// then never wraps.  (Counting both keeps the test independent of which
+// operands a run copies.)
+bool packable(const gemm_f16f32_plan_s &p) {
+    const int64_t outer_a = p.layout_a == GEMM_ROW_MAJOR ? p.M : p.K;
+    const int64_t outer_b = p.layout_b == GEMM_ROW_MAJOR ? p.K : p.N;
+    return p.batch * (outer_a * (p.ld8_a / 8) + outer_b * (p.ld8_b / 8)) < (int64_t(1) << 31);
 }
 
 }  // namespace
@@ -1404,8 +1415,8 @@ extern "C" int gemm_f16f32_run(gemm_f16f32_plan_t plan, const void *A,
     // is not 16-byte aligned.  The staged tiles take a misaligned pointer
     // with element-wide loads instead.
     const bool fast = p.vec_ok && kTiles[p.tile].kind != KIND_STAGED;
-    const bool pack_a = p.K > 0 && ((p.pack & 1) || (fast && packable(p, 0) && (uintptr_t)A % 16 != 0));
-    const bool pack_b = p.K > 0 && ((p.pack & 2) || (fast && packable(p, 1) && (uintptr_t)B % 16 != 0));
+    const bool pack_a = p.K > 0 && ((p.pack & 1) || (fast && packable(p) && (uintptr_t)A % 16 != 0));
+    const bool pack_b = p.K > 0 && ((p.pack & 2) || (fast && packable(p) && (uintptr_t)B % 16 != 0));
     const bool vec = p.vec_ok && (pack_a || (uintptr_t)A % 16 == 0) && (pack_b || (uintptr_t)B % 16 == 0);
     const int64_t celem = p.out_type == GEMM_OUT_F32 ? 4 : 2;
     const bool c_vec = (p.ldc % 4 == 0) && (p.stride_c % 4 == 0) &&
@@ -1475,28 +1486,25 @@ extern "C" int gemm_f16f32_run(gemm_f16f32_plan_t plan, const void *A,
             plan->pack_ws = buf;
             plan->pack_device = dev;
         }
-        auto pack = [&](const void *src, int layout, int64_t rows_rm, int64_t cols_rm, int64_t ld,
-                        int64_t stride, int64_t ld8, _Float16 *dst) {
-            PackArgs pa;
-            pa.src = (const _Float16 *)src;
-            pa.dst = dst;
-            pa.ld = ld;
-            pa.stride = stride;
-            pa.outer = layout == GEMM_ROW_MAJOR ? rows_rm : cols_rm;
-            pa.cols = layout == GEMM_ROW_MAJOR ? cols_rm : rows_rm;
-            pa.ld8 = ld8;
-            pa.batch = p.batch;
-            const int64_t chunks = pa.batch * pa.outer * (ld8 / 8);
-            const int64_t blocks = std::min<int64_t>((chunks + 255) / 256, 8192);
-            void *pargs[] = {&pa};
-            return hipLaunchKernel((const void *)gemm_pack16, dim3((unsigned)blocks), dim3(256),
-                                   pargs, 0, (hipStream_t)stream);
+        auto operand = [&](const void *src, int layout, int64_t rows_rm, int64_t cols_rm,
+                           int64_t ld, int64_t stride, int64_t ld8, _Float16 *dst) {
+            PackOperand o;
+            o.src = (const _Float16 *)src;
+            o.dst = dst;
+            o.ld = ld;
+            o.stride = stride;
+            o.outer = layout == GEMM_ROW_MAJOR ? rows_rm : cols_rm;
+            o.cols = layout == GEMM_ROW_MAJOR ? cols_rm : rows_rm;
+            o.ld8 = ld8;
+            o.chunks = (uint32_t)(p.batch * o.outer * (ld8 / 8));
+            return o;
         };
+        PackArgs pa = {};
+        int nops = 0;
         _Float16 *pa_dst = (_Float16 *)plan->pack_ws;
         _Float16 *pb_dst = (_Float16 *)((char *)plan->pack_ws + p.pack_off_b);
         if (pack_a) {
-            if (pack(A, p.layout_a, p.M, p.K, p.lda, p.stride_a, p.ld8_a, pa_dst) != hipSuccess)
-                return GEMM_ERR_HIP;
+            pa.op[nops++] = operand(A, p.layout_a, p.M, p.K, p.lda, p.stride_a, p.ld8_a, pa_dst);
             const int64_t outer = p.layout_a == GEMM_ROW_MAJOR ? p.M : p.K;
             a.A = pa_dst;
             a.lda = p.ld8_a;
@@ -1504,14 +1512,19 @@ extern "C" int gemm_f16f32_run(gemm_f16f32_plan_t plan, const void *A,
             a.extent_a = outer * p.ld8_a;
         }
         if (pack_b) {
-            if (pack(B, p.layout_b, p.K, p.N, p.ldb, p.stride_b, p.ld8_b, pb_dst) != hipSuccess)
-                return GEMM_ERR_HIP;
+            pa.op[nops++] = operand(B, p.layout_b, p.K, p.N, p.ldb, p.stride_b, p.ld8_b, pb_dst);
             const int64_t outer = p.layout_b == GEMM_ROW_MAJOR ? p.K : p.N;
             a.B = pb_dst;
             a.ldb = p.ld8_b;
             a.sb = outer * p.ld8_b;
             a.extent_b = outer * p.ld8_b;
         }
+        const int64_t chunks = (int64_t)pa.op[0].chunks + pa.op[1].chunks;
+        const int64_t blocks = std::min<int64_t>((chunks + 255) / 256, 8192);
+        void *pargs[] = {&pa};
+        if (hipLaunchKernel((const void *)gemm_pack16, dim3((unsigned)blocks), dim3(256), pargs, 0,
+                            (hipStream_t)stream) != hipSuccess)
+            return GEMM_ERR_HIP;
     }
 
     const int ak = p.layout_a == GEMM_ROW_MAJOR;   // A K-contiguous

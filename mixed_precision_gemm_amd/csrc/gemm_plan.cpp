@@ -158,11 +158,10 @@ extern "C" int gemm_f16f32_plan(gemm_f16f32_plan_t *out, int64_t M, int64_t N,
     if (a_ok && b_ok) {
         p->vec_ok = 1;
     } else if (kTiles[p->tile].kind != KIND_STAGED && K > 0 &&
-               (a_ok || batch * outer_a * (p->ld8_a / 8) < (int64_t(1) << 31)) &&
-               (b_ok || batch * outer_b * (p->ld8_b / 8) < (int64_t(1) << 31))) {
+               batch * (outer_a * (p->ld8_a / 8) + outer_b * (p->ld8_b / 8)) < (int64_t(1) << 31)) {
         // Shapes for the direct or streaming kernels repack the unaligned
         // operands: one extra pass over them instead of element-wide loads
-        // for the whole K loop (copies of fewer than 2^31 16-byte chunks).
+        // for the whole K loop (copies of A and B below 2^31 16-byte chunks).
         p->vec_ok = 1;
         p->pack = (a_ok ? 0 : 1) | (b_ok ? 0 : 2);
     } else {
