@@ -19,7 +19,7 @@ enum TileId : int {
     TILE_STREAM16 = 5,       // skinny M <= 16, K-contiguous A and B
     TILE_STREAM32 = 6,       // skinny M <= 32
     TILE_STREAM64 = 7,       // skinny M <= 64
-    TILE_STREAM128 = 8,      // skinny M <= 128
+    TILE_STREAM32W = 8,      // skinny M <= 32, wide N: 64 columns per workgroup
     NUM_TILES = 9
 };
 
@@ -47,7 +47,7 @@ constexpr TileShape kTiles[NUM_TILES] = {
     {16, 16, 32, 1, 1, 1, KIND_STREAM, "stream16x16"},
     {32, 16, 32, 1, 1, 1, KIND_STREAM, "stream32x16"},
     {64, 16, 32, 1, 1, 1, KIND_STREAM, "stream64x16"},
-    {128, 16, 32, 1, 1, 1, KIND_STREAM, "stream128x16"},
+    {32, 64, 32, 1, 1, 1, KIND_STREAM, "stream32x64"},
 };
 
 // Tile of the staged kernel that serves operands the direct kernel cannot

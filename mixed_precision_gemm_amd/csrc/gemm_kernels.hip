@@ -1195,6 +1195,10 @@ __global__ __launch_bounds__(512) void gemm_stream(GemmArgs p) {
                 fa[u][mb] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(
                     ra, (a_ok[mb] && kin) ? a_off[mb] + kb : kOutOfRange, 0, 0));
         }
+        // All UNROLL steps' loads are issued before the first MFMA waits on
+        // one (the scheduler would otherwise interleave them and keep fewer
+        // bytes in flight).
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
@@ -1371,7 +1375,7 @@ struct KernelTable {
         fill_stream<TILE_STREAM16>(k[TILE_STREAM16]);
         fill_stream<TILE_STREAM32>(k[TILE_STREAM32]);
         fill_stream<TILE_STREAM64>(k[TILE_STREAM64]);
-        fill_stream<TILE_STREAM128>(k[TILE_STREAM128]);
+        fill_stream<TILE_STREAM32W>(k[TILE_STREAM32W]);
     }
 };
 

@@ -39,9 +39,15 @@ int64_t operand_extent(int64_t rows, int64_t cols, int64_t ld, int64_t batch,
 // small staged tiles, the 32-row one for skinny M (token counts of a linear
 // layer).
 int choose_tile(int64_t M, int64_t N, int64_t K, int64_t batch, bool kc_both, bool vec_ok) {
-    // Skinny M with K-contiguous A and B streams B through registers; at
-    // most 64 rows of A are reused per loaded column of B.
-    if (kc_both && M <= 64) return M <= 16 ? TILE_STREAM16 : M <= 32 ? TILE_STREAM32 : TILE_STREAM64;
+    // Skinny M with K-contiguous A and B streams B through registers.  Every
+    // workgroup re-reads its rows of A, so wide N (at least 160 workgroups of
+    // 64 columns) takes 64 columns per workgroup from M = 17 on; from M = 33
+    // on, N that yields 64 or more 128-wide tiles goes to the 128 tile
+    // (split-K) instead, which shares A and B through LDS.  (Measured on the
+    // K = 4096 linear shapes.)
+    if (kc_both && M <= 16) return TILE_STREAM16;
+    if (kc_both && M <= 32) return ceil_div(N, 64) >= 160 ? TILE_STREAM32W : TILE_STREAM32;
+    if (kc_both && M <= 64 && ceil_div(N, 128) < 64) return TILE_STREAM64;
     auto count = [&](int t) {
         return ceil_div(M, kTiles[t].bm) * ceil_div(N, kTiles[t].bn) * batch;
     };

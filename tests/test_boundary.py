@@ -105,6 +105,10 @@ def test_kernel_choice_by_regime():
     # skinny, K-contiguous A and B: streaming kernel; other layouts: small tiles
     assert kern(16, 4096, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_stream16x16")
     assert kern(40, 4096, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_stream64x16")
+    # wide N: 64 columns per streaming workgroup (M <= 32), else the 128 tile
+    assert kern(32, 11008, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_stream32x64")
+    assert kern(32, 4096, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_stream32x16")
+    assert kern(64, 11008, 4096, layout_b=GEMM_COL_MAJOR).endswith("nt_direct_sk3")
     # skinny with row-major B: too few tiles for the CUs, so the 128 tile with
     # its K cut into slices (split-K, suffix _sk<slices>)
     assert kern(16, 4096, 4096) == "gemm_128x128x64m16_nn_direct_sk8"

@@ -58,11 +58,22 @@ def test_square_beta1_sampled(n, lb):
 
 
 @pytest.mark.parametrize("N", [4096, 11008, 12288])
-@pytest.mark.parametrize("M", [16, 128, 2048, 8192])
+@pytest.mark.parametrize("M", [16, 32, 64, 128, 2048, 8192])
 def test_linear_layer_shapes(M, N):
     case = gi.linear_case(M, N)
     rows = None if M <= 128 else sample_rows(M, n_random=96)
     parity(case, rows=rows, what=f"linear M={M} N={N}")
+
+
+@pytest.mark.parametrize("shape", [(24, 10250, 1000), (5, 10260, 77), (31, 16384, 4104)])
+def test_streaming_wide_ragged(shape):
+    """The 64-column streaming workgroup with N off its grid, K off the
+    32-deep step, and rows of A past M."""
+    M, N, K = shape
+    case = gi.make_case(M, N, K, layout_b=COL_MAJOR, alpha=1.5, beta=-1.0, seed=70)
+    with mpg.Plan(M, N, K, ROW_MAJOR, COL_MAJOR) as p:
+        assert "stream" in p.kernel, p.kernel
+    parity(case, what=f"streaming {M}x{N}x{K}")
 
 
 @pytest.mark.parametrize("kind", ["sq64", "qk"])
