@@ -100,6 +100,60 @@ def test_large_tiles_ragged_all_layouts(shape, tile, la, lb):
     parity(case, rows=rows, what=f"{kernel} {M}x{N}x{K}")
 
 
+# ------------------------------------------------------- whole 256 tiles
+
+@pytest.mark.parametrize("out_type", [OUT_F16, OUT_F32])
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+def test_tile256_odd_stage_count_all_layouts(la, lb, out_type):
+    """512 whole 256 x 256 tiles (two per CU) with an odd number of 64-deep
+    stages (K = 192: the last stage sits in ring slot 0), alpha and beta !=
+    0; sampled rows."""
+    M, N, K = 4096, 8192, 192
+    case = gi.make_case(M, N, K, layout_a=la, layout_b=lb, out_type=out_type,
+                        alpha=1.5, beta=-0.5, seed=80)
+    kernel = plan_kernel(case)
+    assert "256x256" in kernel, kernel
+    parity(case, rows=sample_rows(M, n_random=48), what=f"{kernel} {M}x{N}x{K}")
+
+
+def test_tile256_uneven_grid_one_stage():
+    """544 tiles (not a multiple of the CU count) of a single stage each
+    (K = 64)."""
+    M, N, K = 8192, 4352, 64
+    case = gi.make_case(M, N, K, beta=1.0, seed=81)
+    kernel = plan_kernel(case)
+    assert "256x256" in kernel, kernel
+    parity(case, rows=sample_rows(M, n_random=64), what=f"{kernel} {M}x{N}x{K}")
+
+
+def test_tile256_batched():
+    """Strided batch of 8 products of 2048^2 x 320 on the 256 tile, fp32 C."""
+    M, N, K, batch = 2048, 2048, 320, 8
+    case = gi.make_case(M, N, K, batch=batch, out_type=OUT_F32, beta=2.0, seed=82)
+    kernel = plan_kernel(case)
+    assert "256x256" in kernel, kernel
+    rows = sample_rows(M, n_random=24)
+    dC = run_case(case)
+    torch.cuda.synchronize()
+    got = c_logical(case, dC.cpu(), rows)
+    ref, scale = oracle_for(case, rows)
+    check_bound(got, ref, scale, OUT_F32, f"{kernel} batch {batch}")
+
+
+def test_tile256_misaligned_c():
+    """The 256 tile with a C pointer that only allows element-wide access."""
+    M, N, K = 4096, 8192, 128
+    case = gi.make_case(M, N, K, beta=1.0, seed=83)
+    assert "256x256" in plan_kernel(case)
+    C = torch.zeros(case.C.numel() + 1, dtype=torch.float16, device="cuda")
+    C[1:] = case.C.cuda()
+    A, B = case.A.cuda(), case.B.cuda()
+    run_case(case, A, B, C[1:])
+    rows = sample_rows(M, n_random=32)
+    ref, scale = oracle_for(case, rows)
+    check_bound(c_logical(case, C[1:].cpu(), rows), ref, scale, OUT_F16, "misaligned C")
+
+
 # ----------------------------------------------------- layouts and types
 
 SWEEP = [(1, 1, 1), (2, 3, 5), (8, 8, 8), (31, 33, 17), (32, 64, 64),
