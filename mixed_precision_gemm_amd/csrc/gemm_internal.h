@@ -20,7 +20,8 @@ enum TileId : int {
     TILE_STREAM32 = 6,       // skinny M <= 32
     TILE_STREAM64 = 7,       // skinny M <= 64
     TILE_STREAM32W = 8,      // skinny M <= 32, wide N: 64 columns per workgroup
-    NUM_TILES = 9
+    TILE_128x128_D4 = 9,     // the 128 tile on a four-slot ring (one workgroup per CU)
+    NUM_TILES = 10
 };
 
 // Three kernel families share the tile table:
@@ -48,6 +49,7 @@ constexpr TileShape kTiles[NUM_TILES] = {
     {32, 16, 32, 1, 1, 1, KIND_STREAM, "stream32x16"},
     {64, 16, 32, 1, 1, 1, KIND_STREAM, "stream64x16"},
     {32, 64, 32, 1, 1, 1, KIND_STREAM, "stream32x64"},
+    {128, 128, 64, 2, 2, 4, KIND_DIRECT16, "128x128x64m16d4"},
 };
 
 // Tile of the staged kernel that serves operands the direct kernel cannot

@@ -12,7 +12,7 @@
 //     split-K, one K slice of it -- and walks K in steps of BK, keeping the
 //     fp32 accumulators in registers for the whole K loop ([GEMM] §3.2, §6.2);
 //   * each K step stages an A tile (BM x BK) and a B tile (BK x BN) from global
-//     memory into one slot of a two-slot LDS ring ([OPS] §3.5, [GEMM] §4.1):
+//     memory into one slot of a multi-slot LDS ring ([OPS] §3.5, [GEMM] §4.1):
 //     the direct kernels (gemm_direct16) use buffer loads that write LDS
 //     without passing through registers, the staged kernel (gemm_staged)
 //     128-bit loads through registers; the loads for a later step are issued
@@ -842,10 +842,10 @@ struct DirectOperand {
 // wave (rows or columns wb .. wb + 16 NBLK - 1 of a BK = 64 ring slot), so
 // that every fragment read is a base register plus an immediate offset.  Two
 // sets: `cur` addresses the slot of the stage being computed, `nxt` the slot
-// of the next one.  Slot 0 starts at 0 and slot 1 one slot size (a power of
-// two) above it, and every slot-0 address is below the slot size, so
-// advancing a stage is one XOR per register (advance()) and no other address
-// arithmetic is left in the K loop.
+// of the next one.  Slot s starts s slot sizes (a power of two) above slot
+// 0, which starts at 0, and every slot-0 address is below the slot size, so
+// advancing a stage is one add-and-wrap per register (one XOR for a two-slot
+// ring; advance()) and no other address arithmetic is left in the K loop.
 //   K-contiguous: row r = wb + 16 i + l%16 keeps its K chunk kv = 4 s + l/16
 //     at kv ^ swz16(r) = (l/16 ^ swz16(l%16)) ^ 4 s (swz16 depends on r % 16
 //     only): two bases, by s, and 16 rows per block as immediates.
@@ -853,11 +853,13 @@ struct DirectOperand {
 //     k = 32 s + 4 t + 8 (l/16) + (l%16)/4 sits in chunk (n >> 3) ^ mn_swz(k),
 //     and mn_swz(k) depends only on k%4 and bit 3 of k, both fixed by the
 //     lane: one base per block i, rows 32 s + 4 t as immediates.
-template <int R, int BK, bool KC, int NBLK, int SLOT_BYTES>
+template <int R, int BK, bool KC, int NBLK, int SLOT_BYTES, int NSLOT>
 struct Frag16 {
     static_assert(BK == 64, "128-byte K rows");
     static_assert((SLOT_BYTES & (SLOT_BYTES - 1)) == 0 && SLOT_BYTES <= 65536,
-                  "slot size a power of two: advance() flips one address bit");
+                  "slot size a power of two");
+    static_assert((NSLOT & (NSLOT - 1)) == 0 && NSLOT >= 2 && NSLOT * SLOT_BYTES <= 160 * 1024,
+                  "a power-of-two number of slots");
     static constexpr int NCLS = KC ? 2 : NBLK;
     uint32_t cur[NCLS], nxt[NCLS];
 
@@ -880,11 +882,18 @@ struct Frag16 {
         for (int c = 0; c < NCLS; ++c) nxt[c] = cur[c] + SLOT_BYTES;
     }
 
+    // Next stage: every base moves one slot on, wrapping around the ring
+    // (a single XOR for two slots).
     __device__ void advance() {
 #pragma unroll
         for (int c = 0; c < NCLS; ++c) {
-            cur[c] ^= (uint32_t)SLOT_BYTES;
-            nxt[c] ^= (uint32_t)SLOT_BYTES;
+            if constexpr (NSLOT == 2) {
+                cur[c] ^= (uint32_t)SLOT_BYTES;
+                nxt[c] ^= (uint32_t)SLOT_BYTES;
+            } else {
+                cur[c] = (cur[c] + (uint32_t)SLOT_BYTES) & (uint32_t)(NSLOT * SLOT_BYTES - 1);
+                nxt[c] = (nxt[c] + (uint32_t)SLOT_BYTES) & (uint32_t)(NSLOT * SLOT_BYTES - 1);
+            }
         }
     }
 
@@ -919,16 +928,19 @@ struct Frag16 {
 // ones do on gfx950 (measured: 97 % against 75 % of peak for the same 128 x
 // 128 register tile with no memory traffic at all).
 //
-// Stage kt (BK = 64: two K steps) lives in ring slot kt % 2.  The K loop is
-// rotated so that its back edge follows the stage barrier:
+// Stage kt (BK = 64: two K steps) lives in ring slot kt % S (S = 2 or 4
+// slots).  The K loop is rotated so that its back edge follows the stage
+// barrier:
 //   head(kt): K step 0 of stage kt, reading the fragments of K step 1; wait
 //             for this lane's loads of stage kt+1 and for all LDS reads;
-//             barrier -- stage kt+1 is readable and slot kt % 2 is free;
+//             barrier -- stage kt+1 is readable and slot kt % S is free;
 //   tail(kt): K step 1 of stage kt, reading the fragments of stage kt+1 K
-//             step 0 and issuing all loads of stage kt+2 into slot kt % 2.
-// Every load thus has the next two K steps to land.  Each stage issues
-// exactly L loads per lane (stages past the end of K fail the range check
-// and write zeros), so the wait counts are exact.
+//             step 0 and issuing all loads of stage kt+S into slot kt % S.
+// Every load thus has the next 2 (S - 1) K steps to land: a four-slot ring
+// keeps three stages in flight, for grids too small to hide HBM latency
+// with more workgroups.  Each stage issues exactly L loads per lane (stages
+// past the end of K fail the range check and write zeros), so the wait
+// counts are exact.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int BK, int WGM, int WGN, int S, bool AK, bool BKC, bool KFULL>
 __global__ __launch_bounds__(64 * WGM * WGN)
@@ -944,7 +956,8 @@ void gemm_direct16(GemmArgs pin) {
     using OpA = DirectOperand<BM, BK, NW, AK>;
     using OpB = DirectOperand<BN, BK, NW, BKC>;
     constexpr int L = OpA::PER_WAVE + OpB::PER_WAVE;  // loads per lane per stage
-    static_assert(S == 2, "the schedule is a two-slot ring");
+    static_assert(S == 2 || S == 4, "a two- or four-slot ring");
+    static_assert((S - 1) * L < 64, "vmcnt range");
     static_assert(NKS == 2, "head and tail are one K step each");
     static_assert(L < 64, "vmcnt range");
 
@@ -990,8 +1003,8 @@ void gemm_direct16(GemmArgs pin) {
     };
 
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "16-row fragment blocks");
-    Frag16<BM, BK, AK, FM, SLOT * 16> fra;
-    Frag16<BN, BK, BKC, FN, SLOT * 16> frb;
+    Frag16<BM, BK, AK, FM, SLOT * 16, S> fra;
+    Frag16<BN, BK, BKC, FN, SLOT * 16, S> frb;
     fra.setup(lane, wm * WTM, 0);
     frb.setup(lane, wn * WTN, A_CH * 16);
 
@@ -1007,8 +1020,8 @@ void gemm_direct16(GemmArgs pin) {
     // them.  Only K-contiguous operands test K: rows k >= K of an
     // MN-contiguous operand start past its extent and fail the range check.
     // KFULL (K a multiple of BK) tests nothing: every stage inside K is full,
-    // and the loads of the one or two stages past the end (issued by the last
-    // tails) are range-checked reads that land in slots no MFMA reads again.
+    // and the loads of the S stages past the end (issued by the last tails)
+    // are range-checked reads that land in slots no MFMA reads again.
     constexpr int NQ = FM * FN;
     constexpr int NF = FM + FN;
     auto kstep = [&](auto curc, auto nextc, auto rksc, auto loadsc, int64_t dst)
@@ -1016,7 +1029,7 @@ void gemm_direct16(GemmArgs pin) {
         constexpr int CUR = decltype(curc)::value, RKS = decltype(rksc)::value;
         constexpr bool NEXT = decltype(nextc)::value, LOADS = decltype(loadsc)::value;
         constexpr int nl = LOADS ? L : 0;
-        const uint32_t dslot = lds_base + (uint32_t)((dst & 1) * SLOT * 16);
+        const uint32_t dslot = lds_base + (uint32_t)((dst & (S - 1)) * SLOT * 16);
         sgpr4 rsa = {}, rsb = {};
         bool ma = true, mb = true;
         if constexpr (LOADS) {
@@ -1054,21 +1067,23 @@ void gemm_direct16(GemmArgs pin) {
 
     // head(): K step 0 of stage kt, reading its K step 1; then the stage
     // barrier.  tail(kt): K step 1 of stage kt, reading K step 0 of stage
-    // kt+1 and loading stage kt+2 into the slot stage kt used.
+    // kt+1 and loading stage kt+S into the slot stage kt used.  Stages
+    // kt+1 .. kt+S-1 are in flight at the head, so waiting for stage kt+1
+    // leaves the (S-2) L loads of the later ones pending.
     auto head = [&]() __attribute__((always_inline)) {
         kstep(Z{}, std::false_type{}, O{}, std::false_type{}, 0);
-        wait_vmcnt<0>();                // this lane's loads of stage kt+1
+        wait_vmcnt<(S - 2) * L>();      // this lane's loads of stage kt+1
         asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");   // reads of stage kt done
         barrier();
     };
     auto tail = [&](int64_t kt) __attribute__((always_inline)) {
-        kstep(O{}, std::true_type{}, Z{}, std::true_type{}, kt + 2);
+        kstep(O{}, std::true_type{}, Z{}, std::true_type{}, kt + S);
     };
 
-    // Prologue: stages 0 and 1 whole.
-    issue(0);
-    issue(1);
-    wait_vmcnt<L>();                    // stage 0 resident for this lane
+    // Prologue: stages 0 .. S-1 whole.
+#pragma unroll
+    for (int st = 0; st < S; ++st) issue(st);
+    wait_vmcnt<(S - 1) * L>();          // stage 0 resident for this lane
     barrier();                          // ... and for every lane
 #pragma unroll
     for (int j = 0; j < FN; ++j) fb[0][j] = frb.template read<false>(lds, j, 0);
@@ -1346,6 +1361,15 @@ void fill_tile(KernelFn (&t)[2][2][2]) {
 }
 
 template <int T>
+void fill_kfull(KernelFn (&t)[2][2]) {
+    static_assert(kTiles[T].kind == KIND_DIRECT16, "K-full variants are direct16");
+    t[0][0] = pick_direct16<T, false, false, true>();
+    t[0][1] = pick_direct16<T, false, true, true>();
+    t[1][0] = pick_direct16<T, true, false, true>();
+    t[1][1] = pick_direct16<T, true, true, true>();
+}
+
+template <int T>
 void fill_stream(KernelFn (&t)[2][2][2]) {
     // Only the K-contiguous A and B (row-major A, column-major B) 128-bit form.
     t[0][0][0] = t[0][0][1] = t[0][1][0] = t[0][1][1] = nullptr;
@@ -1355,20 +1379,14 @@ void fill_stream(KernelFn (&t)[2][2][2]) {
 
 struct KernelTable {
     KernelFn k[NUM_TILES][2][2][2];
-    KernelFn kfull[2][2][2];   // [tile is 256x256][A K-contiguous][B K-contiguous]: K a multiple of BK
+    KernelFn kfull[NUM_TILES][2][2];   // direct tiles with K a multiple of BK (else null)
     KernelTable() {
-        static_assert(kTiles[TILE_256x256].kind == KIND_DIRECT16 &&
-                      kTiles[TILE_128x128].kind == KIND_DIRECT16, "K-full variants are direct16");
-        kfull[1][0][0] = pick_direct16<TILE_256x256, false, false, true>();
-        kfull[1][0][1] = pick_direct16<TILE_256x256, false, true, true>();
-        kfull[1][1][0] = pick_direct16<TILE_256x256, true, false, true>();
-        kfull[1][1][1] = pick_direct16<TILE_256x256, true, true, true>();
-        kfull[0][0][0] = pick_direct16<TILE_128x128, false, false, true>();
-        kfull[0][0][1] = pick_direct16<TILE_128x128, false, true, true>();
-        kfull[0][1][0] = pick_direct16<TILE_128x128, true, false, true>();
-        kfull[0][1][1] = pick_direct16<TILE_128x128, true, true, true>();
+        fill_kfull<TILE_256x256>(kfull[TILE_256x256]);
+        fill_kfull<TILE_128x128>(kfull[TILE_128x128]);
+        fill_kfull<TILE_128x128_D4>(kfull[TILE_128x128_D4]);
         fill_tile<TILE_256x256>(k[TILE_256x256]);
         fill_tile<TILE_128x128>(k[TILE_128x128]);
+        fill_tile<TILE_128x128_D4>(k[TILE_128x128_D4]);
         fill_tile<TILE_64x64>(k[TILE_64x64]);
         fill_tile<TILE_32x64>(k[TILE_32x64]);
         fill_tile<TILE_128x128_STAGED>(k[TILE_128x128_STAGED]);
@@ -1536,8 +1554,7 @@ extern "C" int gemm_f16f32_run(gemm_f16f32_plan_t plan, const void *A,
     KernelFn fn = kernels().k[tile][ak][bkc][vec ? 1 : 0];
     // K-full variants: every stage inside K (for split-K, every slice: kchunk
     // is a multiple of BK, so K must be too).
-    if ((tile == TILE_256x256 || tile == TILE_128x128) && p.K % kTiles[tile].bk == 0)
-        fn = kernels().kfull[tile == TILE_256x256 ? 1 : 0][ak][bkc];
+    if (ts.kind == KIND_DIRECT16 && p.K % ts.bk == 0) fn = kernels().kfull[tile][ak][bkc];
     if (!fn) return GEMM_ERR_UNSUPPORTED;
     void *args[] = {&a};
     const unsigned threads = ts.kind == KIND_STREAM ? 512u : (unsigned)(64 * ts.wgm * ts.wgn);

@@ -65,20 +65,19 @@ int choose_tile(int64_t M, int64_t N, int64_t K, int64_t batch, bool kc_both, bo
     return TILE_64x64;
 }
 
-// K slices for the direct 128 tile: enough workgroups to cover the CUs, each
-// slice at least 512 deep and a multiple of the 64-deep stage, at most 8
-// slices and 1024 workgroups.  Tiles that already fill a quarter of the CUs
-// (two workgroups per CU) are cut only when K is deep: the partial tiles and
+// K slices for the direct 128 tile: as many as keep the grid within one
+// workgroup per CU (at least two), each slice at least 512 deep and a
+// multiple of the 64-deep stage, at most 8 slices.  Tiles that already fill
+// a quarter of the CUs are cut only when K is deep: the partial tiles and
 // their reduction cost more than they gain at K ~ 1024 (measured at 1024^3).
 void choose_ksplit(gemm_f16f32_plan_s *p, int64_t tiles) {
     p->ksplit = 1;
     p->kchunk = p->K;
     if (p->tile != TILE_128x128 || !p->vec_ok || p->batch != 1 || tiles >= kNumCUs) return;
     if (tiles >= kNumCUs / 4 && p->K < 2048) return;
-    int64_t ks = ceil_div(kNumCUs, tiles);
+    int64_t ks = std::max<int64_t>(2, kNumCUs / tiles);
     ks = std::min<int64_t>(ks, p->K / 512);
     ks = std::min<int64_t>(ks, 8);
-    ks = std::min<int64_t>(ks, 1024 / tiles);
     if (ks < 2) return;
     const int64_t chunk = ceil_div(ceil_div(p->K, ks), 64) * 64;
     p->kchunk = chunk;
@@ -176,7 +175,6 @@ extern "C" int gemm_f16f32_plan(gemm_f16f32_plan_t *out, int64_t M, int64_t N,
         p->vec_ok = 0;
         p->tile = choose_tile(M, N, K, batch, kc_both, false);
     }
-    const int t = p->vec_ok ? p->tile : narrow_tile(p->tile);
     for (int cand : {p->tile, narrow_tile(p->tile)}) {
         const TileShape &c = kTiles[cand];
         if (ceil_div(M, c.bm) * ceil_div(N, c.bn) * batch > 0x7fffffff) {
@@ -185,7 +183,20 @@ extern "C" int gemm_f16f32_plan(gemm_f16f32_plan_t *out, int64_t M, int64_t N,
         }
     }
     p->group_m = 4;
-    choose_ksplit(p, ceil_div(M, kTiles[p->tile].bm) * ceil_div(N, kTiles[p->tile].bn) * batch);
+    const int64_t tiles = ceil_div(M, kTiles[p->tile].bm) * ceil_div(N, kTiles[p->tile].bn) * batch;
+    choose_ksplit(p, tiles);
+    // The 128 tile on a four-slot ring (three stages in flight, one
+    // workgroup per CU) when its grid is one wave at that occupancy, or more
+    // than one wave of the two-slot form (two per CU); K slices of at least
+    // four stages.  (Measured: 1.2-1.5x on 1000^3-2048^3 and on deep-K
+    // split-K shapes; slower when the two-slot form fits its grid in one wave
+    // and the four-slot form does not.)
+    if (p->tile == TILE_128x128 && p->vec_ok) {
+        const int64_t wgs = tiles * p->ksplit;
+        if ((wgs <= kNumCUs || wgs > 2 * kNumCUs) && p->kchunk >= 4 * kTiles[p->tile].bk)
+            p->tile = TILE_128x128_D4;
+    }
+    const int t = p->vec_ok ? p->tile : narrow_tile(p->tile);
     char split[16] = "";
     if (p->ksplit > 1) snprintf(split, sizeof split, "_sk%d", p->ksplit);
     static const char *const kPackSuffix[4] = {"", "_pka", "_pkb", "_pkab"};

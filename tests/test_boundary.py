@@ -108,11 +108,11 @@ def test_kernel_choice_by_regime():
     # wide N: 64 columns per streaming workgroup (M <= 32), else the 128 tile
     assert kern(32, 11008, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_stream32x64")
     assert kern(32, 4096, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_stream32x16")
-    assert kern(64, 11008, 4096, layout_b=GEMM_COL_MAJOR).endswith("nt_direct_sk3")
+    assert kern(64, 11008, 4096, layout_b=GEMM_COL_MAJOR).endswith("d4_nt_direct_sk2")
     # skinny with row-major B: too few tiles for the CUs, so the 128 tile with
     # its K cut into slices (split-K, suffix _sk<slices>)
-    assert kern(16, 4096, 4096) == "gemm_128x128x64m16_nn_direct_sk8"
-    assert kern(128, 11008, 4096, layout_b=GEMM_COL_MAJOR).endswith("nt_direct_sk3")
+    assert kern(16, 4096, 4096) == "gemm_128x128x64m16d4_nn_direct_sk8"
+    assert kern(128, 11008, 4096, layout_b=GEMM_COL_MAJOR).endswith("d4_nt_direct_sk2")
     # 2048^2 already fills the CUs with 128 tiles; short K is not cut
     assert not kern(2048, 2048, 2048).endswith(tuple(f"_sk{k}" for k in range(2, 9)))
     assert "_sk" not in kern(16, 4096, 512)
@@ -120,6 +120,11 @@ def test_kernel_choice_by_regime():
     assert mpg.Plan(64, 64, 64, batch=512, stride_a=4096, stride_b=4096,
                     stride_c=4096).kernel.startswith("gemm_64x64")
     assert kern(1024, 1024, 1024).startswith("gemm_128x128")
+    # the 128 tile on a four-slot ring when its grid is one wave at one
+    # workgroup per CU (or beyond two at two), with four or more stages
+    assert kern(2048, 2048, 2048).startswith("gemm_128x128x64m16d4")
+    assert kern(2048, 4096, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_128x128x64m16_")
+    assert kern(1024, 1024, 128).startswith("gemm_128x128x64m16_")
     assert "narrow" in kern(127, 257, 33)
     assert kern(0, 8, 8) == "none"
 
@@ -140,7 +145,7 @@ def test_repacking_choice():
     assert kern(1024, 1024, 1024, lda=1025).endswith("nn_direct_pka")
     assert kern(1024, 1024, 1024, ldb=1028).endswith("nn_direct_pkb")
     # deep K with few tiles: repacked and split
-    assert kern(50, 333, 4100) == "gemm_128x128x64m16_nn_direct_sk8_pkab"
+    assert kern(50, 333, 4100) == "gemm_128x128x64m16d4_nn_direct_sk8_pkab"
     # skinny NT: streaming kernel on repacked operands
     assert kern(7, 4097, 4099, layout_b=GEMM_COL_MAJOR) == "gemm_stream16x16_nt_direct_pkab"
     # small or batched-small: no copies
