@@ -853,18 +853,20 @@ struct DirectOperand {
 //     k = 32 s + 4 t + 8 (l/16) + (l%16)/4 sits in chunk (n >> 3) ^ mn_swz(k),
 //     and mn_swz(k) depends only on k%4 and bit 3 of k, both fixed by the
 //     lane: one base per block i, rows 32 s + 4 t as immediates.
-template <int R, int BK, bool KC, int NBLK, int SLOT_BYTES, int NSLOT>
+template <int R, int BK, bool KC, int NBLK, int SLOT_BYTES, int NSLOT, int BASE>
 struct Frag16 {
     static_assert(BK == 64, "128-byte K rows");
     static_assert((SLOT_BYTES & (SLOT_BYTES - 1)) == 0 && SLOT_BYTES <= 65536,
                   "slot size a power of two");
-    static_assert((NSLOT & (NSLOT - 1)) == 0 && NSLOT >= 2 && NSLOT * SLOT_BYTES <= 160 * 1024,
-                  "a power-of-two number of slots");
+    static_assert(NSLOT >= 2 && NSLOT <= 4 && BASE + NSLOT * SLOT_BYTES <= 160 * 1024,
+                  "two to four slots inside the LDS");
+    static_assert(NSLOT != 4 || BASE < SLOT_BYTES, "four slots: operand region inside an interleaved slot");
     static constexpr int NCLS = KC ? 2 : NBLK;
     uint32_t cur[NCLS], nxt[NCLS];
 
     // Bases for stage 0 (slot 0) in cur and stage 1 (slot 1) in nxt.
-    __device__ void setup(int lane, int wb, uint32_t region) {
+    __device__ void setup(int lane, int wb) {
+        constexpr uint32_t region = (uint32_t)BASE;
         const int lr = lane & 15, lg = lane >> 4;
         if constexpr (KC) {
             const int X = lg ^ swz16(lr);
@@ -882,18 +884,28 @@ struct Frag16 {
         for (int c = 0; c < NCLS; ++c) nxt[c] = cur[c] + SLOT_BYTES;
     }
 
-    // Next stage: every base moves one slot on, wrapping around the ring
-    // (a single XOR for two slots).
+    // Next stage: every base moves one slot on, wrapping around the ring.
+    // Two slots at BASE and BASE + SLOT_BYTES: one XOR, since every offset
+    // inside a slot lies below the lowest bit in which the two slot addresses
+    // differ.  Three: add and wrap.  Four (interleaved, BASE inside the
+    // first slot): add and mask.
+    __device__ static uint32_t step(uint32_t x) {
+        if constexpr (NSLOT == 2) {
+            constexpr uint32_t flip = (uint32_t)BASE ^ (uint32_t)(BASE + SLOT_BYTES);
+            static_assert((flip & -flip) >= (uint32_t)SLOT_BYTES, "slot offsets below the flipped bits");
+            return x ^ flip;
+        } else if constexpr (NSLOT == 3) {
+            x += (uint32_t)SLOT_BYTES;
+            return x >= (uint32_t)(BASE + 3 * SLOT_BYTES) ? x - (uint32_t)(3 * SLOT_BYTES) : x;
+        } else {
+            return (x + (uint32_t)SLOT_BYTES) & (uint32_t)(NSLOT * SLOT_BYTES - 1);
+        }
+    }
     __device__ void advance() {
 #pragma unroll
         for (int c = 0; c < NCLS; ++c) {
-            if constexpr (NSLOT == 2) {
-                cur[c] ^= (uint32_t)SLOT_BYTES;
-                nxt[c] ^= (uint32_t)SLOT_BYTES;
-            } else {
-                cur[c] = (cur[c] + (uint32_t)SLOT_BYTES) & (uint32_t)(NSLOT * SLOT_BYTES - 1);
-                nxt[c] = (nxt[c] + (uint32_t)SLOT_BYTES) & (uint32_t)(NSLOT * SLOT_BYTES - 1);
-            }
+            cur[c] = step(cur[c]);
+            nxt[c] = step(nxt[c]);
         }
     }
 
@@ -961,7 +973,20 @@ void gemm_direct16(GemmArgs pin) {
     static_assert(NKS == 2, "head and tail are one K step each");
     static_assert(L < 64, "vmcnt range");
 
-    __shared__ u32x4 lds[S * SLOT];
+    // Ring layout.  Interleaved: S slots of [A tile][B tile].  Split (the
+    // two-slot 256 tile): A on three slots and B on two, 5 x 32 KiB = all of
+    // the LDS.  Stage kt + 2's A tile then goes into the slot of stage kt - 1,
+    // free since the barrier ending head(kt - 1), so its loads are issued in
+    // head(kt) and only B's in tail(kt): each K step carries half of a
+    // stage's loads instead of the tail carrying all of them, which kept the
+    // load unit's address and command queues full.
+    constexpr bool SPLIT = S == 2 && BM * BN >= 65536;
+    constexpr int SA = SPLIT ? 3 : S;
+    constexpr int A_SLOT = SPLIT ? A_CH * 16 : SLOT * 16;   // bytes between A slots
+    constexpr int B_SLOT = SPLIT ? B_CH * 16 : SLOT * 16;
+    constexpr int A_BASE = 0, B_BASE = SPLIT ? SA * A_CH * 16 : A_CH * 16;
+    constexpr int PA = OpA::PER_WAVE, PB = OpB::PER_WAVE;
+    __shared__ u32x4 lds[SPLIT ? SA * A_CH + S * B_CH : S * SLOT];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -996,17 +1021,18 @@ void gemm_direct16(GemmArgs pin) {
     const uint32_t lds_base = lds_offset(lds);
 
     auto issue = [&](int64_t st) __attribute__((always_inline)) {
-        const uint32_t slot = lds_base + (uint32_t)((st % S) * SLOT * 16);
+        const uint32_t sa = lds_base + (uint32_t)(A_BASE + (st % SA) * A_SLOT);
+        const uint32_t sb = lds_base + (uint32_t)(B_BASE + (st % S) * B_SLOT);
         const int64_t ao = a_tile + st * a_kstep, bo = b_tile + st * b_kstep;
-        opa.issue(Ab + ao, (p.extent_a - ao) * 2, slot, wave, st * BK, p.K);
-        opb.issue(Bb + bo, (p.extent_b - bo) * 2, slot + A_CH * 16, wave, st * BK, p.K);
+        opa.issue(Ab + ao, (p.extent_a - ao) * 2, sa, wave, st * BK, p.K);
+        opb.issue(Bb + bo, (p.extent_b - bo) * 2, sb, wave, st * BK, p.K);
     };
 
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "16-row fragment blocks");
-    Frag16<BM, BK, AK, FM, SLOT * 16, S> fra;
-    Frag16<BN, BK, BKC, FN, SLOT * 16, S> frb;
-    fra.setup(lane, wm * WTM, 0);
-    frb.setup(lane, wn * WTN, A_CH * 16);
+    Frag16<BM, BK, AK, FM, A_SLOT, SA, A_BASE> fra;
+    Frag16<BN, BK, BKC, FN, B_SLOT, S, B_BASE> frb;
+    fra.setup(lane, wm * WTM);
+    frb.setup(lane, wn * WTN);
 
     half8 fa[2][FM], fb[2][FN];
     using Z = std::integral_constant<int, 0>;
@@ -1024,22 +1050,29 @@ void gemm_direct16(GemmArgs pin) {
     // are range-checked reads that land in slots no MFMA reads again.
     constexpr int NQ = FM * FN;
     constexpr int NF = FM + FN;
-    auto kstep = [&](auto curc, auto nextc, auto rksc, auto loadsc, int64_t dst)
-                     __attribute__((always_inline)) {
+    // LOADS: 0 none, 1 the A loads, 2 the B loads, 3 both, of stage dst;
+    // sa and sb are the LDS byte addresses of its A and B slots.
+    auto kstep = [&](auto curc, auto nextc, auto rksc, auto loadsc, int64_t dst, uint32_t sa,
+                     uint32_t sb) __attribute__((always_inline)) {
         constexpr int CUR = decltype(curc)::value, RKS = decltype(rksc)::value;
-        constexpr bool NEXT = decltype(nextc)::value, LOADS = decltype(loadsc)::value;
-        constexpr int nl = LOADS ? L : 0;
-        const uint32_t dslot = lds_base + (uint32_t)((dst & (S - 1)) * SLOT * 16);
+        constexpr bool NEXT = decltype(nextc)::value;
+        constexpr int LOADS = decltype(loadsc)::value;
+        constexpr bool LA = LOADS & 1, LB = LOADS & 2;
+        constexpr int na = LA ? PA : 0;
+        constexpr int nl = na + (LB ? PB : 0);
         sgpr4 rsa = {}, rsb = {};
         bool ma = true, mb = true;
-        if constexpr (LOADS) {
-            const int64_t ao = a_tile + dst * a_kstep, bo = b_tile + dst * b_kstep;
-            rsa = opa.stage_rsrc(Ab + ao, (p.extent_a - ao) * 2);
-            rsb = opb.stage_rsrc(Bb + bo, (p.extent_b - bo) * 2);
-            if constexpr (!KFULL && (AK || BKC)) {
-                const int left = OpA::stage_left(dst * BK, p.K);
-                if constexpr (AK) ma = opa.kmask(left);
-                if constexpr (BKC) mb = opb.kmask(left);
+        if constexpr (LOADS != 0) {
+            const int left = (!KFULL && (AK || BKC)) ? OpA::stage_left(dst * BK, p.K) : BK;
+            if constexpr (LA) {
+                const int64_t ao = a_tile + dst * a_kstep;
+                rsa = opa.stage_rsrc(Ab + ao, (p.extent_a - ao) * 2);
+                if constexpr (!KFULL && AK) ma = opa.kmask(left);
+            }
+            if constexpr (LB) {
+                const int64_t bo = b_tile + dst * b_kstep;
+                rsb = opb.stage_rsrc(Bb + bo, (p.extent_b - bo) * 2);
+                if constexpr (!KFULL && BKC) mb = opb.kmask(left);
             }
         }
 #pragma unroll
@@ -1048,12 +1081,12 @@ void gemm_direct16(GemmArgs pin) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[CUR][j], fa[CUR][i], acc[i][j], 0, 0, 0);
 #pragma unroll
             for (int l = q * nl / NQ; l < (q + 1) * nl / NQ; ++l) {
-                if (l < OpA::PER_WAVE) {
-                    if constexpr (AK && !KFULL) opa.issue_one_masked(l, rsa, dslot, wave, ma);
-                    else opa.issue_one_full(l, rsa, dslot, wave);
+                if (l < na) {
+                    if constexpr (AK && !KFULL) opa.issue_one_masked(l, rsa, sa, wave, ma);
+                    else opa.issue_one_full(l, rsa, sa, wave);
                 } else {
-                    if constexpr (BKC && !KFULL) opb.issue_one_masked(l - OpA::PER_WAVE, rsb, dslot + A_CH * 16, wave, mb);
-                    else opb.issue_one_full(l - OpA::PER_WAVE, rsb, dslot + A_CH * 16, wave);
+                    if constexpr (BKC && !KFULL) opb.issue_one_masked(l - na, rsb, sb, wave, mb);
+                    else opb.issue_one_full(l - na, rsb, sb, wave);
                 }
             }
 #pragma unroll
@@ -1064,20 +1097,40 @@ void gemm_direct16(GemmArgs pin) {
             __builtin_amdgcn_sched_barrier(0);
         }
     };
+    using NoLd = std::integral_constant<int, 0>;
+    using LdA = std::integral_constant<int, 1>;
+    using LdB = std::integral_constant<int, 2>;
+    using LdAB = std::integral_constant<int, 3>;
 
-    // head(): K step 0 of stage kt, reading its K step 1; then the stage
-    // barrier.  tail(kt): K step 1 of stage kt, reading K step 0 of stage
-    // kt+1 and loading stage kt+S into the slot stage kt used.  Stages
-    // kt+1 .. kt+S-1 are in flight at the head, so waiting for stage kt+1
-    // leaves the (S-2) L loads of the later ones pending.
-    auto head = [&]() __attribute__((always_inline)) {
-        kstep(Z{}, std::false_type{}, O{}, std::false_type{}, 0);
-        wait_vmcnt<(S - 2) * L>();      // this lane's loads of stage kt+1
+    // head(kt): K step 0 of stage kt, reading its K step 1 (split ring: and
+    // loading stage kt+2's A tile); then the stage barrier.  tail(kt): K
+    // step 1 of stage kt, reading K step 0 of stage kt+1 and loading stage
+    // kt+S (split ring: its B tile) into the slots stage kt used.  At the
+    // head's wait only the loads issued after stage kt+1's may be pending:
+    // the (S-2) L of the later stages, or (split ring) the A loads of stage
+    // kt+2 just issued.
+    uint32_t a_ld = (uint32_t)(A_BASE + (2 % SA) * A_SLOT);   // split ring: A slot of stage kt+2
+    auto head = [&](int64_t kt) __attribute__((always_inline)) {
+        if constexpr (SPLIT) {
+            kstep(Z{}, std::false_type{}, O{}, LdA{}, kt + 2, lds_base + a_ld, 0u);
+            a_ld = a_ld + (uint32_t)A_SLOT == (uint32_t)(A_BASE + SA * A_SLOT) ? (uint32_t)A_BASE
+                                                                             : a_ld + (uint32_t)A_SLOT;
+            wait_vmcnt<PA>();           // this lane's loads of stage kt+1
+        } else {
+            kstep(Z{}, std::false_type{}, O{}, NoLd{}, 0, 0u, 0u);
+            wait_vmcnt<(S - 2) * L>();  // this lane's loads of stage kt+1
+        }
         asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");   // reads of stage kt done
         barrier();
     };
     auto tail = [&](int64_t kt) __attribute__((always_inline)) {
-        kstep(O{}, std::true_type{}, Z{}, std::true_type{}, kt + S);
+        const uint32_t sb = lds_base + (uint32_t)(B_BASE + ((kt + S) & (S - 1)) * B_SLOT);
+        if constexpr (SPLIT) {
+            kstep(O{}, std::true_type{}, Z{}, LdB{}, kt + S, 0u, sb);
+        } else {
+            const uint32_t sa = lds_base + (uint32_t)(A_BASE + ((kt + S) & (S - 1)) * A_SLOT);
+            kstep(O{}, std::true_type{}, Z{}, LdAB{}, kt + S, sa, sb);
+        }
     };
 
     // Prologue: stages 0 .. S-1 whole.
@@ -1090,12 +1143,12 @@ void gemm_direct16(GemmArgs pin) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) fa[0][i] = fra.template read<false>(lds, i, 0);
 
-    head();
+    head(0);
     for (int64_t kt = 0; kt + 1 < nk; ++kt) {
         tail(kt);
         fra.advance();
         frb.advance();
-        head();
+        head(kt + 1);
     }
     tail(nk - 1);
 
