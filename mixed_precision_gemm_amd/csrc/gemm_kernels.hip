@@ -698,12 +698,14 @@ __device__ inline void store_tile_splitk(const GemmArgs &p, const AccT (&acc)[FM
     }
     asm volatile("s_waitcnt vmcnt(0)" : : : "memory");   // this lane's partial is in memory
     __syncthreads();
-    __shared__ int last_flag;
+    // The arrival flag lives in the LDS word right after the staging area
+    // (the caller's buffer extends past LDS_BYTES).
+    volatile int *last_flag = (volatile int *)(base + LDS_BYTES);
     if (threadIdx.x == 0)
-        last_flag = __hip_atomic_fetch_add(&p.ws_count[tile], 1, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT) == p.ksplit - 1;
+        *last_flag = __hip_atomic_fetch_add(&p.ws_count[tile], 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT) == p.ksplit - 1;
     __syncthreads();
-    if (!last_flag) return;
+    if (!*last_flag) return;
     const float alpha = p.alpha, beta = p.beta;
     const int64_t n = n0 + 4 * g;
     const bool n_ok = n < p.N;
@@ -973,20 +975,24 @@ void gemm_direct16(GemmArgs pin) {
     static_assert(NKS == 2, "head and tail are one K step each");
     static_assert(L < 64, "vmcnt range");
 
-    // Ring layout.  Interleaved: S slots of [A tile][B tile].  Split (the
-    // two-slot 256 tile): A on three slots and B on two, 5 x 32 KiB = all of
-    // the LDS.  Stage kt + 2's A tile then goes into the slot of stage kt - 1,
+    // Ring layout.  Interleaved (four slots): S slots of [A tile][B tile].
+    // Split (two-slot rings): A on three slots and B on two -- 5 x 32 KiB,
+    // all of the LDS, for the 256 tile; 5 x 16 KiB, two workgroups per CU,
+    // for the 128 tile.  Stage kt + 2's A tile then goes into the slot of stage kt - 1,
     // free since the barrier ending head(kt - 1), so its loads are issued in
     // head(kt) and only B's in tail(kt): each K step carries half of a
     // stage's loads instead of the tail carrying all of them, which kept the
     // load unit's address and command queues full.
-    constexpr bool SPLIT = S == 2 && BM * BN >= 65536;
+    constexpr bool SPLIT = S == 2;
     constexpr int SA = SPLIT ? 3 : S;
     constexpr int A_SLOT = SPLIT ? A_CH * 16 : SLOT * 16;   // bytes between A slots
     constexpr int B_SLOT = SPLIT ? B_CH * 16 : SLOT * 16;
     constexpr int A_BASE = 0, B_BASE = SPLIT ? SA * A_CH * 16 : A_CH * 16;
     constexpr int PA = OpA::PER_WAVE, PB = OpB::PER_WAVE;
-    __shared__ u32x4 lds[SPLIT ? SA * A_CH + S * B_CH : S * SLOT];
+    // Split-K's epilogue stages S * SLOT chunks and keeps one flag word after
+    // them: inside the split ring, one extra chunk for the interleaved one.
+    constexpr int RING = SPLIT ? SA * A_CH + S * B_CH : S * SLOT;
+    __shared__ u32x4 lds[RING > S * SLOT ? RING : S * SLOT + 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
