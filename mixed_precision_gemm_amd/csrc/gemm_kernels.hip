@@ -942,19 +942,21 @@ struct Frag16 {
 // ones do on gfx950 (measured: 97 % against 75 % of peak for the same 128 x
 // 128 register tile with no memory traffic at all).
 //
-// Stage kt (BK = 64: two K steps) lives in ring slot kt % S (S = 2 or 4
-// slots).  The K loop is rotated so that its back edge follows the stage
-// barrier:
-//   head(kt): K step 0 of stage kt, reading the fragments of K step 1; wait
-//             for this lane's loads of stage kt+1 and for all LDS reads;
-//             barrier -- stage kt+1 is readable and slot kt % S is free;
+// Stage kt (BK = 64: two K steps) lives in ring slot kt % S of B's ring (S =
+// 2 or 4 slots) and of A's (S, or 3 for a split two-slot ring).  The K loop
+// is rotated so that its back edge follows the stage barrier:
+//   head(kt): K step 0 of stage kt, reading the fragments of K step 1 (split
+//             ring: and loading stage kt+2's A tile into the A slot of
+//             stage kt-1); wait for this lane's loads of stage kt+1 and for
+//             all LDS reads; barrier -- stage kt+1 is readable and stage
+//             kt's slots are free;
 //   tail(kt): K step 1 of stage kt, reading the fragments of stage kt+1 K
-//             step 0 and issuing all loads of stage kt+S into slot kt % S.
-// Every load thus has the next 2 (S - 1) K steps to land: a four-slot ring
-// keeps three stages in flight, for grids too small to hide HBM latency
-// with more workgroups.  Each stage issues exactly L loads per lane (stages
-// past the end of K fail the range check and write zeros), so the wait
-// counts are exact.
+//             step 0 and issuing the loads of stage kt+S (split ring: its B
+//             tile) into stage kt's slots.
+// A four-slot ring keeps three stages in flight, for grids too small to hide
+// HBM latency with more workgroups.  Each stage issues exactly L loads per
+// lane (stages past the end of K fail the range check and write zeros), so
+// the wait counts are exact.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int BK, int WGM, int WGN, int S, bool AK, bool BKC, bool KFULL>
 __global__ __launch_bounds__(64 * WGM * WGN)
