@@ -66,17 +66,22 @@ def copy_calibration(nbytes, steps):
 
 
 def kernel_source_hash():
-    """Hash of the library sources (kernels, planner, ABI header); a profile
-    taken from other sources no longer describes the kernel."""
+    """Hash of the library's code (kernels, planner, ABI header) with comments
+    and whitespace removed: a profile taken from other code no longer
+    describes the kernel, while a comment edit does not change it."""
     import glob
     import hashlib
+    import re
     files = sorted(glob.glob(os.path.join(ROOT, "mixed_precision_gemm_amd", "csrc", "*"))) + \
         sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
     h = hashlib.sha256()
     for f in files:
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, "r", encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)   # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                 # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
