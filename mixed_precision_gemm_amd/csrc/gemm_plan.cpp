@@ -186,15 +186,14 @@ extern "C" int gemm_f16f32_plan(gemm_f16f32_plan_t *out, int64_t M, int64_t N,
     const int64_t tiles = ceil_div(M, kTiles[p->tile].bm) * ceil_div(N, kTiles[p->tile].bn) * batch;
     choose_ksplit(p, tiles);
     // The 128 tile on a four-slot ring (three stages in flight, one
-    // workgroup per CU) when its grid is one wave at that occupancy, or more
-    // than one wave of the two-slot form (two per CU); K slices of at least
-    // four stages.  (Measured: 1.2-1.5x on 1000^3-2048^3 and on deep-K
-    // split-K shapes; slower when the two-slot form fits its grid in one wave
-    // and the four-slot form does not.)
+    // workgroup per CU) when its grid is one wave at that occupancy, with K
+    // slices of at least four stages.  (Measured against the two-slot split
+    // ring at two workgroups per CU: 1.2-1.5x on 1000^3-2048^3 and on deep-K
+    // split-K shapes; 10-37% slower on grids beyond one wave, 576-2304
+    // workgroups.)
     if (p->tile == TILE_128x128 && p->vec_ok) {
         const int64_t wgs = tiles * p->ksplit;
-        if ((wgs <= kNumCUs || wgs > 2 * kNumCUs) && p->kchunk >= 4 * kTiles[p->tile].bk)
-            p->tile = TILE_128x128_D4;
+        if (wgs <= kNumCUs && p->kchunk >= 4 * kTiles[p->tile].bk) p->tile = TILE_128x128_D4;
     }
     const int t = p->vec_ok ? p->tile : narrow_tile(p->tile);
     char split[16] = "";

@@ -121,9 +121,10 @@ def test_kernel_choice_by_regime():
                     stride_c=4096).kernel.startswith("gemm_64x64")
     assert kern(1024, 1024, 1024).startswith("gemm_128x128")
     # the 128 tile on a four-slot ring when its grid is one wave at one
-    # workgroup per CU (or beyond two at two), with four or more stages
+    # workgroup per CU, with four or more stages
     assert kern(2048, 2048, 2048).startswith("gemm_128x128x64m16d4")
     assert kern(2048, 4096, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_128x128x64m16_")
+    assert kern(3072, 3072, 3072).startswith("gemm_128x128x64m16_")
     assert kern(1024, 1024, 128).startswith("gemm_128x128x64m16_")
     assert "narrow" in kern(127, 257, 33)
     assert kern(0, 8, 8) == "none"
