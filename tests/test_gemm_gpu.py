@@ -389,6 +389,21 @@ def test_split_k_fp32_ragged_alpha_beta():
     parity(case, what="split-K fp32 ragged")
 
 
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+def test_split_k_two_slot_ring(la, lb):
+    """Split-K on the two-slot (split-ring) 128 tile: 144 tiles x 2 slices =
+    288 workgroups, two per CU, the arrival flag inside the ring's LDS; K
+    with and without a tail inside the last stage; fp32 C, beta != 0;
+    sampled rows."""
+    for K in (4096, 4000):
+        M, N = 1536, 1536
+        case = gi.make_case(M, N, K, layout_a=la, layout_b=lb, out_type=OUT_F32,
+                            alpha=0.75, beta=-1.5, seed=90)
+        kernel = plan_kernel(case)
+        assert "128x128x64m16_" in kernel and "_sk2" in kernel, kernel
+        parity(case, rows=sample_rows(M, n_random=24), what=f"{kernel} {M}x{N}x{K}")
+
+
 def test_split_k_repeatable_and_interleaved():
     """The arrival counters return to zero after every launch: a split-K plan
     run twice gives the same bits, also with another split-K plan launched in
