@@ -887,14 +887,14 @@ struct Frag16 {
     }
 
     // Next stage: every base moves one slot on, wrapping around the ring.
-    // Two slots at BASE and BASE + SLOT_BYTES: one XOR, since every offset
-    // inside a slot lies below the lowest bit in which the two slot addresses
-    // differ.  Three: add and wrap.  Four (interleaved, BASE inside the
+    // Two slots at BASE and BASE + SLOT_BYTES: one XOR.  Three: add and wrap.  Four (interleaved, BASE inside the
     // first slot): add and mask.
     __device__ static uint32_t step(uint32_t x) {
         if constexpr (NSLOT == 2) {
+            // One XOR moves base + offset to base + SLOT + offset only if
+            // base + offset == base | offset: a slot-aligned base.
+            static_assert(BASE % SLOT_BYTES == 0, "two slots: slot-aligned base");
             constexpr uint32_t flip = (uint32_t)BASE ^ (uint32_t)(BASE + SLOT_BYTES);
-            static_assert((flip & -flip) >= (uint32_t)SLOT_BYTES, "slot offsets below the flipped bits");
             return x ^ flip;
         } else if constexpr (NSLOT == 3) {
             x += (uint32_t)SLOT_BYTES;
