@@ -1,6 +1,7 @@
 // Host-side planner of the fp16 -> fp32-accumulate GEMM: argument validation,
-// tile choice and grid shape.  Makes no HIP call, so it runs (and is tested)
-// on machines without a GPU.
+// tile, K-split and repacking choice, and grid shape.  Planning makes no HIP
+// call, so it runs (and is tested) on machines without a GPU; destroy frees
+// the device buffers a plan's runs allocated.
 //
 // Pages cited (titles as printed):
 //   [GEMM]    "手写GEMM内核：矩阵乘法性能优化的完整工程实践" (hand-written GEMM kernel)
@@ -59,7 +60,7 @@ int choose_tile(int64_t M, int64_t N, int64_t K, int64_t batch, bool kc_both, bo
     if (count(TILE_256x256) >= kNumCUs && fill(TILE_256x256) >= 0.8) return TILE_256x256;
     if (count(TILE_128x128) >= kNumCUs / 4 && fill(TILE_128x128) >= 0.6) return TILE_128x128;
     // Too few tiles to fill the CUs but enough K to cut: the 128 tile with
-    // split-K (choose_ksplit) moves each operand byte once with 256+ workgroups.
+    // split-K (choose_ksplit) puts up to one workgroup on every CU.
     if (vec_ok && batch == 1 && K >= 1024 && count(TILE_128x128) < kNumCUs) return TILE_128x128;
     if (M <= 32) return TILE_32x64;
     return TILE_64x64;
