@@ -345,6 +345,52 @@ def test_degenerate_extents():
     assert torch.equal(dC.cpu(), (case.C.float() * 2.0).half())
 
 
+# ------------------------------------------------------- 64-bit offsets
+
+@pytest.mark.parametrize("shape,tile", [((600, 4096, 256), "128x128"),
+                                        ((2048, 8192, 128), "256x256")])
+def test_huge_leading_dimension(shape, tile):
+    """A row-major with lda = 2^22 (8 MiB between rows): A spans 4.7 or 16
+    GiB, so tile origins lie beyond 2^32 bytes while each tile's lane
+    offsets stay below 2^31.  The oracle runs on the compact copy."""
+    M, N, K = shape
+    lda = 1 << 22
+    case = gi.make_case(M, N, K, beta=1.0, seed=95)
+    A = torch.zeros((M - 1) * lda + K, dtype=torch.float16, device="cuda")
+    A.as_strided((M, K), (lda, 1)).copy_(case.A.view(M, K).cuda())
+    B, C = case.B.cuda(), case.C.cuda()
+    with mpg.Plan(M, N, K, ROW_MAJOR, ROW_MAJOR, OUT_F16, lda, case.ldb, case.ldc) as p:
+        assert tile in p.kernel, p.kernel
+        p.run(A, B, C, case.alpha, case.beta)
+    torch.cuda.synchronize()
+    del A
+    rows = sample_rows(M, n_random=24)
+    ref, scale = oracle_for(case, rows)
+    check_bound(c_logical(case, C.cpu(), rows), ref, scale, OUT_F16, f"lda=2^22 {shape}")
+
+
+def test_huge_batch_stride():
+    """A strided batch whose A items lie 3 * 2^30 elements (6 GiB) apart, on
+    the 128 tile; the oracle runs on the compact copy."""
+    M, N, K, batch = 1024, 1024, 256, 2
+    sa = 3 << 30
+    case = gi.make_case(M, N, K, batch=batch, beta=0.5, seed=96)
+    A = torch.zeros(sa + M * K, dtype=torch.float16, device="cuda")
+    src = case.A.view(batch, M * K).cuda()
+    for b in range(batch):
+        A[b * sa:b * sa + M * K].copy_(src[b])
+    B, C = case.B.cuda(), case.C.cuda()
+    with mpg.Plan(M, N, K, ROW_MAJOR, ROW_MAJOR, OUT_F16, case.lda, case.ldb, case.ldc,
+                  batch, sa, case.stride_b, case.stride_c) as p:
+        assert "128x128" in p.kernel, p.kernel
+        p.run(A, B, C, case.alpha, case.beta)
+    torch.cuda.synchronize()
+    del A
+    rows = sample_rows(M, n_random=16)
+    ref, scale = oracle_for(case, rows)
+    check_bound(c_logical(case, C.cpu(), rows), ref, scale, OUT_F16, "batch stride 3*2^30")
+
+
 # ---------------------------------------------------------- determinism
 
 def test_run_to_run_bitwise_determinism():
