@@ -57,8 +57,14 @@ int choose_tile(int64_t M, int64_t N, int64_t K, int64_t batch, bool kc_both, bo
         const double pn = (double)ceil_div(N, kTiles[t].bn) * kTiles[t].bn;
         return (double)M * (double)N / (pm * pn);
     };
-    if (count(TILE_256x256) >= kNumCUs && fill(TILE_256x256) >= 0.8) return TILE_256x256;
-    if (count(TILE_128x128) >= kNumCUs / 4 && fill(TILE_128x128) >= 0.6) return TILE_128x128;
+    // Shallow K (at most four stages) is bound by the epilogue's C traffic:
+    // the 128 tile, two workgroups per CU, overlaps one's epilogue with the
+    // other's loads, where the 256 tile (one per CU) cannot.  The 128 tile
+    // also takes half-empty tiles (N or M = 64): such products are bound by
+    // streaming the other operand, not by MFMA.  (Measured: 8192^2 x 128
+    // fp32 C 87 -> 70 us, 128 x (1024 x 64 x 1024) 144 -> 66 us.)
+    if (K > 256 && count(TILE_256x256) >= kNumCUs && fill(TILE_256x256) >= 0.8) return TILE_256x256;
+    if (count(TILE_128x128) >= kNumCUs / 4 && fill(TILE_128x128) >= 0.5) return TILE_128x128;
     // Too few tiles to fill the CUs but enough K to cut: the 128 tile with
     // split-K (choose_ksplit) puts up to one workgroup on every CU.
     if (vec_ok && batch == 1 && K >= 1024 && count(TILE_128x128) < kNumCUs) return TILE_128x128;

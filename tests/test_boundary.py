@@ -125,6 +125,12 @@ def test_kernel_choice_by_regime():
     assert kern(2048, 2048, 2048).startswith("gemm_128x128x64m16d4")
     assert kern(2048, 4096, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_128x128x64m16_")
     assert kern(3072, 3072, 3072).startswith("gemm_128x128x64m16_")
+    # shallow K goes to the 128 tile (epilogue-bound), and so do half-empty
+    # 128 tiles of streaming-bound batched products
+    assert kern(8192, 8192, 256).startswith("gemm_128x128x64m16_")
+    assert kern(8192, 8192, 512).startswith("gemm_256x256")
+    assert mpg.Plan(1024, 64, 1024, batch=128, stride_a=1024 * 1024, stride_b=1024 * 64,
+                    stride_c=1024 * 64).kernel.startswith("gemm_128x128")
     assert kern(1024, 1024, 128).startswith("gemm_128x128x64m16_")
     assert "narrow" in kern(127, 257, 33)
     assert kern(0, 8, 8) == "none"

@@ -106,9 +106,9 @@ def test_large_tiles_ragged_all_layouts(shape, tile, la, lb):
 @pytest.mark.parametrize("la,lb", LAYOUTS)
 def test_tile256_odd_stage_count_all_layouts(la, lb, out_type):
     """512 whole 256 x 256 tiles (two per CU) with an odd number of 64-deep
-    stages (K = 192: the last stage sits in ring slot 0), alpha and beta !=
-    0; sampled rows."""
-    M, N, K = 4096, 8192, 192
+    stages (K = 320: A's three-slot ring wraps mid-sequence, B's last stage
+    sits in slot 0), alpha and beta != 0; sampled rows."""
+    M, N, K = 4096, 8192, 320
     case = gi.make_case(M, N, K, layout_a=la, layout_b=lb, out_type=out_type,
                         alpha=1.5, beta=-0.5, seed=80)
     kernel = plan_kernel(case)
@@ -116,14 +116,25 @@ def test_tile256_odd_stage_count_all_layouts(la, lb, out_type):
     parity(case, rows=sample_rows(M, n_random=48), what=f"{kernel} {M}x{N}x{K}")
 
 
-def test_tile256_uneven_grid_one_stage():
-    """544 tiles (not a multiple of the CU count) of a single stage each
-    (K = 64)."""
-    M, N, K = 8192, 4352, 64
+def test_tile256_uneven_grid():
+    """544 tiles of 256 (not a multiple of the CU count), K = 384."""
+    M, N, K = 8192, 4352, 384
     case = gi.make_case(M, N, K, beta=1.0, seed=81)
     kernel = plan_kernel(case)
     assert "256x256" in kernel, kernel
     parity(case, rows=sample_rows(M, n_random=64), what=f"{kernel} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("lb", [ROW_MAJOR, COL_MAJOR])
+def test_tile128_single_stage(lb):
+    """Shallow K on the two-slot 128 tile: one 64-deep stage (K = 64) and a
+    stage tail (K = 40), 2176 tiles."""
+    for K in (64, 40):
+        M, N = 8192, 4352
+        case = gi.make_case(M, N, K, layout_b=lb, beta=1.0, seed=84)
+        kernel = plan_kernel(case)
+        assert "128x128x64m16_" in kernel, kernel
+        parity(case, rows=sample_rows(M, n_random=48), what=f"{kernel} {M}x{N}x{K}")
 
 
 def test_tile256_batched():
@@ -142,7 +153,7 @@ def test_tile256_batched():
 
 def test_tile256_misaligned_c():
     """The 256 tile with a C pointer that only allows element-wide access."""
-    M, N, K = 4096, 8192, 128
+    M, N, K = 4096, 8192, 384
     case = gi.make_case(M, N, K, beta=1.0, seed=83)
     assert "256x256" in plan_kernel(case)
     C = torch.zeros(case.C.numel() + 1, dtype=torch.float16, device="cuda")
@@ -348,7 +359,7 @@ def test_degenerate_extents():
 # ------------------------------------------------------- 64-bit offsets
 
 @pytest.mark.parametrize("shape,tile", [((600, 4096, 256), "128x128"),
-                                        ((2048, 8192, 128), "256x256")])
+                                        ((2048, 8192, 384), "256x256")])
 def test_huge_leading_dimension(shape, tile):
     """A row-major with lda = 2^22 (8 MiB between rows): A spans 4.7 or 16
     GiB, so tile origins lie beyond 2^32 bytes while each tile's lane
