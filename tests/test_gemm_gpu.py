@@ -402,6 +402,53 @@ def test_huge_batch_stride():
     check_bound(c_logical(case, C.cpu(), rows), ref, scale, OUT_F16, "batch stride 3*2^30")
 
 
+# ------------------------------------------------------- random sweep
+
+def _sweep_cases(n, seed):
+    """Seeded shapes from four classes -- small (staged and streaming
+    kernels), skinny and deep (streaming, split-K), medium (128 tile, two- and
+    four-slot rings), large (256 tile) -- with random layouts, leading
+    dimensions that are multiples of 8 or not (repacking), batch, alpha/beta
+    and output type."""
+    rng = np.random.default_rng(seed)
+
+    def dim(lo, hi):
+        v = int(rng.integers(lo, hi))
+        return v - v % 8 if (rng.random() < 0.5 and v >= 8) else v
+
+    out = []
+    for i in range(n):
+        cls = i % 4
+        if cls == 0:
+            M, N, K = dim(1, 300), dim(1, 300), dim(1, 300)
+        elif cls == 1:
+            M, N, K = dim(1, 160), dim(900, 5000), dim(900, 5000)
+        elif cls == 2:
+            M, N, K = dim(400, 2600), dim(400, 2600), dim(64, 3000)
+        else:
+            M, N = (int(rng.choice([4096, 4352, 5120])) for _ in range(2))
+            K = int(rng.integers(5, 19)) * 64
+        la, lb = (int(x) for x in rng.integers(0, 2, size=2))
+        pad = int(rng.choice([0, 0, 8, 3])) if cls != 3 else 0
+        batch = int(rng.choice([1, 1, 1, 2])) if cls in (0, 2) else 1
+        out_type = int(rng.integers(0, 2))
+        alpha, beta = float(rng.choice([1.0, -0.5])), float(rng.choice([0.0, 1.0, 2.0]))
+        out.append((M, N, K, la, lb, pad, batch, out_type, alpha, beta))
+    return out
+
+
+@pytest.mark.parametrize("case_args", _sweep_cases(40, 2026))
+def test_random_sweep(case_args):
+    M, N, K, la, lb, pad, batch, out_type, alpha, beta = case_args
+    lda = (K if la == ROW_MAJOR else M) + pad
+    ldb = (N if lb == ROW_MAJOR else K) + pad
+    case = gi.make_case(M, N, K, layout_a=la, layout_b=lb, out_type=out_type, alpha=alpha,
+                        beta=beta, batch=batch, lda=lda, ldb=ldb, seed=hash(case_args) % 1000)
+    kernel = plan_kernel(case)
+    rows = None if M * N * K * batch <= (1 << 27) else sample_rows(M, n_random=16, tiles=(256, 128))
+    parity(case, rows=rows, what=f"{kernel} {case_args}")
+
+
 # ---------------------------------------------------------- determinism
 
 def test_run_to_run_bitwise_determinism():
