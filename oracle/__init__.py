@@ -1,11 +1,12 @@
-"""CPU oracle for C = alpha*A*B + beta*C with binary16 A, B (test infrastructure).
+"""CPU oracle for C = alpha*A*B + beta*C with binary16 or bfloat16 A, B (test
+infrastructure).
 
 TEST INFRASTRUCTURE ONLY.  Only tests/, the smoke check in __graft_entry__ and
 the CPU-baseline leg of bench.py may import this package.  It shares no code
 with the GPU path (mixed_precision_gemm_amd) and never imports it.
 
-The arithmetic is in ref_gemm.c (plain fp64 triple loop, own binary16 decoder
-and encoder); this module only marshals numpy arrays through ctypes.  See the
+The arithmetic is in ref_gemm.c (plain fp64 triple loop, own binary16 and
+bfloat16 decoders and encoders); this module only marshals numpy arrays through ctypes.  See the
 header of ref_gemm.c for what each function follows on the pages.
 """
 import ctypes
@@ -15,7 +16,8 @@ import numpy as np
 from . import build as _build
 
 ROW_MAJOR, COL_MAJOR = 0, 1
-OUT_F16, OUT_F32 = 0, 1
+OUT_F16, OUT_F32, OUT_BF16 = 0, 1, 2
+IN_F16, IN_BF16 = 0, 1
 
 _lib = None
 
@@ -28,8 +30,12 @@ def load_library(path):
     lib.oracle_dec16.restype = dbl
     lib.oracle_enc16.argtypes = [dbl]
     lib.oracle_enc16.restype = ctypes.c_uint16
+    lib.oracle_decbf16.argtypes = [ctypes.c_uint16]
+    lib.oracle_decbf16.restype = dbl
+    lib.oracle_encbf16.argtypes = [dbl]
+    lib.oracle_encbf16.restype = ctypes.c_uint16
     lib.oracle_gemm.argtypes = [i64, i64, i64, i64,
-                                ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                 i64, i64, i64, i64, i64, i64,
                                 vp, vp, vp, dbl, dbl, vp, i64, vp, vp,
                                 ctypes.c_int]
@@ -62,25 +68,42 @@ def enc16(values, lib=None) -> np.ndarray:
     return out.reshape(np.shape(values))
 
 
+def decbf16(bits, lib=None) -> np.ndarray:
+    """bfloat16 bit patterns (any int array) -> float64, element by element."""
+    lib = lib or _load()
+    flat = np.asarray(bits, dtype=np.uint16).ravel()
+    out = np.array([lib.oracle_decbf16(int(h)) for h in flat], dtype=np.float64)
+    return out.reshape(np.shape(bits))
+
+
+def encbf16(values, lib=None) -> np.ndarray:
+    """float64 values -> bfloat16 bit patterns (round to nearest, ties even)."""
+    lib = lib or _load()
+    flat = np.asarray(values, dtype=np.float64).ravel()
+    out = np.array([lib.oracle_encbf16(float(v)) for v in flat], dtype=np.uint16)
+    return out.reshape(np.shape(values))
+
+
 def _as_u16(x) -> np.ndarray:
     a = np.ascontiguousarray(x)
     if a.dtype == np.float16:
         a = a.view(np.uint16)
     if a.dtype != np.uint16:
-        raise TypeError(f"expected binary16 storage, got {a.dtype}")
+        raise TypeError(f"expected 16-bit storage, got {a.dtype}")
     return a
 
 
 def gemm(M, N, K, A, B, C=None, *, alpha=1.0, beta=0.0,
          layout_a=ROW_MAJOR, layout_b=ROW_MAJOR, out_type=OUT_F16,
-         lda=None, ldb=None, ldc=None, batch=1,
+         in_type=IN_F16, lda=None, ldb=None, ldc=None, batch=1,
          stride_a=0, stride_b=0, stride_c=0, rows=None, nthreads=None,
          lib=None):
     """Reference result and error scale, each shaped (batch, nrows, N).
 
-    A, B: flat binary16 storage (uint16 or float16 numpy arrays) in the
-    layouts given; C: binary16 (out_type OUT_F16) or float32 storage, read
-    only when beta != 0.  alpha, beta are rounded to fp32 first, as the
+    A, B: flat 16-bit storage (uint16 or float16 numpy arrays) in the
+    layouts given, binary16 (in_type IN_F16) or bfloat16 bits (IN_BF16); C:
+    binary16 (out_type OUT_F16), bfloat16 bits (OUT_BF16) or float32
+    storage, read only when beta != 0.  alpha, beta are rounded to fp32 first, as the
     library receives them.  rows: optional row indices (sampled rows).
     lib: an alternative library handle from load_library (tests only).
     """
@@ -95,7 +118,7 @@ def gemm(M, N, K, A, B, C=None, *, alpha=1.0, beta=0.0,
         if C is None:
             raise ValueError("beta != 0 needs C")
         c = np.ascontiguousarray(C)
-        if out_type == OUT_F16:
+        if out_type in (OUT_F16, OUT_BF16):
             c = _as_u16(c)
         elif c.dtype != np.float32:
             raise TypeError("fp32 C expected")
@@ -112,7 +135,7 @@ def gemm(M, N, K, A, B, C=None, *, alpha=1.0, beta=0.0,
     alpha32 = float(np.float32(alpha))
     beta32 = float(np.float32(beta))
     ptr = lambda x: None if x is None else x.ctypes.data
-    rc = lib.oracle_gemm(batch, M, N, K, layout_a, layout_b, out_type,
+    rc = lib.oracle_gemm(batch, M, N, K, layout_a, layout_b, in_type, out_type,
                          lda, ldb, ldc, stride_a, stride_b, stride_c,
                          ptr(a), ptr(b), ptr(c), alpha32, beta32,
                          ptr(rows_arr), nrows, ptr(ref), ptr(scale), int(nthreads))

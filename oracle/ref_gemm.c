@@ -1,5 +1,6 @@
 /*
- * CPU oracle for C = alpha * A * B + beta * C with binary16 A and B.
+ * CPU oracle for C = alpha * A * B + beta * C with binary16 or bfloat16 A
+ * and B.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg may load this library.  The GPU product path
@@ -22,21 +23,32 @@
  *     j of B, summed over k;
  *   - [CATLASS] §2.1: the GEMM is C = A*B + C; alpha and beta scale the two
  *     terms (C is not read when beta == 0, the BLAS convention);
- *   - [GEMM] §1.3: fp16 inputs, fp32 accumulation, fp16 output.
- * Every binary16 product is exact in double (11 x 11 significant bits), and
- * k is summed in ascending order with no reassociation (-fno-fast-math).
+ *   - [GEMM] §1.3: fp16 inputs, fp32 accumulation, fp16 output;
+ *   - [GEMM] §6 and [CATLASS] §3.2: bfloat16 is the other 16-bit input
+ *     format (the one the pages recommend for training); the same product
+ *     with bfloat16 A and B and a bfloat16 or fp32 C.
+ * Every product of two inputs is exact in double (11 x 11 significant bits
+ * for binary16, 8 x 8 for bfloat16), and k is summed in ascending order with
+ * no reassociation (-fno-fast-math).
  * Besides the value, the oracle returns the error scale
  *   S = |alpha| * sum_k |a_ik * b_kj| + |beta| * |c_ij|
  * used by the acceptance bound.
  *
  * binary16 ([GEMM] §6.1, [CATLASS] §3.2: 1 sign bit, 5 exponent bits,
  * 10 fraction bits, largest finite 65504, subnormals down to 2^-24) is
- * decoded and encoded here from the IEEE-754 definition.
+ * decoded and encoded here from the IEEE-754 definition.  bfloat16
+ * ([CATLASS] §3.2: 1 sign bit, 8 exponent bits -- the exponent range of
+ * fp32 -- and 7 fraction bits) is decoded and encoded from that layout with
+ * the same rules: bias 127, subnormals at exponent field 0, infinities and
+ * NaNs at 255.
  *
  * Parity pins live in tests/test_oracle.py: exhaustive decode against
  * numpy.float16, encode against numpy's round-to-nearest-even, exact
  * rational brute force over tiny shapes and all four layouts, closed forms
- * (all-ones, identity, K = 1) and integer-exact inputs.
+ * (all-ones, identity, K = 1) and integer-exact inputs; for bfloat16,
+ * exhaustive decode against the upper half of binary32, encode against
+ * torch's round-to-nearest-even, the format's landmarks and the same brute
+ * force.
  */
 #include <math.h>
 #include <pthread.h>
@@ -48,6 +60,9 @@
 #define ORACLE_COL_MAJOR 1
 #define ORACLE_OUT_F16 0
 #define ORACLE_OUT_F32 1
+#define ORACLE_OUT_BF16 2
+#define ORACLE_IN_F16 0
+#define ORACLE_IN_BF16 1
 
 /* binary16 -> double.  e = 0: f * 2^-24 (zero or subnormal);
  * 1 <= e <= 30: (1024 + f) * 2^(e - 25); e = 31: inf (f = 0) or NaN. */
@@ -97,9 +112,63 @@ uint16_t oracle_enc16(double x)
     return (uint16_t)(sign | ((uint32_t)(E + 15) << 10) | (ri - 1024));
 }
 
+/* bfloat16 -> double.  e = 0: f * 2^-133 (zero or subnormal: f 2^-7 times
+ * the smallest normal 2^-126); 1 <= e <= 254: (128 + f) * 2^(e - 134);
+ * e = 255: inf (f = 0) or NaN. */
+double oracle_decbf16(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 7) & 255;
+    int f = h & 127;
+    double mag;
+    if (e == 0)
+        mag = ldexp((double)f, -133);
+    else if (e == 255)
+        mag = f ? NAN : INFINITY;
+    else
+        mag = ldexp((double)(128 + f), e - 134);
+    return sign ? -mag : mag;
+}
+
+/* double -> bfloat16, round to nearest, ties to even.  The quantum of the
+ * binade [2^E, 2^(E+1)) is 2^(E-7), and 2^-133 below 2^-126.  A value that
+ * rounds to 2^128 or more (from (2 - 2^-8) 2^127 up, the tie going to the
+ * even neighbour 2^128) becomes infinity.  NaN maps to the quiet NaN 0x7FC0
+ * with the input's sign. */
+uint16_t oracle_encbf16(double x)
+{
+    uint16_t sgn = signbit(x) ? 0x8000 : 0;
+    if (isnan(x))
+        return (uint16_t)(sgn | 0x7FC0);
+    double mag = fabs(x);
+    if (mag == 0.0)
+        return sgn;
+    if (isinf(mag))
+        return (uint16_t)(sgn | 0x7F80);
+    int ex;
+    frexp(mag, &ex);        /* mag = m * 2^ex with m in [0.5, 1) */
+    int E = ex - 1;
+    if (E > 127)
+        return (uint16_t)(sgn | 0x7F80);
+    if (E < -126)
+        E = -126;
+    double t = ldexp(mag, 7 - E);    /* mag / quantum, exact */
+    double q = nearbyint(t);
+    uint32_t qi = (uint32_t)q;
+    if (E == -126 && qi < 128)
+        return (uint16_t)(sgn | qi);   /* subnormal, or zero */
+    if (qi == 256) {                   /* carried into the next binade */
+        qi = 128;
+        E += 1;
+        if (E > 127)
+            return (uint16_t)(sgn | 0x7F80);
+    }
+    return (uint16_t)(sgn | ((uint32_t)(E + 127) << 7) | (qi - 128));
+}
+
 typedef struct {
     int64_t batch, M, N, K;
-    int layout_a, layout_b, out_type;
+    int layout_a, layout_b, in_type, out_type;
     int64_t lda, ldb, ldc, stride_a, stride_b, stride_c;
     const uint16_t *A, *B;
     const void *C;
@@ -117,7 +186,7 @@ static double elem_a(const job_t *j, int64_t b, int64_t i, int64_t k)
     const uint16_t *A = j->A + b * j->stride_a;
     uint16_t h = (j->layout_a == ORACLE_ROW_MAJOR) ? A[i * j->lda + k]
                                                    : A[i + k * j->lda];
-    return oracle_dec16(h);
+    return j->in_type == ORACLE_IN_BF16 ? oracle_decbf16(h) : oracle_dec16(h);
 }
 
 static double elem_b(const job_t *j, int64_t b, int64_t k, int64_t n)
@@ -125,7 +194,7 @@ static double elem_b(const job_t *j, int64_t b, int64_t k, int64_t n)
     const uint16_t *B = j->B + b * j->stride_b;
     uint16_t h = (j->layout_b == ORACLE_ROW_MAJOR) ? B[k * j->ldb + n]
                                                    : B[k + n * j->ldb];
-    return oracle_dec16(h);
+    return j->in_type == ORACLE_IN_BF16 ? oracle_decbf16(h) : oracle_dec16(h);
 }
 
 static double elem_c(const job_t *j, int64_t b, int64_t i, int64_t n)
@@ -133,6 +202,8 @@ static double elem_c(const job_t *j, int64_t b, int64_t i, int64_t n)
     int64_t off = b * j->stride_c + i * j->ldc + n;
     if (j->out_type == ORACLE_OUT_F16)
         return oracle_dec16(((const uint16_t *)j->C)[off]);
+    if (j->out_type == ORACLE_OUT_BF16)
+        return oracle_decbf16(((const uint16_t *)j->C)[off]);
     return (double)((const float *)j->C)[off];
 }
 
@@ -191,14 +262,17 @@ static void *run_job(void *arg)
  *   A(b,i,k) = A[b*stride_a + i*lda + k] (row-major) or A[b*stride_a + i + k*lda]
  *   B(b,k,n) = B[b*stride_b + k*ldb + n] (row-major) or B[b*stride_b + k + n*ldb]
  *   C(b,i,n) = C[b*stride_c + i*ldc + n] (always row-major; binary16 bits when
- *              out_type == ORACLE_OUT_F16, float when ORACLE_OUT_F32)
+ *              out_type == ORACLE_OUT_F16, float when ORACLE_OUT_F32,
+ *              bfloat16 bits when ORACLE_OUT_BF16)
+ * in_type: ORACLE_IN_F16 (A and B hold binary16 bits) or ORACLE_IN_BF16
+ * (bfloat16 bits).
  * rows: optional list of nrows row indices to evaluate (NULL = all M rows,
  * nrows must then equal M).  Results: ref and scale, each batch x nrows x N,
  * dense.  alpha, beta: the fp32 scalars the caller passes, widened.
  * Returns 0, or -1 on bad arguments, -2 when memory runs out.
  */
 int oracle_gemm(int64_t batch, int64_t M, int64_t N, int64_t K,
-                int layout_a, int layout_b, int out_type,
+                int layout_a, int layout_b, int in_type, int out_type,
                 int64_t lda, int64_t ldb, int64_t ldc,
                 int64_t stride_a, int64_t stride_b, int64_t stride_c,
                 const uint16_t *A, const uint16_t *B, const void *C,
@@ -207,6 +281,10 @@ int oracle_gemm(int64_t batch, int64_t M, int64_t N, int64_t K,
                 double *ref, double *scale, int nthreads)
 {
     if (batch < 0 || M < 0 || N < 0 || K < 0 || nrows < 0)
+        return -1;
+    if (in_type != ORACLE_IN_F16 && in_type != ORACLE_IN_BF16)
+        return -1;
+    if (out_type != ORACLE_OUT_F16 && out_type != ORACLE_OUT_F32 && out_type != ORACLE_OUT_BF16)
         return -1;
     if (!rows && nrows != M)
         return -1;
@@ -235,7 +313,7 @@ int oracle_gemm(int64_t batch, int64_t M, int64_t N, int64_t K,
     if (bt) {
         job_t probe;
         memset(&probe, 0, sizeof probe);
-        probe.layout_b = layout_b; probe.ldb = ldb; probe.B = B;
+        probe.layout_b = layout_b; probe.ldb = ldb; probe.B = B; probe.in_type = in_type;
         for (int64_t n = 0; n < N; ++n)
             for (int64_t k = 0; k < K; ++k)
                 bt[n * K + k] = elem_b(&probe, 0, k, n);
@@ -243,7 +321,8 @@ int oracle_gemm(int64_t batch, int64_t M, int64_t N, int64_t K,
     for (int t = 0; t < nthreads; ++t) {
         job_t *j = &jobs[t];
         j->batch = batch; j->M = M; j->N = N; j->K = K;
-        j->layout_a = layout_a; j->layout_b = layout_b; j->out_type = out_type;
+        j->layout_a = layout_a; j->layout_b = layout_b; j->in_type = in_type;
+        j->out_type = out_type;
         j->lda = lda; j->ldb = ldb; j->ldc = ldc;
         j->stride_a = stride_a; j->stride_b = stride_b; j->stride_c = stride_c;
         j->A = A; j->B = B; j->C = C;

@@ -2,9 +2,10 @@
 
 The oracle (oracle/ref_gemm.c) is the plain definition of
 C = alpha*A*B + beta*C in fp64.  These tests pin it to things other than
-itself: numpy's binary16 conversions, exact rational arithmetic on tiny
-inputs (brute force), numpy's int64 matrix product on integer inputs, the
-binary16 landmarks the pages state (tests/golden/), and closed forms.  The
+itself: numpy's binary16 conversions, binary32's bit layout and torch's
+rounding for bfloat16, exact rational arithmetic on tiny inputs (brute
+force), numpy's int64 matrix product on integer inputs, the binary16 and
+bfloat16 landmarks the pages state (tests/golden/), and closed forms.  The
 logical matrices are built first and laid out into storage with numpy
 transposes, so the oracle's own index formulas are checked, not retyped.
 """
@@ -16,7 +17,9 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import COL_MAJOR, OUT_F16, OUT_F32, ROW_MAJOR
+import torch
+
+from oracle import COL_MAJOR, IN_BF16, IN_F16, OUT_BF16, OUT_F16, OUT_F32, ROW_MAJOR
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 LAYOUTS = [(ROW_MAJOR, ROW_MAJOR), (ROW_MAJOR, COL_MAJOR),
@@ -26,12 +29,13 @@ LAYOUTS = [(ROW_MAJOR, ROW_MAJOR), (ROW_MAJOR, COL_MAJOR),
 # ---------------------------------------------------------------- helpers
 
 def to_storage(logical: np.ndarray, layout: int, ld: int, fill=0):
-    """Lays a logical rows x cols fp16 matrix out with leading dimension ld.
-    Row-major: ld >= cols, element (r, c) at r*ld + c.  Column-major: the
-    transpose is stored row-major, element (r, c) at r + c*ld."""
+    """Lays a logical rows x cols matrix (fp16 values, or bfloat16 bit
+    patterns as uint16) out with leading dimension ld.  Row-major: ld >=
+    cols, element (r, c) at r*ld + c.  Column-major: the transpose is stored
+    row-major, element (r, c) at r + c*ld."""
     mat = logical if layout == ROW_MAJOR else logical.T
     rows, cols = mat.shape
-    store = np.full((rows, ld), fill, dtype=np.float16)
+    store = np.full((rows, ld), fill, dtype=logical.dtype)
     store[:, :cols] = mat
     return store.ravel()
 
@@ -63,6 +67,29 @@ def exact_product(A_log, B_log, C_log, alpha, beta):
 
 def rand_f16(rng, shape):
     return (rng.uniform(-1, 1, size=shape)).astype(np.float16)
+
+
+BF16_NAN = 0x7FC0
+
+
+def bf16_bits(values) -> np.ndarray:
+    """float32-representable values -> bfloat16 bits, rounded by torch (a
+    conversion written independently of the oracle)."""
+    t = torch.from_numpy(np.ascontiguousarray(values, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def bf16_values(bits) -> np.ndarray:
+    """bfloat16 bits -> float64: the binary32 whose upper half they are."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    with np.errstate(invalid="ignore"):   # signalling NaN patterns
+        return b.view(np.float32).astype(np.float64)
+
+
+def rand_bf16(rng, shape):
+    """Uniform [-1, 1) rounded to bfloat16: (bits, values)."""
+    bits = bf16_bits(rng.uniform(-1, 1, size=shape).astype(np.float32))
+    return bits, bf16_values(bits)
 
 
 # ------------------------------------------------------- binary16 decoding
@@ -131,57 +158,71 @@ def test_enc16_specials():
 
 # ------------------------------------------------ exact brute force (tiny)
 
-def _run_case(lib, M, N, K, la, lb, out_type, alpha, beta, batch, pad, rng):
-    A_log = [rand_f16(rng, (M, K)) for _ in range(batch)]
-    B_log = [rand_f16(rng, (K, N)) for _ in range(batch)]
-    if out_type == OUT_F16:
-        C_log = [rand_f16(rng, (M, N)) for _ in range(batch)]
+def _draw16(rng, shape, in_bf16):
+    """(storage, values, NaN fill) of a uniform [-1, 1) 16-bit matrix."""
+    if in_bf16:
+        bits, vals = rand_bf16(rng, shape)
+        return bits, vals, BF16_NAN
+    h = rand_f16(rng, shape)
+    return h, h.astype(np.float64), np.nan
+
+
+def _run_case(lib, M, N, K, la, lb, out_type, alpha, beta, batch, pad, rng,
+              in_type=IN_F16):
+    bf = in_type == IN_BF16
+    Ad = [_draw16(rng, (M, K), bf) for _ in range(batch)]
+    Bd = [_draw16(rng, (K, N), bf) for _ in range(batch)]
+    if out_type in (OUT_F16, OUT_BF16):
+        Cd = [_draw16(rng, (M, N), out_type == OUT_BF16) for _ in range(batch)]
     else:
-        C_log = [rng.uniform(-4, 4, (M, N)).astype(np.float32) for _ in range(batch)]
+        Cd = [(c, c.astype(np.float64), np.nan) for c in
+              (rng.uniform(-4, 4, (M, N)).astype(np.float32) for _ in range(batch))]
     lda = (K if la == ROW_MAJOR else M) + pad
     ldb = (N if lb == ROW_MAJOR else K) + pad
     ldc = N + pad
-    A, sa = stack_batches(A_log, la, lda, fill=np.nan)
-    B, sb = stack_batches(B_log, lb, ldb, fill=np.nan)
+    A, sa = stack_batches([d[0] for d in Ad], la, lda, fill=Ad[0][2])
+    B, sb = stack_batches([d[0] for d in Bd], lb, ldb, fill=Bd[0][2])
     cst = []
-    for c in C_log:
-        s = np.full((M, ldc), np.nan, dtype=c.dtype)
+    for c, _, fill in Cd:
+        s = np.full((M, ldc), fill, dtype=c.dtype)
         s[:, :N] = c
         cst.append(s.ravel())
     C = np.concatenate(cst)
     ref, sc = oracle.gemm(M, N, K, A, B, C, alpha=alpha, beta=beta,
                           layout_a=la, layout_b=lb, out_type=out_type,
+                          in_type=in_type,
                           lda=lda, ldb=ldb, ldc=ldc, batch=batch,
                           stride_a=sa, stride_b=sb, stride_c=M * ldc,
                           nthreads=2, lib=lib)
     for b in range(batch):
-        ex, exs = exact_product(A_log[b], B_log[b], C_log[b], alpha, beta)
+        ex, exs = exact_product(Ad[b][1], Bd[b][1], Cd[b][1], alpha, beta)
         for i in range(M):
             for j in range(N):
                 tol = float(exs[i, j]) * 2.0 ** -50
                 assert abs(Fraction(ref[b, i, j]) - ex[i, j]) <= Fraction(tol), \
-                    (M, N, K, la, lb, out_type, alpha, beta, b, i, j)
+                    (M, N, K, la, lb, in_type, out_type, alpha, beta, b, i, j)
                 assert abs(Fraction(sc[b, i, j]) - exs[i, j]) <= Fraction(tol)
 
 
 ALPHA_BETA = [(1.0, 0.0), (-0.5, 2.0), (0.0, 1.0)]
 
 
-def _brute_force(lib, shapes, full_combos):
+def _brute_force(lib, shapes, full_combos, in_type=IN_F16):
     rng = np.random.default_rng(7)
+    outs = (OUT_F16, OUT_F32) if in_type == IN_F16 else (OUT_BF16, OUT_F32)
     n = 0
     for idx, (M, N, K) in enumerate(shapes):
         for li, (la, lb) in enumerate(LAYOUTS):
             if full_combos:
-                combos = [(o, ab) for o in (OUT_F16, OUT_F32) for ab in ALPHA_BETA]
+                combos = [(o, ab) for o in outs for ab in ALPHA_BETA]
             else:
                 k = idx * 4 + li
-                combos = [((OUT_F16, OUT_F32)[k % 2], ALPHA_BETA[k % 3])]
+                combos = [(outs[k % 2], ALPHA_BETA[k % 3])]
             for out_type, (alpha, beta) in combos:
                 batch = 1 + (n % 2)
                 pad = n % 3
                 _run_case(lib, M, N, K, la, lb, out_type, alpha, beta, batch,
-                          pad, rng)
+                          pad, rng, in_type)
                 n += 1
     return n
 
@@ -194,6 +235,96 @@ def test_brute_force_all_small_shapes():
 def test_brute_force_odd_shapes_all_combinations():
     shapes = [(1, 1, 1), (3, 5, 7), (17, 9, 33)]
     _brute_force(None, shapes, full_combos=True)
+
+
+def test_brute_force_bf16_small_shapes():
+    shapes = list(itertools.product(range(1, 7), repeat=3))
+    assert _brute_force(None, shapes, full_combos=False, in_type=IN_BF16) == 216 * 4
+
+
+def test_brute_force_bf16_odd_shapes_all_combinations():
+    shapes = [(1, 1, 1), (3, 5, 7), (17, 9, 33)]
+    _brute_force(None, shapes, full_combos=True, in_type=IN_BF16)
+
+
+# ------------------------------------------------------ bfloat16 decoding
+
+def test_decbf16_exhaustive_against_binary32_upper_half():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.decbf16(bits)
+    want = bf16_values(bits)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+    # and torch's own bfloat16 -> float64 conversion agrees
+    t = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(got[~nan], t[~nan])
+
+
+def test_bfloat16_landmarks_golden():
+    path = os.path.join(GOLDEN, "bfloat16_landmarks.txt")
+    rows = []
+    with open(path) as fh:
+        for line in fh:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            parts = line.split()
+            rows.append((int(parts[0], 16), float(parts[1])))
+    assert len(rows) >= 10
+    for bits, value in rows:
+        got = float(oracle.decbf16(np.array([bits]))[0])
+        assert got == value and np.signbit(got) == np.signbit(value), hex(bits)
+        if not np.isinf(value):
+            assert int(oracle.encbf16(np.array([value]))[0]) == bits, hex(bits)
+    # the page's rounded figures: largest finite about 3.4e38, smallest
+    # normal about 1e-38, the exponent range of fp32
+    assert abs(oracle.decbf16(np.array([0x7F7F]))[0] / 3.4e38 - 1) < 0.01
+    assert 1e-38 < oracle.decbf16(np.array([0x0080]))[0] < 1.2e-38
+    assert oracle.decbf16(np.array([0x0080]))[0] == float(np.finfo(np.float32).tiny)
+
+
+# ------------------------------------------------------ bfloat16 encoding
+
+def _encode_bf16_probe_values():
+    """Values exactly representable in float32 (torch rounds float32 to
+    bfloat16 once, so its result is the correctly rounded one)."""
+    rng = np.random.default_rng(2)
+    fin = bf16_values(np.arange(0, 0x7F80, dtype=np.uint32).astype(np.uint16))
+    f32 = lambda x: np.asarray(x, dtype=np.float32)
+    mids = f32((fin[:-1] + fin[1:]) / 2)               # exact ties (9 bits)
+    up = np.nextafter(mids, f32(np.inf))
+    dn = np.nextafter(mids, f32(0))
+    rnd = f32(np.exp2(rng.uniform(-140, 128, 40000)))
+    edge = f32([3.3895313892515355e38, 3.3961775292304e38, 3.4028234663852886e38,
+                2.0 ** -133, 2.0 ** -134, 3 * 2.0 ** -134, 2.0 ** -126 - 2.0 ** -134,
+                1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 255.5, 256.5, 257.0])
+    v = np.concatenate([f32(fin), mids, up, dn, rnd, edge]).astype(np.float64)
+    return np.concatenate([v, -v])
+
+
+def test_encbf16_matches_torch_round_to_nearest_even():
+    v = _encode_bf16_probe_values()
+    got = oracle.encbf16(v)
+    want = bf16_bits(v.astype(np.float32))
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(v[i], hex(got[i]), hex(want[i])) for i in bad[:5]]
+
+
+def test_encbf16_double_only_values_and_specials():
+    # values no float32 holds, checked against the rounding rule by hand
+    cases = {1e300: 0x7F80, -1e300: 0xFF80, 1e-300: 0x0000, -1e-300: 0x8000,
+             (2 - 2.0 ** -8) * 2.0 ** 127: 0x7F80,                 # tie at the top -> inf
+             (2 - 2.0 ** -8) * 2.0 ** 127 * (1 - 2.0 ** -40): 0x7F7F,
+             1.0 + 2.0 ** -8 + 2.0 ** -40: 0x3F81,                 # just above a tie
+             2.0 ** -134 * (1 + 2.0 ** -40): 0x0001}
+    for x, bits in cases.items():
+        assert int(oracle.encbf16(np.array([x]))[0]) == bits, (x, hex(bits))
+    got = oracle.encbf16(np.array([np.inf, -np.inf, np.nan, -0.0, 0.0]))
+    assert got[0] == 0x7F80 and got[1] == 0xFF80
+    assert (got[2] & 0x7F80) == 0x7F80 and (got[2] & 0x7F) != 0
+    assert got[3] == 0x8000 and got[4] == 0x0000
 
 
 # -------------------------------------------------------------- closed forms
@@ -242,8 +373,9 @@ def test_rank_one_K1_is_a_single_exact_product():
 
 # ------------------------------------------------------------ integer exact
 
+@pytest.mark.parametrize("in_type", [IN_F16, IN_BF16])
 @pytest.mark.parametrize("la,lb", LAYOUTS)
-def test_integer_inputs_match_int64_matmul(la, lb):
+def test_integer_inputs_match_int64_matmul(la, lb, in_type):
     rng = np.random.default_rng(5)
     M, N, K, batch = 33, 41, 113, 3
     Ai = rng.integers(-3, 4, (batch, M, K))
@@ -251,16 +383,34 @@ def test_integer_inputs_match_int64_matmul(la, lb):
     Ci = rng.integers(-8, 9, (batch, M, N))
     lda = (K if la == ROW_MAJOR else M) + 5
     ldb = (N if lb == ROW_MAJOR else K) + 2
-    A, sa = stack_batches([m.astype(np.float16) for m in Ai], la, lda, fill=np.nan)
-    B, sb = stack_batches([m.astype(np.float16) for m in Bi], lb, ldb, fill=np.nan)
-    C = Ci.astype(np.float16).ravel()
+    if in_type == IN_F16:
+        enc, fill, out = (lambda m: m.astype(np.float16)), np.nan, OUT_F16
+    else:   # small integers are exact in bfloat16 (8 significant bits)
+        enc, fill, out = (lambda m: bf16_bits(m.astype(np.float32))), BF16_NAN, OUT_BF16
+    A, sa = stack_batches([enc(m) for m in Ai], la, lda, fill=fill)
+    B, sb = stack_batches([enc(m) for m in Bi], lb, ldb, fill=fill)
+    C = enc(Ci).ravel()
     ref, sc = oracle.gemm(M, N, K, A, B, C, alpha=1.0, beta=1.0, layout_a=la,
                           layout_b=lb, lda=lda, ldb=ldb, batch=batch,
-                          stride_a=sa, stride_b=sb, stride_c=M * N)
+                          stride_a=sa, stride_b=sb, stride_c=M * N,
+                          in_type=in_type, out_type=out)
     want = np.matmul(Ai, Bi) + Ci
     assert np.array_equal(ref, want.astype(np.float64))
     want_s = np.matmul(np.abs(Ai), np.abs(Bi)) + np.abs(Ci)
     assert np.array_equal(sc, want_s.astype(np.float64))
+
+
+def test_all_ones_bf16_rounds_K_to_bfloat16():
+    """K ones: the sum is exactly K; its bfloat16 is the nearest of the
+    values 2^e (1 + f/128) -- 4097 and 4100 round to 4096, 4112 to 4096 (a
+    tie, to even), 4113 to 4128."""
+    M, N = 3, 2
+    for K, bits in [(7, 0x40E0), (256, 0x4380), (4097, 0x4580), (4112, 0x4580), (4113, 0x4581)]:
+        A = np.full(M * K, 0x3F80, np.uint16)
+        B = np.full(K * N, 0x3F80, np.uint16)
+        ref, sc = oracle.gemm(M, N, K, A, B, in_type=IN_BF16, out_type=OUT_BF16)
+        assert np.all(ref == K) and np.all(sc == K)
+        assert np.all(oracle.encbf16(ref.ravel()) == bits), K
 
 
 def test_fp32_c_is_read_as_fp32():

@@ -15,7 +15,9 @@ import pytest
 import oracle
 from oracle import build as oracle_build
 
-from test_oracle import _brute_force, _encode_probe_values
+from oracle import IN_BF16
+from test_oracle import (_brute_force, _encode_bf16_probe_values, _encode_probe_values,
+                         bf16_bits, bf16_values)
 
 MUTANTS = {
     "transposed_A_row_major": ("A[i * j->lda + k]", "A[k * j->lda + i]"),
@@ -31,6 +33,16 @@ MUTANTS = {
     "scale_without_abs": ("t += fabs(p);", "t += p;"),
     "subnormal_exponent": ("mag = ldexp((double)f, -24);", "mag = ldexp((double)f, -25);"),
     "ties_away_from_zero": ("double r = nearbyint(n);", "double r = floor(n + 0.5);"),
+    "bf16_exponent_bias": ("mag = ldexp((double)(128 + f), e - 134);",
+                           "mag = ldexp((double)(128 + f), e - 133);"),
+    "bf16_fraction_width": ("int f = h & 127;", "int f = h & 255;"),
+    "bf16_ties_away_from_zero": ("double q = nearbyint(t);", "double q = floor(t + 0.5);"),
+    "bf16_no_carry_on_rounding": ("        qi = 128;\n        E += 1;\n", "        qi = 128;\n"),
+    "bf16_A_decoded_as_binary16": (
+        "A[i + k * j->lda];\n    return j->in_type == ORACLE_IN_BF16 ? oracle_decbf16(h) : oracle_dec16(h);",
+        "A[i + k * j->lda];\n    return oracle_dec16(h);"),
+    "bf16_C_decoded_as_binary16": ("return oracle_decbf16(((const uint16_t *)j->C)[off]);",
+                                   "return oracle_dec16(((const uint16_t *)j->C)[off]);"),
 }
 
 SHAPES = [(1, 1, 1), (2, 3, 4), (3, 5, 7), (4, 1, 6)]
@@ -48,6 +60,14 @@ def _pins_pass(lib) -> bool:
             assert np.array_equal(oracle.enc16(v, lib=lib),
                                   v.astype(np.float16).view(np.uint16))
         _brute_force(lib, SHAPES, full_combos=True)
+        bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+        got = oracle.decbf16(bits, lib=lib)
+        want = bf16_values(bits)
+        ok = ~np.isnan(want)
+        assert np.array_equal(got[ok], want[ok])
+        v = _encode_bf16_probe_values()
+        assert np.array_equal(oracle.encbf16(v, lib=lib), bf16_bits(v.astype(np.float32)))
+        _brute_force(lib, SHAPES, full_combos=True, in_type=IN_BF16)
     except (AssertionError, ValueError, OverflowError):
         return False   # a pin failed (or met a NaN/inf where a number was due)
     return True
