@@ -1,7 +1,7 @@
 """Benchmark of the fp16 -> fp32-accumulate GEMM on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--layout nn|nt]
-                    [--shape M N K] [--no-cpu-baseline]
+                    [--shape M N K] [--dtype f16|bf16] [--no-cpu-baseline]
 
 A step is one C = A*B + C GEMM (the whole hot path: staging, MFMA K loop,
 epilogue) on the square workload M = N = K = 8192, fp16 A, B, C uniform
@@ -9,7 +9,8 @@ epilogue) on the square workload M = N = K = 8192, fp16 A, B, C uniform
 in HBM before timing starts.  W untimed warm-up steps, then K timed steps
 bracketed by device synchronisation; the kernel's own duration is measured
 with HIP events recorded on the stream the kernel is launched on.  Prints one
-JSON line (value = TFLOP/s, 2*M*N*K flops per step).
+JSON line (value = TFLOP/s, 2*M*N*K flops per step).  --dtype bf16 runs the
+same workload with bfloat16 A, B and C (the bfloat16 entry points).
 
 The CPU baseline is the oracle (a plain fp64 triple loop on the host cores),
 timed on a bounded sample of the same workload: a fixed set of rows of C.
@@ -23,7 +24,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_F16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 dense fp16 flop/clk/CU
+PEAK_F16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 dense fp16 (or bf16) flop/clk/CU
 PEAK_HBM_GBS = 8000.0
 
 
@@ -34,6 +35,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layout", choices=["nn", "nt"], default="nn")
     ap.add_argument("--shape", type=int, nargs=3, default=[8192, 8192, 8192])
+    ap.add_argument("--dtype", choices=["f16", "bf16"], default="f16",
+                    help="element type of A, B and C (default f16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -85,13 +88,14 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def profiled_traffic(layout, shape):
+def profiled_traffic(layout, shape, dtype="f16"):
     """HBM-side bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by the copy
     calibration) from the committed rocprofv3 summary of this workload, or
     None when there is none or the kernels have changed since it was taken."""
     if tuple(shape) != (8192, 8192, 8192):
         return None
-    path = os.path.join(ROOT, "profiles", f"gemm_direct_256x256_8192cube_{layout}.md")
+    suffix = "" if dtype == "f16" else f"_{dtype}"
+    path = os.path.join(ROOT, "profiles", f"gemm_direct_256x256_8192cube_{layout}{suffix}.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -117,9 +121,12 @@ def cpu_baseline(case, nrows):
     rows = np.linspace(0, case.M - 1, num=min(nrows, case.M)).astype(np.int64)
     threads = min(16, os.cpu_count() or 1)
     t0 = time.perf_counter()
+    bf = case.meta.get("in_dtype") == "bf16"
     oracle.gemm(case.M, case.N, case.K, u16(case.A), u16(case.B), u16(case.C),
                 alpha=case.alpha, beta=case.beta, layout_a=case.layout_a,
-                layout_b=case.layout_b, rows=rows, nthreads=threads)
+                layout_b=case.layout_b, out_type=case.out_type,
+                in_type=oracle.IN_BF16 if bf else oracle.IN_F16,
+                rows=rows, nthreads=threads)
     dt = time.perf_counter() - t0
     flops = 2.0 * rows.size * case.N * case.K
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
@@ -145,13 +152,16 @@ def main():
 
     M, N, K = args.shape
     lb = gi.COL_MAJOR if args.layout == "nt" else gi.ROW_MAJOR
-    case = gi.make_case(M, N, K, layout_b=lb, alpha=1.0, beta=1.0, seed=0)
+    case = gi.make_case(M, N, K, layout_b=lb, alpha=1.0, beta=1.0, seed=0,
+                        in_dtype=args.dtype,
+                        out_type=gi.OUT_BF16 if args.dtype == "bf16" else gi.OUT_F16)
     dev = torch.device("cuda:0")
     dA, dB, dC = case.A.to(dev), case.B.to(dev), case.C.to(dev)
     plan = mpg.Plan(M, N, K, case.layout_a, case.layout_b, case.out_type,
-                    case.lda, case.ldb, case.ldc)
+                    case.lda, case.ldb, case.ldc, dtype=args.dtype)
     stream = torch.cuda.current_stream(dev)
-    print(f"# kernel {plan.kernel}, {M}x{N}x{K} {args.layout.upper()}", file=sys.stderr, flush=True)
+    print(f"# kernel {plan.kernel}, {M}x{N}x{K} {args.layout.upper()} {args.dtype}",
+          file=sys.stderr, flush=True)
 
     for _ in range(args.warmup):
         plan.run(dA, dB, dC, 1.0, 1.0, stream=stream)
@@ -172,8 +182,10 @@ def main():
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     plan.close()
 
+    tname = "bf16" if args.dtype == "bf16" else "fp16"
     out = {
-        "metric": "FP16 GEMM TFLOP/s (fp32 acc) at M=N=K=8192; % of MFMA FP16 peak",
+        "metric": (f"{tname.upper()} GEMM TFLOP/s (fp32 acc) at M=N=K=8192; "
+                   f"% of MFMA {tname.upper()} peak"),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -183,10 +195,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": args.dtype,
         "data": "synthetic",
         "config": {"workload": f"gemm {M}x{N}x{K} {args.layout.upper()} alpha=1 beta=1, "
-                               "fp16 A/B/C uniform[-1,1) seed 0, fp32 accumulation, fp16 out",
+                               f"{tname} A/B/C uniform[-1,1) seed 0, fp32 accumulation, "
+                               f"{tname} out",
                    "M": M, "N": N, "K": K, "layout": args.layout.upper(),
                    "kernel": plan.kernel},
         "pct_of_peak": round(100.0 * tflops / PEAK_F16_TFLOPS, 2),
@@ -194,7 +207,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
                      "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_F16_TFLOPS, 4),
-                     "traffic": profiled_traffic(args.layout, (M, N, K))},
+                     "traffic": profiled_traffic(args.layout, (M, N, K), args.dtype)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_rows)

@@ -1,7 +1,8 @@
-"""Python binding of the MI355X fp16 -> fp32-accumulate GEMM library.
+"""Python binding of the MI355X fp16 / bf16 -> fp32-accumulate GEMM library.
 
-Thin ctypes marshalling over the C ABI declared in include/gemm_f16f32.h: the
-functions below carry the same names and arguments as the C entry points, and
+Thin ctypes marshalling over the C ABI declared in include/gemm_f16f32.h and
+include/gemm_bf16f32.h: the functions below carry the same names and
+arguments as the C entry points, and
 every step of the computation runs in the HIP kernels of libmpgemm.so.  There
 is no fallback: if the library is missing, loading raises.  torch is used only
 for device buffers and streams (in `gemm`, the convenience wrapper).
@@ -13,7 +14,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmpgemm.so")
 
 GEMM_ROW_MAJOR, GEMM_COL_MAJOR = 0, 1
-GEMM_OUT_F16, GEMM_OUT_F32 = 0, 1
+GEMM_OUT_F16, GEMM_OUT_F32, GEMM_OUT_BF16 = 0, 1, 2
 GEMM_OK = 0
 GEMM_ERR_INVALID_ARG = -1
 GEMM_ERR_UNSUPPORTED = -2
@@ -21,7 +22,8 @@ GEMM_ERR_HIP = -3
 GEMM_ERR_NOMEM = -4
 
 EXPORTED = ("gemm_f16f32_plan", "gemm_f16f32_run", "gemm_f16f32_destroy",
-            "gemm_f16f32_status_string", "gemm_f16f32_plan_kernel")
+            "gemm_f16f32_status_string", "gemm_f16f32_plan_kernel",
+            "gemm_bf16f32_plan", "gemm_bf16f32_run")
 
 _lib = None
 
@@ -42,13 +44,15 @@ def library() -> ctypes.CDLL:
                 "`python -m mixed_precision_gemm_amd.build` (no fallback exists)")
         lib = ctypes.CDLL(LIB_PATH)
         i64, vp = ctypes.c_int64, ctypes.c_void_p
-        lib.gemm_f16f32_plan.argtypes = [ctypes.POINTER(vp), i64, i64, i64,
-                                         ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                         i64, i64, i64, i64, i64, i64, i64]
-        lib.gemm_f16f32_plan.restype = ctypes.c_int
-        lib.gemm_f16f32_run.argtypes = [vp, vp, vp, vp, ctypes.c_float,
-                                        ctypes.c_float, vp]
-        lib.gemm_f16f32_run.restype = ctypes.c_int
+        for fam in ("f16f32", "bf16f32"):
+            plan_fn = getattr(lib, f"gemm_{fam}_plan")
+            plan_fn.argtypes = [ctypes.POINTER(vp), i64, i64, i64,
+                                ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                i64, i64, i64, i64, i64, i64, i64]
+            plan_fn.restype = ctypes.c_int
+            run_fn = getattr(lib, f"gemm_{fam}_run")
+            run_fn.argtypes = [vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp]
+            run_fn.restype = ctypes.c_int
         lib.gemm_f16f32_destroy.argtypes = [vp]
         lib.gemm_f16f32_destroy.restype = ctypes.c_int
         lib.gemm_f16f32_status_string.argtypes = [ctypes.c_int]
@@ -76,6 +80,22 @@ def gemm_f16f32_run(plan, A, B, C, alpha, beta, stream=None):
     return library().gemm_f16f32_run(plan, A, B, C, alpha, beta, stream)
 
 
+def gemm_bf16f32_plan(M, N, K, layout_a, layout_b, out_type, lda, ldb, ldc,
+                      batch=1, stride_a=0, stride_b=0, stride_c=0):
+    """bfloat16 A and B; out_type GEMM_OUT_BF16 or GEMM_OUT_F32.  Returns
+    (status, plan_handle); the handle is None unless status == 0."""
+    h = ctypes.c_void_p()
+    st = library().gemm_bf16f32_plan(ctypes.byref(h), M, N, K, layout_a, layout_b,
+                                     out_type, lda, ldb, ldc, batch, stride_a,
+                                     stride_b, stride_c)
+    return st, (h.value if st == GEMM_OK else None)
+
+
+def gemm_bf16f32_run(plan, A, B, C, alpha, beta, stream=None):
+    """Runs a plan made by gemm_bf16f32_plan (device addresses as ints)."""
+    return library().gemm_bf16f32_run(plan, A, B, C, alpha, beta, stream)
+
+
 def gemm_f16f32_destroy(plan):
     return library().gemm_f16f32_destroy(plan)
 
@@ -92,18 +112,26 @@ def gemm_f16f32_plan_kernel(plan):
 
 class Plan:
     """Owns a plan handle; `run` launches on a stream (torch's current one by
-    default)."""
+    default).  dtype: "f16" (binary16 A and B, C binary16 or fp32) or
+    "bf16" (bfloat16 A and B; out_type defaults to GEMM_OUT_BF16)."""
 
     def __init__(self, M, N, K, layout_a=GEMM_ROW_MAJOR, layout_b=GEMM_ROW_MAJOR,
-                 out_type=GEMM_OUT_F16, lda=None, ldb=None, ldc=None, batch=1,
-                 stride_a=0, stride_b=0, stride_c=0):
+                 out_type=None, lda=None, ldb=None, ldc=None, batch=1,
+                 stride_a=0, stride_b=0, stride_c=0, dtype="f16"):
+        if dtype not in ("f16", "bf16"):
+            raise ValueError(f"dtype must be 'f16' or 'bf16', not {dtype!r}")
         lda = lda if lda is not None else (K if layout_a == GEMM_ROW_MAJOR else M)
         ldb = ldb if ldb is not None else (N if layout_b == GEMM_ROW_MAJOR else K)
         ldc = ldc if ldc is not None else N
-        st, h = gemm_f16f32_plan(M, N, K, layout_a, layout_b, out_type, lda, ldb,
-                                 ldc, batch, stride_a, stride_b, stride_c)
+        if out_type is None:
+            out_type = GEMM_OUT_BF16 if dtype == "bf16" else GEMM_OUT_F16
+        plan_fn = gemm_bf16f32_plan if dtype == "bf16" else gemm_f16f32_plan
+        st, h = plan_fn(M, N, K, layout_a, layout_b, out_type, lda, ldb,
+                        ldc, batch, stride_a, stride_b, stride_c)
         if st != GEMM_OK:
-            raise GemmError(st, "gemm_f16f32_plan")
+            raise GemmError(st, plan_fn.__name__)
+        self.dtype = dtype
+        self._run = gemm_bf16f32_run if dtype == "bf16" else gemm_f16f32_run
         self.handle = h
         self.shape = (M, N, K)
         self.kernel = gemm_f16f32_plan_kernel(h)
@@ -116,10 +144,9 @@ class Plan:
             stream = torch.cuda.current_stream().cuda_stream
         elif not isinstance(stream, int):
             stream = stream.cuda_stream
-        st = gemm_f16f32_run(self.handle, ptr(A), ptr(B), ptr(C), alpha, beta,
-                             stream)
+        st = self._run(self.handle, ptr(A), ptr(B), ptr(C), alpha, beta, stream)
         if st != GEMM_OK:
-            raise GemmError(st, "gemm_f16f32_run")
+            raise GemmError(st, self._run.__name__)
 
     def close(self):
         if self.handle is not None:
@@ -150,12 +177,14 @@ def _layout_of(t, rows, cols):
 
 
 def gemm(A, B, C=None, alpha=1.0, beta=0.0, out_dtype=None):
-    """C = alpha * A @ B + beta * C for fp16 CUDA tensors A (.., M, K) and
-    B (.., K, N); layouts and leading dimensions come from the strides.
-    Returns C (allocated when None; fp16 unless out_dtype is torch.float32)."""
+    """C = alpha * A @ B + beta * C for float16 (or bfloat16) CUDA tensors A
+    (.., M, K) and B (.., K, N); layouts and leading dimensions come from the
+    strides.  Returns C (allocated when None; the input type unless
+    out_dtype is torch.float32)."""
     import torch
-    if A.dtype != torch.float16 or B.dtype != torch.float16:
-        raise TypeError("A and B must be float16")
+    if A.dtype != B.dtype or A.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("A and B must both be float16 or both bfloat16")
+    dtype = "bf16" if A.dtype == torch.bfloat16 else "f16"
     batched = A.dim() == 3
     M, K = A.shape[-2:]
     K2, N = B.shape[-2:]
@@ -169,10 +198,13 @@ def gemm(A, B, C=None, alpha=1.0, beta=0.0, out_dtype=None):
     if lb is None:
         B = B.contiguous(); lb = _layout_of(B, K, N)
     if C is None:
-        dt = out_dtype or torch.float16
+        dt = out_dtype or A.dtype
         C = torch.empty((batch, M, N) if batched else (M, N), dtype=dt, device=A.device)
         beta = 0.0
-    out_type = GEMM_OUT_F32 if C.dtype == torch.float32 else GEMM_OUT_F16
+    if C.dtype not in (torch.float32, A.dtype):
+        raise TypeError("C must be float32 or the input type")
+    out_type = (GEMM_OUT_F32 if C.dtype == torch.float32 else
+                GEMM_OUT_BF16 if dtype == "bf16" else GEMM_OUT_F16)
     if C.stride(-1) != 1:
         raise ValueError("C must be row-major")
     ldc = max(C.stride(-2), N, 1)
@@ -180,6 +212,6 @@ def gemm(A, B, C=None, alpha=1.0, beta=0.0, out_dtype=None):
     sb = B.stride(0) if batched else 0
     sc = C.stride(0) if batched else 0
     with Plan(M, N, K, la[0], lb[0], out_type, la[1], lb[1], ldc, batch,
-              sa, sb, sc) as p:
+              sa, sb, sc, dtype=dtype) as p:
         p.run(A, B, C, alpha, beta)
     return C

@@ -25,7 +25,7 @@ enum TileId : int {
 };
 
 // Three kernel families share the tile table:
-//   KIND_DIRECT16: a two-slot LDS ring filled by direct-to-LDS buffer loads
+//   KIND_DIRECT16: a two- or four-slot LDS ring filled by direct-to-LDS buffer loads
 //                (no register staging) and computed with 16 x 16 x 32 MFMAs,
 //                for 16-byte-aligned operands; split-K capable;
 //   KIND_STAGED: a two-slot ring filled through registers (global -> VGPR ->
@@ -61,11 +61,15 @@ constexpr int narrow_tile(int t) {
 
 constexpr int kNumCUs = 256;
 
+// Element type of A and B (and of a 16-bit C): IEEE binary16, or bfloat16.
+enum InputType : int { IN_F16 = 0, IN_BF16 = 1 };
+
 }  // namespace mpgemm
 
 struct gemm_f16f32_plan_s {
     int64_t M, N, K;
     int layout_a, layout_b, out_type;
+    int in_type;           // mpgemm::InputType of A and B (and of a 16-bit C)
     int64_t lda, ldb, ldc;
     int64_t batch, stride_a, stride_b, stride_c;
     int tile;              // mpgemm::TileId for 16-byte-aligned operands

@@ -1,5 +1,5 @@
-// fp16 x fp16 -> fp32-accumulate GEMM kernels for gfx950 (MI355X), and the
-// C-ABI entry point that launches them.
+// fp16 x fp16 (or bf16 x bf16) -> fp32-accumulate GEMM kernels for gfx950
+// (MI355X), and the C-ABI entry points that launch them.
 //
 // Pages cited (titles as printed):
 //   [GEMM]    "手写GEMM内核：矩阵乘法性能优化的完整工程实践" (hand-written GEMM kernel)
@@ -31,12 +31,18 @@
 //     products, fp32 sums ([GEMM] §2.3, §6.2);
 //   * the epilogue forms alpha*acc + beta*C in fp32, rounds once to fp16 (RNE)
 //     or stores fp32, and masks the tile edges ([CATLASS] §2.1, [OPS] §3.2).
+// Every kernel is a template on the input type TI: _Float16, or __bf16 for
+// bfloat16 A and B ([CATLASS] §3.2, [GEMM] §6: the wide-range 16-bit format).
+// Loads, LDS layouts and fragment reads move 16-bit elements and do not
+// depend on TI; only the MFMA (the _bf16 forms of the same shapes) and the
+// 16-bit C of the epilogue (bfloat16 C, rounded to nearest even) change.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <algorithm>
 #include <type_traits>
 
+#include "gemm_bf16f32.h"
 #include "gemm_f16f32.h"
 #include "gemm_internal.h"
 
@@ -46,6 +52,8 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -57,8 +65,8 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 constexpr int kRsrcWord3 = 0x00020000;
 
 struct GemmArgs {
-    const _Float16 *A;
-    const _Float16 *B;
+    const uint16_t *A;            // 16-bit elements of the kernel's input type
+    const uint16_t *B;
     void *C;
     int64_t M, N, K;
     int64_t lda, ldb, ldc;
@@ -95,6 +103,32 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t byt
     const int32_t n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int32_t)bytes);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, kRsrcWord3);
 }
+
+// The MFMAs of input type TI on fragments of 8 16-bit values per lane (held
+// in half8 registers whatever TI is), fp32 accumulation.
+template <typename TI>
+__device__ inline floatx4 mfma16(half8 a, half8 b, floatx4 c) {
+    if constexpr (std::is_same<TI, __bf16>::value)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+template <typename TI>
+__device__ inline floatx16 mfma32(half8 a, half8 b, floatx16 c) {
+    if constexpr (std::is_same<TI, __bf16>::value)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Four consecutive C elements of type T (fp32, fp16 or bf16) as one vector.
+template <typename T> struct C4 { using type = half4; };
+template <> struct C4<float> { using type = floatx4; };
+template <> struct C4<__bf16> { using type = bf16x4; };
+template <typename T>
+using c4_t = typename C4<T>::type;
 
 // XOR swizzle of the 16-byte vector index within an LDS row of VPR vectors,
 // chosen so that the ds_read_b128 fragment reads (32 consecutive rows at one
@@ -184,7 +218,7 @@ struct TileLoader {
 
     // Issues the global loads of the K step whose first K index is k0.
     // base points at element (r0, k0) of the operand.
-    __device__ void load(const _Float16 *base, int64_t bytes_left, int64_t k0,
+    __device__ void load(const uint16_t *base, int64_t bytes_left, int64_t k0,
                          int64_t K, int64_t ld) {
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, bytes_left);
 #pragma unroll
@@ -273,7 +307,7 @@ __device__ inline void tile_coords(const GemmArgs &p, int wg, int &b, int &tm, i
 // masked at the M and N edges.  Accumulator register r of lane l in block
 // (i, j) holds C(m, n) with m = l % 32 and n = 8*(r/4) + 4*(l/32) + r%4
 // (block-local), so each lane owns runs of 4 consecutive n of one row.
-template <int FM, int FN, int WTM, int WTN>
+template <typename T16, int FM, int FN, int WTM, int WTN>
 __device__ inline void store_tile(const GemmArgs &p, const floatx16 (&acc)[FM][FN],
                                   int b, int64_t m0, int64_t n0, int wm, int wn,
                                   int lane) {
@@ -311,20 +345,20 @@ __device__ inline void store_tile(const GemmArgs &p, const floatx16 (&acc)[FM][F
                         }
                     }
                 } else {
-                    _Float16 *C = (_Float16 *)p.C + off;
+                    T16 *C = (T16 *)p.C + off;
                     if (full) {
                         if (beta != 0.0f) {
-                            const half4 c = *(const half4 *)C;
+                            const c4_t<T16> c = *(const c4_t<T16> *)C;
 #pragma unroll
                             for (int e = 0; e < 4; ++e) v[e] += beta * (float)c[e];
                         }
-                        half4 o = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-                        *(half4 *)C = o;
+                        c4_t<T16> o = {(T16)v[0], (T16)v[1], (T16)v[2], (T16)v[3]};
+                        *(c4_t<T16> *)C = o;
                     } else {
                         for (int e = 0; e < 4 && n + e < p.N; ++e) {
                             float o = v[e];
                             if (beta != 0.0f) o += beta * (float)C[e];
-                            C[e] = (_Float16)o;
+                            C[e] = (T16)o;
                         }
                     }
                 }
@@ -333,7 +367,7 @@ __device__ inline void store_tile(const GemmArgs &p, const floatx16 (&acc)[FM][F
     }
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, bool AK, bool BKC, bool VEC>
+template <typename TI, int BM, int BN, int BK, int WGM, int WGN, bool AK, bool BKC, bool VEC>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_staged(GemmArgs p) {
     constexpr int NT = 64 * WGM * WGN;
     constexpr int VPR = BK / 8;
@@ -354,8 +388,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_staged(GemmArgs p) {
     tile_coords(p, blockIdx.x, b, tm, tn);
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
-    const _Float16 *Ab = p.A + b * p.sa;
-    const _Float16 *Bb = p.B + b * p.sb;
+    const uint16_t *Ab = p.A + b * p.sa;
+    const uint16_t *Bb = p.B + b * p.sb;
     // Per-tile bases and K-step strides (elements) of each operand.
     const int64_t a_tile = AK ? m0 * p.lda : m0;
     const int64_t a_kstep = AK ? BK : BK * p.lda;
@@ -419,7 +453,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_staged(GemmArgs p) {
                     // src0 = B fragment (rows n), src1 = A fragment (columns m):
                     // the block accumulates C^T, so each lane ends up holding
                     // runs of 4 consecutive n of one row m of C.
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
+                    acc[i][j] = mfma32<TI>(bf[j], af[i], acc[i][j]);
         }
 
         if (more) {
@@ -430,7 +464,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_staged(GemmArgs p) {
         __syncthreads();
     }
 
-    store_tile<FM, FN, WTM, WTN>(p, acc, b, m0, n0, wm, wn, lane);
+    store_tile<TI, FM, FN, WTM, WTN>(p, acc, b, m0, n0, wm, wn, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -518,9 +552,6 @@ __device__ inline void barrier() { asm volatile("s_barrier" : : : "memory"); }
 // access where the row and alignment allow it (vec), element by element (up
 // to N, zeros beyond) otherwise.
 template <typename T>
-using c4_t = typename std::conditional<sizeof(T) == 4, floatx4, half4>::type;
-
-template <typename T>
 __device__ inline c4_t<T> load_c4(const GemmArgs &p, int64_t off, int64_t n, bool vec) {
     const T *C = (const T *)p.C + off;
     if (vec) return *(const c4_t<T> *)C;
@@ -541,8 +572,7 @@ __device__ inline void store_c4(const GemmArgs &p, int64_t off, int64_t n, bool 
         if constexpr (sizeof(T) == 4)
             __builtin_nontemporal_store(v, (floatx4 *)C);
         else
-            __builtin_nontemporal_store(half4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]},
-                                        (half4 *)C);
+            __builtin_nontemporal_store(c4_t<T>{(T)v[0], (T)v[1], (T)v[2], (T)v[3]}, (c4_t<T> *)C);
         return;
     }
     for (int e = 0; e < 4 && n + e < p.N; ++e) C[e] = (T)v[e];
@@ -803,7 +833,7 @@ struct DirectOperand {
         const int64_t left64 = K - k0;
         return __builtin_amdgcn_readfirstlane(left64 <= 0 ? 0 : (left64 >= BK ? BK : (int)left64));
     }
-    __device__ sgpr4 stage_rsrc(const _Float16 *base, int64_t bytes_left) const {
+    __device__ sgpr4 stage_rsrc(const uint16_t *base, int64_t bytes_left) const {
         return make_rsrc_words(base, bytes_left);
     }
     // For K-contiguous 128-byte rows the K index of load i depends on i only
@@ -836,7 +866,7 @@ struct DirectOperand {
     // Issues this wave's share of one stage.  base: element (r0, k0) of the
     // operand; lds: the operand's region of the ring slot.  Stages at or
     // beyond the end of K fail every range check and write zeros.
-    __device__ void issue(const _Float16 *base, int64_t bytes_left, uint32_t lds_addr,
+    __device__ void issue(const uint16_t *base, int64_t bytes_left, uint32_t lds_addr,
                           int wave, int64_t k0, int64_t K) {
         const sgpr4 rs = make_rsrc_words(base, bytes_left);
         const int left = stage_left(k0, K);
@@ -964,7 +994,7 @@ struct Frag16 {
 // lane (stages past the end of K fail the range check and write zeros), so
 // the wait counts are exact.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int WGM, int WGN, int S, bool AK, bool BKC, bool KFULL>
+template <typename TI, int BM, int BN, int BK, int WGM, int WGN, int S, bool AK, bool BKC, bool KFULL>
 __global__ __launch_bounds__(64 * WGM * WGN)
 __attribute__((amdgpu_waves_per_eu(BM * BN >= 65536 ? 1 : 2, BM * BN >= 65536 ? 1 : 2)))
 void gemm_direct16(GemmArgs pin) {
@@ -1013,8 +1043,8 @@ void gemm_direct16(GemmArgs pin) {
     int b, tm, tn;
     tile_coords(p, tile, b, tm, tn);
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-    const _Float16 *Ab = p.A + b * p.sa;
-    const _Float16 *Bb = p.B + b * p.sb;
+    const uint16_t *Ab = p.A + b * p.sa;
+    const uint16_t *Bb = p.B + b * p.sb;
     const int64_t a_tile = AK ? m0 * p.lda : m0;
     const int64_t a_kstep = AK ? BK : BK * p.lda;
     const int64_t b_tile = BKC ? n0 * p.ldb : n0;
@@ -1092,7 +1122,7 @@ void gemm_direct16(GemmArgs pin) {
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             const int i = q / FN, j = q % FN;
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[CUR][j], fa[CUR][i], acc[i][j], 0, 0, 0);
+            acc[i][j] = mfma16<TI>(fb[CUR][j], fa[CUR][i], acc[i][j]);
 #pragma unroll
             for (int l = q * nl / NQ; l < (q + 1) * nl / NQ; ++l) {
                 if (l < na) {
@@ -1178,7 +1208,7 @@ void gemm_direct16(GemmArgs pin) {
             if (p.out_f32)
                 store_tile_splitk<float, BM, BN, WGM, WGN, S * SLOT * 16, 16>(p, acc, lds, tile, slice, b, m0, n0, wave, lane);
             else
-                store_tile_splitk<_Float16, BM, BN, WGM, WGN, S * SLOT * 16, 16>(p, acc, lds, tile, slice, b, m0, n0, wave, lane);
+                store_tile_splitk<TI, BM, BN, WGM, WGN, S * SLOT * 16, 16>(p, acc, lds, tile, slice, b, m0, n0, wave, lane);
             return;
         }
     }
@@ -1190,9 +1220,9 @@ void gemm_direct16(GemmArgs pin) {
             store_tile_lds<float, false, BM, BN, WGM, WGN, S * SLOT * 16, 16>(p, acc, lds, b, m0, n0, wave, lane);
     } else {
         if (full)
-            store_tile_lds<_Float16, true, BM, BN, WGM, WGN, S * SLOT * 16, 16>(p, acc, lds, b, m0, n0, wave, lane);
+            store_tile_lds<TI, true, BM, BN, WGM, WGN, S * SLOT * 16, 16>(p, acc, lds, b, m0, n0, wave, lane);
         else
-            store_tile_lds<_Float16, false, BM, BN, WGM, WGN, S * SLOT * 16, 16>(p, acc, lds, b, m0, n0, wave, lane);
+            store_tile_lds<TI, false, BM, BN, WGM, WGN, S * SLOT * 16, 16>(p, acc, lds, b, m0, n0, wave, lane);
     }
 }
 
@@ -1215,7 +1245,7 @@ void gemm_direct16(GemmArgs pin) {
 // ---------------------------------------------------------------------------
 typedef float floatx4v __attribute__((ext_vector_type(4)));
 
-template <int MB, int NB>
+template <typename TI, int MB, int NB>
 __global__ __launch_bounds__(512) void gemm_stream(GemmArgs p) {
     constexpr int NW = 8;
     constexpr int UNROLL = 4;   // K steps whose loads are issued together (8: 1-3% slower)
@@ -1229,8 +1259,8 @@ __global__ __launch_bounds__(512) void gemm_stream(GemmArgs p) {
     int b, tm, tn;
     tile_coords(p, blockIdx.x, b, tm, tn);
     const int64_t m0 = (int64_t)tm * (MB * 16), n0 = (int64_t)tn * (NB * 16);
-    const _Float16 *Ab = p.A + b * p.sa;
-    const _Float16 *Bb = p.B + b * p.sb;
+    const uint16_t *Ab = p.A + b * p.sa;
+    const uint16_t *Bb = p.B + b * p.sb;
 
     // K range of this wave, in steps of 32.
     const int64_t steps = (p.K + 31) / 32;
@@ -1287,7 +1317,7 @@ __global__ __launch_bounds__(512) void gemm_stream(GemmArgs p) {
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[u][mb], fb[u][nb], acc[mb][nb], 0, 0, 0);
+                    acc[mb][nb] = mfma16<TI>(fa[u][mb], fb[u][nb], acc[mb][nb]);
     }
 
     // Accumulator register r of lane l holds row 4*(l/16) + r, column l % 16
@@ -1316,9 +1346,9 @@ __global__ __launch_bounds__(512) void gemm_stream(GemmArgs p) {
             if (beta != 0.0f) v += beta * *C;
             *C = v;
         } else {
-            _Float16 *C = (_Float16 *)p.C + off;
+            TI *C = (TI *)p.C + off;
             if (beta != 0.0f) v += beta * (float)*C;
-            *C = (_Float16)v;
+            *C = (TI)v;
         }
     }
 }
@@ -1336,8 +1366,8 @@ __global__ __launch_bounds__(512) void gemm_stream(GemmArgs p) {
 // is read once and written once.
 // ---------------------------------------------------------------------------
 struct PackOperand {
-    const _Float16 *src;
-    _Float16 *dst;
+    const uint16_t *src;
+    uint16_t *dst;
     int64_t ld, stride, outer, cols, ld8;
     uint32_t chunks;   // batch * outer * ld8 / 8
 };
@@ -1393,74 +1423,82 @@ __global__ __launch_bounds__(256) void gemm_pack16(PackArgs a) {
 
 typedef void (*KernelFn)(GemmArgs);
 
-template <int T, bool AK, bool BKC, bool VEC>
+template <typename TI, int T, bool AK, bool BKC, bool VEC>
 constexpr KernelFn pick_staged() {
-    return gemm_staged<kTiles[T].bm, kTiles[T].bn, kTiles[T].bk, kTiles[T].wgm,
+    return gemm_staged<TI, kTiles[T].bm, kTiles[T].bn, kTiles[T].bk, kTiles[T].wgm,
                        kTiles[T].wgn, AK, BKC, VEC>;
 }
 
-template <int T, bool AK, bool BKC, bool KFULL = false>
+template <typename TI, int T, bool AK, bool BKC, bool KFULL = false>
 constexpr KernelFn pick_direct16() {
-    return gemm_direct16<kTiles[T].bm, kTiles[T].bn, kTiles[T].bk, kTiles[T].wgm,
+    return gemm_direct16<TI, kTiles[T].bm, kTiles[T].bn, kTiles[T].bk, kTiles[T].wgm,
                          kTiles[T].wgn, kTiles[T].stages, AK, BKC, KFULL>;
 }
 
-// Kernel table indexed [tile][A K-contiguous][B K-contiguous][vec].  Direct
-// tiles have only the vec entry; staged tiles have both.
-template <int T>
+// Kernel table indexed [input type][tile][A K-contiguous][B K-contiguous][vec].
+// Direct tiles have only the vec entry; staged tiles have both.
+template <typename TI, int T>
 void fill_tile(KernelFn (&t)[2][2][2]) {
     if constexpr (kTiles[T].kind == KIND_DIRECT16) {
-        t[0][0][1] = pick_direct16<T, false, false>();
-        t[0][1][1] = pick_direct16<T, false, true>();
-        t[1][0][1] = pick_direct16<T, true, false>();
-        t[1][1][1] = pick_direct16<T, true, true>();
+        t[0][0][1] = pick_direct16<TI, T, false, false>();
+        t[0][1][1] = pick_direct16<TI, T, false, true>();
+        t[1][0][1] = pick_direct16<TI, T, true, false>();
+        t[1][1][1] = pick_direct16<TI, T, true, true>();
         t[0][0][0] = t[0][1][0] = t[1][0][0] = t[1][1][0] = nullptr;
     } else {
-        t[0][0][0] = pick_staged<T, false, false, false>();
-        t[0][0][1] = pick_staged<T, false, false, true>();
-        t[0][1][0] = pick_staged<T, false, true, false>();
-        t[0][1][1] = pick_staged<T, false, true, true>();
-        t[1][0][0] = pick_staged<T, true, false, false>();
-        t[1][0][1] = pick_staged<T, true, false, true>();
-        t[1][1][0] = pick_staged<T, true, true, false>();
-        t[1][1][1] = pick_staged<T, true, true, true>();
+        t[0][0][0] = pick_staged<TI, T, false, false, false>();
+        t[0][0][1] = pick_staged<TI, T, false, false, true>();
+        t[0][1][0] = pick_staged<TI, T, false, true, false>();
+        t[0][1][1] = pick_staged<TI, T, false, true, true>();
+        t[1][0][0] = pick_staged<TI, T, true, false, false>();
+        t[1][0][1] = pick_staged<TI, T, true, false, true>();
+        t[1][1][0] = pick_staged<TI, T, true, true, false>();
+        t[1][1][1] = pick_staged<TI, T, true, true, true>();
     }
 }
 
-template <int T>
+template <typename TI, int T>
 void fill_kfull(KernelFn (&t)[2][2]) {
     static_assert(kTiles[T].kind == KIND_DIRECT16, "K-full variants are direct16");
-    t[0][0] = pick_direct16<T, false, false, true>();
-    t[0][1] = pick_direct16<T, false, true, true>();
-    t[1][0] = pick_direct16<T, true, false, true>();
-    t[1][1] = pick_direct16<T, true, true, true>();
+    t[0][0] = pick_direct16<TI, T, false, false, true>();
+    t[0][1] = pick_direct16<TI, T, false, true, true>();
+    t[1][0] = pick_direct16<TI, T, true, false, true>();
+    t[1][1] = pick_direct16<TI, T, true, true, true>();
 }
 
-template <int T>
+template <typename TI, int T>
 void fill_stream(KernelFn (&t)[2][2][2]) {
     // Only the K-contiguous A and B (row-major A, column-major B) 128-bit form.
     t[0][0][0] = t[0][0][1] = t[0][1][0] = t[0][1][1] = nullptr;
     t[1][0][0] = t[1][0][1] = t[1][1][0] = nullptr;
-    t[1][1][1] = gemm_stream<kTiles[T].bm / 16, kTiles[T].bn / 16>;
+    t[1][1][1] = gemm_stream<TI, kTiles[T].bm / 16, kTiles[T].bn / 16>;
+}
+
+template <typename TI>
+void fill_type(KernelFn (&k)[NUM_TILES][2][2][2], KernelFn (&kfull)[NUM_TILES][2][2]) {
+    for (auto &t : kfull)
+        t[0][0] = t[0][1] = t[1][0] = t[1][1] = nullptr;
+    fill_kfull<TI, TILE_256x256>(kfull[TILE_256x256]);
+    fill_kfull<TI, TILE_128x128>(kfull[TILE_128x128]);
+    fill_kfull<TI, TILE_128x128_D4>(kfull[TILE_128x128_D4]);
+    fill_tile<TI, TILE_256x256>(k[TILE_256x256]);
+    fill_tile<TI, TILE_128x128>(k[TILE_128x128]);
+    fill_tile<TI, TILE_128x128_D4>(k[TILE_128x128_D4]);
+    fill_tile<TI, TILE_64x64>(k[TILE_64x64]);
+    fill_tile<TI, TILE_32x64>(k[TILE_32x64]);
+    fill_tile<TI, TILE_128x128_STAGED>(k[TILE_128x128_STAGED]);
+    fill_stream<TI, TILE_STREAM16>(k[TILE_STREAM16]);
+    fill_stream<TI, TILE_STREAM32>(k[TILE_STREAM32]);
+    fill_stream<TI, TILE_STREAM64>(k[TILE_STREAM64]);
+    fill_stream<TI, TILE_STREAM32W>(k[TILE_STREAM32W]);
 }
 
 struct KernelTable {
-    KernelFn k[NUM_TILES][2][2][2];
-    KernelFn kfull[NUM_TILES][2][2];   // direct tiles with K a multiple of BK (else null)
+    KernelFn k[2][NUM_TILES][2][2][2];
+    KernelFn kfull[2][NUM_TILES][2][2];   // direct tiles with K a multiple of BK (else null)
     KernelTable() {
-        fill_kfull<TILE_256x256>(kfull[TILE_256x256]);
-        fill_kfull<TILE_128x128>(kfull[TILE_128x128]);
-        fill_kfull<TILE_128x128_D4>(kfull[TILE_128x128_D4]);
-        fill_tile<TILE_256x256>(k[TILE_256x256]);
-        fill_tile<TILE_128x128>(k[TILE_128x128]);
-        fill_tile<TILE_128x128_D4>(k[TILE_128x128_D4]);
-        fill_tile<TILE_64x64>(k[TILE_64x64]);
-        fill_tile<TILE_32x64>(k[TILE_32x64]);
-        fill_tile<TILE_128x128_STAGED>(k[TILE_128x128_STAGED]);
-        fill_stream<TILE_STREAM16>(k[TILE_STREAM16]);
-        fill_stream<TILE_STREAM32>(k[TILE_STREAM32]);
-        fill_stream<TILE_STREAM64>(k[TILE_STREAM64]);
-        fill_stream<TILE_STREAM32W>(k[TILE_STREAM32W]);
+        fill_type<_Float16>(k[IN_F16], kfull[IN_F16]);
+        fill_type<__bf16>(k[IN_BF16], kfull[IN_BF16]);
     }
 };
 
@@ -1484,12 +1522,10 @@ bool packable(const gemm_f16f32_plan_s &p) {
     return p.batch * (outer_a * (p.ld8_a / 8) + outer_b * (p.ld8_b / 8)) < (int64_t(1) << 31);
 }
 
-}  // namespace
-
-extern "C" int gemm_f16f32_run(gemm_f16f32_plan_t plan, const void *A,
-                               const void *B, void *C, float alpha, float beta,
-                               void *stream) {
-    if (!plan) return GEMM_ERR_INVALID_ARG;
+// One run of a plan of either input type (the entry points below check the
+// type against the one they serve).
+int run_plan(gemm_f16f32_plan_t plan, const void *A, const void *B, void *C, float alpha,
+             float beta, void *stream) {
     const gemm_f16f32_plan_s &p = *plan;
     if (p.M == 0 || p.N == 0) return GEMM_OK;
     if (!C) return GEMM_ERR_INVALID_ARG;
@@ -1516,8 +1552,8 @@ extern "C" int gemm_f16f32_run(gemm_f16f32_plan_t plan, const void *A,
     const int64_t tiles_n = (p.N + ts.bn - 1) / ts.bn;
 
     GemmArgs a;
-    a.A = (const _Float16 *)A;
-    a.B = (const _Float16 *)B;
+    a.A = (const uint16_t *)A;
+    a.B = (const uint16_t *)B;
     a.C = C;
     a.M = p.M; a.N = p.N; a.K = p.K;
     a.lda = p.lda; a.ldb = p.ldb; a.ldc = p.ldc;
@@ -1576,9 +1612,9 @@ extern "C" int gemm_f16f32_run(gemm_f16f32_plan_t plan, const void *A,
             plan->pack_device = dev;
         }
         auto operand = [&](const void *src, int layout, int64_t rows_rm, int64_t cols_rm,
-                           int64_t ld, int64_t stride, int64_t ld8, _Float16 *dst) {
+                           int64_t ld, int64_t stride, int64_t ld8, uint16_t *dst) {
             PackOperand o;
-            o.src = (const _Float16 *)src;
+            o.src = (const uint16_t *)src;
             o.dst = dst;
             o.ld = ld;
             o.stride = stride;
@@ -1590,8 +1626,8 @@ extern "C" int gemm_f16f32_run(gemm_f16f32_plan_t plan, const void *A,
         };
         PackArgs pa = {};
         int nops = 0;
-        _Float16 *pa_dst = (_Float16 *)plan->pack_ws;
-        _Float16 *pb_dst = (_Float16 *)((char *)plan->pack_ws + p.pack_off_b);
+        uint16_t *pa_dst = (uint16_t *)plan->pack_ws;
+        uint16_t *pb_dst = (uint16_t *)((char *)plan->pack_ws + p.pack_off_b);
         if (pack_a) {
             pa.op[nops++] = operand(A, p.layout_a, p.M, p.K, p.lda, p.stride_a, p.ld8_a, pa_dst);
             const int64_t outer = p.layout_a == GEMM_ROW_MAJOR ? p.M : p.K;
@@ -1618,10 +1654,11 @@ extern "C" int gemm_f16f32_run(gemm_f16f32_plan_t plan, const void *A,
 
     const int ak = p.layout_a == GEMM_ROW_MAJOR;   // A K-contiguous
     const int bkc = p.layout_b == GEMM_COL_MAJOR;  // B K-contiguous
-    KernelFn fn = kernels().k[tile][ak][bkc][vec ? 1 : 0];
+    const int ti = p.in_type == IN_BF16 ? IN_BF16 : IN_F16;
+    KernelFn fn = kernels().k[ti][tile][ak][bkc][vec ? 1 : 0];
     // K-full variants: every stage inside K (for split-K, every slice: kchunk
     // is a multiple of BK, so K must be too).
-    if (ts.kind == KIND_DIRECT16 && p.K % ts.bk == 0) fn = kernels().kfull[tile][ak][bkc];
+    if (ts.kind == KIND_DIRECT16 && p.K % ts.bk == 0) fn = kernels().kfull[ti][tile][ak][bkc];
     if (!fn) return GEMM_ERR_UNSUPPORTED;
     void *args[] = {&a};
     const unsigned threads = ts.kind == KIND_STREAM ? 512u : (unsigned)(64 * ts.wgm * ts.wgn);
@@ -1629,4 +1666,20 @@ extern "C" int gemm_f16f32_run(gemm_f16f32_plan_t plan, const void *A,
                                    dim3(threads), args, 0,
                                    (hipStream_t)stream);
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int gemm_f16f32_run(gemm_f16f32_plan_t plan, const void *A,
+                               const void *B, void *C, float alpha, float beta,
+                               void *stream) {
+    if (!plan || plan->in_type != IN_F16) return GEMM_ERR_INVALID_ARG;
+    return run_plan(plan, A, B, C, alpha, beta, stream);
+}
+
+extern "C" int gemm_bf16f32_run(gemm_f16f32_plan_t plan, const void *A,
+                                const void *B, void *C, float alpha, float beta,
+                                void *stream) {
+    if (!plan || plan->in_type != IN_BF16) return GEMM_ERR_INVALID_ARG;
+    return run_plan(plan, A, B, C, alpha, beta, stream);
 }

@@ -1,4 +1,4 @@
-// Host-side planner of the fp16 -> fp32-accumulate GEMM: argument validation,
+// Host-side planner of the fp16 (or bf16) -> fp32-accumulate GEMM: argument validation,
 // tile, K-split and repacking choice, and grid shape.  Planning makes no HIP
 // call, so it runs (and is tested) on machines without a GPU; destroy frees
 // the device buffers a plan's runs allocated.
@@ -15,6 +15,7 @@
 #include <hip/hip_runtime.h>
 #include <new>
 
+#include "gemm_bf16f32.h"
 #include "gemm_f16f32.h"
 #include "gemm_internal.h"
 
@@ -93,13 +94,13 @@ void choose_ksplit(gemm_f16f32_plan_s *p, int64_t tiles) {
     p->ws_bytes = (int64_t)p->ksplit * tiles * 128 * 128 * 4 + tiles * 4;
 }
 
-}  // namespace
-
-extern "C" int gemm_f16f32_plan(gemm_f16f32_plan_t *out, int64_t M, int64_t N,
-                                int64_t K, int layout_a, int layout_b,
-                                int out_type, int64_t lda, int64_t ldb,
-                                int64_t ldc, int64_t batch, int64_t stride_a,
-                                int64_t stride_b, int64_t stride_c) {
+// A plan for A and B of input type in_type (IN_F16 or IN_BF16).  The tile,
+// split and repacking rules do not depend on the type: both run the same
+// kernels, only the MFMA and the 16-bit C conversion differ.
+int make_plan(int in_type, gemm_f16f32_plan_t *out, int64_t M, int64_t N, int64_t K,
+              int layout_a, int layout_b, int out_type, int64_t lda, int64_t ldb,
+              int64_t ldc, int64_t batch, int64_t stride_a, int64_t stride_b,
+              int64_t stride_c) {
     if (!out) return GEMM_ERR_INVALID_ARG;
     *out = nullptr;
     if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_ARG;
@@ -107,7 +108,9 @@ extern "C" int gemm_f16f32_plan(gemm_f16f32_plan_t *out, int64_t M, int64_t N,
         return GEMM_ERR_INVALID_ARG;
     if (layout_b != GEMM_ROW_MAJOR && layout_b != GEMM_COL_MAJOR)
         return GEMM_ERR_INVALID_ARG;
-    if (out_type != GEMM_OUT_F16 && out_type != GEMM_OUT_F32)
+    // C is fp32 or the 16-bit type of the inputs.
+    const int out16 = in_type == IN_BF16 ? GEMM_OUT_BF16 : GEMM_OUT_F16;
+    if (out_type != out16 && out_type != GEMM_OUT_F32)
         return GEMM_ERR_INVALID_ARG;
     if (batch < 1) return GEMM_ERR_INVALID_ARG;
     const int64_t min_lda = layout_a == GEMM_ROW_MAJOR ? K : M;
@@ -133,6 +136,7 @@ extern "C" int gemm_f16f32_plan(gemm_f16f32_plan_t *out, int64_t M, int64_t N,
     if (!p) return GEMM_ERR_NOMEM;
     p->M = M; p->N = N; p->K = K;
     p->layout_a = layout_a; p->layout_b = layout_b; p->out_type = out_type;
+    p->in_type = in_type;
     p->lda = lda; p->ldb = ldb; p->ldc = ldc;
     p->batch = batch;
     p->stride_a = stride_a; p->stride_b = stride_b; p->stride_c = stride_c;
@@ -206,13 +210,33 @@ extern "C" int gemm_f16f32_plan(gemm_f16f32_plan_t *out, int64_t M, int64_t N,
     char split[16] = "";
     if (p->ksplit > 1) snprintf(split, sizeof split, "_sk%d", p->ksplit);
     static const char *const kPackSuffix[4] = {"", "_pka", "_pkb", "_pkab"};
-    snprintf(p->kernel_name, sizeof p->kernel_name, "gemm_%s_%c%c_%s%s%s",
-             kTiles[t].name, layout_a == GEMM_ROW_MAJOR ? 'n' : 't',
+    snprintf(p->kernel_name, sizeof p->kernel_name, "gemm_%s%s_%c%c_%s%s%s",
+             in_type == IN_BF16 ? "bf16_" : "", kTiles[t].name, layout_a == GEMM_ROW_MAJOR ? 'n' : 't',
              layout_b == GEMM_ROW_MAJOR ? 'n' : 't',
              p->vec_ok ? (kTiles[t].kind == KIND_STAGED ? "vec16" : "direct")
                        : "narrow", split, kPackSuffix[p->pack]);
     *out = p;
     return GEMM_OK;
+}
+
+}  // namespace
+
+extern "C" int gemm_f16f32_plan(gemm_f16f32_plan_t *out, int64_t M, int64_t N,
+                                int64_t K, int layout_a, int layout_b,
+                                int out_type, int64_t lda, int64_t ldb,
+                                int64_t ldc, int64_t batch, int64_t stride_a,
+                                int64_t stride_b, int64_t stride_c) {
+    return make_plan(IN_F16, out, M, N, K, layout_a, layout_b, out_type, lda, ldb, ldc,
+                     batch, stride_a, stride_b, stride_c);
+}
+
+extern "C" int gemm_bf16f32_plan(gemm_f16f32_plan_t *out, int64_t M, int64_t N,
+                                 int64_t K, int layout_a, int layout_b,
+                                 int out_type, int64_t lda, int64_t ldb,
+                                 int64_t ldc, int64_t batch, int64_t stride_a,
+                                 int64_t stride_b, int64_t stride_c) {
+    return make_plan(IN_BF16, out, M, N, K, layout_a, layout_b, out_type, lda, ldb, ldc,
+                     batch, stride_a, stride_b, stride_c);
 }
 
 namespace {

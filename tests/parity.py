@@ -2,7 +2,7 @@
 compute the oracle on the same inputs, and apply the acceptance bound.
 
 Acceptance bound (per output element, both operands finite):
-    |gpu - ref| <= 2e-3 * S + (fp16 C ? ulp16(|ref|) : 0)
+    |gpu - ref| <= 2e-3 * S + (fp16 C ? ulp16(|ref|) : bf16 C ? ulpbf16(|ref|) : 0)
 where ref is the oracle's fp64 value and S = |alpha| sum_k |a_ik b_kj| +
 |beta| |c_ij| its error scale.  fp32 accumulation over K <= 8192 terms errs by
 at most K * 2^-24 * S <= 4.9e-4 * S in any order, the fp32 epilogue by
@@ -11,6 +11,12 @@ bound holds for any correct summation order.  ulp16(x) = 2^(max(floor(log2
 x), -14) - 10), ulp16(0) = 2^-24.  A reference whose magnitude reaches 65520
 rounds to infinity in binary16: the GPU must then return infinity of the same
 sign (or, within the bound, the largest finite value).
+
+bfloat16 inputs: a product of two bfloat16 values (8 significant bits each)
+is exact in fp32 just as a binary16 product is, so the same 2e-3 * S covers
+the fp32 sum; a bfloat16 C adds half a bfloat16 ulp, ulpbf16(x) =
+2^(max(floor(log2 x), -126) - 7), ulpbf16(0) = 2^-133, and overflows only
+from (2 - 2^-8) 2^127 on.
 """
 import os
 
@@ -23,6 +29,7 @@ import oracle
 
 REL_TOL = 2e-3
 F16_OVERFLOW = 65520.0
+BF16_OVERFLOW = (2 - 2.0 ** -8) * 2.0 ** 127
 
 
 def oracle_threads():
@@ -37,6 +44,14 @@ def ulp16(x):
     return np.where(x > 0, u, 2.0 ** -24)
 
 
+def ulpbf16(x):
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.where(x > 0, x, 1.0)))
+    e = np.maximum(e, -126)
+    u = np.exp2(e - 7)
+    return np.where(x > 0, u, 2.0 ** -133)
+
+
 def check_bound(gpu, ref, scale, out_type, what=""):
     """Asserts the acceptance bound element-wise; returns the worst ratio
     |gpu - ref| / bound over finite references."""
@@ -45,13 +60,16 @@ def check_bound(gpu, ref, scale, out_type, what=""):
     bound = REL_TOL * scale
     if out_type == gi.OUT_F16:
         bound = bound + ulp16(ref)
+    elif out_type == gi.OUT_BF16:
+        bound = bound + ulpbf16(ref)
     with np.errstate(invalid="ignore"):
         err = np.abs(gpu - ref)
     ok = err <= bound
     inf_gpu = np.isinf(gpu)
     # infinity accepted where the reference (plus the bound) reaches overflow
-    if out_type == gi.OUT_F16:
-        reach = np.abs(ref) + REL_TOL * scale >= F16_OVERFLOW
+    if out_type in (gi.OUT_F16, gi.OUT_BF16):
+        top = F16_OVERFLOW if out_type == gi.OUT_F16 else BF16_OVERFLOW
+        reach = np.abs(ref) + REL_TOL * scale >= top
         ok |= inf_gpu & reach & (np.sign(gpu) == np.sign(ref))
     bad = ~ok
     if bad.any():
@@ -74,13 +92,17 @@ def run_case(case, dA=None, dB=None, dC=None, stream=None, alpha=None, beta=None
         dA, dB, dC = to_device(case)
     p = mpg.Plan(case.M, case.N, case.K, case.layout_a, case.layout_b,
                  case.out_type, case.lda, case.ldb, case.ldc, case.batch,
-                 case.stride_a, case.stride_b, case.stride_c)
+                 case.stride_a, case.stride_b, case.stride_c, dtype=in_dtype(case))
     try:
         p.run(dA, dB, dC, case.alpha if alpha is None else alpha,
               case.beta if beta is None else beta, stream=stream)
     finally:
         p.close()
     return dC
+
+
+def in_dtype(case):
+    return case.meta.get("in_dtype", "f16")
 
 
 def c_logical(case, C_flat, rows=None):
@@ -94,13 +116,14 @@ def c_logical(case, C_flat, rows=None):
 def oracle_for(case, rows=None):
     A = case.A.view(torch.int16).numpy().view(np.uint16)
     B = case.B.view(torch.int16).numpy().view(np.uint16)
-    if case.out_type == gi.OUT_F16:
+    if case.out_type in (gi.OUT_F16, gi.OUT_BF16):
         C = case.C.view(torch.int16).numpy().view(np.uint16)
     else:
         C = case.C.numpy()
     return oracle.gemm(case.M, case.N, case.K, A, B, C, alpha=case.alpha,
                        beta=case.beta, layout_a=case.layout_a,
                        layout_b=case.layout_b, out_type=case.out_type,
+                       in_type=oracle.IN_BF16 if in_dtype(case) == "bf16" else oracle.IN_F16,
                        lda=case.lda, ldb=case.ldb, ldc=case.ldc,
                        batch=case.batch, stride_a=case.stride_a,
                        stride_b=case.stride_b, stride_c=case.stride_c,

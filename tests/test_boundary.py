@@ -184,3 +184,53 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(mpg, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(ImportError):
         mpg.library()
+
+
+# ------------------------------------------------------------- bfloat16
+
+def test_bf16_plan_out_types():
+    from mixed_precision_gemm_amd import GEMM_OUT_BF16
+
+    def st(fn, out):
+        s, h = fn(64, 64, 64, GEMM_ROW_MAJOR, GEMM_ROW_MAJOR, out, 64, 64, 64)
+        if h is not None:
+            mpg.gemm_f16f32_destroy(h)
+        return s
+    assert st(mpg.gemm_bf16f32_plan, GEMM_OUT_BF16) == GEMM_OK
+    assert st(mpg.gemm_bf16f32_plan, GEMM_OUT_F32) == GEMM_OK
+    assert st(mpg.gemm_bf16f32_plan, GEMM_OUT_F16) == GEMM_ERR_INVALID_ARG
+    assert st(mpg.gemm_f16f32_plan, GEMM_OUT_BF16) == GEMM_ERR_INVALID_ARG
+    assert st(mpg.gemm_bf16f32_plan, 3) == GEMM_ERR_INVALID_ARG
+    # the other rules are the fp16 family's
+    s, h = mpg.gemm_bf16f32_plan(64, 64, 64, 0, 0, GEMM_OUT_BF16, 63, 64, 64)
+    assert s == GEMM_ERR_INVALID_ARG and h is None
+
+
+def test_run_rejects_plan_of_the_other_input_type():
+    """Checked before any HIP call: no launch happens."""
+    base = 1 << 30
+    with mpg.Plan(64, 64, 64) as p16, mpg.Plan(64, 64, 64, dtype="bf16") as pbf:
+        assert mpg.gemm_bf16f32_run(p16.handle, base, base + (1 << 20), base + (2 << 20),
+                                    1.0, 0.0, None) == GEMM_ERR_INVALID_ARG
+        assert mpg.gemm_f16f32_run(pbf.handle, base, base + (1 << 20), base + (2 << 20),
+                                   1.0, 0.0, None) == GEMM_ERR_INVALID_ARG
+    assert mpg.gemm_bf16f32_run(None, 0, 0, 0, 1.0, 0.0, None) == GEMM_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("shape,kw", [
+    ((8192, 8192, 8192), {}), ((8192, 8192, 8192), dict(layout_b=GEMM_COL_MAJOR)),
+    ((16, 4096, 4096), dict(layout_b=GEMM_COL_MAJOR)), ((32, 11008, 4096), dict(layout_b=GEMM_COL_MAJOR)),
+    ((64, 11008, 4096), dict(layout_b=GEMM_COL_MAJOR)), ((16, 4096, 4096), {}),
+    ((2048, 2048, 2048), {}), ((3072, 3072, 3072), {}), ((4095, 4095, 4095), {}),
+    ((127, 257, 33), {}), ((50, 333, 4100), {}), ((0, 8, 8), {}),
+    ((64, 64, 64), dict(batch=512, stride_a=4096, stride_b=4096, stride_c=4096)),
+])
+def test_bf16_kernel_choice_matches_fp16(shape, kw):
+    with mpg.Plan(*shape, **kw) as a, mpg.Plan(*shape, dtype="bf16", **kw) as b:
+        if a.kernel == "none":
+            assert b.kernel == "none"
+        else:
+            assert b.kernel == a.kernel.replace("gemm_", "gemm_bf16_", 1)
+    assert mpg.Plan(128, 128, 128, dtype="bf16").kernel.startswith("gemm_bf16_")
+    with pytest.raises(ValueError):
+        mpg.Plan(8, 8, 8, dtype="fp8")
