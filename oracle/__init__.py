@@ -18,6 +18,7 @@ from . import build as _build
 ROW_MAJOR, COL_MAJOR = 0, 1
 OUT_F16, OUT_F32, OUT_BF16 = 0, 1, 2
 IN_F16, IN_BF16 = 0, 1
+ACT_NONE, ACT_RELU, ACT_GELU, ACT_SILU = 0, 1, 2, 3
 
 _lib = None
 
@@ -34,10 +35,12 @@ def load_library(path):
     lib.oracle_decbf16.restype = dbl
     lib.oracle_encbf16.argtypes = [dbl]
     lib.oracle_encbf16.restype = ctypes.c_uint16
+    lib.oracle_activate.argtypes = [ctypes.c_int, dbl]
+    lib.oracle_activate.restype = dbl
     lib.oracle_gemm.argtypes = [i64, i64, i64, i64,
                                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                 i64, i64, i64, i64, i64, i64,
-                                vp, vp, vp, dbl, dbl, vp, i64, vp, vp,
+                                vp, vp, vp, dbl, dbl, vp, ctypes.c_int, vp, i64, vp, vp,
                                 ctypes.c_int]
     lib.oracle_gemm.restype = ctypes.c_int
     return lib
@@ -84,6 +87,14 @@ def encbf16(values, lib=None) -> np.ndarray:
     return out.reshape(np.shape(values))
 
 
+def activate(act, values, lib=None) -> np.ndarray:
+    """The epilogue activation ACT_* applied to float64 values."""
+    lib = lib or _load()
+    flat = np.asarray(values, dtype=np.float64).ravel()
+    out = np.array([lib.oracle_activate(int(act), float(v)) for v in flat], dtype=np.float64)
+    return out.reshape(np.shape(values))
+
+
 def _as_u16(x) -> np.ndarray:
     a = np.ascontiguousarray(x)
     if a.dtype == np.float16:
@@ -95,7 +106,7 @@ def _as_u16(x) -> np.ndarray:
 
 def gemm(M, N, K, A, B, C=None, *, alpha=1.0, beta=0.0,
          layout_a=ROW_MAJOR, layout_b=ROW_MAJOR, out_type=OUT_F16,
-         in_type=IN_F16, lda=None, ldb=None, ldc=None, batch=1,
+         in_type=IN_F16, bias=None, activation=ACT_NONE, lda=None, ldb=None, ldc=None, batch=1,
          stride_a=0, stride_b=0, stride_c=0, rows=None, nthreads=None,
          lib=None):
     """Reference result and error scale, each shaped (batch, nrows, N).
@@ -103,7 +114,9 @@ def gemm(M, N, K, A, B, C=None, *, alpha=1.0, beta=0.0,
     A, B: flat 16-bit storage (uint16 or float16 numpy arrays) in the
     layouts given, binary16 (in_type IN_F16) or bfloat16 bits (IN_BF16); C:
     binary16 (out_type OUT_F16), bfloat16 bits (OUT_BF16) or float32
-    storage, read only when beta != 0.  alpha, beta are rounded to fp32 first, as the
+    storage, read only when beta != 0.  bias: None or N float32 values added
+    to every row; activation: ACT_* applied last (the returned scale is that
+    of the pre-activation value).  alpha, beta are rounded to fp32 first, as the
     library receives them.  rows: optional row indices (sampled rows).
     lib: an alternative library handle from load_library (tests only).
     """
@@ -122,6 +135,11 @@ def gemm(M, N, K, A, B, C=None, *, alpha=1.0, beta=0.0,
             c = _as_u16(c)
         elif c.dtype != np.float32:
             raise TypeError("fp32 C expected")
+    bias_arr = None
+    if bias is not None:
+        bias_arr = np.ascontiguousarray(np.asarray(bias, dtype=np.float32))
+        if bias_arr.size < N:
+            raise ValueError("bias needs N values")
     rows_arr = None
     nrows = M
     if rows is not None:
@@ -138,7 +156,7 @@ def gemm(M, N, K, A, B, C=None, *, alpha=1.0, beta=0.0,
     rc = lib.oracle_gemm(batch, M, N, K, layout_a, layout_b, in_type, out_type,
                          lda, ldb, ldc, stride_a, stride_b, stride_c,
                          ptr(a), ptr(b), ptr(c), alpha32, beta32,
-                         ptr(rows_arr), nrows, ptr(ref), ptr(scale), int(nthreads))
+                         ptr(bias_arr), int(activation), ptr(rows_arr), nrows, ptr(ref), ptr(scale), int(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_gemm failed with {rc}")
     return ref, scale

@@ -26,7 +26,15 @@
  *   - [GEMM] §1.3: fp16 inputs, fp32 accumulation, fp16 output;
  *   - [GEMM] §6 and [CATLASS] §3.2: bfloat16 is the other 16-bit input
  *     format (the one the pages recommend for training); the same product
- *     with bfloat16 A and B and a bfloat16 or fp32 C.
+ *     with bfloat16 A and B and a bfloat16 or fp32 C;
+ *   - [CATLASS] §5.2 (keep the GEMM main loop, replace the epilogue) and the
+ *     page's opening case (a linear layer fused with its residual): an
+ *     optional fused epilogue, taken here in its plainest general form
+ *       C = act(alpha * A*B + beta * C + bias[n])
+ *     with bias a per-column vector (residual = the beta * C term) and act
+ *     one of ReLU max(x, 0), GELU x * Phi(x) = x/2 erfc(-x / sqrt 2),
+ *     SiLU x / (1 + e^-x).  The scale S then includes |bias[n]| and is the
+ *     scale of the pre-activation value.
  * Every product of two inputs is exact in double (11 x 11 significant bits
  * for binary16, 8 x 8 for bfloat16), and k is summed in ascending order with
  * no reassociation (-fno-fast-math).
@@ -63,6 +71,10 @@
 #define ORACLE_OUT_BF16 2
 #define ORACLE_IN_F16 0
 #define ORACLE_IN_BF16 1
+#define ORACLE_ACT_NONE 0
+#define ORACLE_ACT_RELU 1
+#define ORACLE_ACT_GELU 2
+#define ORACLE_ACT_SILU 3
 
 /* binary16 -> double.  e = 0: f * 2^-24 (zero or subnormal);
  * 1 <= e <= 30: (1024 + f) * 2^(e - 25); e = 31: inf (f = 0) or NaN. */
@@ -166,6 +178,21 @@ uint16_t oracle_encbf16(double x)
     return (uint16_t)(sgn | ((uint32_t)(E + 127) << 7) | (qi - 128));
 }
 
+/* The epilogue's activation of a pre-activation value x, by definition. */
+double oracle_activate(int act, double x)
+{
+    switch (act) {
+    case ORACLE_ACT_RELU:
+        return x > 0.0 ? x : 0.0;
+    case ORACLE_ACT_GELU:   /* Phi(x) = erfc(-x / sqrt 2) / 2, accurate in the left tail too */
+        return 0.5 * x * erfc(-x / sqrt(2.0));
+    case ORACLE_ACT_SILU:
+        return x / (1.0 + exp(-x));
+    default:
+        return x;
+    }
+}
+
 typedef struct {
     int64_t batch, M, N, K;
     int layout_a, layout_b, in_type, out_type;
@@ -173,6 +200,8 @@ typedef struct {
     const uint16_t *A, *B;
     const void *C;
     double alpha, beta;
+    const float *bias;       /* per-column bias (N values) or NULL */
+    int act;                 /* ORACLE_ACT_* */
     const int64_t *rows;
     int64_t nrows;
     double *ref, *scale;
@@ -250,6 +279,11 @@ static void *run_job(void *arg)
             double cin = (j->beta != 0.0) ? elem_c(j, b, i, n) : 0.0;
             out[n] = j->alpha * s + j->beta * cin;
             sc[n] = fabs(j->alpha) * t + fabs(j->beta) * fabs(cin);
+            if (j->bias) {
+                out[n] += (double)j->bias[n];
+                sc[n] += fabs((double)j->bias[n]);
+            }
+            out[n] = oracle_activate(j->act, out[n]);
         }
     }
     free(arow);
@@ -266,6 +300,8 @@ static void *run_job(void *arg)
  *              bfloat16 bits when ORACLE_OUT_BF16)
  * in_type: ORACLE_IN_F16 (A and B hold binary16 bits) or ORACLE_IN_BF16
  * (bfloat16 bits).
+ * bias: NULL or N floats added to every row before the activation; act:
+ * ORACLE_ACT_* applied last (ref holds act(x), scale the scale of x).
  * rows: optional list of nrows row indices to evaluate (NULL = all M rows,
  * nrows must then equal M).  Results: ref and scale, each batch x nrows x N,
  * dense.  alpha, beta: the fp32 scalars the caller passes, widened.
@@ -276,7 +312,7 @@ int oracle_gemm(int64_t batch, int64_t M, int64_t N, int64_t K,
                 int64_t lda, int64_t ldb, int64_t ldc,
                 int64_t stride_a, int64_t stride_b, int64_t stride_c,
                 const uint16_t *A, const uint16_t *B, const void *C,
-                double alpha, double beta,
+                double alpha, double beta, const float *bias, int act,
                 const int64_t *rows, int64_t nrows,
                 double *ref, double *scale, int nthreads)
 {
@@ -285,6 +321,8 @@ int oracle_gemm(int64_t batch, int64_t M, int64_t N, int64_t K,
     if (in_type != ORACLE_IN_F16 && in_type != ORACLE_IN_BF16)
         return -1;
     if (out_type != ORACLE_OUT_F16 && out_type != ORACLE_OUT_F32 && out_type != ORACLE_OUT_BF16)
+        return -1;
+    if (act < ORACLE_ACT_NONE || act > ORACLE_ACT_SILU)
         return -1;
     if (!rows && nrows != M)
         return -1;
@@ -327,6 +365,7 @@ int oracle_gemm(int64_t batch, int64_t M, int64_t N, int64_t K,
         j->stride_a = stride_a; j->stride_b = stride_b; j->stride_c = stride_c;
         j->A = A; j->B = B; j->C = C;
         j->alpha = alpha; j->beta = beta;
+        j->bias = bias; j->act = act;
         j->rows = rows; j->nrows = nrows;
         j->ref = ref; j->scale = scale;
         j->shared_bt = bt;

@@ -505,3 +505,96 @@ def test_fp32_accumulation_beats_fp16_accumulation():
             s32 = np.float32(s32 + p)
         ratios.append(abs(float(s16) - exact) / max(abs(float(s32) - exact), 1e-30))
     assert np.median(ratios) > 10.0
+
+
+# --------------------------------------------------------- fused epilogue
+
+from oracle import ACT_GELU, ACT_NONE, ACT_RELU, ACT_SILU  # noqa: E402
+
+
+def scipy_activation(act, x):
+    """The activations from library routines: ReLU max(x, 0), GELU
+    x * Phi(x) (scipy.special.ndtr), SiLU x * sigmoid(x) (scipy.special.expit)."""
+    import scipy.special as sp
+    x = np.asarray(x, dtype=np.float64)
+    if act == ACT_RELU:
+        return np.maximum(x, 0.0)
+    if act == ACT_GELU:
+        return x * sp.ndtr(x)
+    if act == ACT_SILU:
+        return x * sp.expit(x)
+    return x
+
+
+ACT_PROBE = np.concatenate([np.linspace(-12, 12, 4801), [0.0, 1e-300, -1e-300, 1e-8, -1e-8,
+                                                          40.0, -40.0, 700.0, -700.0, 1e4, -1e4]])
+
+
+@pytest.mark.parametrize("act", [ACT_NONE, ACT_RELU, ACT_GELU, ACT_SILU])
+def test_activation_against_scipy(act):
+    got = oracle.activate(act, ACT_PROBE)
+    want = scipy_activation(act, ACT_PROBE)
+    assert np.allclose(got, want, rtol=1e-13, atol=1e-300), act
+
+
+def test_activation_odd_part_and_landmarks():
+    x = np.linspace(-9, 9, 3601)
+    for act in (ACT_GELU, ACT_SILU):
+        # x Phi(x) + x Phi(-x) = x, and x s(x) + x s(-x) = x
+        d = oracle.activate(act, x) - oracle.activate(act, -x)
+        assert np.allclose(d, x, rtol=1e-14, atol=1e-14), act
+    # Phi(1) from the normal table, 1 / (1 + e^-1)
+    assert abs(oracle.activate(ACT_GELU, [1.0])[0] - 0.8413447460685429) < 1e-15
+    assert abs(oracle.activate(ACT_SILU, [1.0])[0] - 0.7310585786300049) < 1e-15
+    assert oracle.activate(ACT_RELU, [-3.0, 2.5]).tolist() == [0.0, 2.5]
+    assert oracle.activate(ACT_GELU, [0.0])[0] == 0.0 and oracle.activate(ACT_SILU, [0.0])[0] == 0.0
+
+
+def _epilogue_case(lib, M, N, K, la, lb, act, rng, alpha=-0.75, beta=0.5):
+    A_log = rand_f16(rng, (M, K))
+    B_log = rand_f16(rng, (K, N))
+    C_log = rng.uniform(-2, 2, (M, N)).astype(np.float32)
+    bias = rng.uniform(-1, 1, N).astype(np.float32)
+    lda = K if la == ROW_MAJOR else M
+    ldb = N if lb == ROW_MAJOR else K
+    A = to_storage(A_log, la, lda)
+    B = to_storage(B_log, lb, ldb)
+    ref, sc = oracle.gemm(M, N, K, A, B, C_log.ravel(), alpha=alpha, beta=beta,
+                          layout_a=la, layout_b=lb, out_type=OUT_F32, bias=bias,
+                          activation=act, lib=lib)
+    ex, exs = exact_product(A_log, B_log, C_log, alpha, beta)
+    for i in range(M):
+        for j in range(N):
+            x = ex[i, j] + Fraction(float(bias[j]))
+            s_x = exs[i, j] + abs(Fraction(float(bias[j])))
+            assert abs(Fraction(sc[0, i, j]) - s_x) <= s_x * Fraction(2.0 ** -50), (i, j)
+            if act == ACT_NONE:
+                assert abs(Fraction(ref[0, i, j]) - x) <= s_x * Fraction(2.0 ** -50), (i, j)
+            else:
+                want = float(scipy_activation(act, float(x)))
+                tol = 1.2 * 2.0 ** -48 * float(s_x) + 1e-13 * abs(want) + 1e-300
+                assert abs(ref[0, i, j] - want) <= tol, (M, N, K, la, lb, act, i, j)
+
+
+def test_epilogue_bias_and_activation_brute_force(lib=None):
+    rng = np.random.default_rng(13)
+    for (M, N, K) in [(1, 1, 1), (3, 5, 7), (6, 4, 9), (2, 9, 3)]:
+        for la, lb in LAYOUTS:
+            for act in (ACT_NONE, ACT_RELU, ACT_GELU, ACT_SILU):
+                _epilogue_case(lib, M, N, K, la, lb, act, rng)
+
+
+def test_epilogue_activation_follows_the_residual_add():
+    """act(alpha A B + beta C + bias): with A B = 2, beta C = -3 and bias 0
+    ReLU gives 0 (ReLU before the add would give -1)."""
+    A = np.array([1.0, 1.0], np.float16)          # 1 x 2
+    B = np.array([1.0, 1.0], np.float16)          # 2 x 1
+    C = np.array([-3.0], np.float32)
+    ref, sc = oracle.gemm(1, 1, 2, A, B, C, beta=1.0, out_type=OUT_F32,
+                          bias=np.zeros(1, np.float32), activation=ACT_RELU)
+    assert ref[0, 0, 0] == 0.0 and sc[0, 0, 0] == 5.0
+    ref, _ = oracle.gemm(1, 1, 2, A, B, C, beta=1.0, out_type=OUT_F32,
+                         bias=np.array([4.5], np.float32), activation=ACT_RELU)
+    assert ref[0, 0, 0] == 3.5
+    with pytest.raises(RuntimeError):
+        oracle.gemm(1, 1, 2, A, B, C, beta=1.0, out_type=OUT_F32, activation=7)

@@ -16,8 +16,9 @@ import oracle
 from oracle import build as oracle_build
 
 from oracle import IN_BF16
-from test_oracle import (_brute_force, _encode_bf16_probe_values, _encode_probe_values,
-                         bf16_bits, bf16_values)
+from test_oracle import (ACT_PROBE, _brute_force, _encode_bf16_probe_values,
+                         _encode_probe_values, bf16_bits, bf16_values, scipy_activation,
+                         test_epilogue_bias_and_activation_brute_force)
 
 MUTANTS = {
     "transposed_A_row_major": ("A[i * j->lda + k]", "A[k * j->lda + i]"),
@@ -43,6 +44,14 @@ MUTANTS = {
         "A[i + k * j->lda];\n    return oracle_dec16(h);"),
     "bf16_C_decoded_as_binary16": ("return oracle_decbf16(((const uint16_t *)j->C)[off]);",
                                    "return oracle_dec16(((const uint16_t *)j->C)[off]);"),
+    "bias_scaled_by_alpha": ("out[n] += (double)j->bias[n];",
+                             "out[n] += j->alpha * (double)j->bias[n];"),
+    "scale_without_bias": ("sc[n] += fabs((double)j->bias[n]);", "sc[n] += 0.0;"),
+    "activation_dropped": ("out[n] = oracle_activate(j->act, out[n]);", "(void)0;"),
+    "gelu_tanh_approximation": ("return 0.5 * x * erfc(-x / sqrt(2.0));",
+                                "return 0.5 * x * (1.0 + tanh(0.7978845608028654 * (x + 0.044715 * x * x * x)));"),
+    "silu_wrong_sign": ("return x / (1.0 + exp(-x));", "return x / (1.0 + exp(x));"),
+    "relu_leaky": ("return x > 0.0 ? x : 0.0;", "return x > 0.0 ? x : 0.01 * x;"),
 }
 
 SHAPES = [(1, 1, 1), (2, 3, 4), (3, 5, 7), (4, 1, 6)]
@@ -68,6 +77,10 @@ def _pins_pass(lib) -> bool:
         v = _encode_bf16_probe_values()
         assert np.array_equal(oracle.encbf16(v, lib=lib), bf16_bits(v.astype(np.float32)))
         _brute_force(lib, SHAPES, full_combos=True, in_type=IN_BF16)
+        for act in range(4):
+            assert np.allclose(oracle.activate(act, ACT_PROBE, lib=lib),
+                               scipy_activation(act, ACT_PROBE), rtol=1e-13, atol=1e-300)
+        test_epilogue_bias_and_activation_brute_force(lib)
     except (AssertionError, ValueError, OverflowError):
         return False   # a pin failed (or met a NaN/inf where a number was due)
     return True
