@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--layout nn|nt]
                     [--shape M N K] [--dtype f16|bf16] [--no-cpu-baseline]
+                    [--epilogue none|bias|relu|gelu|silu]
 
 A step is one C = A*B + C GEMM (the whole hot path: staging, MFMA K loop,
 epilogue) on the square workload M = N = K = 8192, fp16 A, B, C uniform
@@ -10,7 +11,9 @@ in HBM before timing starts.  W untimed warm-up steps, then K timed steps
 bracketed by device synchronisation; the kernel's own duration is measured
 with HIP events recorded on the stream the kernel is launched on.  Prints one
 JSON line (value = TFLOP/s, 2*M*N*K flops per step).  --dtype bf16 runs the
-same workload with bfloat16 A, B and C (the bfloat16 entry points).
+same workload with bfloat16 A, B and C (the bfloat16 entry points);
+--epilogue adds the fused epilogue C = act(A*B + C + bias) (a seeded fp32
+bias of N values; "bias" alone, or with ReLU / GELU / SiLU).
 
 The CPU baseline is the oracle (a plain fp64 triple loop on the host cores),
 timed on a bounded sample of the same workload: a fixed set of rows of C.
@@ -37,6 +40,8 @@ def parse():
     ap.add_argument("--shape", type=int, nargs=3, default=[8192, 8192, 8192])
     ap.add_argument("--dtype", choices=["f16", "bf16"], default="f16",
                     help="element type of A, B and C (default f16)")
+    ap.add_argument("--epilogue", choices=["none", "bias", "relu", "gelu", "silu"],
+                    default="none", help="fused epilogue (default none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -112,7 +117,7 @@ def profiled_traffic(layout, shape, dtype="f16"):
         return None
 
 
-def cpu_baseline(case, nrows):
+def cpu_baseline(case, nrows, bias=None, act=0):
     """Times the oracle on `nrows` rows of C (fixed, spread over M)."""
     import numpy as np
     import torch
@@ -126,6 +131,7 @@ def cpu_baseline(case, nrows):
                 alpha=case.alpha, beta=case.beta, layout_a=case.layout_a,
                 layout_b=case.layout_b, out_type=case.out_type,
                 in_type=oracle.IN_BF16 if bf else oracle.IN_F16,
+                bias=None if bias is None else bias.cpu().numpy(), activation=act,
                 rows=rows, nthreads=threads)
     dt = time.perf_counter() - t0
     flops = 2.0 * rows.size * case.N * case.K
@@ -160,6 +166,12 @@ def main():
     plan = mpg.Plan(M, N, K, case.layout_a, case.layout_b, case.out_type,
                     case.lda, case.ldb, case.ldc, dtype=args.dtype)
     stream = torch.cuda.current_stream(dev)
+    bias = None
+    act = {"none": 0, "bias": 0, "relu": 1, "gelu": 2, "silu": 3}[args.epilogue]
+    if args.epilogue != "none":
+        g = torch.Generator("cpu").manual_seed(1)
+        bias = (torch.rand(N, generator=g) * 2 - 1).to(dev)
+        plan.set_epilogue(bias, act)
     print(f"# kernel {plan.kernel}, {M}x{N}x{K} {args.layout.upper()} {args.dtype}",
           file=sys.stderr, flush=True)
 
@@ -201,16 +213,17 @@ def main():
                                f"{tname} A/B/C uniform[-1,1) seed 0, fp32 accumulation, "
                                f"{tname} out",
                    "M": M, "N": N, "K": K, "layout": args.layout.upper(),
-                   "kernel": plan.kernel},
+                   "kernel": plan.kernel, "epilogue": args.epilogue},
         "pct_of_peak": round(100.0 * tflops / PEAK_F16_TFLOPS, 2),
         "wall_s_timed": round(wall, 4),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
                      "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_F16_TFLOPS, 4),
-                     "traffic": profiled_traffic(args.layout, (M, N, K), args.dtype)},
+                     "traffic": (profiled_traffic(args.layout, (M, N, K), args.dtype)
+                                 if args.epilogue == "none" else None)},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(case, args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(case, args.cpu_rows, bias, act)
     print(json.dumps(out), flush=True)
 
 

@@ -74,6 +74,9 @@ typedef struct gemm_f16f32_plan_s *gemm_f16f32_plan_t; /* opaque, host only */
 enum { GEMM_ROW_MAJOR = 0, GEMM_COL_MAJOR = 1 };  /* storage of A and of B */
 enum { GEMM_OUT_F16 = 0, GEMM_OUT_F32 = 1 };      /* element type of C     */
 
+/* Activation of the fused epilogue (gemm_f16f32_set_epilogue). */
+enum { GEMM_ACT_NONE = 0, GEMM_ACT_RELU = 1, GEMM_ACT_GELU = 2, GEMM_ACT_SILU = 3 };
+
 enum {
     GEMM_OK = 0,
     GEMM_ERR_INVALID_ARG = -1,  /* argument violates a rule stated below    */
@@ -134,6 +137,34 @@ int gemm_f16f32_plan(gemm_f16f32_plan_t *out,
 int gemm_f16f32_run(gemm_f16f32_plan_t plan,
                     const void *A, const void *B, void *C,
                     float alpha, float beta, void *stream);
+
+/*
+ * Sets the plan's fused epilogue, used by every later run of the plan:
+ *   C(b,i,j) <- act( fp32(alpha) * sum_k A(b,i,k) B(b,k,j)
+ *                    + fp32(beta) * C(b,i,j) + bias[j] )
+ * in fp32, then rounded once to C's type.  This is the pages' "keep the GEMM
+ * main loop, replace the epilogue" pattern ([CATLASS] §5.2) in the form a
+ * linear layer needs: a per-column bias, the residual as beta * C, and one
+ * of the activations
+ *   GEMM_ACT_NONE  x
+ *   GEMM_ACT_RELU  max(x, 0)
+ *   GEMM_ACT_GELU  x * Phi(x) = x/2 * erfc(-x / sqrt(2))   (exact GELU)
+ *   GEMM_ACT_SILU  x / (1 + exp(-x))
+ * applied last (after the residual add).
+ *   plan        a plan of either input type (gemm_f16f32_plan or
+ *               gemm_bf16f32_plan).
+ *   bias        device pointer to N fp32 values (one per column of C, shared
+ *               by all rows and batch items; 4-byte aligned), or NULL for no
+ *               bias.  Owned by the caller; read by the runs, so it must stay
+ *               valid until the stream has passed them, and must not overlap
+ *               C (checked at run -> INVALID_ARG).
+ *   activation  GEMM_ACT_*.
+ * Host only, no HIP call.  NULL plan, a misaligned bias or an unknown
+ * activation -> INVALID_ARG (the plan is left unchanged).  Setting NULL and
+ * GEMM_ACT_NONE restores the plain GEMM.  Changing the epilogue of a plan
+ * while one of its runs may still be launched from another thread is a race.
+ */
+int gemm_f16f32_set_epilogue(gemm_f16f32_plan_t plan, const void *bias, int activation);
 
 /* Frees a plan (and its device buffers, after waiting for the device to
  * finish its work).  NULL is a no-op.  Returns GEMM_OK. */

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libmpgemm.so")
 
 GEMM_ROW_MAJOR, GEMM_COL_MAJOR = 0, 1
 GEMM_OUT_F16, GEMM_OUT_F32, GEMM_OUT_BF16 = 0, 1, 2
+GEMM_ACT_NONE, GEMM_ACT_RELU, GEMM_ACT_GELU, GEMM_ACT_SILU = 0, 1, 2, 3
 GEMM_OK = 0
 GEMM_ERR_INVALID_ARG = -1
 GEMM_ERR_UNSUPPORTED = -2
@@ -23,7 +24,7 @@ GEMM_ERR_NOMEM = -4
 
 EXPORTED = ("gemm_f16f32_plan", "gemm_f16f32_run", "gemm_f16f32_destroy",
             "gemm_f16f32_status_string", "gemm_f16f32_plan_kernel",
-            "gemm_bf16f32_plan", "gemm_bf16f32_run")
+            "gemm_bf16f32_plan", "gemm_bf16f32_run", "gemm_f16f32_set_epilogue")
 
 _lib = None
 
@@ -53,6 +54,8 @@ def library() -> ctypes.CDLL:
             run_fn = getattr(lib, f"gemm_{fam}_run")
             run_fn.argtypes = [vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp]
             run_fn.restype = ctypes.c_int
+        lib.gemm_f16f32_set_epilogue.argtypes = [vp, vp, ctypes.c_int]
+        lib.gemm_f16f32_set_epilogue.restype = ctypes.c_int
         lib.gemm_f16f32_destroy.argtypes = [vp]
         lib.gemm_f16f32_destroy.restype = ctypes.c_int
         lib.gemm_f16f32_status_string.argtypes = [ctypes.c_int]
@@ -94,6 +97,11 @@ def gemm_bf16f32_plan(M, N, K, layout_a, layout_b, out_type, lda, ldb, ldc,
 def gemm_bf16f32_run(plan, A, B, C, alpha, beta, stream=None):
     """Runs a plan made by gemm_bf16f32_plan (device addresses as ints)."""
     return library().gemm_bf16f32_run(plan, A, B, C, alpha, beta, stream)
+
+
+def gemm_f16f32_set_epilogue(plan, bias, activation):
+    """bias: device address of N fp32 values (int) or None; activation GEMM_ACT_*."""
+    return library().gemm_f16f32_set_epilogue(plan, bias, activation)
 
 
 def gemm_f16f32_destroy(plan):
@@ -148,6 +156,20 @@ class Plan:
         if st != GEMM_OK:
             raise GemmError(st, self._run.__name__)
 
+    def set_epilogue(self, bias=None, activation=GEMM_ACT_NONE):
+        """Fused epilogue of later runs: C = act(alpha A B + beta C + bias).
+        bias: None, a device address, or a CUDA float32 tensor of N values
+        (the caller keeps it alive while runs use it)."""
+        addr = bias if bias is None or isinstance(bias, int) else bias.data_ptr()
+        if bias is not None and not isinstance(bias, int):
+            import torch
+            if bias.dtype != torch.float32 or bias.numel() < self.shape[1] or not bias.is_contiguous():
+                raise TypeError("bias must be a contiguous float32 tensor of N values")
+        st = gemm_f16f32_set_epilogue(self.handle, addr, activation)
+        if st != GEMM_OK:
+            raise GemmError(st, "gemm_f16f32_set_epilogue")
+        self._bias = bias
+
     def close(self):
         if self.handle is not None:
             gemm_f16f32_destroy(self.handle)
@@ -176,11 +198,13 @@ def _layout_of(t, rows, cols):
     return None
 
 
-def gemm(A, B, C=None, alpha=1.0, beta=0.0, out_dtype=None):
+def gemm(A, B, C=None, alpha=1.0, beta=0.0, out_dtype=None, bias=None,
+         activation=GEMM_ACT_NONE):
     """C = alpha * A @ B + beta * C for float16 (or bfloat16) CUDA tensors A
     (.., M, K) and B (.., K, N); layouts and leading dimensions come from the
     strides.  Returns C (allocated when None; the input type unless
-    out_dtype is torch.float32)."""
+    out_dtype is torch.float32).  bias (float32, N values) and activation
+    (GEMM_ACT_*) select the fused epilogue C = act(alpha A B + beta C + bias)."""
     import torch
     if A.dtype != B.dtype or A.dtype not in (torch.float16, torch.bfloat16):
         raise TypeError("A and B must both be float16 or both bfloat16")
@@ -213,5 +237,7 @@ def gemm(A, B, C=None, alpha=1.0, beta=0.0, out_dtype=None):
     sc = C.stride(0) if batched else 0
     with Plan(M, N, K, la[0], lb[0], out_type, la[1], lb[1], ldc, batch,
               sa, sb, sc, dtype=dtype) as p:
+        if bias is not None or activation != GEMM_ACT_NONE:
+            p.set_epilogue(bias, activation)
         p.run(A, B, C, alpha, beta)
     return C

@@ -64,6 +64,9 @@ constexpr int kNumCUs = 256;
 // Element type of A and B (and of a 16-bit C): IEEE binary16, or bfloat16.
 enum InputType : int { IN_F16 = 0, IN_BF16 = 1 };
 
+// Activation of the fused epilogue (the values of GEMM_ACT_*).
+enum Activation : int { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2, ACT_SILU = 3 };
+
 }  // namespace mpgemm
 
 struct gemm_f16f32_plan_s {
@@ -91,5 +94,8 @@ struct gemm_f16f32_plan_s {
     int64_t pack_bytes;    // bytes of both copies
     void *pack_ws;         // device buffer of the copies, allocated by the first run that packs
     int pack_device;       // device that holds pack_ws
+    // Fused epilogue (gemm_f16f32_set_epilogue): C = act(alpha A B + beta C + bias).
+    const float *bias;     // device pointer to N fp32 values, or NULL
+    int act;               // mpgemm::Activation
     char kernel_name[64];
 };

@@ -36,6 +36,9 @@
 // Loads, LDS layouts and fragment reads move 16-bit elements and do not
 // depend on TI; only the MFMA (the _bf16 forms of the same shapes) and the
 // 16-bit C of the epilogue (bfloat16 C, rounded to nearest even) change.
+// An optional fused epilogue ([CATLASS] §5.2: keep the main loop, replace the
+// epilogue) turns the final value into act(alpha*acc + beta*C + bias[n]),
+// applied once per output just before its rounding and store.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -78,6 +81,11 @@ struct GemmArgs {
     int total_tiles;
     int out_f32;
     int c_vec;                    // C rows allow 4-element vector access
+    // Fused epilogue: epi != 0 when a bias (N fp32 values) or an activation
+    // (mpgemm::Activation) is set.
+    int epi;
+    int act;
+    const float *bias;
     // Split-K (direct 128 x 128 tile only): K is cut into ksplit slices of
     // kchunk indices; grid = total_tiles * ksplit, block id = slice *
     // total_tiles + tile.  ws holds one fp32 partial tile per (slice, tile),
@@ -302,16 +310,56 @@ __device__ inline void tile_coords(const GemmArgs &p, int wg, int &b, int &tm, i
     tn = tw / gsz;
 }
 
+// Fused-epilogue activations in fp32 (with the device library's erfcf and
+// expf): ReLU max(x, 0); GELU x Phi(x) = x/2 erfc(-x / sqrt 2) (erfc keeps
+// the left tail); SiLU x / (1 + e^-x), which tends to -0 as e^-x overflows.
+__device__ inline float activate(int act, float x) {
+    switch (act) {
+    case ACT_RELU: return fmaxf(x, 0.0f);
+    case ACT_GELU: return 0.5f * x * erfcf(-x * 0.70710678118654752f);
+    case ACT_SILU: return x / (1.0f + expf(-x));
+    default: return x;
+    }
+}
+
+// Bias of columns n..n+3 (zeros past N, or without a bias).
+__device__ inline floatx4 load_bias4(const GemmArgs &p, int64_t n) {
+    floatx4 b = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (p.bias) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (n + e < p.N) b[e] = p.bias[n + e];
+    }
+    return b;
+}
+
+// The epilogue of four columns on their pre-activation values.  Only the
+// kernels instantiated with EPI = true contain it (the others clear p.epi at
+// compile time, so the code is dead there): compiled into every kernel, the
+// activations raised the register pressure of the whole kernel until the
+// 256 tile's accumulators spilled inside its K loop (measured 17x slower with
+// no epilogue set), and a call instead of inlining made every kernel need
+// scratch (+3 us per launch on the short split-K grids).
+__device__ inline floatx4 epilogue4(const GemmArgs &p, floatx4 v, floatx4 bias4) {
+    v += bias4;
+    if (p.act != ACT_NONE) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = activate(p.act, v[e]);
+    }
+    return v;
+}
+
 // Epilogue shared by both kernels: C = alpha * acc + beta * C on the wave's
 // FM x FN blocks of 32 x 32, rounded once to fp16 (RNE) or stored as fp32,
 // masked at the M and N edges.  Accumulator register r of lane l in block
 // (i, j) holds C(m, n) with m = l % 32 and n = 8*(r/4) + 4*(l/32) + r%4
 // (block-local), so each lane owns runs of 4 consecutive n of one row.
-template <typename T16, int FM, int FN, int WTM, int WTN>
+template <typename T16, bool EPI, int FM, int FN, int WTM, int WTN>
 __device__ inline void store_tile(const GemmArgs &p, const floatx16 (&acc)[FM][FN],
                                   int b, int64_t m0, int64_t n0, int wm, int wn,
                                   int lane) {
     const float alpha = p.alpha, beta = p.beta;
+    const bool epi = EPI && p.epi;   // no epilogue code unless EPI
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         const int64_t m = m0 + wm * WTM + i * 32 + (lane & 31);
@@ -336,13 +384,23 @@ __device__ inline void store_tile(const GemmArgs &p, const floatx16 (&acc)[FM][F
                             for (int e = 0; e < 4; ++e) v[e] += beta * c[e];
                         }
                         floatx4 o = {v[0], v[1], v[2], v[3]};
+                        if (epi) o = epilogue4(p, o, load_bias4(p, n));
                         *(floatx4 *)C = o;
-                    } else {
+                    } else if (!epi) {
                         for (int e = 0; e < 4 && n + e < p.N; ++e) {
                             float o = v[e];
                             if (beta != 0.0f) o += beta * C[e];
                             C[e] = o;
                         }
+                    } else {
+                        floatx4 o = {v[0], v[1], v[2], v[3]};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (beta != 0.0f && n + e < p.N) o[e] += beta * C[e];
+                        o = epilogue4(p, o, load_bias4(p, n));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e < p.N) C[e] = o[e];
                     }
                 } else {
                     T16 *C = (T16 *)p.C + off;
@@ -352,14 +410,28 @@ __device__ inline void store_tile(const GemmArgs &p, const floatx16 (&acc)[FM][F
 #pragma unroll
                             for (int e = 0; e < 4; ++e) v[e] += beta * (float)c[e];
                         }
+                        if (epi) {
+                            const floatx4 w = epilogue4(p, floatx4{v[0], v[1], v[2], v[3]}, load_bias4(p, n));
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) v[e] = w[e];
+                        }
                         c4_t<T16> o = {(T16)v[0], (T16)v[1], (T16)v[2], (T16)v[3]};
                         *(c4_t<T16> *)C = o;
-                    } else {
+                    } else if (!epi) {
                         for (int e = 0; e < 4 && n + e < p.N; ++e) {
                             float o = v[e];
                             if (beta != 0.0f) o += beta * (float)C[e];
                             C[e] = (T16)o;
                         }
+                    } else {
+                        floatx4 o = {v[0], v[1], v[2], v[3]};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (beta != 0.0f && n + e < p.N) o[e] += beta * (float)C[e];
+                        o = epilogue4(p, o, load_bias4(p, n));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e < p.N) C[e] = (T16)o[e];
                     }
                 }
             }
@@ -367,7 +439,8 @@ __device__ inline void store_tile(const GemmArgs &p, const floatx16 (&acc)[FM][F
     }
 }
 
-template <typename TI, int BM, int BN, int BK, int WGM, int WGN, bool AK, bool BKC, bool VEC>
+template <typename TI, int BM, int BN, int BK, int WGM, int WGN, bool AK, bool BKC, bool VEC,
+          bool EPI>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_staged(GemmArgs p) {
     constexpr int NT = 64 * WGM * WGN;
     constexpr int VPR = BK / 8;
@@ -464,7 +537,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_staged(GemmArgs p) {
         __syncthreads();
     }
 
-    store_tile<TI, FM, FN, WTM, WTN>(p, acc, b, m0, n0, wm, wn, lane);
+    store_tile<TI, EPI, FM, FN, WTM, WTN>(p, acc, b, m0, n0, wm, wn, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -592,7 +665,7 @@ __device__ inline void store_c4(const GemmArgs &p, int64_t off, int64_t n, bool 
 // g ^ (r & 15), so neither the column-wise writes nor the row-wise reads
 // conflict on banks.
 template <typename T, bool FULL, int BM, int BN, int WGM, int WGN, int LDS_BYTES, int MB,
-          typename AccT, int FM, int FN>
+          bool EPI, typename AccT, int FM, int FN>
 __device__ inline void store_tile_lds(const GemmArgs &p, const AccT (&acc)[FM][FN],
                                       u32x4 *lds, int b, int64_t m0, int64_t n0,
                                       int wave, int lane) {
@@ -619,6 +692,7 @@ __device__ inline void store_tile_lds(const GemmArgs &p, const AccT (&acc)[FM][F
     const bool n_ok = FULL || n < p.N;
     const bool vec = FULL || (p.c_vec && n + 4 <= p.N);
     const int64_t cbase = b * p.sc + n;
+    const floatx4 bias4 = (p.epi && n_ok) ? load_bias4(p, n) : floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     // Two register batches of C: batch k + 1 is in flight while batch k is
     // combined and stored.
     c4_t<T> cv[2][CB];
@@ -657,20 +731,55 @@ __device__ inline void store_tile_lds(const GemmArgs &p, const AccT (&acc)[FM][F
         }
         asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
         barrier();
+        if constexpr (EPI) {
+            // Fused epilogue: the same batched C loads; each lane writes its
+            // pre-activation values back into its own staging slots (one
+            // reader per slot, so no other lane is affected).  Then a loop
+            // after the batched one (not inside it: a partly unrolled loop
+            // inside a fully unrolled one kept the latter rolled, and its
+            // register arrays went to scratch) activates and stores them,
+            // four row groups per iteration: 16 activations in flight, as
+            // one wave per SIMD hides no latency.
 #pragma unroll
-        for (int it0 = 0; it0 < IT; it0 += CB) {
-            const int buf = (it0 / CB) & 1;
-            if (it0 + CB < IT) load_batch(pass, it0 + CB, buf ^ 1);
+            for (int it0 = 0; it0 < IT; it0 += CB) {
+                const int buf = (it0 / CB) & 1;
+                if (it0 + CB < IT) load_batch(pass, it0 + CB, buf ^ 1);
 #pragma unroll
-            for (int t = 0; t < CB; ++t) {
-                const int r = ((it0 + t) * NW + wave) * RPI + r_in;
+                for (int t = 0; t < CB; ++t) {
+                    const int r = ((it0 + t) * NW + wave) * RPI + r_in;
+                    floatx4 *slot = (floatx4 *)(base + r * BN * 4 + ((g ^ (r & SW)) << 4));
+                    floatx4 v = *slot;
+                    if (beta != 0.0f) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] += beta * (float)cv[buf][t][e];
+                    }
+                    *slot = v + bias4;
+                }
+            }
+#pragma unroll 4
+            for (int it = 0; it < IT; ++it) {
+                const int r = (it * NW + wave) * RPI + r_in;
                 const int64_t m = m0 + pass * PR + r;
                 floatx4 v = *(const floatx4 *)(base + r * BN * 4 + ((g ^ (r & SW)) << 4));
-                if (beta != 0.0f) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] += beta * (float)cv[buf][t][e];
-                }
+                v = epilogue4(p, v, floatx4{0.0f, 0.0f, 0.0f, 0.0f});
                 if (FULL || (m < p.M && n_ok)) store_c4<T>(p, cbase + m * p.ldc, n, vec, v);
+            }
+        } else {
+#pragma unroll
+            for (int it0 = 0; it0 < IT; it0 += CB) {
+                const int buf = (it0 / CB) & 1;
+                if (it0 + CB < IT) load_batch(pass, it0 + CB, buf ^ 1);
+#pragma unroll
+                for (int t = 0; t < CB; ++t) {
+                    const int r = ((it0 + t) * NW + wave) * RPI + r_in;
+                    const int64_t m = m0 + pass * PR + r;
+                    floatx4 v = *(const floatx4 *)(base + r * BN * 4 + ((g ^ (r & SW)) << 4));
+                    if (beta != 0.0f) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] += beta * (float)cv[buf][t][e];
+                    }
+                    if (FULL || (m < p.M && n_ok)) store_c4<T>(p, cbase + m * p.ldc, n, vec, v);
+                }
             }
         }
         if (pass + 1 < NPASS) {
@@ -746,6 +855,7 @@ __device__ inline void store_tile_splitk(const GemmArgs &p, const AccT (&acc)[FM
     const int64_t n = n0 + 4 * g;
     const bool n_ok = n < p.N;
     const bool vec = p.c_vec && n + 4 <= p.N;
+    const floatx4 bias4 = (p.epi && n_ok) ? load_bias4(p, n) : floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     const uint32_t tile0 = (uint32_t)((int64_t)tile * tile_elems * 4);
     const uint32_t slice_stride = (uint32_t)((int64_t)p.total_tiles * tile_elems * 4);
     // All slices of RB row groups (and their C) are requested before any is
@@ -783,6 +893,7 @@ __device__ inline void store_tile_splitk(const GemmArgs &p, const AccT (&acc)[FM
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] += beta * (float)cv[u][e];
                 }
+                if (p.epi) v = epilogue4(p, v, bias4);
                 store_c4<T>(p, b * p.sc + m * p.ldc + n, n, vec, v);
             }
         }
@@ -994,11 +1105,13 @@ struct Frag16 {
 // lane (stages past the end of K fail the range check and write zeros), so
 // the wait counts are exact.
 // ---------------------------------------------------------------------------
-template <typename TI, int BM, int BN, int BK, int WGM, int WGN, int S, bool AK, bool BKC, bool KFULL>
+template <typename TI, int BM, int BN, int BK, int WGM, int WGN, int S, bool AK, bool BKC, bool KFULL,
+          bool EPI>
 __global__ __launch_bounds__(64 * WGM * WGN)
 __attribute__((amdgpu_waves_per_eu(BM * BN >= 65536 ? 1 : 2, BM * BN >= 65536 ? 1 : 2)))
 void gemm_direct16(GemmArgs pin) {
     GemmArgs p = pin;
+    if constexpr (!EPI) p.epi = 0;   // no epilogue code in this instantiation
     constexpr int NW = WGM * WGN;
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
     constexpr int FM = WTM / 16, FN = WTN / 16;
@@ -1215,14 +1328,14 @@ void gemm_direct16(GemmArgs pin) {
     const bool full = p.c_vec && m0 + BM <= p.M && n0 + BN <= p.N;
     if (p.out_f32) {
         if (full)
-            store_tile_lds<float, true, BM, BN, WGM, WGN, S * SLOT * 16, 16>(p, acc, lds, b, m0, n0, wave, lane);
+            store_tile_lds<float, true, BM, BN, WGM, WGN, S * SLOT * 16, 16, EPI>(p, acc, lds, b, m0, n0, wave, lane);
         else
-            store_tile_lds<float, false, BM, BN, WGM, WGN, S * SLOT * 16, 16>(p, acc, lds, b, m0, n0, wave, lane);
+            store_tile_lds<float, false, BM, BN, WGM, WGN, S * SLOT * 16, 16, EPI>(p, acc, lds, b, m0, n0, wave, lane);
     } else {
         if (full)
-            store_tile_lds<TI, true, BM, BN, WGM, WGN, S * SLOT * 16, 16>(p, acc, lds, b, m0, n0, wave, lane);
+            store_tile_lds<TI, true, BM, BN, WGM, WGN, S * SLOT * 16, 16, EPI>(p, acc, lds, b, m0, n0, wave, lane);
         else
-            store_tile_lds<TI, false, BM, BN, WGM, WGN, S * SLOT * 16, 16>(p, acc, lds, b, m0, n0, wave, lane);
+            store_tile_lds<TI, false, BM, BN, WGM, WGN, S * SLOT * 16, 16, EPI>(p, acc, lds, b, m0, n0, wave, lane);
     }
 }
 
@@ -1245,8 +1358,10 @@ void gemm_direct16(GemmArgs pin) {
 // ---------------------------------------------------------------------------
 typedef float floatx4v __attribute__((ext_vector_type(4)));
 
-template <typename TI, int MB, int NB>
-__global__ __launch_bounds__(512) void gemm_stream(GemmArgs p) {
+template <typename TI, int MB, int NB, bool EPI>
+__global__ __launch_bounds__(512) void gemm_stream(GemmArgs pin) {
+    GemmArgs p = pin;
+    if constexpr (!EPI) p.epi = 0;   // no epilogue code in this instantiation
     constexpr int NW = 8;
     constexpr int UNROLL = 4;   // K steps whose loads are issued together (8: 1-3% slower)
     static_assert(MB * NB <= 8, "reduction buffer within 64 KiB");
@@ -1344,10 +1459,12 @@ __global__ __launch_bounds__(512) void gemm_stream(GemmArgs p) {
         if (p.out_f32) {
             float *C = (float *)p.C + off;
             if (beta != 0.0f) v += beta * *C;
+            if (p.epi) v = activate(p.act, p.bias ? v + p.bias[nn] : v);
             *C = v;
         } else {
             TI *C = (TI *)p.C + off;
             if (beta != 0.0f) v += beta * (float)*C;
+            if (p.epi) v = activate(p.act, p.bias ? v + p.bias[nn] : v);
             *C = (TI)v;
         }
     }
@@ -1423,82 +1540,85 @@ __global__ __launch_bounds__(256) void gemm_pack16(PackArgs a) {
 
 typedef void (*KernelFn)(GemmArgs);
 
-template <typename TI, int T, bool AK, bool BKC, bool VEC>
+template <typename TI, bool EPI, int T, bool AK, bool BKC, bool VEC>
 constexpr KernelFn pick_staged() {
     return gemm_staged<TI, kTiles[T].bm, kTiles[T].bn, kTiles[T].bk, kTiles[T].wgm,
-                       kTiles[T].wgn, AK, BKC, VEC>;
+                       kTiles[T].wgn, AK, BKC, VEC, EPI>;
 }
 
-template <typename TI, int T, bool AK, bool BKC, bool KFULL = false>
+template <typename TI, bool EPI, int T, bool AK, bool BKC, bool KFULL = false>
 constexpr KernelFn pick_direct16() {
     return gemm_direct16<TI, kTiles[T].bm, kTiles[T].bn, kTiles[T].bk, kTiles[T].wgm,
-                         kTiles[T].wgn, kTiles[T].stages, AK, BKC, KFULL>;
+                         kTiles[T].wgn, kTiles[T].stages, AK, BKC, KFULL, EPI>;
 }
 
-// Kernel table indexed [input type][tile][A K-contiguous][B K-contiguous][vec].
-// Direct tiles have only the vec entry; staged tiles have both.
-template <typename TI, int T>
+// Kernel table indexed [input type][fused epilogue][tile][A K-contiguous]
+// [B K-contiguous][vec].  Direct tiles have only the vec entry; staged tiles
+// have both.
+template <typename TI, bool EPI, int T>
 void fill_tile(KernelFn (&t)[2][2][2]) {
     if constexpr (kTiles[T].kind == KIND_DIRECT16) {
-        t[0][0][1] = pick_direct16<TI, T, false, false>();
-        t[0][1][1] = pick_direct16<TI, T, false, true>();
-        t[1][0][1] = pick_direct16<TI, T, true, false>();
-        t[1][1][1] = pick_direct16<TI, T, true, true>();
+        t[0][0][1] = pick_direct16<TI, EPI, T, false, false>();
+        t[0][1][1] = pick_direct16<TI, EPI, T, false, true>();
+        t[1][0][1] = pick_direct16<TI, EPI, T, true, false>();
+        t[1][1][1] = pick_direct16<TI, EPI, T, true, true>();
         t[0][0][0] = t[0][1][0] = t[1][0][0] = t[1][1][0] = nullptr;
     } else {
-        t[0][0][0] = pick_staged<TI, T, false, false, false>();
-        t[0][0][1] = pick_staged<TI, T, false, false, true>();
-        t[0][1][0] = pick_staged<TI, T, false, true, false>();
-        t[0][1][1] = pick_staged<TI, T, false, true, true>();
-        t[1][0][0] = pick_staged<TI, T, true, false, false>();
-        t[1][0][1] = pick_staged<TI, T, true, false, true>();
-        t[1][1][0] = pick_staged<TI, T, true, true, false>();
-        t[1][1][1] = pick_staged<TI, T, true, true, true>();
+        t[0][0][0] = pick_staged<TI, EPI, T, false, false, false>();
+        t[0][0][1] = pick_staged<TI, EPI, T, false, false, true>();
+        t[0][1][0] = pick_staged<TI, EPI, T, false, true, false>();
+        t[0][1][1] = pick_staged<TI, EPI, T, false, true, true>();
+        t[1][0][0] = pick_staged<TI, EPI, T, true, false, false>();
+        t[1][0][1] = pick_staged<TI, EPI, T, true, false, true>();
+        t[1][1][0] = pick_staged<TI, EPI, T, true, true, false>();
+        t[1][1][1] = pick_staged<TI, EPI, T, true, true, true>();
     }
 }
 
-template <typename TI, int T>
+template <typename TI, bool EPI, int T>
 void fill_kfull(KernelFn (&t)[2][2]) {
     static_assert(kTiles[T].kind == KIND_DIRECT16, "K-full variants are direct16");
-    t[0][0] = pick_direct16<TI, T, false, false, true>();
-    t[0][1] = pick_direct16<TI, T, false, true, true>();
-    t[1][0] = pick_direct16<TI, T, true, false, true>();
-    t[1][1] = pick_direct16<TI, T, true, true, true>();
+    t[0][0] = pick_direct16<TI, EPI, T, false, false, true>();
+    t[0][1] = pick_direct16<TI, EPI, T, false, true, true>();
+    t[1][0] = pick_direct16<TI, EPI, T, true, false, true>();
+    t[1][1] = pick_direct16<TI, EPI, T, true, true, true>();
 }
 
-template <typename TI, int T>
+template <typename TI, bool EPI, int T>
 void fill_stream(KernelFn (&t)[2][2][2]) {
     // Only the K-contiguous A and B (row-major A, column-major B) 128-bit form.
     t[0][0][0] = t[0][0][1] = t[0][1][0] = t[0][1][1] = nullptr;
     t[1][0][0] = t[1][0][1] = t[1][1][0] = nullptr;
-    t[1][1][1] = gemm_stream<TI, kTiles[T].bm / 16, kTiles[T].bn / 16>;
+    t[1][1][1] = gemm_stream<TI, kTiles[T].bm / 16, kTiles[T].bn / 16, EPI>;
 }
 
-template <typename TI>
+template <typename TI, bool EPI>
 void fill_type(KernelFn (&k)[NUM_TILES][2][2][2], KernelFn (&kfull)[NUM_TILES][2][2]) {
     for (auto &t : kfull)
         t[0][0] = t[0][1] = t[1][0] = t[1][1] = nullptr;
-    fill_kfull<TI, TILE_256x256>(kfull[TILE_256x256]);
-    fill_kfull<TI, TILE_128x128>(kfull[TILE_128x128]);
-    fill_kfull<TI, TILE_128x128_D4>(kfull[TILE_128x128_D4]);
-    fill_tile<TI, TILE_256x256>(k[TILE_256x256]);
-    fill_tile<TI, TILE_128x128>(k[TILE_128x128]);
-    fill_tile<TI, TILE_128x128_D4>(k[TILE_128x128_D4]);
-    fill_tile<TI, TILE_64x64>(k[TILE_64x64]);
-    fill_tile<TI, TILE_32x64>(k[TILE_32x64]);
-    fill_tile<TI, TILE_128x128_STAGED>(k[TILE_128x128_STAGED]);
-    fill_stream<TI, TILE_STREAM16>(k[TILE_STREAM16]);
-    fill_stream<TI, TILE_STREAM32>(k[TILE_STREAM32]);
-    fill_stream<TI, TILE_STREAM64>(k[TILE_STREAM64]);
-    fill_stream<TI, TILE_STREAM32W>(k[TILE_STREAM32W]);
+    fill_kfull<TI, EPI, TILE_256x256>(kfull[TILE_256x256]);
+    fill_kfull<TI, EPI, TILE_128x128>(kfull[TILE_128x128]);
+    fill_kfull<TI, EPI, TILE_128x128_D4>(kfull[TILE_128x128_D4]);
+    fill_tile<TI, EPI, TILE_256x256>(k[TILE_256x256]);
+    fill_tile<TI, EPI, TILE_128x128>(k[TILE_128x128]);
+    fill_tile<TI, EPI, TILE_128x128_D4>(k[TILE_128x128_D4]);
+    fill_tile<TI, EPI, TILE_64x64>(k[TILE_64x64]);
+    fill_tile<TI, EPI, TILE_32x64>(k[TILE_32x64]);
+    fill_tile<TI, EPI, TILE_128x128_STAGED>(k[TILE_128x128_STAGED]);
+    fill_stream<TI, EPI, TILE_STREAM16>(k[TILE_STREAM16]);
+    fill_stream<TI, EPI, TILE_STREAM32>(k[TILE_STREAM32]);
+    fill_stream<TI, EPI, TILE_STREAM64>(k[TILE_STREAM64]);
+    fill_stream<TI, EPI, TILE_STREAM32W>(k[TILE_STREAM32W]);
 }
 
 struct KernelTable {
-    KernelFn k[2][NUM_TILES][2][2][2];
-    KernelFn kfull[2][NUM_TILES][2][2];   // direct tiles with K a multiple of BK (else null)
+    KernelFn k[2][2][NUM_TILES][2][2][2];
+    KernelFn kfull[2][2][NUM_TILES][2][2];   // direct tiles with K a multiple of BK (else null)
     KernelTable() {
-        fill_type<_Float16>(k[IN_F16], kfull[IN_F16]);
-        fill_type<__bf16>(k[IN_BF16], kfull[IN_BF16]);
+        fill_type<_Float16, false>(k[IN_F16][0], kfull[IN_F16][0]);
+        fill_type<_Float16, true>(k[IN_F16][1], kfull[IN_F16][1]);
+        fill_type<__bf16, false>(k[IN_BF16][0], kfull[IN_BF16][0]);
+        fill_type<__bf16, true>(k[IN_BF16][1], kfull[IN_BF16][1]);
     }
 };
 
@@ -1533,6 +1653,8 @@ int run_plan(gemm_f16f32_plan_t plan, const void *A, const void *B, void *C, flo
     const int64_t cbytes = p.extent_c * (p.out_type == GEMM_OUT_F32 ? 4 : 2);
     if (p.K > 0 && (ranges_overlap((uintptr_t)C, cbytes, (uintptr_t)A, p.extent_a * 2) ||
                     ranges_overlap((uintptr_t)C, cbytes, (uintptr_t)B, p.extent_b * 2)))
+        return GEMM_ERR_INVALID_ARG;
+    if (p.bias && ranges_overlap((uintptr_t)C, cbytes, (uintptr_t)p.bias, p.N * 4))
         return GEMM_ERR_INVALID_ARG;
 
     // Operands copied into the plan's padded buffers first: those whose shape
@@ -1572,6 +1694,9 @@ int run_plan(gemm_f16f32_plan_t plan, const void *A, const void *B, void *C, flo
     a.total_tiles = (int)(tiles_m * tiles_n * p.batch);
     a.out_f32 = p.out_type == GEMM_OUT_F32;
     a.c_vec = c_vec;
+    a.bias = p.bias;
+    a.act = p.act;
+    a.epi = p.bias != nullptr || p.act != ACT_NONE;
     a.ksplit = 1;
     a.kchunk = p.K;
     a.ws = nullptr;
@@ -1655,10 +1780,11 @@ int run_plan(gemm_f16f32_plan_t plan, const void *A, const void *B, void *C, flo
     const int ak = p.layout_a == GEMM_ROW_MAJOR;   // A K-contiguous
     const int bkc = p.layout_b == GEMM_COL_MAJOR;  // B K-contiguous
     const int ti = p.in_type == IN_BF16 ? IN_BF16 : IN_F16;
-    KernelFn fn = kernels().k[ti][tile][ak][bkc][vec ? 1 : 0];
+    const int ep = a.epi ? 1 : 0;
+    KernelFn fn = kernels().k[ti][ep][tile][ak][bkc][vec ? 1 : 0];
     // K-full variants: every stage inside K (for split-K, every slice: kchunk
     // is a multiple of BK, so K must be too).
-    if (ts.kind == KIND_DIRECT16 && p.K % ts.bk == 0) fn = kernels().kfull[ti][tile][ak][bkc];
+    if (ts.kind == KIND_DIRECT16 && p.K % ts.bk == 0) fn = kernels().kfull[ti][ep][tile][ak][bkc];
     if (!fn) return GEMM_ERR_UNSUPPORTED;
     void *args[] = {&a};
     const unsigned threads = ts.kind == KIND_STREAM ? 512u : (unsigned)(64 * ts.wgm * ts.wgn);

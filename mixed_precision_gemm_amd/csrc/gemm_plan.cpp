@@ -254,6 +254,16 @@ void free_plan_buffer(void *buf, int device) {
 
 }  // namespace
 
+extern "C" int gemm_f16f32_set_epilogue(gemm_f16f32_plan_t plan, const void *bias,
+                                        int activation) {
+    if (!plan) return GEMM_ERR_INVALID_ARG;
+    if (activation < ACT_NONE || activation > ACT_SILU) return GEMM_ERR_INVALID_ARG;
+    if ((uintptr_t)bias % 4 != 0) return GEMM_ERR_INVALID_ARG;
+    plan->bias = (const float *)bias;
+    plan->act = activation;
+    return GEMM_OK;
+}
+
 extern "C" int gemm_f16f32_destroy(gemm_f16f32_plan_t plan) {
     if (plan) {
         free_plan_buffer(plan->ws, plan->ws_device);

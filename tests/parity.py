@@ -17,6 +17,12 @@ is exact in fp32 just as a binary16 product is, so the same 2e-3 * S covers
 the fp32 sum; a bfloat16 C adds half a bfloat16 ulp, ulpbf16(x) =
 2^(max(floor(log2 x), -126) - 7), ulpbf16(0) = 2^-133, and overflows only
 from (2 - 2^-8) 2^127 on.
+
+Fused epilogue C = act(alpha A B + beta C + bias): S (from the oracle)
+includes |bias|, so 2e-3 S bounds the error of the pre-activation value x;
+an activation with Lipschitz constant L (ReLU 1, GELU and SiLU below 1.13)
+carries it into at most L * 2e-3 * S, and its fp32 evaluation (erfcf, expf
+and a division, a few ulp) adds 1e-5 |ref|.
 """
 import os
 
@@ -52,12 +58,18 @@ def ulpbf16(x):
     return np.where(x > 0, u, 2.0 ** -133)
 
 
-def check_bound(gpu, ref, scale, out_type, what=""):
+LIPSCHITZ = {0: 1.0, 1: 1.0, 2: 1.13, 3: 1.13}   # oracle.ACT_*
+
+
+def check_bound(gpu, ref, scale, out_type, what="", act=0):
     """Asserts the acceptance bound element-wise; returns the worst ratio
-    |gpu - ref| / bound over finite references."""
+    |gpu - ref| / bound over finite references.  act: the fused epilogue's
+    activation (oracle.ACT_*), 0 for none."""
     gpu = np.asarray(gpu, dtype=np.float64)
     assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
-    bound = REL_TOL * scale
+    bound = LIPSCHITZ[act] * REL_TOL * scale
+    if act != 0:
+        bound = bound + 1e-5 * np.abs(ref)
     if out_type == gi.OUT_F16:
         bound = bound + ulp16(ref)
     elif out_type == gi.OUT_BF16:
@@ -86,14 +98,18 @@ def to_device(case, device="cuda"):
     return (case.A.to(device), case.B.to(device), case.C.to(device))
 
 
-def run_case(case, dA=None, dB=None, dC=None, stream=None, alpha=None, beta=None):
-    """Runs a gemm_inputs.Case through the C ABI; returns the device C."""
+def run_case(case, dA=None, dB=None, dC=None, stream=None, alpha=None, beta=None,
+             bias=None, act=0):
+    """Runs a gemm_inputs.Case through the C ABI; returns the device C.
+    bias (a device float32 tensor) and act set the fused epilogue."""
     if dA is None:
         dA, dB, dC = to_device(case)
     p = mpg.Plan(case.M, case.N, case.K, case.layout_a, case.layout_b,
                  case.out_type, case.lda, case.ldb, case.ldc, case.batch,
                  case.stride_a, case.stride_b, case.stride_c, dtype=in_dtype(case))
     try:
+        if bias is not None or act != 0:
+            p.set_epilogue(bias, act)
         p.run(dA, dB, dC, case.alpha if alpha is None else alpha,
               case.beta if beta is None else beta, stream=stream)
     finally:
@@ -113,7 +129,7 @@ def c_logical(case, C_flat, rows=None):
     return C.to(torch.float64).numpy()
 
 
-def oracle_for(case, rows=None):
+def oracle_for(case, rows=None, bias=None, act=0):
     A = case.A.view(torch.int16).numpy().view(np.uint16)
     B = case.B.view(torch.int16).numpy().view(np.uint16)
     if case.out_type in (gi.OUT_F16, gi.OUT_BF16):
@@ -127,6 +143,7 @@ def oracle_for(case, rows=None):
                        lda=case.lda, ldb=case.ldb, ldc=case.ldc,
                        batch=case.batch, stride_a=case.stride_a,
                        stride_b=case.stride_b, stride_c=case.stride_c,
+                       bias=None if bias is None else bias.cpu().numpy()[:case.N], activation=act,
                        rows=rows, nthreads=oracle_threads())
 
 

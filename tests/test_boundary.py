@@ -234,3 +234,31 @@ def test_bf16_kernel_choice_matches_fp16(shape, kw):
     assert mpg.Plan(128, 128, 128, dtype="bf16").kernel.startswith("gemm_bf16_")
     with pytest.raises(ValueError):
         mpg.Plan(8, 8, 8, dtype="fp8")
+
+
+# ------------------------------------------------------------ fused epilogue
+
+def test_set_epilogue_validation():
+    from mixed_precision_gemm_amd import GEMM_ACT_GELU, GEMM_ACT_NONE, GEMM_ACT_SILU
+    assert mpg.gemm_f16f32_set_epilogue(None, None, GEMM_ACT_NONE) == GEMM_ERR_INVALID_ARG
+    with mpg.Plan(64, 64, 64) as p, mpg.Plan(64, 64, 64, dtype="bf16") as q:
+        for plan in (p, q):
+            assert mpg.gemm_f16f32_set_epilogue(plan.handle, None, GEMM_ACT_SILU) == GEMM_OK
+            assert mpg.gemm_f16f32_set_epilogue(plan.handle, 1 << 30, GEMM_ACT_GELU) == GEMM_OK
+            assert mpg.gemm_f16f32_set_epilogue(plan.handle, (1 << 30) + 2, 0) == GEMM_ERR_INVALID_ARG
+            assert mpg.gemm_f16f32_set_epilogue(plan.handle, None, 4) == GEMM_ERR_INVALID_ARG
+            assert mpg.gemm_f16f32_set_epilogue(plan.handle, None, -1) == GEMM_ERR_INVALID_ARG
+            assert mpg.gemm_f16f32_set_epilogue(plan.handle, None, GEMM_ACT_NONE) == GEMM_OK
+        with pytest.raises(mpg.GemmError):
+            p.set_epilogue(None, 9)
+
+
+def test_run_rejects_bias_overlapping_c_before_launch():
+    """The bias range [bias, bias + 4N) may not overlap C; checked before
+    any HIP call."""
+    base = 1 << 30
+    with mpg.Plan(64, 64, 64) as p:
+        C = base + (1 << 24)
+        assert mpg.gemm_f16f32_set_epilogue(p.handle, C + 64, 1) == GEMM_OK
+        assert mpg.gemm_f16f32_run(p.handle, base, base + (1 << 20), C, 1.0, 0.0,
+                                   None) == GEMM_ERR_INVALID_ARG
