@@ -28,6 +28,7 @@
  *            = B[b*stride_b + k + j*ldb]  (GEMM_COL_MAJOR, ldb >= K)
  *   C(b,i,j) = C[b*stride_c + i*ldc + j]  (always row-major, ldc >= N)
  *   C(b,i,j) <- fp32(alpha) * sum_k A(b,i,k) B(b,k,j) + fp32(beta) * C(b,i,j)
+ * (with a fused epilogue, gemm_f16f32_set_epilogue: act(... + bias[j])).
  * The sum is taken in fp32 in an order the kernel chooses; the fp32 result is
  * rounded once to binary16 (round to nearest even, overflow to +-inf) for a
  * binary16 C, or stored as is for an fp32 C.  When beta == 0, C is not read
