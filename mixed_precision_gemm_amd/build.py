@@ -2,6 +2,7 @@
 
     python -m mixed_precision_gemm_amd.build [--verbose]
 """
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -12,6 +13,10 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmpgemm.so")
 SOURCES = ["gemm_plan.cpp", "gemm_kernels.hip"]
+# gemm_kernels.hip is compiled in parts, in parallel: part 0 is the host code
+# and the kernel table, parts 1-4 the GEMM kernels of one input type and
+# epilogue flag each (see the top of that file).
+KERNEL_PARTS = 5
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -27,25 +32,40 @@ def _hipcc():
     return os.path.join(rocm, "bin", "hipcc")
 
 
+def _compile(src, obj, defines, extra_flags, verbose):
+    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    cmd = [_hipcc(), *HIPCC_FLAGS, *(extra_flags or []), *defines, "-I", INCLUDE,
+           "-I", CSRC, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    errs = "\n".join(l for l in r.stderr.splitlines()
+                     if "packed-fp32-ops" not in l)   # host-pass notice
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src} {' '.join(defines)}:\n{errs}")
+    return " ".join(cmd), errs
+
+
 def build(verbose: bool = False, extra_flags=None) -> str:
-    objs = []
     bdir = os.path.join(HERE, "_build")
     os.makedirs(bdir, exist_ok=True)
+    jobs = []
     for src in SOURCES:
-        obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
-        lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [_hipcc(), *HIPCC_FLAGS, *(extra_flags or []), "-I", INCLUDE,
-               "-I", CSRC, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        errs = "\n".join(l for l in r.stderr.splitlines()
-                         if "packed-fp32-ops" not in l)   # host-pass notice
-        if r.returncode != 0:
-            raise RuntimeError(f"hipcc failed on {src}:\n{errs}")
-        if verbose and errs.strip():
-            print(errs, file=sys.stderr)
-        objs.append(obj)
+        stem = os.path.splitext(src)[0]
+        if src.endswith(".hip"):
+            for part in range(KERNEL_PARTS):
+                jobs.append((src, os.path.join(bdir, f"{stem}_part{part}.o"),
+                             [f"-DMPGEMM_PART={part}"]))
+        else:
+            jobs.append((src, os.path.join(bdir, stem + ".o"), []))
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        futs = [ex.submit(_compile, s, o, d, extra_flags, verbose) for s, o, d in jobs]
+        for f in futs:
+            cmd, errs = f.result()
+            if verbose:
+                print(cmd, flush=True)
+                if errs.strip():
+                    print(errs, file=sys.stderr)
+    objs = [o for _, o, _ in jobs]
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs,
            "-o", LIB + ".tmp"]
     if verbose:

@@ -49,23 +49,17 @@
 #include "gemm_f16f32.h"
 #include "gemm_internal.h"
 
-using namespace mpgemm;
+// The library is built either as one translation unit (MPGEMM_PART unset)
+// or in parts compiled in parallel from this same file: part 0 holds the
+// host code, the kernel table and the copy kernel; parts 1-4 instantiate the
+// GEMM kernels of one input type and epilogue flag each (fp16 plain, fp16
+// epilogue, bf16 plain, bf16 epilogue) and fill their entries of the table.
+#ifndef MPGEMM_PART
+#define MPGEMM_PART -1
+#endif
+#define MPGEMM_HOST_PART (MPGEMM_PART <= 0)
 
-namespace {
-
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-// Byte offset that fails the buffer range check: the load returns zeros.
-constexpr uint32_t kOutOfRange = 0x80000000u;
-// Word 3 of a gfx9 buffer descriptor: 32-bit data format, raw addressing.
-constexpr int kRsrcWord3 = 0x00020000;
+namespace mpgemm {
 
 struct GemmArgs {
     const uint16_t *A;            // 16-bit elements of the kernel's input type
@@ -95,6 +89,37 @@ struct GemmArgs {
     float *ws;
     int *ws_count;
 };
+
+typedef void (*KernelFn)(GemmArgs);
+typedef KernelFn TileKernels[NUM_TILES][2][2][2];   // [tile][A K-contig][B K-contig][vec]
+typedef KernelFn FullKernels[NUM_TILES][2][2];      // K a multiple of BK: [tile][A][B]
+
+// Table entries of one input type and epilogue flag (one part each).
+void fill_kernels_f16_plain(TileKernels &k, FullKernels &kfull);
+void fill_kernels_f16_epi(TileKernels &k, FullKernels &kfull);
+void fill_kernels_bf16_plain(TileKernels &k, FullKernels &kfull);
+void fill_kernels_bf16_epi(TileKernels &k, FullKernels &kfull);
+
+}  // namespace mpgemm
+
+using namespace mpgemm;
+
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Byte offset that fails the buffer range check: the load returns zeros.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+// Word 3 of a gfx9 buffer descriptor: 32-bit data format, raw addressing.
+constexpr int kRsrcWord3 = 0x00020000;
+
 
 // Restricts the arguments to K slice `slice` (split-K): operands advance by
 // the slice's first K index, K shrinks to the slice.
@@ -1484,6 +1509,7 @@ __global__ __launch_bounds__(512) void gemm_stream(GemmArgs pin) {
     }
 }
 
+#if MPGEMM_HOST_PART
 // ---------------------------------------------------------------------------
 // Repacking of an operand whose rows are not 16-byte aligned ([GEMM] §3.4:
 // edges are handled by zero padding).  Copies `outer` rows of `cols`
@@ -1552,7 +1578,7 @@ __global__ __launch_bounds__(256) void gemm_pack16(PackArgs a) {
     }
 }
 
-typedef void (*KernelFn)(GemmArgs);
+#endif  // MPGEMM_HOST_PART
 
 template <typename TI, bool EPI, int T, bool AK, bool BKC, bool VEC>
 constexpr KernelFn pick_staged() {
@@ -1607,7 +1633,7 @@ void fill_stream(KernelFn (&t)[2][2][2]) {
 }
 
 template <typename TI, bool EPI>
-void fill_type(KernelFn (&k)[NUM_TILES][2][2][2], KernelFn (&kfull)[NUM_TILES][2][2]) {
+void fill_type(TileKernels &k, FullKernels &kfull) {
     for (auto &t : kfull)
         t[0][0] = t[0][1] = t[1][0] = t[1][1] = nullptr;
     fill_kfull<TI, EPI, TILE_256x256>(kfull[TILE_256x256]);
@@ -1625,14 +1651,32 @@ void fill_type(KernelFn (&k)[NUM_TILES][2][2][2], KernelFn (&kfull)[NUM_TILES][2
     fill_stream<TI, EPI, TILE_STREAM32W>(k[TILE_STREAM32W]);
 }
 
+}  // namespace
+
+#if MPGEMM_PART < 0 || MPGEMM_PART == 1
+void mpgemm::fill_kernels_f16_plain(TileKernels &k, FullKernels &kfull) { fill_type<_Float16, false>(k, kfull); }
+#endif
+#if MPGEMM_PART < 0 || MPGEMM_PART == 2
+void mpgemm::fill_kernels_f16_epi(TileKernels &k, FullKernels &kfull) { fill_type<_Float16, true>(k, kfull); }
+#endif
+#if MPGEMM_PART < 0 || MPGEMM_PART == 3
+void mpgemm::fill_kernels_bf16_plain(TileKernels &k, FullKernels &kfull) { fill_type<__bf16, false>(k, kfull); }
+#endif
+#if MPGEMM_PART < 0 || MPGEMM_PART == 4
+void mpgemm::fill_kernels_bf16_epi(TileKernels &k, FullKernels &kfull) { fill_type<__bf16, true>(k, kfull); }
+#endif
+
+#if MPGEMM_HOST_PART
+namespace {
+
 struct KernelTable {
-    KernelFn k[2][2][NUM_TILES][2][2][2];
+    KernelFn k[2][2][NUM_TILES][2][2][2];    // [input type][epilogue][tile][A][B][vec]
     KernelFn kfull[2][2][NUM_TILES][2][2];   // direct tiles with K a multiple of BK (else null)
     KernelTable() {
-        fill_type<_Float16, false>(k[IN_F16][0], kfull[IN_F16][0]);
-        fill_type<_Float16, true>(k[IN_F16][1], kfull[IN_F16][1]);
-        fill_type<__bf16, false>(k[IN_BF16][0], kfull[IN_BF16][0]);
-        fill_type<__bf16, true>(k[IN_BF16][1], kfull[IN_BF16][1]);
+        fill_kernels_f16_plain(k[IN_F16][0], kfull[IN_F16][0]);
+        fill_kernels_f16_epi(k[IN_F16][1], kfull[IN_F16][1]);
+        fill_kernels_bf16_plain(k[IN_BF16][0], kfull[IN_BF16][0]);
+        fill_kernels_bf16_epi(k[IN_BF16][1], kfull[IN_BF16][1]);
     }
 };
 
@@ -1823,3 +1867,5 @@ extern "C" int gemm_bf16f32_run(gemm_f16f32_plan_t plan, const void *A,
     if (!plan || plan->in_type != IN_BF16) return GEMM_ERR_INVALID_ARG;
     return run_plan(plan, A, B, C, alpha, beta, stream);
 }
+
+#endif  // MPGEMM_HOST_PART
