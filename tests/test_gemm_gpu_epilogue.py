@@ -143,3 +143,13 @@ def test_epilogue_torch_wrapper():
     ref, scale = oracle_for(case, bias=bias, act=SILU)
     check_bound(C.cpu().to(torch.float64).numpy()[None], ref, scale, OUT_F16, "wrapper silu",
                 act=SILU)
+
+
+@pytest.mark.parametrize("act", ACTS)
+def test_epilogue_degenerate_sizes(act):
+    """K = 0: C = act(beta C + bias); M = 0: no-op even with an epilogue."""
+    case = gi.make_case(300, 136, 0, lda=1, beta=1.5, seed=102)
+    epilogue_parity(case, act, what=f"K=0 {ANAME[act]}")
+    with mpg.Plan(0, 64, 64) as p:
+        p.set_epilogue(None, act)
+        p.run(0, 0, 0, 1.0, 0.0)
