@@ -56,7 +56,8 @@
  * (all-ones, identity, K = 1) and integer-exact inputs; for bfloat16,
  * exhaustive decode against the upper half of binary32, encode against
  * torch's round-to-nearest-even, the format's landmarks and the same brute
- * force.
+ * force; for the epilogue, the activations against scipy (ndtr, expit), their
+ * odd-part identities, Phi(1) and sigma(1), and exact brute force with a bias.
  */
 #include <math.h>
 #include <pthread.h>
