@@ -162,7 +162,9 @@ int gemm_f16f32_run(gemm_f16f32_plan_t plan,
  *   activation  GEMM_ACT_*.
  * Host only, no HIP call.  NULL plan, a misaligned bias or an unknown
  * activation -> INVALID_ARG (the plan is left unchanged).  Setting NULL and
- * GEMM_ACT_NONE restores the plain GEMM.  Changing the epilogue of a plan
+ * GEMM_ACT_NONE restores the plain GEMM.  A plan with an epilogue runs the
+ * epilogue form of the same kernel; gemm_f16f32_plan_kernel reports the same
+ * name.  Changing the epilogue of a plan
  * while one of its runs may still be launched from another thread is a race.
  */
 int gemm_f16f32_set_epilogue(gemm_f16f32_plan_t plan, const void *bias, int activation);
