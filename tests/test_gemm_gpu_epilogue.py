@@ -62,6 +62,8 @@ FAMILIES = [
     ((40, 4096, 1024), dict(layout_b=COL_MAJOR), "stream64x16", False),
     ((127, 257, 33), {}, "narrow", False),
     ((64, 96, 200), dict(layout_a=COL_MAJOR, layout_b=COL_MAJOR), "vec16", False),
+    ((4097, 63, 1025), {}, "_sk2_pkab", False),                   # repacked, split-K
+    ((7, 4097, 4099), dict(layout_b=COL_MAJOR), "stream16x16_nt_direct_pkab", False),
 ]
 
 
@@ -153,3 +155,28 @@ def test_epilogue_degenerate_sizes(act):
     with mpg.Plan(0, 64, 64) as p:
         p.set_epilogue(None, act)
         p.run(0, 0, 0, 1.0, 0.0)
+
+
+def _sweep_with_epilogue(n, seed):
+    """The plain GEMM sweep's seeded shapes (every kernel class, random
+    layouts, padding, batch, alpha/beta), each with a random activation and
+    input type and a bias on two cases of three."""
+    from test_gemm_gpu import _sweep_cases
+    rng = np.random.default_rng(seed)
+    return [(args, int(rng.integers(0, 4)), bool(rng.random() < 0.67),
+             "bf16" if rng.random() < 0.4 else "f16") for args in _sweep_cases(n, seed)]
+
+
+@pytest.mark.parametrize("sweep", _sweep_with_epilogue(24, 4242))
+def test_epilogue_random_sweep(sweep):
+    (M, N, K, la, lb, pad, batch, out_type, alpha, beta), act, with_bias, dt = sweep
+    lda = (K if la == ROW_MAJOR else M) + pad
+    ldb = (N if lb == ROW_MAJOR else K) + pad
+    if dt == "bf16" and out_type == OUT_F16:
+        out_type = OUT_BF16
+    case = gi.make_case(M, N, K, layout_a=la, layout_b=lb, out_type=out_type, alpha=alpha,
+                        beta=beta, batch=batch, lda=lda, ldb=ldb, in_dtype=dt,
+                        seed=(M * 7919 + N * 31 + K) % 1000)
+    rows = None if M * N * K * batch <= (1 << 27) else sample_rows(M, n_random=16, tiles=(256, 128))
+    epilogue_parity(case, act, rows=rows, with_bias=with_bias,
+                    what=f"{kernel_of(case)} {sweep}")
