@@ -177,3 +177,44 @@ def test_bf16_torch_wrapper_views():
     check_bound(C.cpu().to(torch.float64).numpy()[None], ref, scale, OUT_BF16, "bf16 wrapper")
     with pytest.raises(TypeError):
         mpg.gemm(A, Bt.t().to(torch.float16))
+
+
+def _bf16_sweep(n, seed):
+    from test_gemm_gpu import _sweep_cases
+    return _sweep_cases(n, seed)
+
+
+@pytest.mark.parametrize("case_args", _bf16_sweep(24, 3131))
+def test_bf16_random_sweep(case_args):
+    """The plain sweep's seeded shapes (every kernel class, random layouts,
+    padding, batch, alpha/beta, output type) in bfloat16."""
+    M, N, K, la, lb, pad, batch, out_type, alpha, beta = case_args
+    lda = (K if la == ROW_MAJOR else M) + pad
+    ldb = (N if lb == ROW_MAJOR else K) + pad
+    case = bf16_case(M, N, K, layout_a=la, layout_b=lb,
+                     out_type=OUT_BF16 if out_type == 0 else OUT_F32, alpha=alpha, beta=beta,
+                     batch=batch, lda=lda, ldb=ldb, seed=(M * 7919 + N * 31 + K) % 1000)
+    rows = None if M * N * K * batch <= (1 << 27) else sample_rows(M, n_random=16, tiles=(256, 128))
+    parity(case, rows=rows, what=f"{kernel_of(case)} {case_args}")
+
+
+@pytest.mark.parametrize("epilogue", [False, True])
+def test_bf16_run_to_run_bitwise_determinism(epilogue):
+    """Same plan and inputs: bitwise identical bf16 output on repeated runs
+    and on another stream, with and without a fused epilogue (split-K plan)."""
+    case = bf16_case(256, 384, 8192, beta=1.0, seed=17)
+    assert "_sk" in kernel_of(case)
+    dA, dB, dC0 = case.A.cuda(), case.B.cuda(), case.C.cuda()
+    bias = torch.linspace(-1, 1, case.N, device="cuda")
+    s2 = torch.cuda.Stream()
+    outs = []
+    with mpg.Plan(case.M, case.N, case.K, dtype="bf16") as p:
+        if epilogue:
+            p.set_epilogue(bias, mpg.GEMM_ACT_GELU)
+        for stream in (None, None, s2):
+            dC = dC0.clone()
+            torch.cuda.synchronize()
+            p.run(dA, dB, dC, 1.0, 1.0, stream=stream)
+            torch.cuda.synchronize()
+            outs.append(dC.cpu().view(torch.int16))
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
