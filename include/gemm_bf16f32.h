@@ -17,13 +17,14 @@
  *             (wide range, coarse precision); §1.3 and §3.4 fix the problem and
  *             the edge rule exactly as for fp16.
  * Everything gemm_f16f32.h states about semantics, leading dimensions,
- * batches, alignment, repacking, plan-owned device buffers, streams and
+ * batches, alignment, repacking, the caller-owned workspace, streams and
  * errors holds here unchanged, with "binary16" read as "bfloat16".  The
  * fp32 result is rounded once to bfloat16 (round to nearest even; overflow
  * to +-inf) for a bfloat16 C.
  *
  * A bfloat16 plan is a gemm_f16f32_plan_t made by gemm_bf16f32_plan.  It is
  * run with gemm_bf16f32_run and freed with gemm_f16f32_destroy;
+ * gemm_f16f32_workspace_size, gemm_f16f32_workspace_init,
  * gemm_f16f32_plan_kernel and gemm_f16f32_status_string serve both kinds of
  * plan (kernel names of bfloat16 plans start "gemm_bf16_").  Passing a plan
  * to the run function of the other input type -> GEMM_ERR_INVALID_ARG.
@@ -61,13 +62,16 @@ int gemm_bf16f32_plan(gemm_f16f32_plan_t *out,
  *   C      device pointer to bfloat16 or fp32 storage, read (beta != 0) and
  *          written.
  *   alpha, beta  fp32 scalars, by value.
+ *   workspace, workspace_bytes  as gemm_f16f32_run (sized by
+ *          gemm_f16f32_workspace_size on this plan).
  *   stream a hipStream_t; NULL means the default stream.
  * Rules and status codes as gemm_f16f32_run; a plan made by
  * gemm_f16f32_plan -> INVALID_ARG (nothing is launched).
  */
 int gemm_bf16f32_run(gemm_f16f32_plan_t plan,
                      const void *A, const void *B, void *C,
-                     float alpha, float beta, void *stream);
+                     float alpha, float beta,
+                     void *workspace, int64_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

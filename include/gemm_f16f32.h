@@ -37,24 +37,29 @@
  * A column-major C is obtained by the caller by swapping operands
  * (C^T = B^T A^T).
  *
- * Ownership: the caller owns A, B, C and the stream.  A plan owns its host
- * memory and up to two device buffers, each allocated on the current device
- * by the first run that needs it and freed by gemm_f16f32_destroy:
- *   - split-K (kernel name contains "_sk<slices>"): fp32 partial tiles
- *     (slices x tiles x 64 KiB, plus 4 bytes per tile), cleared when
- *     allocated;
- *   - repacking (kernel name ends in "_pka", "_pkb" or "_pkab", or a run of a
- *     direct or streaming plan given an A or B pointer that is not 16-byte
- *     aligned): dense copies of A and B with rows padded to a multiple of 8
- *     elements (2 x batch x rows x padded row length bytes for A and B
- *     together, at most).
- * Runs of one plan that holds such a buffer share it: they may follow each
- * other on a stream but must not execute concurrently (on two streams at
- * once); a plan with neither may be run concurrently on several streams.
- * gemm_f16f32_run is asynchronous on the given stream: A, B, C must stay
- * valid until the stream has passed the launched kernels.  A plan may be
- * destroyed as soon as gemm_f16f32_run returns; destroying a plan that holds
- * a device buffer first waits for the device to finish its work.
+ * Ownership: the caller owns A, B, C, the stream and the workspace.  A plan
+ * is host memory only: planning, running and destroying it allocate no device
+ * memory, and no entry point synchronises the device or a stream.  A plan is
+ * immutable once made (except through gemm_f16f32_set_epilogue), so one plan
+ * may be run concurrently on several streams, each run with its own workspace.
+ *
+ * Workspace: some plans need device scratch memory, supplied by the caller to
+ * every run (gemm_f16f32_workspace_size gives the bytes; 0 means none):
+ *   - split-K (kernel name contains "_sk<slices>"): one word per output tile,
+ *     counting the K slices that have finished it, in the first 4096 bytes,
+ *     then slices x tiles x 64 KiB of fp32 partial tiles;
+ *   - repacking (kernel name ends in "_pka", "_pkb" or "_pkab"): dense copies
+ *     of the operands whose rows do not allow 128-bit loads, rows padded to a
+ *     multiple of 8 elements.
+ * The workspace is 256-byte aligned and belongs to one run at a time: runs
+ * that may execute at the same time (on different streams) need distinct
+ * workspaces.  The counter words (bytes 0..4095) must be zero when a split-K
+ * run starts; every split-K run leaves them zero when it ends.  A buffer
+ * zero-filled once (gemm_f16f32_workspace_init, hipMemset, a zeroed tensor)
+ * therefore serves any sequence of runs of any plans.
+ * gemm_f16f32_run is asynchronous on the given stream: A, B, C and the
+ * workspace must stay valid until the stream has passed the launched kernels.
+ * A plan may be destroyed as soon as gemm_f16f32_run returns.
  *
  * Errors: every function returns a status code (GEMM_OK == 0 or a negative
  * GEMM_ERR_*); no exception crosses this boundary and there is no global
@@ -83,7 +88,7 @@ enum {
     GEMM_ERR_INVALID_ARG = -1,  /* argument violates a rule stated below    */
     GEMM_ERR_UNSUPPORTED = -2,  /* valid but outside what the kernels cover */
     GEMM_ERR_HIP = -3,          /* the HIP runtime refused the launch       */
-    GEMM_ERR_NOMEM = -4         /* host or workspace allocation failed      */
+    GEMM_ERR_NOMEM = -4         /* host allocation of a plan failed         */
 };
 
 /*
@@ -103,8 +108,12 @@ enum {
  *                       ignored when batch == 1; must be >= 0, and
  *                       stride_c must be at least M*ldc (batch items of C may
  *                       not overlap), else INVALID_ARG.
- * Offsets that do not fit the kernels' 32-bit per-tile addressing
- * (an operand's leading dimension above 2^22 elements) -> UNSUPPORTED.
+ * Leading dimensions of any size are accepted.  The kernels address an
+ * operand tile with 32-bit byte offsets, so an A or B whose leading dimension
+ * exceeds 2^22 elements is copied into the workspace (both operands are then
+ * repacked) before the product; an operand row or column that is itself
+ * longer than 2^22 elements (lda > 2^22 would then be unavoidable) ->
+ * UNSUPPORTED.
  */
 int gemm_f16f32_plan(gemm_f16f32_plan_t *out,
                      int64_t M, int64_t N, int64_t K,
@@ -114,30 +123,59 @@ int gemm_f16f32_plan(gemm_f16f32_plan_t *out,
                      int64_t stride_c);
 
 /*
+ * Device workspace, in bytes, that gemm_f16f32_run needs for this plan
+ * (0: none; the plan runs with workspace == NULL).
+ *   flags  0: operands at 16-byte-aligned addresses (torch allocations are).
+ *          GEMM_WS_ANY_ALIGNMENT: enough to also repack operands whose
+ *          pointers turn out not to be 16-byte aligned at run time (a run
+ *          given less reads such operands in place with element-wide loads:
+ *          correct, slower).
+ *   bytes  receives the size.
+ * Host only, no HIP call.  NULL plan or bytes, unknown flags -> INVALID_ARG.
+ */
+enum { GEMM_WS_ANY_ALIGNMENT = 1 };
+int gemm_f16f32_workspace_size(gemm_f16f32_plan_t plan, int flags, int64_t *bytes);
+
+/*
+ * Prepares a workspace for its first run: zero-fills its counter words
+ * (the first min(bytes, 4096) bytes) with one small kernel launched on
+ * `stream`, asynchronously.  Nothing is allocated.  Needed once per buffer
+ * (runs leave the counters zero); a buffer already zero-filled needs no call.
+ *   workspace  device pointer (256-byte aligned), or NULL when bytes == 0.
+ * NULL with bytes > 0, bytes < 0 or a misaligned pointer -> INVALID_ARG;
+ * a failed launch -> GEMM_ERR_HIP.
+ */
+int gemm_f16f32_workspace_init(void *workspace, int64_t bytes, void *stream);
+
+/*
  * Runs a plan: launches its kernels on `stream` (the GEMM, preceded by one
- * copy kernel per repacked operand) and returns without waiting.
+ * copy kernel when operands are repacked) and returns without waiting.  No
+ * device memory is allocated and nothing is synchronised.
  *   A, B   device pointers to binary16 storage (const), described by the plan.
  *   C      device pointer to binary16 or fp32 storage, read (beta != 0) and
  *          written.
  *   alpha, beta  fp32 scalars, by value.
+ *   workspace, workspace_bytes  device scratch owned by the caller (see
+ *          Ownership): at least gemm_f16f32_workspace_size(plan, 0) bytes,
+ *          256-byte aligned, counter words zero; NULL and 0 for a plan that
+ *          needs none.
  *   stream a hipStream_t; NULL means the default stream.
  * Rules: plan != NULL; A, B, C non-NULL unless the plan's M*N == 0 (then the
  * call is a no-op and returns GEMM_OK) -- else INVALID_ARG.  The address range
- * of C must not overlap those of A or B -> INVALID_ARG.  Pointer alignment is
- * never an error: 16-byte-aligned operands whose leading dimensions,
- * contiguous extents and batch strides are multiples of 8 are read in place
- * with 128-bit loads; other operands are either copied first into the
- * plan's padded buffer (direct and streaming kernels) or read with
- * element-wide loads (the small staged tiles, which do not split K), with
- * the same results up to summation order.  The first run that needs a
- * device buffer allocates it (failure -> NOMEM; the split-K buffer's first
- * run also synchronises the device once); running the plan later on another
- * device than the one holding the buffer -> INVALID_ARG.  A failed launch ->
+ * of C must not overlap those of A, B or the workspace -> INVALID_ARG.  A
+ * workspace smaller than the plan needs, misaligned or NULL with a nonzero
+ * size -> INVALID_ARG.  Pointer alignment of A and B is never an error:
+ * 16-byte-aligned operands whose leading dimensions, contiguous extents and
+ * batch strides are multiples of 8 are read in place with 128-bit loads;
+ * others are either copied first into the workspace (direct and streaming
+ * kernels, when the workspace holds the copy) or read with element-wide
+ * loads, with the same results up to summation order.  A failed launch ->
  * GEMM_ERR_HIP.
  */
 int gemm_f16f32_run(gemm_f16f32_plan_t plan,
                     const void *A, const void *B, void *C,
-                    float alpha, float beta, void *stream);
+                    float alpha, float beta,
+                    void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
  * Sets the plan's fused epilogue, used by every later run of the plan:
@@ -169,8 +207,8 @@ int gemm_f16f32_run(gemm_f16f32_plan_t plan,
  */
 int gemm_f16f32_set_epilogue(gemm_f16f32_plan_t plan, const void *bias, int activation);
 
-/* Frees a plan (and its device buffers, after waiting for the device to
- * finish its work).  NULL is a no-op.  Returns GEMM_OK. */
+/* Frees a plan (host memory only; runs already launched are unaffected).
+ * NULL is a no-op.  Returns GEMM_OK. */
 int gemm_f16f32_destroy(gemm_f16f32_plan_t plan);
 
 /* A static, NUL-terminated description of a status code (never NULL). */

@@ -5,7 +5,8 @@ include/gemm_bf16f32.h: the functions below carry the same names and
 arguments as the C entry points, and
 every step of the computation runs in the HIP kernels of libmpgemm.so.  There
 is no fallback: if the library is missing, loading raises.  torch is used only
-for device buffers and streams (in `gemm`, the convenience wrapper).
+for device buffers (operands and the caller-owned workspace) and streams, in
+the convenience layer (`Plan`, `gemm`).
 """
 import ctypes
 import os
@@ -21,10 +22,12 @@ GEMM_ERR_INVALID_ARG = -1
 GEMM_ERR_UNSUPPORTED = -2
 GEMM_ERR_HIP = -3
 GEMM_ERR_NOMEM = -4
+GEMM_WS_ANY_ALIGNMENT = 1
 
 EXPORTED = ("gemm_f16f32_plan", "gemm_f16f32_run", "gemm_f16f32_destroy",
             "gemm_f16f32_status_string", "gemm_f16f32_plan_kernel",
-            "gemm_bf16f32_plan", "gemm_bf16f32_run", "gemm_f16f32_set_epilogue")
+            "gemm_bf16f32_plan", "gemm_bf16f32_run", "gemm_f16f32_set_epilogue",
+            "gemm_f16f32_workspace_size", "gemm_f16f32_workspace_init")
 
 _lib = None
 
@@ -52,8 +55,12 @@ def library() -> ctypes.CDLL:
                                 i64, i64, i64, i64, i64, i64, i64]
             plan_fn.restype = ctypes.c_int
             run_fn = getattr(lib, f"gemm_{fam}_run")
-            run_fn.argtypes = [vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp]
+            run_fn.argtypes = [vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp, i64, vp]
             run_fn.restype = ctypes.c_int
+        lib.gemm_f16f32_workspace_size.argtypes = [vp, ctypes.c_int, ctypes.POINTER(i64)]
+        lib.gemm_f16f32_workspace_size.restype = ctypes.c_int
+        lib.gemm_f16f32_workspace_init.argtypes = [vp, i64, vp]
+        lib.gemm_f16f32_workspace_init.restype = ctypes.c_int
         lib.gemm_f16f32_set_epilogue.argtypes = [vp, vp, ctypes.c_int]
         lib.gemm_f16f32_set_epilogue.restype = ctypes.c_int
         lib.gemm_f16f32_destroy.argtypes = [vp]
@@ -78,9 +85,24 @@ def gemm_f16f32_plan(M, N, K, layout_a, layout_b, out_type, lda, ldb, ldc,
     return st, (h.value if st == GEMM_OK else None)
 
 
-def gemm_f16f32_run(plan, A, B, C, alpha, beta, stream=None):
-    """A, B, C: device addresses (ints); stream: hipStream_t as int or None."""
-    return library().gemm_f16f32_run(plan, A, B, C, alpha, beta, stream)
+def gemm_f16f32_run(plan, A, B, C, alpha, beta, workspace=None, workspace_bytes=0,
+                    stream=None):
+    """A, B, C, workspace: device addresses (ints; workspace None when the
+    plan needs none); stream: hipStream_t as int or None."""
+    return library().gemm_f16f32_run(plan, A, B, C, alpha, beta, workspace,
+                                     workspace_bytes, stream)
+
+
+def gemm_f16f32_workspace_size(plan, flags=0):
+    """Returns (status, bytes)."""
+    n = ctypes.c_int64(-1)
+    st = library().gemm_f16f32_workspace_size(plan, flags, ctypes.byref(n))
+    return st, n.value
+
+
+def gemm_f16f32_workspace_init(workspace, nbytes, stream=None):
+    """Zero-fills the workspace's counter words on the stream (no allocation)."""
+    return library().gemm_f16f32_workspace_init(workspace, nbytes, stream)
 
 
 def gemm_bf16f32_plan(M, N, K, layout_a, layout_b, out_type, lda, ldb, ldc,
@@ -94,9 +116,11 @@ def gemm_bf16f32_plan(M, N, K, layout_a, layout_b, out_type, lda, ldb, ldc,
     return st, (h.value if st == GEMM_OK else None)
 
 
-def gemm_bf16f32_run(plan, A, B, C, alpha, beta, stream=None):
+def gemm_bf16f32_run(plan, A, B, C, alpha, beta, workspace=None, workspace_bytes=0,
+                     stream=None):
     """Runs a plan made by gemm_bf16f32_plan (device addresses as ints)."""
-    return library().gemm_bf16f32_run(plan, A, B, C, alpha, beta, stream)
+    return library().gemm_bf16f32_run(plan, A, B, C, alpha, beta, workspace,
+                                      workspace_bytes, stream)
 
 
 def gemm_f16f32_set_epilogue(plan, bias, activation):
@@ -121,7 +145,14 @@ def gemm_f16f32_plan_kernel(plan):
 class Plan:
     """Owns a plan handle; `run` launches on a stream (torch's current one by
     default).  dtype: "f16" (binary16 A and B, C binary16 or fp32) or
-    "bf16" (bfloat16 A and B; out_type defaults to GEMM_OUT_BF16)."""
+    "bf16" (bfloat16 A and B; out_type defaults to GEMM_OUT_BF16).
+
+    The workspace a run needs is the caller's: pass one (a zero-filled CUDA
+    tensor of at least `workspace_bytes()` bytes, or a raw address with its
+    size) to `run`, or let the Plan keep its own -- a zero-filled torch
+    tensor, made on first need and enlarged when misaligned operands call
+    for room to repack them -- used by the runs that pass none.  Runs that
+    may execute at the same time need distinct workspaces."""
 
     def __init__(self, M, N, K, layout_a=GEMM_ROW_MAJOR, layout_b=GEMM_ROW_MAJOR,
                  out_type=None, lda=None, ldb=None, ldc=None, batch=1,
@@ -143,16 +174,46 @@ class Plan:
         self.handle = h
         self.shape = (M, N, K)
         self.kernel = gemm_f16f32_plan_kernel(h)
+        self._ws = None
 
-    def run(self, A, B, C, alpha=1.0, beta=0.0, stream=None):
-        """A, B, C: torch tensors (device) or raw device addresses."""
+    def workspace_bytes(self, flags=0):
+        st, n = gemm_f16f32_workspace_size(self.handle, flags)
+        if st != GEMM_OK:
+            raise GemmError(st, "gemm_f16f32_workspace_size")
+        return n
+
+    def _own_workspace(self, A, B, device):
+        """The Plan's own workspace, large enough for these operands."""
+        import torch
+        ptr = lambda t: t if isinstance(t, int) else t.data_ptr()
+        misaligned = ptr(A) % 16 != 0 or ptr(B) % 16 != 0
+        need = self.workspace_bytes(GEMM_WS_ANY_ALIGNMENT if misaligned else 0)
+        if need == 0:
+            return None, 0
+        if self._ws is None or self._ws.numel() < need:
+            # zero-filled on torch's current stream: the counter words start at 0
+            self._ws = torch.zeros(need, dtype=torch.uint8, device=device)
+        return self._ws.data_ptr(), self._ws.numel()
+
+    def run(self, A, B, C, alpha=1.0, beta=0.0, stream=None, workspace=None,
+            workspace_bytes=None):
+        """A, B, C: torch tensors (device) or raw device addresses.  workspace:
+        a CUDA tensor, a raw address (with workspace_bytes), or None for the
+        Plan's own."""
         ptr = lambda t: t if isinstance(t, int) or t is None else t.data_ptr()
+        import torch
         if stream is None:
-            import torch
             stream = torch.cuda.current_stream().cuda_stream
         elif not isinstance(stream, int):
             stream = stream.cuda_stream
-        st = self._run(self.handle, ptr(A), ptr(B), ptr(C), alpha, beta, stream)
+        if workspace is None:
+            dev = C.device if hasattr(C, "device") else torch.device("cuda", torch.cuda.current_device())
+            ws, nbytes = self._own_workspace(A, B, dev)
+        elif isinstance(workspace, int):
+            ws, nbytes = workspace, int(workspace_bytes or 0)
+        else:
+            ws, nbytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+        st = self._run(self.handle, ptr(A), ptr(B), ptr(C), alpha, beta, ws, nbytes, stream)
         if st != GEMM_OK:
             raise GemmError(st, self._run.__name__)
 
@@ -174,6 +235,7 @@ class Plan:
         if self.handle is not None:
             gemm_f16f32_destroy(self.handle)
             self.handle = None
+        self._ws = None
 
     def __del__(self):
         try:
@@ -235,9 +297,23 @@ def gemm(A, B, C=None, alpha=1.0, beta=0.0, out_dtype=None, bias=None,
     sa = A.stride(0) if batched else 0
     sb = B.stride(0) if batched else 0
     sc = C.stride(0) if batched else 0
-    with Plan(M, N, K, la[0], lb[0], out_type, la[1], lb[1], ldc, batch,
-              sa, sb, sc, dtype=dtype) as p:
-        if bias is not None or activation != GEMM_ACT_NONE:
-            p.set_epilogue(bias, activation)
-        p.run(A, B, C, alpha, beta)
+    key = (M, N, K, la, lb, out_type, ldc, batch, sa, sb, sc, dtype, C.device)
+    p = _plan_cache.get(key)
+    if p is None:
+        if len(_plan_cache) >= _PLAN_CACHE_SIZE:
+            _plan_cache.pop(next(iter(_plan_cache))).close()
+        p = Plan(M, N, K, la[0], lb[0], out_type, la[1], lb[1], ldc, batch,
+                 sa, sb, sc, dtype=dtype)
+        _plan_cache[key] = p
+    # The epilogue is part of the plan: set for this call (host only).
+    p.set_epilogue(bias, activation)
+    p.run(A, B, C, alpha, beta)
     return C
+
+
+# Plans (with their workspaces) of recent `gemm` calls, by problem description.
+# Runs of one cached plan on the same stream share its workspace in order; a
+# caller that runs the same shape on several streams at once should make its
+# own Plan per stream.
+_PLAN_CACHE_SIZE = 64
+_plan_cache = {}

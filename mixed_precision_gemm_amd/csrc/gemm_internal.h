@@ -67,6 +67,27 @@ enum InputType : int { IN_F16 = 0, IN_BF16 = 1 };
 // Activation of the fused epilogue (the values of GEMM_ACT_*).
 enum Activation : int { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2, ACT_SILU = 3 };
 
+// Workspace layout (caller-owned device memory, 256-byte aligned):
+//   [0, 4096)                        split-K arrival counters, one int per tile
+//                                    (zero between runs);
+//   [4096, 4096 + split_bytes)       split-K fp32 partial tiles;
+//   then, 256-byte aligned           the packed copy of A, then that of B
+//                                    (only those the run makes).
+// A plan that needs neither needs no workspace.  The counter area is reserved
+// whenever a workspace is used, so copies never land on another plan's
+// counters when runs of several plans share one buffer.
+constexpr int64_t kCounterBytes = 4096;
+constexpr int kMaxCounters = (int)(kCounterBytes / 4);
+
+// Workspace bytes of a run that splits K (split_bytes) and repacks the
+// operands in pack_mask (bit 0 A, bit 1 B); 0 if it does neither.
+inline int64_t workspace_bytes(int64_t split_bytes, int pack_mask, int64_t pack_a_bytes,
+                               int64_t pack_b_bytes) {
+    const int64_t packs = ((pack_mask & 1) ? pack_a_bytes : 0) + ((pack_mask & 2) ? pack_b_bytes : 0);
+    if (split_bytes == 0 && packs == 0) return 0;
+    return kCounterBytes + split_bytes + packs;
+}
+
 }  // namespace mpgemm
 
 struct gemm_f16f32_plan_s {
@@ -81,19 +102,16 @@ struct gemm_f16f32_plan_s {
     int64_t extent_a, extent_b, extent_c;  // elements spanned by each operand
     int ksplit;            // K slices per output tile (split-K when > 1)
     int64_t kchunk;        // K indices per slice, a multiple of 64
-    int64_t ws_bytes;      // workspace: ksplit * tiles fp32 partial tiles + tile counters
-    void *ws;              // device workspace, allocated by the first split-K run
-    int ws_device;         // device that holds ws
+    int64_t split_bytes;   // fp32 partial tiles of split-K (ksplit * tiles * 64 KiB), else 0
     // Repacking: an operand whose rows do not allow 128-bit loads (leading
-    // dimension, contiguous extent or batch stride not a multiple of 8) is
-    // copied, before a direct or streaming kernel runs, into a dense buffer
-    // with rows padded to a multiple of 8 elements (zeros in the padding).
+    // dimension, contiguous extent or batch stride not a multiple of 8), or
+    // whose leading dimension is too large for 32-bit tile offsets, is copied,
+    // before the product, into the workspace as a dense array with rows padded
+    // to a multiple of 8 elements (zeros in the padding).
     int pack;              // operands repacked because of their shape: bit 0 A, bit 1 B
+    int fast;              // a direct or streaming kernel: misaligned pointers are repacked too
     int64_t ld8_a, ld8_b;  // leading dimensions of the packed copies
-    int64_t pack_off_b;    // byte offset of B's copy in pack_ws
-    int64_t pack_bytes;    // bytes of both copies
-    void *pack_ws;         // device buffer of the copies, allocated by the first run that packs
-    int pack_device;       // device that holds pack_ws
+    int64_t pack_a_bytes, pack_b_bytes;  // bytes of each copy (256-byte multiples)
     // Fused epilogue (gemm_f16f32_set_epilogue): C = act(alpha A B + beta C + bias).
     const float *bias;     // device pointer to N fp32 values, or NULL
     int act;               // mpgemm::Activation

@@ -879,9 +879,17 @@ __device__ inline void store_tile_splitk(const GemmArgs &p, const AccT (&acc)[FM
     barrier();
     const int r_in = lane / GPR, g = lane % GPR;
     const int64_t tile_elems = (int64_t)BM * BN;
-    // Partials bypass the per-XCD L2 (cache policy sc0 sc1: written through
-    // to memory and read from there), so the slices of a tile may run on
-    // different XCDs without an L2-wide write-back or invalidate.
+    // Partials bypass the per-XCD L2 (cache policy sc0 sc1, system scope:
+    // stores are written through to memory, loads miss in the L2 and read
+    // memory), so the slices of a tile may run on different XCDs without an
+    // L2-wide write-back or invalidate.  Ordering then needs no fence: the
+    // device-scope atomic below is coherent across XCDs by itself (an
+    // acquire-release version differs only by a whole-L2 write-back before
+    // and invalidate after it, which protect cached data, and no L2 ever
+    // holds a partial); each lane waits for its stores' acknowledgement
+    // (vmcnt(0)) and the barrier puts all of them before lane 0's atomic;
+    // the reducer's loads are issued only after the atomic's result has
+    // passed a second barrier.
     constexpr int kCoherent = 1 | 16;
     const __amdgpu_buffer_rsrc_t rws = make_rsrc(p.ws, (int64_t)p.ksplit * p.total_tiles * tile_elems * 4);
     const uint32_t mine = (uint32_t)(((int64_t)slice * p.total_tiles + tile) * tile_elems * 4);
@@ -1433,21 +1441,25 @@ __global__ __launch_bounds__(512) void gemm_stream(GemmArgs pin) {
 
     const int r16 = lane & 15;            // row of A / column of B this lane loads
     const int kq = 8 * (lane >> 4);       // first of its 8 consecutive k
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab, p.extent_a * 2);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb, p.extent_b * 2);
+    // Descriptors based at the workgroup's first row of A and first column
+    // of B, so that lane offsets span only MB*16 rows (NB*16 columns) of at
+    // most 2^22 elements plus K: below 2^31 bytes however large N * ldb is.
+    const int64_t a_base = m0 * p.lda, b_base = n0 * p.ldb;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + a_base, (p.extent_a - a_base) * 2);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + b_base, (p.extent_b - b_base) * 2);
     bool a_ok[MB], b_ok[NB];
     uint32_t a_off[MB], b_off[NB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-        const int64_t m = m0 + mb * 16 + r16;
-        a_ok[mb] = m < p.M;
-        a_off[mb] = (uint32_t)((m * p.lda + kq) * 2);
+        const int64_t ml = mb * 16 + r16;   // row within the workgroup's rows
+        a_ok[mb] = m0 + ml < p.M;
+        a_off[mb] = (uint32_t)((ml * p.lda + kq) * 2);
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-        const int64_t n = n0 + nb * 16 + r16;
-        b_ok[nb] = n < p.N;
-        b_off[nb] = (uint32_t)((n * p.ldb + kq) * 2);
+        const int64_t nl = nb * 16 + r16;   // column within the workgroup's columns
+        b_ok[nb] = n0 + nl < p.N;
+        b_off[nb] = (uint32_t)((nl * p.ldb + kq) * 2);
     }
 
     floatx4v acc[MB][NB];
@@ -1701,39 +1713,46 @@ bool ranges_overlap(uintptr_t a, int64_t a_bytes, uintptr_t b, int64_t b_bytes) 
     return a < b + (uintptr_t)b_bytes && b < a + (uintptr_t)a_bytes;
 }
 
-// Whether the packed copies of A and B together have fewer than 2^31 16-byte
-// chunks: the pack kernel's 32-bit index plus its grid stride (at most 2^21)
-// then never wraps.  (Counting both keeps the test independent of which
-// operands a run copies.)
-bool packable(const gemm_f16f32_plan_s &p) {
-    const int64_t outer_a = p.layout_a == GEMM_ROW_MAJOR ? p.M : p.K;
-    const int64_t outer_b = p.layout_b == GEMM_ROW_MAJOR ? p.K : p.N;
-    return p.batch * (outer_a * (p.ld8_a / 8) + outer_b * (p.ld8_b / 8)) < (int64_t(1) << 31);
+// Zero-fills the first `words` 32-bit words of a workspace (its split-K
+// counters).  A kernel rather than hipMemsetAsync, so that the call is an
+// ordinary stream-ordered launch wherever it is made.
+__global__ __launch_bounds__(256) void gemm_zero_words(uint32_t *p, int words) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < words; i += gridDim.x * 256) p[i] = 0u;
 }
 
+bool aligned16(const void *ptr) { return (uintptr_t)ptr % 16 == 0; }
+
 // One run of a plan of either input type (the entry points below check the
-// type against the one they serve).
+// type against the one they serve) with the caller's workspace.
 int run_plan(gemm_f16f32_plan_t plan, const void *A, const void *B, void *C, float alpha,
-             float beta, void *stream) {
+             float beta, void *ws, int64_t ws_bytes, void *stream) {
     const gemm_f16f32_plan_s &p = *plan;
     if (p.M == 0 || p.N == 0) return GEMM_OK;
-    if (!C) return GEMM_ERR_INVALID_ARG;
-    if (p.K > 0 && (!A || !B)) return GEMM_ERR_INVALID_ARG;
+    if (!C || !A || !B) return GEMM_ERR_INVALID_ARG;
+    if (ws_bytes < 0 || (ws_bytes > 0 && !ws) || (uintptr_t)ws % 256 != 0) return GEMM_ERR_INVALID_ARG;
+    if (ws_bytes < workspace_bytes(p.split_bytes, p.pack, p.pack_a_bytes, p.pack_b_bytes))
+        return GEMM_ERR_INVALID_ARG;
     const int64_t cbytes = p.extent_c * (p.out_type == GEMM_OUT_F32 ? 4 : 2);
     if (p.K > 0 && (ranges_overlap((uintptr_t)C, cbytes, (uintptr_t)A, p.extent_a * 2) ||
                     ranges_overlap((uintptr_t)C, cbytes, (uintptr_t)B, p.extent_b * 2)))
         return GEMM_ERR_INVALID_ARG;
+    if (ranges_overlap((uintptr_t)C, cbytes, (uintptr_t)ws, ws_bytes)) return GEMM_ERR_INVALID_ARG;
     if (p.bias && ranges_overlap((uintptr_t)C, cbytes, (uintptr_t)p.bias, p.N * 4))
         return GEMM_ERR_INVALID_ARG;
 
-    // Operands copied into the plan's padded buffers first: those whose shape
-    // needs it, and, for the direct and streaming kernels, any whose pointer
-    // is not 16-byte aligned.  The staged tiles take a misaligned pointer
-    // with element-wide loads instead.
-    const bool fast = p.vec_ok && kTiles[p.tile].kind != KIND_STAGED;
-    const bool pack_a = p.K > 0 && ((p.pack & 1) || (fast && packable(p) && (uintptr_t)A % 16 != 0));
-    const bool pack_b = p.K > 0 && ((p.pack & 2) || (fast && packable(p) && (uintptr_t)B % 16 != 0));
-    const bool vec = p.vec_ok && (pack_a || (uintptr_t)A % 16 == 0) && (pack_b || (uintptr_t)B % 16 == 0);
+    // Operands copied into the workspace first: those whose shape needs it,
+    // and, for the direct and streaming kernels, any whose pointer is not
+    // 16-byte aligned -- if the workspace holds those copies too.  Otherwise
+    // (and always for the staged tiles) a misaligned operand is read in
+    // place with element-wide loads by the staged kernel.
+    int mask = p.K > 0 ? p.pack : 0;
+    if (p.fast) {
+        const int want = mask | (aligned16(A) ? 0 : 1) | (aligned16(B) ? 0 : 2);
+        if (want != mask && ws_bytes >= workspace_bytes(p.split_bytes, want, p.pack_a_bytes, p.pack_b_bytes))
+            mask = want;
+    }
+    const bool pack_a = mask & 1, pack_b = mask & 2;
+    const bool vec = p.vec_ok && (pack_a || aligned16(A)) && (pack_b || aligned16(B));
     const int64_t celem = p.out_type == GEMM_OUT_F32 ? 4 : 2;
     const bool c_vec = (p.ldc % 4 == 0) && (p.stride_c % 4 == 0) &&
                        ((uintptr_t)C % (4 * celem) == 0);
@@ -1750,11 +1769,12 @@ int run_plan(gemm_f16f32_plan_t plan, const void *A, const void *B, void *C, flo
     a.lda = p.lda; a.ldb = p.ldb; a.ldc = p.ldc;
     a.sa = p.stride_a; a.sb = p.stride_b; a.sc = p.stride_c;
     // Elements reachable from each batch item's base (the range check of the
-    // buffer descriptor never lets a load leave the operand).
-    a.extent_a = p.layout_a == GEMM_ROW_MAJOR ? (p.M - 1) * p.lda + p.K
-                                              : (p.K - 1) * p.lda + p.M;
-    a.extent_b = p.layout_b == GEMM_ROW_MAJOR ? (p.K - 1) * p.ldb + p.N
-                                              : (p.N - 1) * p.ldb + p.K;
+    // buffer descriptor never lets a load leave the operand).  With K = 0 no
+    // element of A or B is read at all.
+    a.extent_a = p.K == 0 ? 0 : p.layout_a == GEMM_ROW_MAJOR ? (p.M - 1) * p.lda + p.K
+                                                             : (p.K - 1) * p.lda + p.M;
+    a.extent_b = p.K == 0 ? 0 : p.layout_b == GEMM_ROW_MAJOR ? (p.K - 1) * p.ldb + p.N
+                                                             : (p.N - 1) * p.ldb + p.K;
     a.alpha = alpha;
     a.beta = beta;
     a.tiles_m = (int)tiles_m;
@@ -1771,40 +1791,15 @@ int run_plan(gemm_f16f32_plan_t plan, const void *A, const void *B, void *C, flo
     a.ws = nullptr;
     a.ws_count = nullptr;
     if (tile == p.tile && p.ksplit > 1) {
-        // The workspace is allocated and its counters cleared on the plan's
-        // first split-K run; they return to zero at the end of every launch.
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
-        if (plan->ws && plan->ws_device != dev) return GEMM_ERR_INVALID_ARG;
-        if (!plan->ws) {
-            void *ws = nullptr;
-            if (hipMalloc(&ws, (size_t)p.ws_bytes) != hipSuccess) return GEMM_ERR_NOMEM;
-            const int64_t partial = p.ws_bytes - a.total_tiles * 4;
-            // Cleared before any stream can use it (a one-time synchronisation).
-            if (hipMemset((char *)ws + partial, 0, (size_t)a.total_tiles * 4) != hipSuccess ||
-                hipDeviceSynchronize() != hipSuccess) {
-                (void)hipFree(ws);
-                return GEMM_ERR_HIP;
-            }
-            plan->ws = ws;
-            plan->ws_device = dev;
-        }
+        // Counters at the workspace's start (zero between runs: the workgroup
+        // that reduces a tile resets its counter), partial tiles after them.
         a.ksplit = p.ksplit;
         a.kchunk = p.kchunk;
-        a.ws = (float *)plan->ws;
-        a.ws_count = (int *)((char *)plan->ws + (p.ws_bytes - a.total_tiles * 4));
+        a.ws_count = (int *)ws;
+        a.ws = (float *)((char *)ws + kCounterBytes);
     }
 
     if (pack_a || pack_b) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
-        if (plan->pack_ws && plan->pack_device != dev) return GEMM_ERR_INVALID_ARG;
-        if (!plan->pack_ws) {
-            void *buf = nullptr;
-            if (hipMalloc(&buf, (size_t)p.pack_bytes) != hipSuccess) return GEMM_ERR_NOMEM;
-            plan->pack_ws = buf;
-            plan->pack_device = dev;
-        }
         auto operand = [&](const void *src, int layout, int64_t rows_rm, int64_t cols_rm,
                            int64_t ld, int64_t stride, int64_t ld8, uint16_t *dst) {
             PackOperand o;
@@ -1820,20 +1815,22 @@ int run_plan(gemm_f16f32_plan_t plan, const void *A, const void *B, void *C, flo
         };
         PackArgs pa = {};
         int nops = 0;
-        uint16_t *pa_dst = (uint16_t *)plan->pack_ws;
-        uint16_t *pb_dst = (uint16_t *)((char *)plan->pack_ws + p.pack_off_b);
+        char *next = (char *)ws + kCounterBytes + p.split_bytes;
         if (pack_a) {
-            pa.op[nops++] = operand(A, p.layout_a, p.M, p.K, p.lda, p.stride_a, p.ld8_a, pa_dst);
+            uint16_t *dst = (uint16_t *)next;
+            next += p.pack_a_bytes;
+            pa.op[nops++] = operand(A, p.layout_a, p.M, p.K, p.lda, p.stride_a, p.ld8_a, dst);
             const int64_t outer = p.layout_a == GEMM_ROW_MAJOR ? p.M : p.K;
-            a.A = pa_dst;
+            a.A = dst;
             a.lda = p.ld8_a;
             a.sa = outer * p.ld8_a;
             a.extent_a = outer * p.ld8_a;
         }
         if (pack_b) {
-            pa.op[nops++] = operand(B, p.layout_b, p.K, p.N, p.ldb, p.stride_b, p.ld8_b, pb_dst);
+            uint16_t *dst = (uint16_t *)next;
+            pa.op[nops++] = operand(B, p.layout_b, p.K, p.N, p.ldb, p.stride_b, p.ld8_b, dst);
             const int64_t outer = p.layout_b == GEMM_ROW_MAJOR ? p.K : p.N;
-            a.B = pb_dst;
+            a.B = dst;
             a.ldb = p.ld8_b;
             a.sb = outer * p.ld8_b;
             a.extent_b = outer * p.ld8_b;
@@ -1852,8 +1849,9 @@ int run_plan(gemm_f16f32_plan_t plan, const void *A, const void *B, void *C, flo
     const int ep = a.epi ? 1 : 0;
     KernelFn fn = kernels().k[ti][ep][tile][ak][bkc][vec ? 1 : 0];
     // K-full variants: every stage inside K (for split-K, every slice: kchunk
-    // is a multiple of BK, so K must be too).
-    if (ts.kind == KIND_DIRECT16 && p.K % ts.bk == 0) fn = kernels().kfull[ti][ep][tile][ak][bkc];
+    // is a multiple of BK, so K must be too).  K = 0 takes the variant with K
+    // tests, whose loads then all fail the range check.
+    if (ts.kind == KIND_DIRECT16 && p.K > 0 && p.K % ts.bk == 0) fn = kernels().kfull[ti][ep][tile][ak][bkc];
     if (!fn) return GEMM_ERR_UNSUPPORTED;
     void *args[] = {&a};
     const unsigned threads = ts.kind == KIND_STREAM ? 512u : (unsigned)(64 * ts.wgm * ts.wgn);
@@ -1867,16 +1865,28 @@ int run_plan(gemm_f16f32_plan_t plan, const void *A, const void *B, void *C, flo
 
 extern "C" int gemm_f16f32_run(gemm_f16f32_plan_t plan, const void *A,
                                const void *B, void *C, float alpha, float beta,
-                               void *stream) {
+                               void *workspace, int64_t workspace_bytes, void *stream) {
     if (!plan || plan->in_type != IN_F16) return GEMM_ERR_INVALID_ARG;
-    return run_plan(plan, A, B, C, alpha, beta, stream);
+    return run_plan(plan, A, B, C, alpha, beta, workspace, workspace_bytes, stream);
 }
 
 extern "C" int gemm_bf16f32_run(gemm_f16f32_plan_t plan, const void *A,
                                 const void *B, void *C, float alpha, float beta,
-                                void *stream) {
+                                void *workspace, int64_t workspace_bytes, void *stream) {
     if (!plan || plan->in_type != IN_BF16) return GEMM_ERR_INVALID_ARG;
-    return run_plan(plan, A, B, C, alpha, beta, stream);
+    return run_plan(plan, A, B, C, alpha, beta, workspace, workspace_bytes, stream);
+}
+
+extern "C" int gemm_f16f32_workspace_init(void *workspace, int64_t bytes, void *stream) {
+    if (bytes < 0 || (bytes > 0 && !workspace) || (uintptr_t)workspace % 256 != 0)
+        return GEMM_ERR_INVALID_ARG;
+    const int words = (int)(std::min<int64_t>(bytes, kCounterBytes) / 4);
+    if (words == 0) return GEMM_OK;
+    uint32_t *w = (uint32_t *)workspace;
+    int n = words;
+    void *args[] = {&w, &n};
+    return hipLaunchKernel((const void *)gemm_zero_words, dim3(1), dim3(256), args, 0,
+                           (hipStream_t)stream) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
 
 #endif  // MPGEMM_HOST_PART

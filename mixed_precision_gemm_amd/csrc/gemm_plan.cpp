@@ -1,7 +1,7 @@
 // Host-side planner of the fp16 (or bf16) -> fp32-accumulate GEMM: argument validation,
-// tile, K-split and repacking choice, and grid shape.  Planning makes no HIP
-// call, so it runs (and is tested) on machines without a GPU; destroy frees
-// the device buffers a plan's runs allocated.
+// tile, K-split and repacking choice, grid shape and workspace size.  Nothing
+// here makes a HIP call, so it runs (and is tested) on machines without a
+// GPU; a plan is host memory only.
 //
 // Pages cited (titles as printed):
 //   [GEMM]    "手写GEMM内核：矩阵乘法性能优化的完整工程实践" (hand-written GEMM kernel)
@@ -12,7 +12,6 @@
 #include <string.h>
 
 #include <algorithm>
-#include <hip/hip_runtime.h>
 #include <new>
 
 #include "gemm_bf16f32.h"
@@ -86,12 +85,12 @@ void choose_ksplit(gemm_f16f32_plan_s *p, int64_t tiles) {
     int64_t ks = std::max<int64_t>(2, kNumCUs / tiles);
     ks = std::min<int64_t>(ks, p->K / 512);
     ks = std::min<int64_t>(ks, 8);
-    if (ks < 2) return;
+    if (ks < 2 || tiles > kMaxCounters) return;
     const int64_t chunk = ceil_div(ceil_div(p->K, ks), 64) * 64;
     p->kchunk = chunk;
     p->ksplit = (int)ceil_div(p->K, chunk);
     if (p->ksplit < 2) { p->ksplit = 1; p->kchunk = p->K; return; }
-    p->ws_bytes = (int64_t)p->ksplit * tiles * 128 * 128 * 4 + tiles * 4;
+    p->split_bytes = (int64_t)p->ksplit * tiles * 128 * 128 * 4;
 }
 
 // A plan for A and B of input type in_type (IN_F16 or IN_BF16).  The tile,
@@ -125,11 +124,6 @@ int make_plan(int in_type, gemm_f16f32_plan_t *out, int64_t M, int64_t N, int64_
     } else {
         stride_a = stride_b = stride_c = 0;
     }
-    // Per-tile lane offsets are 32-bit byte offsets: a tile spans at most
-    // 256 rows (or 64 K steps) of an operand, so leading dimensions up to 2^22
-    // elements keep them below 2^31.
-    const int64_t kMaxLd = int64_t(1) << 22;
-    if (lda > kMaxLd || ldb > kMaxLd || ldc > kMaxLd) return GEMM_ERR_UNSUPPORTED;
     if (batch > (int64_t(1) << 24)) return GEMM_ERR_UNSUPPORTED;
 
     gemm_f16f32_plan_s *p = new (std::nothrow) gemm_f16f32_plan_s();
@@ -163,18 +157,33 @@ int make_plan(int in_type, gemm_f16f32_plan_t *out, int64_t M, int64_t N, int64_
     const bool a_ok = (contig_a % 8 == 0) && (lda % 8 == 0) && (stride_a % 8 == 0);
     const bool b_ok = (contig_b % 8 == 0) && (ldb % 8 == 0) && (stride_b % 8 == 0);
     const bool kc_both = layout_a == GEMM_ROW_MAJOR && layout_b == GEMM_COL_MAJOR;
-    // Copies padded to 8-element rows; sized here, allocated only by a run
-    // that packs (an operand of this shape, or a misaligned pointer).
+    // Copies padded to 8-element rows; sized here, made only by a run that
+    // packs (an operand of this shape, or a misaligned pointer).
     p->ld8_a = ceil_div(contig_a, 8) * 8;
     p->ld8_b = ceil_div(contig_b, 8) * 8;
-    const int64_t bytes_a = ceil_div(batch * outer_a * p->ld8_a * 2, 256) * 256;
-    p->pack_off_b = bytes_a;
-    p->pack_bytes = bytes_a + batch * outer_b * p->ld8_b * 2;
+    p->pack_a_bytes = ceil_div(batch * outer_a * p->ld8_a * 2, 256) * 256;
+    p->pack_b_bytes = ceil_div(batch * outer_b * p->ld8_b * 2, 256) * 256;
+    // Lane offsets within an operand tile are 32-bit byte offsets: a tile
+    // spans at most 256 rows (or 64 K steps) of an operand, so leading
+    // dimensions up to 2^22 elements keep them below 2^31.  Larger ones are
+    // read from packed copies (whose leading dimension is the row length
+    // rounded up to 8); both operands are then copied, so that no kernel
+    // ever reads the large-pitch operand in place.
+    const int64_t kMaxLd = int64_t(1) << 22;
+    const bool chunks_ok =
+        batch * (outer_a * (p->ld8_a / 8) + outer_b * (p->ld8_b / 8)) < (int64_t(1) << 31);
+    const bool huge_ld = K > 0 && (lda > kMaxLd || ldb > kMaxLd);
+    if (huge_ld && (p->ld8_a > kMaxLd || p->ld8_b > kMaxLd || !chunks_ok)) {
+        delete p;
+        return GEMM_ERR_UNSUPPORTED;
+    }
     p->tile = choose_tile(M, N, K, batch, kc_both, true);
-    if (a_ok && b_ok) {
+    if (huge_ld) {
         p->vec_ok = 1;
-    } else if (kTiles[p->tile].kind != KIND_STAGED && K > 0 &&
-               batch * (outer_a * (p->ld8_a / 8) + outer_b * (p->ld8_b / 8)) < (int64_t(1) << 31)) {
+        p->pack = 3;
+    } else if (a_ok && b_ok) {
+        p->vec_ok = 1;
+    } else if (kTiles[p->tile].kind != KIND_STAGED && K > 0 && chunks_ok) {
         // Shapes for the direct or streaming kernels repack the unaligned
         // operands: one extra pass over them instead of element-wide loads
         // for the whole K loop (copies of A and B below 2^31 16-byte chunks).
@@ -186,6 +195,10 @@ int make_plan(int in_type, gemm_f16f32_plan_t *out, int64_t M, int64_t N, int64_
         p->vec_ok = 0;
         p->tile = choose_tile(M, N, K, batch, kc_both, false);
     }
+    // Operands given at misaligned addresses are repacked at run time only
+    // for the direct and streaming kernels (and only when the workspace
+    // holds the copies); the staged tiles read them with element-wide loads.
+    p->fast = p->vec_ok && kTiles[p->tile].kind != KIND_STAGED && K > 0 && chunks_ok;
     for (int cand : {p->tile, narrow_tile(p->tile)}) {
         const TileShape &c = kTiles[cand];
         if (ceil_div(M, c.bm) * ceil_div(N, c.bn) * batch > 0x7fffffff) {
@@ -239,21 +252,6 @@ extern "C" int gemm_bf16f32_plan(gemm_f16f32_plan_t *out, int64_t M, int64_t N,
                      batch, stride_a, stride_b, stride_c);
 }
 
-namespace {
-
-// Frees a device buffer of the plan once no launch can still use it.
-void free_plan_buffer(void *buf, int device) {
-    if (!buf) return;
-    int cur = 0;
-    const bool swap = hipGetDevice(&cur) == hipSuccess && cur != device;
-    if (swap) (void)hipSetDevice(device);
-    (void)hipDeviceSynchronize();
-    (void)hipFree(buf);
-    if (swap) (void)hipSetDevice(cur);
-}
-
-}  // namespace
-
 extern "C" int gemm_f16f32_set_epilogue(gemm_f16f32_plan_t plan, const void *bias,
                                         int activation) {
     if (!plan) return GEMM_ERR_INVALID_ARG;
@@ -264,12 +262,17 @@ extern "C" int gemm_f16f32_set_epilogue(gemm_f16f32_plan_t plan, const void *bia
     return GEMM_OK;
 }
 
+extern "C" int gemm_f16f32_workspace_size(gemm_f16f32_plan_t plan, int flags, int64_t *bytes) {
+    if (!plan || !bytes || (flags & ~GEMM_WS_ANY_ALIGNMENT) != 0) return GEMM_ERR_INVALID_ARG;
+    int mask = plan->pack;
+    if ((flags & GEMM_WS_ANY_ALIGNMENT) && plan->fast) mask = 3;
+    *bytes = plan->tile < 0 ? 0 : workspace_bytes(plan->split_bytes, mask, plan->pack_a_bytes,
+                                                  plan->pack_b_bytes);
+    return GEMM_OK;
+}
+
 extern "C" int gemm_f16f32_destroy(gemm_f16f32_plan_t plan) {
-    if (plan) {
-        free_plan_buffer(plan->ws, plan->ws_device);
-        free_plan_buffer(plan->pack_ws, plan->pack_device);
-    }
-    delete plan;
+    delete plan;   // host memory only: runs never depend on the plan after launch
     return GEMM_OK;
 }
 
@@ -279,7 +282,7 @@ extern "C" const char *gemm_f16f32_status_string(int status) {
     case GEMM_ERR_INVALID_ARG: return "GEMM_ERR_INVALID_ARG: an argument violates the documented rules";
     case GEMM_ERR_UNSUPPORTED: return "GEMM_ERR_UNSUPPORTED: valid, but outside what the kernels cover";
     case GEMM_ERR_HIP: return "GEMM_ERR_HIP: the HIP runtime refused the launch";
-    case GEMM_ERR_NOMEM: return "GEMM_ERR_NOMEM: allocation failed (plan, or device workspace at run)";
+    case GEMM_ERR_NOMEM: return "GEMM_ERR_NOMEM: host allocation of a plan failed";
     default: return "unknown status";
     }
 }

@@ -95,7 +95,11 @@ def check_bound(gpu, ref, scale, out_type, what="", act=0):
 
 
 def to_device(case, device="cuda"):
-    return (case.A.to(device), case.B.to(device), case.C.to(device))
+    """Device copies of the case's storage.  An empty operand (K = 0) gets a
+    small zero buffer instead: run() requires non-NULL A and B whenever
+    M * N > 0, and a zero-size tensor has no address."""
+    dev = lambda t: t.to(device) if t.numel() else torch.zeros(8, dtype=t.dtype, device=device)
+    return (dev(case.A), dev(case.B), case.C.to(device))
 
 
 def run_case(case, dA=None, dB=None, dC=None, stream=None, alpha=None, beta=None,

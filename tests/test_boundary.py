@@ -76,8 +76,40 @@ def test_invalid_plans(kw):
     assert plan(**kw) == GEMM_ERR_INVALID_ARG
 
 
-def test_unsupported_leading_dimension():
-    assert plan(lda=(1 << 22) + 8) == GEMM_ERR_UNSUPPORTED
+def test_large_leading_dimensions_repack_both_operands():
+    """Tile offsets are 32-bit: A or B with a leading dimension above 2^22
+    elements is read from packed copies (both operands), C's is unlimited;
+    only a row or column longer than 2^22 elements is unsupported."""
+    def kern(*a, **k):
+        with mpg.Plan(*a, **k) as p:
+            return p.kernel, p.workspace_bytes()
+    big = (1 << 22) + 8
+    for shape, kw in [((64, 64, 64), dict(lda=big)),
+                      ((2048, 2048, 2048), dict(ldb=big)),
+                      ((16, 4096, 4096), dict(layout_b=GEMM_COL_MAJOR, ldb=big)),
+                      ((8192, 8192, 1024), dict(lda=big))]:
+        name, ws = kern(*shape, **kw)
+        assert name.endswith("_pkab"), (shape, kw, name)
+        M, N, K = shape
+        assert ws >= 4096 + 2 * (M * K + K * N)
+    name, ws = kern(64, 64, 64, ldc=big)
+    assert "_pk" not in name and ws == 0
+    assert plan(lda=1 << 22) == GEMM_OK
+    # K = 0 reads no operand: no copies whatever the leading dimension
+    assert kern(64, 64, 0, lda=big)[1] == 0
+    assert plan(M=8, N=8, K=(1 << 22) + 1, lda=big) == GEMM_ERR_UNSUPPORTED
+    assert plan(M=(1 << 22) + 1, N=8, K=8, la=GEMM_COL_MAJOR, lda=big) == GEMM_ERR_UNSUPPORTED
+
+
+def test_streaming_plan_with_large_column_pitch():
+    """A streaming plan whose B spans far more than 2^31 bytes (ldb = 2^22,
+    N = 512) is accepted and reads B in place: its lane offsets are taken
+    from each workgroup's first column."""
+    with mpg.Plan(16, 512, 64, layout_b=GEMM_COL_MAJOR, ldb=1 << 22) as p:
+        assert p.kernel == "gemm_stream16x16_nt_direct"
+        assert p.workspace_bytes() == 0
+    with mpg.Plan(16, 152064, 8192, layout_b=GEMM_COL_MAJOR) as p:
+        assert p.kernel.startswith("gemm_stream16x16")
 
 
 def test_null_out_pointer():
@@ -161,6 +193,59 @@ def test_repacking_choice():
                 stride_c=33 * 33).endswith("narrow")
     # K = 0 reads no operand
     assert "_pk" not in kern(1000, 1000, 0, lda=1)
+
+
+def test_workspace_size_rules():
+    """Workspace: none for plain plans; 4096 counter bytes plus 64 KiB per
+    (slice, tile) for split-K; the shape-driven copies; and, on request,
+    room to repack misaligned pointers (direct and streaming kernels only)."""
+    from mixed_precision_gemm_amd import GEMM_WS_ANY_ALIGNMENT as ANY
+    with mpg.Plan(8192, 8192, 8192) as p:
+        assert p.workspace_bytes() == 0
+        assert p.workspace_bytes(ANY) == 4096 + 2 * 2 * 8192 * 8192
+    with mpg.Plan(16, 4096, 4096) as p:          # 32 tiles x 8 slices
+        assert p.kernel.endswith("_sk8")
+        assert p.workspace_bytes() == 4096 + 8 * 32 * 128 * 128 * 4
+        assert p.workspace_bytes(ANY) == 4096 + 8 * 32 * 65536 + 2 * (16 * 4096 + 4096 * 4096)
+    with mpg.Plan(1000, 1000, 999) as p:         # A repacked: 1000 rows of 1000
+        assert p.kernel.endswith("_pka")
+        assert p.workspace_bytes() == 4096 + (1000 * 1000 * 2 + 255) // 256 * 256
+    with mpg.Plan(127, 257, 33) as p:            # staged tile: reads in place
+        assert p.workspace_bytes() == 0 and p.workspace_bytes(ANY) == 0
+    with mpg.Plan(0, 64, 64) as p:
+        assert p.workspace_bytes(ANY) == 0
+    with mpg.Plan(64, 64, 64) as p:
+        assert mpg.gemm_f16f32_workspace_size(p.handle, 2)[0] == GEMM_ERR_INVALID_ARG
+        lib = mpg.library()
+        assert lib.gemm_f16f32_workspace_size(p.handle, 0, None) == GEMM_ERR_INVALID_ARG
+    assert mpg.gemm_f16f32_workspace_size(None, 0)[0] == GEMM_ERR_INVALID_ARG
+
+
+def test_run_and_init_reject_bad_workspaces_before_launch():
+    base = 1 << 30
+    A, B, C = base, base + (1 << 26), base + (2 << 26)
+    with mpg.Plan(16, 4096, 4096) as p:          # split-K: needs a workspace
+        need = p.workspace_bytes()
+        ws = base + (3 << 26)
+        run = lambda w, n: mpg.gemm_f16f32_run(p.handle, A, B, C, 1.0, 0.0, w, n, None)
+        assert run(None, 0) == GEMM_ERR_INVALID_ARG
+        assert run(ws, need - 1) == GEMM_ERR_INVALID_ARG
+        assert run(ws + 16, need) == GEMM_ERR_INVALID_ARG      # not 256-byte aligned
+        assert run(None, need) == GEMM_ERR_INVALID_ARG
+        assert run(ws, -1) == GEMM_ERR_INVALID_ARG
+        assert run(C - 256, need) == GEMM_ERR_INVALID_ARG      # overlaps C
+    assert mpg.gemm_f16f32_workspace_init(None, 4096) == GEMM_ERR_INVALID_ARG
+    assert mpg.gemm_f16f32_workspace_init(base + 8, 4096) == GEMM_ERR_INVALID_ARG
+    assert mpg.gemm_f16f32_workspace_init(base, -1) == GEMM_ERR_INVALID_ARG
+    assert mpg.gemm_f16f32_workspace_init(None, 0) == GEMM_OK   # nothing to clear
+
+
+def test_run_rejects_null_operands_even_when_k_is_zero():
+    """A and B must be non-NULL whenever M * N > 0 (K = 0 reads neither)."""
+    base = 1 << 30
+    with mpg.Plan(1024, 1024, 0, lda=1) as p:
+        assert mpg.gemm_f16f32_run(p.handle, 0, base, base + (1 << 26), 1.0, 1.0) == GEMM_ERR_INVALID_ARG
+        assert mpg.gemm_f16f32_run(p.handle, base, 0, base + (1 << 26), 1.0, 1.0) == GEMM_ERR_INVALID_ARG
 
 
 def test_run_rejects_bad_arguments_before_launch():

@@ -356,28 +356,115 @@ def test_degenerate_extents():
     assert torch.equal(dC.cpu(), (case.C.float() * 2.0).half())
 
 
+def test_k_zero_on_the_direct_tile():
+    """K = 0 on a shape the direct 128 tile serves (aligned leading
+    dimensions): C <- beta * C, with every load failing its range check --
+    the operands hold NaN, and none of it may reach C."""
+    M, N = 1024, 1024
+    with mpg.Plan(M, N, 0, lda=8) as p:
+        assert p.kernel == "gemm_128x128x64m16_nn_direct", p.kernel
+        A = torch.full((M * 8,), float("nan"), dtype=torch.float16, device="cuda")
+        B = torch.full((N * 8,), float("nan"), dtype=torch.float16, device="cuda")
+        g = torch.Generator("cpu").manual_seed(15)
+        C0 = (torch.rand(M * N, generator=g) * 2 - 1).half()
+        C = C0.cuda()
+        p.run(A, B, C, 1.0, -0.5)
+        torch.cuda.synchronize()
+    assert torch.equal(C.cpu(), (C0.float() * -0.5).half())
+
+
+def test_split_k_on_two_streams_with_own_workspaces():
+    """One split-K plan run concurrently on two streams, each run with its
+    own workspace (a plan is immutable host data): both results match the
+    oracle, and each workspace's counter words are zero again afterwards."""
+    c1 = gi.make_case(64, 4096, 4096, beta=1.0, seed=41)
+    c2 = gi.make_case(64, 4096, 4096, beta=1.0, seed=42)
+    p = mpg.Plan(c1.M, c1.N, c1.K, c1.layout_a, c1.layout_b, c1.out_type, c1.lda, c1.ldb, c1.ldc)
+    assert "_sk" in p.kernel, p.kernel
+    need = p.workspace_bytes()
+    ws = [torch.zeros(need, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    (A1, B1, C1), (A2, B2, C2) = to_device(c1), to_device(c2)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        C1.copy_(c1.C.cuda())
+        C2.copy_(c2.C.cuda())
+        torch.cuda.synchronize()
+        p.run(A1, B1, C1, c1.alpha, c1.beta, stream=s1, workspace=ws[0])
+        p.run(A2, B2, C2, c2.alpha, c2.beta, stream=s2, workspace=ws[1])
+        torch.cuda.synchronize()
+    p.close()
+    for case, C in ((c1, C1), (c2, C2)):
+        ref, scale = oracle_for(case)
+        check_bound(c_logical(case, C.cpu()), ref, scale, OUT_F16, "split-K, two streams")
+    for w in ws:
+        assert torch.count_nonzero(w[:4096]).item() == 0
+
+
+def test_workspace_init_clears_counters():
+    """gemm_f16f32_workspace_init zero-fills a dirty buffer's counter words
+    (stream-ordered, no allocation), after which a split-K run is correct."""
+    case = gi.make_case(16, 4096, 4096, seed=43)
+    with mpg.Plan(case.M, case.N, case.K) as p:
+        need = p.workspace_bytes()
+        ws = torch.full((need,), 7, dtype=torch.uint8, device="cuda")
+        stream = torch.cuda.current_stream().cuda_stream
+        assert mpg.gemm_f16f32_workspace_init(ws.data_ptr(), need, stream) == 0
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(ws[:4096]).item() == 0
+        assert torch.all(ws[4096:] == 7)
+        A, B, C = to_device(case)
+        p.run(A, B, C, 1.0, 0.0, workspace=ws)
+        torch.cuda.synchronize()
+    ref, scale = oracle_for(case)
+    check_bound(c_logical(case, C.cpu()), ref, scale, OUT_F16, "after workspace_init")
+
+
 # ------------------------------------------------------- 64-bit offsets
 
-@pytest.mark.parametrize("shape,tile", [((600, 4096, 256), "128x128"),
-                                        ((2048, 8192, 384), "256x256")])
-def test_huge_leading_dimension(shape, tile):
+@pytest.mark.parametrize("shape,tile,lda", [((600, 4096, 256), "128x128", 1 << 22),
+                                            ((2048, 8192, 384), "256x256", 1 << 22),
+                                            ((600, 4096, 256), "128x128", (1 << 22) + 8)])
+def test_huge_leading_dimension(shape, tile, lda):
     """A row-major with lda = 2^22 (8 MiB between rows): A spans 4.7 or 16
     GiB, so tile origins lie beyond 2^32 bytes while each tile's lane
-    offsets stay below 2^31.  The oracle runs on the compact copy."""
+    offsets stay below 2^31.  Above 2^22 the plan repacks both operands
+    into the workspace first.  The oracle runs on the compact copy."""
     M, N, K = shape
-    lda = 1 << 22
     case = gi.make_case(M, N, K, beta=1.0, seed=95)
     A = torch.zeros((M - 1) * lda + K, dtype=torch.float16, device="cuda")
     A.as_strided((M, K), (lda, 1)).copy_(case.A.view(M, K).cuda())
     B, C = case.B.cuda(), case.C.cuda()
     with mpg.Plan(M, N, K, ROW_MAJOR, ROW_MAJOR, OUT_F16, lda, case.ldb, case.ldc) as p:
         assert tile in p.kernel, p.kernel
+        assert p.kernel.endswith("_pkab") == (lda > (1 << 22)), p.kernel
         p.run(A, B, C, case.alpha, case.beta)
     torch.cuda.synchronize()
     del A
     rows = sample_rows(M, n_random=24)
     ref, scale = oracle_for(case, rows)
-    check_bound(c_logical(case, C.cpu(), rows), ref, scale, OUT_F16, f"lda=2^22 {shape}")
+    check_bound(c_logical(case, C.cpu(), rows), ref, scale, OUT_F16, f"lda={lda} {shape}")
+
+
+@pytest.mark.parametrize("N", [512, 1040])
+def test_streaming_kernel_large_column_pitch(N):
+    """The streaming kernel with column-major B at ldb = 2^22: B spans 4 or
+    8 GiB, so columns past the first 256 (512) lie beyond 2^31 (2^32) bytes
+    from B's base.  Each workgroup's descriptor starts at its own first
+    column, so every lane offset stays small; the oracle runs on a compact
+    copy of B."""
+    M, K, ldb = 16, 64, 1 << 22
+    case = gi.make_case(M, N, K, layout_b=COL_MAJOR, beta=0.5, seed=97)
+    B = torch.zeros((N - 1) * ldb + K, dtype=torch.float16, device="cuda")
+    B.as_strided((N, K), (ldb, 1)).copy_(case.B.view(N, K).cuda())
+    A, C = case.A.cuda(), case.C.cuda()
+    with mpg.Plan(M, N, K, ROW_MAJOR, COL_MAJOR, OUT_F16, case.lda, ldb, case.ldc) as p:
+        assert p.kernel == "gemm_stream16x16_nt_direct", p.kernel
+        p.run(A, B, C, case.alpha, case.beta)
+    torch.cuda.synchronize()
+    del B
+    ref, scale = oracle_for(case)
+    check_bound(c_logical(case, C.cpu()), ref, scale, OUT_F16, f"stream ldb=2^22 N={N}")
 
 
 def test_huge_batch_stride():
@@ -536,8 +623,8 @@ def test_split_k_repeatable_and_interleaved():
 
 
 def test_split_k_plan_with_misaligned_pointer_repacks():
-    """A split-K plan run with a misaligned A: A is copied into the plan's
-    padded buffer and the split kernel runs on the copy."""
+    """A split-K plan run with a misaligned A: A is copied into the padded
+    area of the workspace and the split kernel runs on the copy."""
     M, N, K = 16, 1024, 2048
     case = gi.make_case(M, N, K, beta=1.0, seed=34)
     p = mpg.Plan(M, N, K)
