@@ -88,7 +88,9 @@ enum {
     GEMM_ERR_INVALID_ARG = -1,  /* argument violates a rule stated below    */
     GEMM_ERR_UNSUPPORTED = -2,  /* valid but outside what the kernels cover */
     GEMM_ERR_HIP = -3,          /* the HIP runtime refused the launch       */
-    GEMM_ERR_NOMEM = -4         /* host allocation of a plan failed         */
+    GEMM_ERR_NOMEM = -4,        /* host allocation of a plan failed         */
+    GEMM_ERR_SCRATCH = -5       /* gemm_f16f32_run_noalloc: the plan needs
+                                   more scratch than the library holds      */
 };
 
 /*
@@ -176,6 +178,29 @@ int gemm_f16f32_run(gemm_f16f32_plan_t plan,
                     const void *A, const void *B, void *C,
                     float alpha, float beta,
                     void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * gemm_f16f32_run without a workspace argument, for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace is the library's own
+ * static device array of 64 MiB per device, held from the library's first
+ * use on a device until the process ends; on the first call on a device its
+ * counter words are zero-filled by a small kernel on `stream`.  Nothing is
+ * allocated or synchronised, at any call.
+ *   plan   a plan of either input type (gemm_f16f32_plan or gemm_bf16f32_plan).
+ *   A, B, C, alpha, beta, stream  as gemm_f16f32_run (for a bfloat16 plan,
+ *          as gemm_bf16f32_run).
+ * A plan whose gemm_f16f32_workspace_size(plan, 0) exceeds 64 MiB ->
+ * GEMM_ERR_SCRATCH, before any HIP call.  Operands at misaligned addresses
+ * are repacked into the array when the copies fit, else read in place.
+ * Every call on a device shares that device's array (which keeps the last
+ * call's contents): calls on one device that may execute at the same time --
+ * on different streams, or from different threads -- race on it and must be
+ * serialised by the caller.  Other rules and status codes as gemm_f16f32_run.
+ */
+int gemm_f16f32_run_noalloc(gemm_f16f32_plan_t plan,
+                            const void *A, const void *B, void *C,
+                            float alpha, float beta, void *stream);
 
 /*
  * Sets the plan's fused epilogue, used by every later run of the plan:

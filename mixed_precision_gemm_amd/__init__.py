@@ -22,12 +22,14 @@ GEMM_ERR_INVALID_ARG = -1
 GEMM_ERR_UNSUPPORTED = -2
 GEMM_ERR_HIP = -3
 GEMM_ERR_NOMEM = -4
+GEMM_ERR_SCRATCH = -5
 GEMM_WS_ANY_ALIGNMENT = 1
 
 EXPORTED = ("gemm_f16f32_plan", "gemm_f16f32_run", "gemm_f16f32_destroy",
             "gemm_f16f32_status_string", "gemm_f16f32_plan_kernel",
             "gemm_bf16f32_plan", "gemm_bf16f32_run", "gemm_f16f32_set_epilogue",
-            "gemm_f16f32_workspace_size", "gemm_f16f32_workspace_init")
+            "gemm_f16f32_workspace_size", "gemm_f16f32_workspace_init",
+            "gemm_f16f32_run_noalloc")
 
 _lib = None
 
@@ -61,6 +63,8 @@ def library() -> ctypes.CDLL:
         lib.gemm_f16f32_workspace_size.restype = ctypes.c_int
         lib.gemm_f16f32_workspace_init.argtypes = [vp, i64, vp]
         lib.gemm_f16f32_workspace_init.restype = ctypes.c_int
+        lib.gemm_f16f32_run_noalloc.argtypes = [vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp]
+        lib.gemm_f16f32_run_noalloc.restype = ctypes.c_int
         lib.gemm_f16f32_set_epilogue.argtypes = [vp, vp, ctypes.c_int]
         lib.gemm_f16f32_set_epilogue.restype = ctypes.c_int
         lib.gemm_f16f32_destroy.argtypes = [vp]
@@ -91,6 +95,13 @@ def gemm_f16f32_run(plan, A, B, C, alpha, beta, workspace=None, workspace_bytes=
     plan needs none); stream: hipStream_t as int or None."""
     return library().gemm_f16f32_run(plan, A, B, C, alpha, beta, workspace,
                                      workspace_bytes, stream)
+
+
+def gemm_f16f32_run_noalloc(plan, A, B, C, alpha, beta, stream=None):
+    """Runs a plan of either input type with the library's static device
+    scratch as workspace (no allocation; calls on one device must not
+    overlap in time)."""
+    return library().gemm_f16f32_run_noalloc(plan, A, B, C, alpha, beta, stream)
 
 
 def gemm_f16f32_workspace_size(plan, flags=0):

@@ -43,6 +43,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "gemm_bf16f32.h"
@@ -1887,6 +1888,68 @@ extern "C" int gemm_f16f32_workspace_init(void *workspace, int64_t bytes, void *
     void *args[] = {&w, &n};
     return hipLaunchKernel((const void *)gemm_zero_words, dim3(1), dim3(256), args, 0,
                            (hipStream_t)stream) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// No-allocation entry point, for callers that cannot allocate device memory
+// (code under stream capture, tight serving loops, harnesses that forbid
+// hipMalloc): the workspace is this library's own static device array.  Each
+// device that runs the library holds its copy of the array, at its own
+// address, for the life of the process.  That address is taken once per
+// device with hipGetSymbolAddress (the array's name in host code is only a
+// host-side stand-in, never a device address) and is what the kernels get.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int64_t kScratchBytes = int64_t(64) << 20;
+static __device__ __align__(256) __attribute__((used)) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];   // device address of scratch per device, once set up
+
+// The current device's scratch: its address, looked up on the first call on
+// the device (with the device current), and its counter words zero-filled
+// once by a kernel on `stream` (split-K runs leave them zero after that).
+int device_scratch(void **out, hipStream_t stream) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return GEMM_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return GEMM_ERR_HIP;
+        uint32_t *w = (uint32_t *)ptr;
+        int words = kMaxCounters;
+        void *args[] = {&w, &words};
+        if (hipLaunchKernel((const void *)gemm_zero_words, dim3(1), dim3(256), args, 0, stream) != hipSuccess)
+            return GEMM_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return GEMM_OK;
+}
+
+}  // namespace
+
+extern "C" int gemm_f16f32_run_noalloc(gemm_f16f32_plan_t plan, const void *A, const void *B,
+                                       void *C, float alpha, float beta, void *stream) {
+    if (!plan) return GEMM_ERR_INVALID_ARG;
+    if (plan->M == 0 || plan->N == 0) return GEMM_OK;
+    if (workspace_bytes(plan->split_bytes, plan->pack, plan->pack_a_bytes, plan->pack_b_bytes) >
+        kScratchBytes)
+        return GEMM_ERR_SCRATCH;
+    if (!A || !B || !C) return GEMM_ERR_INVALID_ARG;
+    void *ws = nullptr;
+    int64_t ws_bytes = 0;
+    // Plans that need scratch, and those that repack misaligned operands into
+    // it when it holds the copies, use the device's array.
+    if (plan->split_bytes > 0 || plan->pack != 0 || plan->fast) {
+        const int st = device_scratch(&ws, (hipStream_t)stream);
+        if (st != GEMM_OK) return st;
+        ws_bytes = kScratchBytes;
+    }
+    return run_plan(plan, A, B, C, alpha, beta, ws, ws_bytes, stream);
 }
 
 #endif  // MPGEMM_HOST_PART

@@ -283,6 +283,9 @@ extern "C" const char *gemm_f16f32_status_string(int status) {
     case GEMM_ERR_UNSUPPORTED: return "GEMM_ERR_UNSUPPORTED: valid, but outside what the kernels cover";
     case GEMM_ERR_HIP: return "GEMM_ERR_HIP: the HIP runtime refused the launch";
     case GEMM_ERR_NOMEM: return "GEMM_ERR_NOMEM: host allocation of a plan failed";
+    case GEMM_ERR_SCRATCH:
+        return "GEMM_ERR_SCRATCH: the plan needs more device scratch than the no-allocation "
+               "entry point holds (64 MiB per device)";
     default: return "unknown status";
     }
 }

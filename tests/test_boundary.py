@@ -119,7 +119,7 @@ def test_null_out_pointer():
 
 def test_destroy_null_and_status_strings():
     assert mpg.gemm_f16f32_destroy(None) == GEMM_OK
-    for st in (0, -1, -2, -3, -4):
+    for st in (0, -1, -2, -3, -4, -5):
         s = mpg.gemm_f16f32_status_string(st)
         assert s.startswith("GEMM_")
     assert mpg.gemm_f16f32_status_string(12345) == "unknown status"
@@ -238,6 +238,22 @@ def test_run_and_init_reject_bad_workspaces_before_launch():
     assert mpg.gemm_f16f32_workspace_init(base + 8, 4096) == GEMM_ERR_INVALID_ARG
     assert mpg.gemm_f16f32_workspace_init(base, -1) == GEMM_ERR_INVALID_ARG
     assert mpg.gemm_f16f32_workspace_init(None, 0) == GEMM_OK   # nothing to clear
+
+
+def test_noalloc_refuses_plans_beyond_its_scratch_before_any_hip_call():
+    """gemm_f16f32_run_noalloc holds 64 MiB of static scratch per device: a
+    plan needing more is refused with GEMM_ERR_SCRATCH, checked on the host
+    before the device is touched (so this runs without a GPU)."""
+    from mixed_precision_gemm_amd import GEMM_ERR_SCRATCH
+    base = 1 << 30
+    with mpg.Plan(4201, 4201, 4201) as p:            # both operands repacked: 2 x 35 MB
+        assert p.kernel.endswith("_pkab")
+        assert p.workspace_bytes() > 64 << 20
+        assert mpg.gemm_f16f32_run_noalloc(p.handle, base, base + (1 << 26),
+                                           base + (2 << 26), 1.0, 0.0) == GEMM_ERR_SCRATCH
+    assert mpg.gemm_f16f32_run_noalloc(None, base, base, base, 1.0, 0.0) == GEMM_ERR_INVALID_ARG
+    with mpg.Plan(0, 64, 64) as p:
+        assert mpg.gemm_f16f32_run_noalloc(p.handle, 0, 0, 0, 1.0, 0.0) == GEMM_OK
 
 
 def test_run_rejects_null_operands_even_when_k_is_zero():
