@@ -35,5 +35,20 @@ def test_source_hash_ignores_comments_and_whitespace(tmp_path, monkeypatch):
 
 
 def test_traffic_only_for_the_profiled_workload():
-    assert bench.profiled_traffic("nn", (4096, 4096, 4096)) is None
-    assert bench.profiled_traffic("tt", (8192, 8192, 8192)) is None
+    assert bench.profiled_traffic("square nn 4096x4096x4096 f16") is None
+    assert bench.profiled_traffic("square tt 8192x8192x8192 f16") is None
+    args = bench.parse(["--workload", "linear", "--case", "16,11008"])
+    assert bench.bench_key(args) == "linear 16,11008 f16"
+    assert bench.bench_key(bench.parse([])) == "square nn 8192x8192x8192 f16"
+
+
+def test_committed_profiles_name_their_run():
+    """Every committed summary carries the key of the bench run it profiled,
+    the hash of the code it profiled and the commands that made it."""
+    import glob
+    paths = glob.glob(os.path.join(ROOT, "profiles", "*.md"))
+    assert paths
+    for p in paths:
+        f = bench.profile_fields(p)
+        assert "kernel_source_hash" in f, p
+        assert "rocprofv3" in open(p).read(), p
