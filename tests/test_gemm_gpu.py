@@ -221,6 +221,76 @@ def test_integer_inputs_bit_exact_f32(la, lb):
     assert np.array_equal(got, ref)
 
 
+# The headline kernels bit for bit.  Integer A, B in {-8..8} and C in
+# {-64..64} with K <= 4104 keep every partial sum an integer below 2^24, so
+# an fp32 C is exact in any summation order: a missing, repeated or
+# misplaced K term, row or column anywhere in a stage, its tail or the
+# epilogue changes the bits.
+EXACT_KERNELS = [
+    ((4096, 4096, 4104), "gemm_256x256x64m16_", True),    # 256 tile, ragged K (K tests)
+    ((4096, 4096, 4096), "gemm_256x256x64m16_", True),    # 256 tile, K-full variant
+    ((3072, 3072, 1000), "gemm_128x128x64m16_", True),    # 128 tile, two slots, no split
+    ((1000, 1000, 1000), "gemm_128x128x64m16d4_", False),  # 128 tile, four slots
+]
+
+
+@pytest.mark.parametrize("shape,prefix,sampled", EXACT_KERNELS)
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+def test_integer_inputs_bit_exact_direct_tiles(shape, prefix, sampled, la, lb):
+    M, N, K = shape
+    case = gi.make_case(M, N, K, layout_a=la, layout_b=lb, out_type=OUT_F32, alpha=1.0,
+                        beta=1.0, dist_a="integer", dist_b="integer", dist_c="integer",
+                        int_range=(-8, 8), c_int_range=(-64, 64), seed=6)
+    kernel = plan_kernel(case)
+    assert kernel.startswith(prefix) and "_sk" not in kernel and "_pk" not in kernel, kernel
+    dC = run_case(case)
+    rows = sample_rows(M, n_random=48) if sampled else None
+    got = c_logical(case, dC.cpu(), rows)
+    ref, _ = oracle_for(case, rows)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{kernel}: {len(bad)} inexact, first {bad[:4].tolist()}"
+
+
+@pytest.mark.parametrize("M,N", [(16, 4096), (32, 11008), (64, 4096)])
+def test_integer_inputs_bit_exact_streaming(M, N):
+    case = gi.make_case(M, N, 4096, layout_b=COL_MAJOR, out_type=OUT_F32,
+                        dist_a="integer", dist_b="integer", int_range=(-8, 8), seed=7)
+    kernel = plan_kernel(case)
+    assert kernel.startswith("gemm_stream"), kernel
+    dC = run_case(case)
+    ref, _ = oracle_for(case)
+    assert np.array_equal(c_logical(case, dC.cpu()), ref), kernel
+
+
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+@pytest.mark.parametrize("side", ["A", "B"])
+def test_one_hot_permutation_on_the_256_tile(la, lb, side):
+    """A (or B) is a permutation matrix, the other operand holds distinct
+    integers: C is the other operand with its rows (columns) permuted, bit
+    for bit, on all 16.8 M outputs of the 256 tile's 16 x 16 x 32 fragments
+    (every lane, register, fragment and K step of the fragment maps)."""
+    n = 4096
+    perm = (torch.arange(n) * 1237 + 91) % n                      # a permutation (1237 odd)
+    vals = ((torch.arange(n)[:, None] * 31 + torch.arange(n)[None, :] * 17) % 2001 - 1000).half()
+    P = torch.zeros(n, n, dtype=torch.float16)
+    if side == "A":
+        P[torch.arange(n), perm] = 1.0          # C[i, :] = vals[perm[i], :]
+        Am, Bm, want = P, vals, vals[perm, :]
+    else:
+        P[perm, torch.arange(n)] = 1.0          # C[:, j] = vals[:, perm[j]]
+        Am, Bm, want = vals, P, vals[:, perm]
+    A = Am if la == ROW_MAJOR else Am.t().contiguous()
+    B = Bm if lb == ROW_MAJOR else Bm.t().contiguous()
+    C = torch.full((n, n), 7.0, dtype=torch.float16, device="cuda")
+    with mpg.Plan(n, n, n, la, lb, OUT_F16, n, n, n) as p:
+        assert p.kernel.startswith("gemm_256x256x64m16_"), p.kernel
+        p.run(A.cuda(), B.cuda(), C)
+    torch.cuda.synchronize()
+    got = C.cpu()
+    bad = (got != want).nonzero()
+    assert bad.numel() == 0, f"{LNAME[(la, lb)]} {side}: {bad.shape[0]} wrong, first {bad[:4].tolist()}"
+
+
 @pytest.mark.parametrize("K", [1, 7, 64, 2048, 4097])
 def test_all_ones_gives_K(K):
     case = gi.make_case(96, 80, K, dist_a="ones", dist_b="ones", seed=0)
