@@ -1,13 +1,15 @@
-"""CPU oracle for C = alpha*A*B + beta*C with binary16 or bfloat16 A, B (test
-infrastructure).
+"""CPU oracle for C = alpha*A*B + beta*C with binary16 or bfloat16 A, B, and
+for row softmax and attention (test infrastructure).
 
 TEST INFRASTRUCTURE ONLY.  Only tests/, the smoke check in __graft_entry__ and
 the CPU-baseline leg of bench.py may import this package.  It shares no code
 with the GPU path (mixed_precision_gemm_amd) and never imports it.
 
 The arithmetic is in ref_gemm.c (plain fp64 triple loop, own binary16 and
-bfloat16 decoders and encoders); this module only marshals numpy arrays through ctypes.  See the
-header of ref_gemm.c for what each function follows on the pages.
+bfloat16 decoders and encoders) and ref_attention.c (softmax by its
+definition and by the online recurrence, attention in fp64); this module only
+marshals numpy arrays through ctypes.  See the headers of the C files for what
+each function follows on the pages.
 """
 import ctypes
 import os
@@ -43,6 +45,20 @@ def load_library(path):
                                 vp, vp, vp, dbl, dbl, vp, ctypes.c_int, vp, i64, vp, vp,
                                 ctypes.c_int]
     lib.oracle_gemm.restype = ctypes.c_int
+    if hasattr(lib, "oracle_attention"):
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.oracle_softmax_row.argtypes = [vp, i64, vp]
+        lib.oracle_softmax_row.restype = None
+        lib.oracle_softmax_row_online.argtypes = [vp, i64, i64, vp]
+        lib.oracle_softmax_row_online.restype = None
+        lib.oracle_softmax.argtypes = [i64, i64, vp, ctypes.c_int, i64, vp]
+        lib.oracle_softmax.restype = ctypes.c_int
+        lib.oracle_attention.argtypes = [i64, i64, i64, i64, i64, i64,
+                                         vp, i64, i64, i64, vp, i64, i64, i64,
+                                         vp, i64, i64, i64, dbl, ctypes.c_int, vp, i64,
+                                         vp, vp, vp, ctypes.c_int]
+        lib.oracle_attention.restype = ctypes.c_int
+        del dp
     return lib
 
 
@@ -160,3 +176,77 @@ def gemm(M, N, K, A, B, C=None, *, alpha=1.0, beta=0.0,
     if rc != 0:
         raise RuntimeError(f"oracle_gemm failed with {rc}")
     return ref, scale
+
+
+# ------------------------------------------------------------ softmax, attention
+
+def softmax_row(x, lib=None) -> np.ndarray:
+    """Softmax of one float64 row by the definition (two passes)."""
+    lib = lib or _load()
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    y = np.zeros_like(x)
+    lib.oracle_softmax_row(x.ctypes.data, x.size, y.ctypes.data)
+    return y
+
+
+def softmax_row_online(x, block, lib=None) -> np.ndarray:
+    """The same softmax by the online recurrence, `block` elements at a time."""
+    lib = lib or _load()
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    y = np.zeros_like(x)
+    lib.oracle_softmax_row_online(x.ctypes.data, x.size, int(block), y.ctypes.data)
+    return y
+
+
+def softmax(rows, cols, X, ld=None, lib=None) -> np.ndarray:
+    """Row softmax of a rows x cols matrix stored with leading dimension ld:
+    binary16 storage (uint16/float16 arrays) or float32.  Returns float64
+    (rows, cols)."""
+    lib = lib or _load()
+    ld = cols if ld is None else ld
+    x = np.ascontiguousarray(X)
+    in_f32 = x.dtype == np.float32
+    if not in_f32:
+        x = _as_u16(x)
+    y = np.zeros((max(rows, 0), max(cols, 0)), dtype=np.float64)
+    rc = lib.oracle_softmax(rows, cols, x.ctypes.data, int(in_f32), ld, y.ctypes.data)
+    if rc != 0:
+        raise RuntimeError(f"oracle_softmax failed with {rc}")
+    return y
+
+
+def attention(batch, heads, Sq, Sk, D, Q, K, V, *, Dv=None, scale=None, causal=False,
+              q_strides=None, k_strides=None, v_strides=None, rows=None, nthreads=None,
+              lib=None):
+    """Reference O = softmax(scale Q K^T [causal mask]) V in float64.
+
+    Q, K, V: flat binary16 storage (uint16 or float16 arrays); strides are
+    (batch, head, row) in elements, defaulting to dense [batch][heads][S][D]
+    (Dv for V).  scale defaults to 1/sqrt(D) and is rounded to fp32 first, as
+    the GPU library receives it.  rows: optional query rows.  Returns (O,
+    err, smax): O and err shaped (batch, heads, nrows, Dv), smax shaped
+    (batch, heads, nrows) -- see ref_attention.c."""
+    lib = lib or _load()
+    Dv = D if Dv is None else Dv
+    scale = (1.0 / np.sqrt(D)) if scale is None else scale
+    scale32 = float(np.float32(scale))
+    qs = q_strides or (heads * Sq * D, Sq * D, D)
+    ks = k_strides or (heads * Sk * D, Sk * D, D)
+    vs = v_strides or (heads * Sk * Dv, Sk * Dv, Dv)
+    q, k, v = _as_u16(Q), _as_u16(K), _as_u16(V)
+    rows_arr, nrows = None, Sq
+    if rows is not None:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows = rows_arr.size
+    out = np.zeros((batch, heads, nrows, Dv), dtype=np.float64)
+    err = np.zeros_like(out)
+    smax = np.zeros((batch, heads, nrows), dtype=np.float64)
+    if nthreads is None:
+        nthreads = os.cpu_count() or 1
+    ptr = lambda x: None if x is None else x.ctypes.data
+    rc = lib.oracle_attention(batch, heads, Sq, Sk, D, Dv, ptr(q), *qs, ptr(k), *ks,
+                              ptr(v), *vs, scale32, int(bool(causal)), ptr(rows_arr), nrows,
+                              ptr(out), ptr(err), ptr(smax), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attention failed with {rc}")
+    return out, err, smax

@@ -7,14 +7,16 @@ import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "ref_gemm.c")
+SRC = os.path.join(HERE, "ref_gemm.c")              # GEMM, codecs, activations
+SRC_ATTENTION = os.path.join(HERE, "ref_attention.c")   # softmax, attention
+SOURCES = [SRC, SRC_ATTENTION]
 LIB = os.path.join(HERE, "liboracle.so")
+CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c11", "-Wall", "-Wextra",
+          "-shared", "-fPIC", "-pthread"]
 
 
 def build(verbose: bool = False) -> str:
-    cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c11",
-           "-Wall", "-Wextra", "-shared", "-fPIC", "-pthread",
-           SRC, "-o", LIB + ".tmp", "-lm"]
+    cmd = ["gcc", *CFLAGS, *SOURCES, "-o", LIB + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)

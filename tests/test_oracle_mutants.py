@@ -108,3 +108,73 @@ def test_mutant_is_caught(tmp_path, name):
     assert src.count(old) == 1, f"mutation site for {name} not unique"
     lib = _build_variant(tmp_path, name, src.replace(old, new))
     assert not _pins_pass(lib), f"pins did not catch {name}"
+
+
+# ------------------------------------------------------------ attention oracle
+
+ATTN_MUTANTS = {
+    "softmax_sum_without_max": ("        s += exp(x[j] - m);\n", "        s += exp(x[j]);\n"),
+    "online_sum_not_rescaled": ("s = (m == -INFINITY ? 0.0 : s * exp(m - m2)) + acc;",
+                                "s = s + acc;"),
+    "causal_off_by_one": ("nvis = i + Sk - j->Sq + 1;", "nvis = i + Sk - j->Sq;"),
+    "causal_top_left_aligned": ("nvis = i + Sk - j->Sq + 1;", "nvis = i + 1;"),
+    "scale_dropped": ("s[k] = j->scale * dot;", "s[k] = dot;"),
+    "v_transposed": ("Vb[k * j->v_ld + c]", "Vb[c * j->v_ld + k]"),
+    "k_head_stride_of_q": ("j->K + b * j->k_sb + h * j->k_sh", "j->K + b * j->k_sb + h * j->q_sh"),
+    "error_scale_without_abs": ("aacc += p[k] * fabs(v);", "aacc += p[k] * v;"),
+    "masked_row_divides_zero_by_zero": ("    if (m == -INFINITY) {\n        for (int64_t j = 0; j < n; ++j)\n            y[j] = 0.0;\n        return;\n    }\n",
+                                        ""),
+}
+
+
+def _attn_pins_pass(lib, monkeypatch) -> bool:
+    import test_oracle_attention as T
+    monkeypatch.setattr(oracle, "_lib", lib)
+    try:
+        for n in (1, 7, 333):
+            T.test_softmax_row_matches_scipy(n)
+        T.test_softmax_row_masked_elements_and_rows()
+        for b in (1, 3, 64):
+            T.test_online_recurrence_equals_two_pass(b)
+        T.test_softmax_matrix_on_binary16_and_fp32_storage()
+        for args in [(1, 1, 5, 9, 8, 8), (2, 3, 33, 47, 64, 64), (2, 1, 17, 65, 16, 24)]:
+            T.test_attention_matches_torch_sdpa(*args)
+        T.test_attention_matches_torch_sdpa(1, 2, 16, 16, 16, 16)
+        T.test_causal_mask_aligns_the_last_query_with_the_last_key()
+        T.test_fully_masked_rows_and_no_keys_give_zeros()
+        T.test_uniform_scores_give_the_mean_of_the_visible_values()
+        T.test_one_dominant_score_closed_form()
+        T.test_common_key_component_and_key_permutation_leave_o_unchanged()
+        T.test_strides_describe_the_tensors()
+        for args in [(3, 5, 4, 2, False), (5, 3, 4, 3, True)]:
+            T.test_attention_pure_python_brute_force(*args)
+        T.test_error_scales()
+    except (AssertionError, ValueError, OverflowError, RuntimeError):
+        return False
+    finally:
+        monkeypatch.undo()
+    return True
+
+
+def _build_attention_variant(tmp_path, name, attn_src):
+    c = tmp_path / f"{name}_attention.c"
+    so = tmp_path / f"{name}.so"
+    c.write_text(attn_src)
+    subprocess.run(["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c11",
+                    "-shared", "-fPIC", "-pthread", oracle_build.SRC, str(c), "-o", str(so), "-lm"],
+                   check=True)
+    return oracle.load_library(str(so))
+
+
+def test_unmodified_attention_oracle_passes(tmp_path, monkeypatch):
+    src = open(oracle_build.SRC_ATTENTION).read()
+    assert _attn_pins_pass(_build_attention_variant(tmp_path, "clean", src), monkeypatch)
+
+
+@pytest.mark.parametrize("name", sorted(ATTN_MUTANTS))
+def test_attention_mutant_is_caught(tmp_path, monkeypatch, name):
+    old, new = ATTN_MUTANTS[name]
+    src = open(oracle_build.SRC_ATTENTION).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique"
+    lib = _build_attention_variant(tmp_path, name, src.replace(old, new))
+    assert not _attn_pins_pass(lib, monkeypatch), f"pins did not catch {name}"
