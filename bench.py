@@ -22,6 +22,12 @@ Other workloads, one GEMM configuration per run (--case picks it):
            4096,11008,12288);
   batched  512 x (64x64 @ 64x64) NN, or 256 x Q(128x64) @ K^T(64x128)
            (--case sq64|qk); values N(0,1)/8, fp32 C, beta = 0.
+  attention  fused softmax(Q K^T / sqrt(D)) V, fp16 Q, K, V, O ~ N(0,1):
+           --case qk (256 heads of 128 x 128, D = 64: the batched Q K^T shape),
+           prefill (4 x 16 heads of 4096 x 4096, D = 128) or prefill_causal;
+           flops 4 Sq Sk D per head (half of that, plus the diagonal, causal).
+  softmax  row softmax of 8192 rows x --case cols (default 4096), fp16 in
+           and out, x ~ N(0, 4); HBM-bound: 4 bytes per element.
 Products bound by HBM bytes (intensity below the ridge of 2516.6 TFLOP/s /
 8 TB/s = 315 flop/B) report their roofline in GB/s of algorithmic bytes
 (each operand once, C read when beta != 0 and written) against 8 TB/s; the
@@ -66,7 +72,8 @@ def parse(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", choices=["square", "small", "edge", "linear", "batched"],
+    ap.add_argument("--workload", choices=["square", "small", "edge", "linear", "batched",
+                                           "attention", "softmax"],
                     default="square")
     ap.add_argument("--case", default=None,
                     help="edge: 0..3; linear: M,N; batched: sq64|qk")
@@ -319,6 +326,114 @@ def cpu_baseline(case, nrows, bias=None, act=0):
                       f"full K={case.K}){batch}, {dt:.2f} s wall including operand decode"}
 
 
+ATTN_CASES = {"qk": (2, 128, 128, 128, 64, False), "prefill": (4, 16, 4096, 4096, 128, False),
+              "prefill_causal": (4, 16, 4096, 4096, 128, True)}
+
+
+def run_attention_bench(args):
+    """The fused attention or row-softmax workload: one launch per step,
+    timed like the GEMM workloads (graph replay by default, rotating input
+    sets when HBM-bound)."""
+    import torch
+    import mixed_precision_gemm_amd as mpg
+    dev = torch.device("cuda:0")
+    g = torch.Generator("cpu").manual_seed(0)
+    stream = torch.cuda.current_stream(dev)
+    if args.workload == "attention":
+        case = args.case or "prefill"
+        B, H, S, _, D, causal = ATTN_CASES[case]
+        q, k, v = ((torch.randn((B, H, S, D), generator=g)).half().to(dev) for _ in range(3))
+        o = torch.empty_like(q)
+        st3 = lambda t: (t.stride(0), t.stride(1), t.stride(2))
+        st, h = mpg.attn_f16_plan(B, H, S, S, D, st3(q), st3(k), st3(v), st3(o), int(causal), 0)
+        if st != mpg.GEMM_OK:
+            raise mpg.GemmError(st, "attn_f16_plan")
+        kernel = mpg.attn_f16_plan_kernel(h)
+        pairs = S * (S + 1) / 2 if causal else S * S
+        flops = 4.0 * pairs * D * B * H
+        abytes = 4 * B * H * S * D * 2
+        unit_sets = [(q, k, v, o)]
+        set_bytes = abytes
+        run = lambda t: mpg.library().attn_f16_run(h, t[0].data_ptr(), t[1].data_ptr(),
+                                                   t[2].data_ptr(), t[3].data_ptr(),
+                                                   1.0 / math.sqrt(D), stream.cuda_stream)
+        desc = (f"fused attention {B}x{H} heads, Sq=Sk={S}, D={D}{' causal' if causal else ''}, "
+                f"fp16 Q/K/V/O ~ N(0,1), scale 1/sqrt(D)")
+        cfg = {"batch": B, "heads": H, "Sq": S, "Sk": S, "D": D, "causal": causal}
+    else:
+        cols = int(args.case or 4096)
+        rows = 8192
+        x = (torch.randn((rows, cols), generator=g) * 4).half().to(dev)
+        y = torch.empty_like(x)
+        kernel = "softmax_rows_reg" if cols <= 8192 else "softmax_rows_online"
+        flops = 0.0
+        abytes = rows * cols * 4
+        unit_sets = [(x, y)]
+        set_bytes = abytes
+        run = lambda t: mpg.library().attn_softmax_rows(rows, cols, t[0].data_ptr(), cols, 0,
+                                                        t[1].data_ptr(), cols, 0, stream.cuda_stream)
+        desc = f"row softmax {rows} x {cols}, fp16 in and out, x ~ N(0, 4)"
+        cfg = {"rows": rows, "cols": cols}
+    hbm_bound = flops / abytes < RIDGE
+    nsets = (math.ceil(ROTATE_BYTES / set_bytes) + 1 if hbm_bound and set_bytes < ROTATE_BYTES else 1)
+    sets = unit_sets + [tuple(t.clone() for t in unit_sets[0]) for _ in range(nsets - 1)]
+    print(f"# kernel {kernel}, {desc}, {nsets} input set(s)", file=sys.stderr, flush=True)
+
+    def step(i):
+        st = run(sets[i % nsets])
+        if st != mpg.GEMM_OK:
+            raise mpg.GemmError(st, args.workload)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    graph = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        gs = torch.cuda.Stream()
+        gs.wait_stream(stream)
+        outer = stream
+        stream = gs
+        with torch.cuda.graph(graph, stream=gs):
+            for i in range(args.steps):
+                step(i)
+        stream = outer
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    if args.workload == "attention":
+        mpg.attn_f16_destroy(h)
+    tflops = flops / (ms * 1e-3) / 1e12
+    gbs = abytes / (ms * 1e-3) / 1e9
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "algorithmic_bytes": abytes}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_F16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / PEAK_F16_TFLOPS, 4), "traffic": None,
+                "algorithmic_bytes": abytes}
+    out = {"metric": f"FP16 {args.workload} {'GB/s' if hbm_bound else 'TFLOP/s'} (fp32 softmax)",
+           "value": round(gbs if hbm_bound else tflops, 2),
+           "unit": "GB/s" if hbm_bound else "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+           "config": dict(workload=desc, kernel=kernel, input_sets=nsets,
+                          timing="hip graph replay" if graph is not None else "stream launches", **cfg),
+           "roofline": roof}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.graph is None:
@@ -330,6 +445,10 @@ def main():
 
     if args.copy_bytes:
         copy_calibration(args.copy_bytes, args.steps)
+        return
+
+    if args.workload in ("attention", "softmax"):
+        run_attention_bench(args)
         return
 
     import torch

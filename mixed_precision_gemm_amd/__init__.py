@@ -29,7 +29,9 @@ EXPORTED = ("gemm_f16f32_plan", "gemm_f16f32_run", "gemm_f16f32_destroy",
             "gemm_f16f32_status_string", "gemm_f16f32_plan_kernel",
             "gemm_bf16f32_plan", "gemm_bf16f32_run", "gemm_f16f32_set_epilogue",
             "gemm_f16f32_workspace_size", "gemm_f16f32_workspace_init",
-            "gemm_f16f32_run_noalloc")
+            "gemm_f16f32_run_noalloc",
+            "attn_f16_plan", "attn_f16_run", "attn_f16_destroy", "attn_f16_plan_kernel",
+            "attn_softmax_rows")
 
 _lib = None
 
@@ -65,6 +67,18 @@ def library() -> ctypes.CDLL:
         lib.gemm_f16f32_workspace_init.restype = ctypes.c_int
         lib.gemm_f16f32_run_noalloc.argtypes = [vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp]
         lib.gemm_f16f32_run_noalloc.restype = ctypes.c_int
+        st3 = ctypes.c_int64 * 3
+        lib.attn_f16_plan.argtypes = [ctypes.POINTER(vp), i64, i64, i64, i64, i64,
+                                      st3, st3, st3, st3, ctypes.c_int, ctypes.c_int]
+        lib.attn_f16_plan.restype = ctypes.c_int
+        lib.attn_f16_run.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp]
+        lib.attn_f16_run.restype = ctypes.c_int
+        lib.attn_f16_destroy.argtypes = [vp]
+        lib.attn_f16_destroy.restype = ctypes.c_int
+        lib.attn_f16_plan_kernel.argtypes = [vp]
+        lib.attn_f16_plan_kernel.restype = ctypes.c_char_p
+        lib.attn_softmax_rows.argtypes = [i64, i64, vp, i64, ctypes.c_int, vp, i64, ctypes.c_int, vp]
+        lib.attn_softmax_rows.restype = ctypes.c_int
         lib.gemm_f16f32_set_epilogue.argtypes = [vp, vp, ctypes.c_int]
         lib.gemm_f16f32_set_epilogue.restype = ctypes.c_int
         lib.gemm_f16f32_destroy.argtypes = [vp]
@@ -328,3 +342,88 @@ def gemm(A, B, C=None, alpha=1.0, beta=0.0, out_dtype=None, bias=None,
 # own Plan per stream.
 _PLAN_CACHE_SIZE = 64
 _plan_cache = {}
+
+
+# ------------------------------------------------------------ attention, softmax
+
+def attn_f16_plan(batch, heads, Sq, Sk, D, q_strides, k_strides, v_strides, o_strides,
+                  causal=0, out_type=GEMM_OUT_F16):
+    """Returns (status, plan_handle); strides are (batch, head, row) in elements."""
+    st3 = ctypes.c_int64 * 3
+    h = ctypes.c_void_p()
+    st = library().attn_f16_plan(ctypes.byref(h), batch, heads, Sq, Sk, D, st3(*q_strides),
+                                 st3(*k_strides), st3(*v_strides), st3(*o_strides),
+                                 int(causal), out_type)
+    return st, (h.value if st == GEMM_OK else None)
+
+
+def attn_f16_run(plan, Q, K, V, O, scale, stream=None):
+    """Q, K, V, O: device addresses (ints); stream: hipStream_t as int or None."""
+    return library().attn_f16_run(plan, Q, K, V, O, scale, stream)
+
+
+def attn_f16_destroy(plan):
+    return library().attn_f16_destroy(plan)
+
+
+def attn_f16_plan_kernel(plan):
+    return library().attn_f16_plan_kernel(plan).decode()
+
+
+def attn_softmax_rows(rows, cols, x, ldx, in_type, y, ldy, out_type, stream=None):
+    """Row softmax of device storage x into y (addresses as ints)."""
+    return library().attn_softmax_rows(rows, cols, x, ldx, in_type, y, ldy, out_type, stream)
+
+
+def _strides3(t):
+    """(batch, head, row) element strides of a (B, H, S, D) tensor view."""
+    if t.stride(-1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    return (t.stride(0), t.stride(1), t.stride(2))
+
+
+def attention(q, k, v, scale=None, causal=False, out=None, out_dtype=None):
+    """O = softmax(scale Q K^T [causal]) V for float16 CUDA tensors of shape
+    (batch, heads, S, D) (any strides with the last dimension contiguous;
+    D = 64 or 128).  Returns O (allocated when None: float16 unless out_dtype
+    is torch.float32)."""
+    import math
+    import torch
+    if q.dtype != torch.float16 or k.dtype != torch.float16 or v.dtype != torch.float16:
+        raise TypeError("Q, K and V must be float16")
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if out is None:
+        out = torch.empty((B, H, Sq, D), dtype=out_dtype or torch.float16, device=q.device)
+    out_type = GEMM_OUT_F32 if out.dtype == torch.float32 else GEMM_OUT_F16
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    st, h = attn_f16_plan(B, H, Sq, Sk, D, _strides3(q), _strides3(k), _strides3(v),
+                          _strides3(out), int(causal), out_type)
+    if st != GEMM_OK:
+        raise GemmError(st, "attn_f16_plan")
+    try:
+        st = attn_f16_run(h, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), scale,
+                          torch.cuda.current_stream().cuda_stream)
+        if st != GEMM_OK:
+            raise GemmError(st, "attn_f16_run")
+    finally:
+        attn_f16_destroy(h)
+    return out
+
+
+def softmax(x, out=None):
+    """Row softmax of a 2-D float16 or float32 CUDA tensor (rows contiguous).
+    out: a tensor of the same shape (float16 or float32), or None for one of
+    x's type; may be x itself."""
+    import torch
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with contiguous rows")
+    if out is None:
+        out = torch.empty_like(x)
+    types = {torch.float16: GEMM_OUT_F16, torch.float32: GEMM_OUT_F32}
+    st = attn_softmax_rows(x.shape[0], x.shape[1], x.data_ptr(), max(x.stride(0), x.shape[1]),
+                           types[x.dtype], out.data_ptr(), max(out.stride(0), out.shape[1]),
+                           types[out.dtype], torch.cuda.current_stream().cuda_stream)
+    if st != GEMM_OK:
+        raise GemmError(st, "attn_softmax_rows")
+    return out

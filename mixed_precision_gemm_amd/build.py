@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmpgemm.so")
-SOURCES = ["gemm_plan.cpp", "gemm_kernels.hip"]
+SOURCES = ["gemm_plan.cpp", "gemm_kernels.hip", "attention_kernels.hip"]
 # gemm_kernels.hip is compiled in parts, in parallel: part 0 is the host code
 # and the kernel table, parts 1-4 the GEMM kernels of one input type and
 # epilogue flag each (see the top of that file).
@@ -50,7 +50,7 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     jobs = []
     for src in SOURCES:
         stem = os.path.splitext(src)[0]
-        if src.endswith(".hip"):
+        if src == "gemm_kernels.hip":
             for part in range(KERNEL_PARTS):
                 jobs.append((src, os.path.join(bdir, f"{stem}_part{part}.o"),
                              [f"-DMPGEMM_PART={part}"]))

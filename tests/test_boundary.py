@@ -24,7 +24,7 @@ def declared_functions():
     for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
         text = open(h).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        for m in re.finditer(r"\b(gemm_\w+)\s*\(", text):
+        for m in re.finditer(r"\b((?:gemm|attn)_\w+)\s*\(", text):
             names.add(m.group(1))
     return names
 
@@ -363,3 +363,51 @@ def test_run_rejects_bias_overlapping_c_before_launch():
         assert mpg.gemm_f16f32_set_epilogue(p.handle, C + 64, 1) == GEMM_OK
         assert mpg.gemm_f16f32_run(p.handle, base, base + (1 << 20), C, 1.0, 0.0,
                                    None) == GEMM_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------ attention
+
+def attn_plan(B=2, H=3, Sq=100, Sk=130, D=64, qs=None, ks=None, vs=None, os_=None,
+              causal=0, out=GEMM_OUT_F16):
+    dense = lambda S: (H * S * D, S * D, D)
+    st, h = mpg.attn_f16_plan(B, H, Sq, Sk, D, qs or dense(Sq), ks or dense(Sk),
+                              vs or dense(Sk), os_ or dense(Sq), causal, out)
+    name = mpg.attn_f16_plan_kernel(h) if h else None
+    if h:
+        mpg.attn_f16_destroy(h)
+    return st, name
+
+
+def test_attention_plan_rules():
+    assert attn_plan() == (GEMM_OK, "attn_fwd_d64_q128_k64_f16")
+    assert attn_plan(D=128, causal=1, out=GEMM_OUT_F32) == (GEMM_OK, "attn_fwd_d128_q128_k64_causal_f32")
+    assert attn_plan(Sq=0) == (GEMM_OK, "none")
+    assert attn_plan(Sk=0)[0] == GEMM_OK                 # every row fully masked: zeros
+    for kw in [dict(B=0), dict(H=0), dict(Sq=-1), dict(Sk=-1), dict(causal=2), dict(out=2),
+               dict(qs=(0, 0, 63)), dict(ks=(-8, 0, 64))]:
+        assert attn_plan(**kw)[0] == GEMM_ERR_INVALID_ARG, kw
+    for kw in [dict(D=96), dict(D=32), dict(qs=(100 * 64 * 3, 100 * 64, 68)),
+               dict(os_=(1, 1, 64)), dict(Sk=1 << 25, ks=(0, 0, 64), vs=(0, 0, 64))]:
+        assert attn_plan(**kw)[0] == GEMM_ERR_UNSUPPORTED, kw
+    assert mpg.attn_f16_plan_kernel(None) == "invalid"
+    assert mpg.attn_f16_destroy(None) == GEMM_OK
+
+
+def test_attention_run_and_softmax_reject_bad_arguments_before_launch():
+    base = 1 << 30
+    st, h = mpg.attn_f16_plan(1, 1, 64, 64, 64, (0, 0, 64), (0, 0, 64), (0, 0, 64), (0, 0, 64), 0, 0)
+    assert st == GEMM_OK
+    try:
+        Q, K, V, O = base, base + (1 << 20), base + (2 << 20), base + (3 << 20)
+        assert mpg.attn_f16_run(None, Q, K, V, O, 0.125) == GEMM_ERR_INVALID_ARG
+        assert mpg.attn_f16_run(h, 0, K, V, O, 0.125) == GEMM_ERR_INVALID_ARG
+        assert mpg.attn_f16_run(h, Q + 8, K, V, O, 0.125) == GEMM_ERR_INVALID_ARG   # misaligned
+        assert mpg.attn_f16_run(h, Q, K, V, Q + 64, 0.125) == GEMM_ERR_INVALID_ARG  # O overlaps Q
+    finally:
+        mpg.attn_f16_destroy(h)
+    sm = mpg.attn_softmax_rows
+    assert sm(-1, 8, base, 8, 0, base + 4096, 8, 0) == GEMM_ERR_INVALID_ARG
+    assert sm(4, 8, base, 7, 0, base + 4096, 8, 0) == GEMM_ERR_INVALID_ARG       # ldx < cols
+    assert sm(4, 8, base, 8, 3, base + 4096, 8, 0) == GEMM_ERR_INVALID_ARG       # type
+    assert sm(4, 8, base, 8, 0, base + 8, 8, 0) == GEMM_ERR_INVALID_ARG          # partial overlap
+    assert sm(0, 8, 0, 8, 0, 0, 8, 0) == GEMM_OK                                 # empty: no-op
