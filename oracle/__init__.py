@@ -6,8 +6,10 @@ the CPU-baseline leg of bench.py may import this package.  It shares no code
 with the GPU path (mixed_precision_gemm_amd) and never imports it.
 
 The arithmetic is in ref_gemm.c (plain fp64 triple loop, own binary16 and
-bfloat16 decoders and encoders) and ref_attention.c (softmax by its
-definition and by the online recurrence, attention in fp64); this module only
+bfloat16 decoders and encoders), ref_attention.c (softmax by its
+definition and by the online recurrence, attention in fp64) and
+ref_layernorm.c (the linear layer fused with its residual and LayerNorm);
+this module only
 marshals numpy arrays through ctypes.  See the headers of the C files for what
 each function follows on the pages.
 """
@@ -59,6 +61,15 @@ def load_library(path):
                                          vp, vp, vp, ctypes.c_int]
         lib.oracle_attention.restype = ctypes.c_int
         del dp
+    if hasattr(lib, "oracle_gemm_layernorm"):
+        lib.oracle_layernorm_row.argtypes = [vp, i64, vp, vp, dbl, vp, vp]
+        lib.oracle_layernorm_row.restype = None
+        lib.oracle_gemm_layernorm.argtypes = [i64, i64, i64, i64,
+                                              ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                              i64, i64, i64, i64, i64, i64,
+                                              vp, vp, vp, dbl, dbl, vp, vp, vp, dbl, vp, i64,
+                                              vp, vp, vp, ctypes.c_int]
+        lib.oracle_gemm_layernorm.restype = ctypes.c_int
     return lib
 
 
@@ -250,3 +261,60 @@ def attention(batch, heads, Sq, Sk, D, Q, K, V, *, Dv=None, scale=None, causal=F
     if rc != 0:
         raise RuntimeError(f"oracle_attention failed with {rc}")
     return out, err, smax
+
+
+# ------------------------------------------------------------ residual + LayerNorm linear
+
+def layernorm_row(z, gamma, beta_ln, eps, lib=None):
+    """LayerNorm of one float64 row; returns (y, (mu, s, mean|z|))."""
+    lib = lib or _load()
+    z = np.ascontiguousarray(np.asarray(z, dtype=np.float64))
+    g = np.ascontiguousarray(np.asarray(gamma, dtype=np.float32))
+    b = np.ascontiguousarray(np.asarray(beta_ln, dtype=np.float32))
+    y = np.zeros_like(z)
+    st = np.zeros(3)
+    lib.oracle_layernorm_row(z.ctypes.data, z.size, g.ctypes.data, b.ctypes.data, float(eps),
+                             y.ctypes.data, st.ctypes.data)
+    return y, tuple(st)
+
+
+def gemm_layernorm(M, N, K, A, B, C=None, *, gamma, beta_ln, eps, alpha=1.0, beta=0.0,
+                   bias=None, layout_a=ROW_MAJOR, layout_b=ROW_MAJOR, out_type=OUT_F16,
+                   in_type=IN_F16, lda=None, ldb=None, ldc=None, batch=1, stride_a=0,
+                   stride_b=0, stride_c=0, rows=None, nthreads=None, lib=None):
+    """Reference Y = LayerNorm(alpha A B + beta C + bias) * gamma + beta_ln per
+    row, with the arguments of gemm().  Returns (Y, T, stats): Y and the bound
+    term T shaped (batch, nrows, N), stats (batch, nrows, 3) = mu, s =
+    sqrt(var + eps), mean |Z| (see ref_layernorm.c).  eps is rounded to fp32
+    first, as the library receives it."""
+    lib = lib or _load()
+    lda = lda if lda is not None else (K if layout_a == ROW_MAJOR else M)
+    ldb = ldb if ldb is not None else (N if layout_b == ROW_MAJOR else K)
+    ldc = ldc if ldc is not None else N
+    a, b = _as_u16(A), _as_u16(B)
+    c = None
+    if beta != 0.0:
+        c = np.ascontiguousarray(C)
+        c = _as_u16(c) if out_type in (OUT_F16, OUT_BF16) else c
+    g = np.ascontiguousarray(np.asarray(gamma, dtype=np.float32))
+    bl = np.ascontiguousarray(np.asarray(beta_ln, dtype=np.float32))
+    bias_arr = None if bias is None else np.ascontiguousarray(np.asarray(bias, dtype=np.float32))
+    rows_arr, nrows = None, M
+    if rows is not None:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows = rows_arr.size
+    y = np.zeros((batch, nrows, N))
+    t = np.zeros_like(y)
+    stats = np.zeros((batch, nrows, 3))
+    if nthreads is None:
+        nthreads = os.cpu_count() or 1
+    ptr = lambda x: None if x is None else x.ctypes.data
+    rc = lib.oracle_gemm_layernorm(batch, M, N, K, layout_a, layout_b, in_type, out_type,
+                                   lda, ldb, ldc, stride_a, stride_b, stride_c,
+                                   ptr(a), ptr(b), ptr(c), float(np.float32(alpha)),
+                                   float(np.float32(beta)), ptr(bias_arr), ptr(g), ptr(bl),
+                                   float(np.float32(eps)), ptr(rows_arr), nrows, ptr(y), ptr(t),
+                                   ptr(stats), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm_layernorm failed with {rc}")
+    return y, t, stats

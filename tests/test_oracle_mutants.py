@@ -178,3 +178,62 @@ def test_attention_mutant_is_caught(tmp_path, monkeypatch, name):
     assert src.count(old) == 1, f"mutation site for {name} not unique"
     lib = _build_attention_variant(tmp_path, name, src.replace(old, new))
     assert not _attn_pins_pass(lib, monkeypatch), f"pins did not catch {name}"
+
+
+# ------------------------------------------------------------ residual + LayerNorm oracle
+
+LN_MUTANTS = {
+    "unbiased_variance": ("const double var = n > 0 ? sq / (double)n : 0.0;",
+                          "const double var = n > 1 ? sq / (double)(n - 1) : 0.0;"),
+    "eps_outside_sqrt": ("const double s = sqrt(var + eps);", "const double s = sqrt(var) + eps;"),
+    "gamma_beta_swapped": ("y[j] = (z[j] - mu) / s * (double)gamma[j] + (double)beta_ln[j];",
+                           "y[j] = (z[j] - mu) / s * (double)beta_ln[j] + (double)gamma[j];"),
+    "mean_of_magnitudes": ("        sum += z[j];\n", "        sum += fabs(z[j]);\n"),
+    "residual_dropped": ("A, B, C, alpha, beta, bias, 0, rows,", "A, B, C, alpha, 0.0, bias, 0, rows,"),
+    "bias_dropped": ("alpha, beta, bias, 0, rows,", "alpha, beta, NULL, 0, rows,"),
+    "bound_without_deviation_term": ("(2.0 * Di + fabs(zr[j] - st[0]) * Di / s) / s", "(2.0 * Di) / s"),
+    "shift_not_subtracted": ("sq += (z[j] - mu) * (z[j] - mu);", "sq += z[j] * z[j];"),
+}
+
+
+def _ln_pins_pass(lib, monkeypatch) -> bool:
+    import test_oracle_layernorm as T
+    monkeypatch.setattr(oracle, "_lib", lib)
+    try:
+        for args in [(5, 64, 32, 0.0), (17, 333, 70, 1.0), (3, 1, 9, 0.5)]:
+            T.test_layernorm_matches_torch_on_the_gemm_oracle(*args)
+        T.test_constant_row_gives_beta_ln()
+        T.test_two_point_row_closed_form()
+        T.test_row_constant_residual_and_positive_alpha_change_nothing()
+        for args in [(3, 7, 5), (4, 16, 9)]:
+            T.test_layer_pure_python_brute_force(*args)
+        T.test_bound_term_definition()
+    except (AssertionError, ValueError, OverflowError, RuntimeError):
+        return False
+    finally:
+        monkeypatch.undo()
+    return True
+
+
+def _build_layernorm_variant(tmp_path, name, ln_src):
+    c = tmp_path / f"{name}_layernorm.c"
+    so = tmp_path / f"{name}.so"
+    c.write_text(ln_src)
+    subprocess.run(["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c11",
+                    "-shared", "-fPIC", "-pthread", oracle_build.SRC, str(c), "-o", str(so), "-lm"],
+                   check=True)
+    return oracle.load_library(str(so))
+
+
+def test_unmodified_layernorm_oracle_passes(tmp_path, monkeypatch):
+    src = open(oracle_build.SRC_LAYERNORM).read()
+    assert _ln_pins_pass(_build_layernorm_variant(tmp_path, "clean", src), monkeypatch)
+
+
+@pytest.mark.parametrize("name", sorted(LN_MUTANTS))
+def test_layernorm_mutant_is_caught(tmp_path, monkeypatch, name):
+    old, new = LN_MUTANTS[name]
+    src = open(oracle_build.SRC_LAYERNORM).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique"
+    lib = _build_layernorm_variant(tmp_path, name, src.replace(old, new))
+    assert not _ln_pins_pass(lib, monkeypatch), f"pins did not catch {name}"
