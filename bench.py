@@ -22,6 +22,10 @@ Other workloads, one GEMM configuration per run (--case picks it):
            4096,11008,12288);
   batched  512 x (64x64 @ 64x64) NN, or 256 x Q(128x64) @ K^T(64x128)
            (--case sq64|qk); values N(0,1)/8, fp32 C, beta = 0.
+  layernorm  the linear layer with its residual and LayerNorm: Y =
+           LayerNorm(X W^T + bias + R) gamma + beta_ln, X (M x 4096) ~ N(0,1),
+           W stored N x 4096 ~ N(0, 0.02), residual R ~ N(0,1) (beta = 1)
+           (--case M,N, default 2048,4096); a step is the GEMM and the row pass.
   attention  fused softmax(Q K^T / sqrt(D)) V, fp16 Q, K, V, O ~ N(0,1):
            --case qk (256 heads of 128 x 128, D = 64: the batched Q K^T shape),
            prefill (4 x 16 heads of 4096 x 4096, D = 128) or prefill_causal;
@@ -73,7 +77,7 @@ def parse(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", choices=["square", "small", "edge", "linear", "batched",
-                                           "attention", "softmax"],
+                                           "layernorm", "attention", "softmax"],
                     default="square")
     ap.add_argument("--case", default=None,
                     help="edge: 0..3; linear: M,N; batched: sq64|qk")
@@ -134,6 +138,14 @@ def make_workload(args):
         case = gi.linear_case(M, N, in_dtype=dt)
         return case, (f"linear layer X({M}x4096) W^T, W stored {N}x4096 (NT), X~N(0,1), "
                       f"W~N(0,0.02), beta=0, {tname} out"), min(M, 256)
+    if w == "layernorm":
+        M, N = (int(v) for v in (args.case or "2048,4096").split(","))
+        out = gi.OUT_BF16 if dt == "bf16" else gi.OUT_F16
+        case = gi.make_case(M, N, 4096, layout_b=gi.COL_MAJOR, dist_a="normal", dist_b="normal",
+                            dist_c="normal", sigma_a=1.0, sigma_b=0.02, sigma_c=1.0, beta=1.0,
+                            seed=0, in_dtype=dt, out_type=out)
+        return case, (f"linear layer + residual + LayerNorm: X({M}x4096) W^T + bias + R, W stored "
+                      f"{N}x4096, X~N(0,1), W~N(0,0.02), R~N(0,1), eps 1e-5, {tname} out"), min(M, 256)
     if w == "batched":
         kind = args.case or "sq64"
         case = gi.batched_case(kind)
@@ -294,7 +306,7 @@ def profiled_traffic(key):
     return None
 
 
-def cpu_baseline(case, nrows, bias=None, act=0):
+def cpu_baseline(case, nrows, bias=None, act=0, ln=None):
     """Times the oracle on `nrows` rows of C (fixed, spread over M; every
     batch item) -- about 5-15 s on 16 host threads for the largest
     workloads."""
@@ -309,14 +321,24 @@ def cpu_baseline(case, nrows, bias=None, act=0):
     bf = case.meta.get("in_dtype") == "bf16"
     cdata = u16(case.C) if case.out_type != 1 else case.C.numpy()
     t0 = time.perf_counter()
-    oracle.gemm(case.M, case.N, case.K, u16(case.A), u16(case.B), cdata,
-                alpha=case.alpha, beta=case.beta, layout_a=case.layout_a,
-                layout_b=case.layout_b, out_type=case.out_type,
-                in_type=oracle.IN_BF16 if bf else oracle.IN_F16,
-                lda=case.lda, ldb=case.ldb, ldc=case.ldc, batch=case.batch,
-                stride_a=case.stride_a, stride_b=case.stride_b, stride_c=case.stride_c,
-                bias=None if bias is None else bias.cpu().numpy(), activation=act,
-                rows=rows, nthreads=threads)
+    if ln is not None:
+        gamma, beta_ln, eps = ln
+        oracle.gemm_layernorm(case.M, case.N, case.K, u16(case.A), u16(case.B), cdata,
+                              gamma=gamma.cpu().numpy(), beta_ln=beta_ln.cpu().numpy(), eps=eps,
+                              alpha=case.alpha, beta=case.beta,
+                              bias=None if bias is None else bias.cpu().numpy(),
+                              layout_a=case.layout_a, layout_b=case.layout_b,
+                              out_type=case.out_type, in_type=oracle.IN_BF16 if bf else oracle.IN_F16,
+                              lda=case.lda, ldb=case.ldb, ldc=case.ldc, rows=rows, nthreads=threads)
+    else:
+        oracle.gemm(case.M, case.N, case.K, u16(case.A), u16(case.B), cdata,
+                    alpha=case.alpha, beta=case.beta, layout_a=case.layout_a,
+                    layout_b=case.layout_b, out_type=case.out_type,
+                    in_type=oracle.IN_BF16 if bf else oracle.IN_F16,
+                    lda=case.lda, ldb=case.ldb, ldc=case.ldc, batch=case.batch,
+                    stride_a=case.stride_a, stride_b=case.stride_b, stride_c=case.stride_c,
+                    bias=None if bias is None else bias.cpu().numpy(), activation=act,
+                    rows=rows, nthreads=threads)
     dt = time.perf_counter() - t0
     flops = 2.0 * rows.size * case.N * case.K * case.batch
     batch = f" x {case.batch} batch items" if case.batch > 1 else ""
@@ -464,10 +486,15 @@ def main():
     stream = torch.cuda.current_stream(dev)
     bias = None
     act = {"none": 0, "bias": 0, "relu": 1, "gelu": 2, "silu": 3}[args.epilogue]
-    if args.epilogue != "none":
+    if args.epilogue != "none" or args.workload == "layernorm":
         g = torch.Generator("cpu").manual_seed(1)
         bias = (torch.rand(N, generator=g) * 2 - 1).to(dev)
         plan.set_epilogue(bias, act)
+    if args.workload == "layernorm":
+        g = torch.Generator("cpu").manual_seed(2)
+        ln_gamma = (1 + 0.3 * torch.randn(N, generator=g)).to(dev)
+        ln_beta = (0.2 * torch.randn(N, generator=g)).to(dev)
+        plan.set_layernorm(ln_gamma, ln_beta, 1e-5)
 
     # HBM-bound products rotate through independent input sets past the
     # Infinity Cache when one set is small; compute-bound ones (the headline
@@ -606,7 +633,8 @@ def main():
     if mhz is None and clock.error:
         out["clock_note"] = clock.error
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(case, cpu_rows, bias, act)
+        out["cpu_baseline"] = cpu_baseline(case, cpu_rows, bias, act,
+                                           (ln_gamma, ln_beta, 1e-5) if args.workload == "layernorm" else None)
     print(json.dumps(out), flush=True)
 
 

@@ -232,6 +232,34 @@ int gemm_f16f32_run_noalloc(gemm_f16f32_plan_t plan,
  */
 int gemm_f16f32_set_epilogue(gemm_f16f32_plan_t plan, const void *bias, int activation);
 
+/*
+ * Makes the plan's later runs the linear layer fused with its residual and
+ * LayerNorm ([CATLASS] opening paragraph; the page names the fusion, this is
+ * its plainest form, a post-norm layer):
+ *   Z(b,i,j) = fp32(alpha) * sum_k A(b,i,k) B(b,k,j) + fp32(beta) * C(b,i,j) + bias[j]
+ *   C(b,i,j) <- (Z(b,i,j) - mu) / sqrt(var + eps) * gamma[j] + beta_ln[j]
+ * with mu and var the mean and the biased variance (divided by N) of row
+ * (b, i) of Z, all in fp32, then one rounding to C's type.  The bias is the
+ * one set with gemm_f16f32_set_epilogue (or none); the activation must be
+ * GEMM_ACT_NONE.
+ *   plan        a plan of either input type.
+ *   gamma, beta_ln  device pointers to N fp32 values each (4-byte aligned),
+ *               owned by the caller and read by the runs; gamma == NULL
+ *               removes the normalisation (beta_ln is then ignored).
+ *   eps         >= 0 and finite.
+ * Host only, no HIP call.  NULL plan, a misaligned or missing beta_ln, a bad
+ * eps, or an activation set on the plan -> INVALID_ARG (plan unchanged);
+ * afterwards gemm_f16f32_set_epilogue refuses an activation.
+ * Such a plan needs more workspace -- gemm_f16f32_workspace_size, queried
+ * after this call, includes it: Z in fp32 (batch * M * (N rounded up to 4)
+ * * 4 bytes) occupies the workspace's last bytes.  A run makes two launches:
+ * the GEMM writing Z, then one workgroup per row normalising it into C.
+ * Changing the setting while a run of the plan may still be launched from
+ * another thread is a race.
+ */
+int gemm_f16f32_set_layernorm(gemm_f16f32_plan_t plan, const void *gamma, const void *beta_ln,
+                              float eps);
+
 /* Frees a plan (host memory only; runs already launched are unaffected).
  * NULL is a no-op.  Returns GEMM_OK. */
 int gemm_f16f32_destroy(gemm_f16f32_plan_t plan);

@@ -29,7 +29,7 @@ EXPORTED = ("gemm_f16f32_plan", "gemm_f16f32_run", "gemm_f16f32_destroy",
             "gemm_f16f32_status_string", "gemm_f16f32_plan_kernel",
             "gemm_bf16f32_plan", "gemm_bf16f32_run", "gemm_f16f32_set_epilogue",
             "gemm_f16f32_workspace_size", "gemm_f16f32_workspace_init",
-            "gemm_f16f32_run_noalloc",
+            "gemm_f16f32_run_noalloc", "gemm_f16f32_set_layernorm",
             "attn_f16_plan", "attn_f16_run", "attn_f16_destroy", "attn_f16_plan_kernel",
             "attn_softmax_rows")
 
@@ -81,6 +81,8 @@ def library() -> ctypes.CDLL:
         lib.attn_softmax_rows.restype = ctypes.c_int
         lib.gemm_f16f32_set_epilogue.argtypes = [vp, vp, ctypes.c_int]
         lib.gemm_f16f32_set_epilogue.restype = ctypes.c_int
+        lib.gemm_f16f32_set_layernorm.argtypes = [vp, vp, vp, ctypes.c_float]
+        lib.gemm_f16f32_set_layernorm.restype = ctypes.c_int
         lib.gemm_f16f32_destroy.argtypes = [vp]
         lib.gemm_f16f32_destroy.restype = ctypes.c_int
         lib.gemm_f16f32_status_string.argtypes = [ctypes.c_int]
@@ -151,6 +153,12 @@ def gemm_bf16f32_run(plan, A, B, C, alpha, beta, workspace=None, workspace_bytes
 def gemm_f16f32_set_epilogue(plan, bias, activation):
     """bias: device address of N fp32 values (int) or None; activation GEMM_ACT_*."""
     return library().gemm_f16f32_set_epilogue(plan, bias, activation)
+
+
+def gemm_f16f32_set_layernorm(plan, gamma, beta_ln, eps):
+    """gamma, beta_ln: device addresses of N fp32 values (ints), gamma None to
+    remove the normalisation; eps: fp32."""
+    return library().gemm_f16f32_set_layernorm(plan, gamma, beta_ln, eps)
 
 
 def gemm_f16f32_destroy(plan):
@@ -255,6 +263,22 @@ class Plan:
         if st != GEMM_OK:
             raise GemmError(st, "gemm_f16f32_set_epilogue")
         self._bias = bias
+
+    def set_layernorm(self, gamma=None, beta_ln=None, eps=1e-5):
+        """Later runs: C = LayerNorm(alpha A B + beta C + bias) * gamma + beta_ln
+        per row.  gamma, beta_ln: contiguous CUDA float32 tensors of N values
+        (kept alive here), or None to remove the normalisation."""
+        addr = lambda t: None if t is None else (t if isinstance(t, int) else t.data_ptr())
+        for t in (gamma, beta_ln):
+            if t is not None and not isinstance(t, int):
+                import torch
+                if t.dtype != torch.float32 or t.numel() < self.shape[1] or not t.is_contiguous():
+                    raise TypeError("gamma and beta_ln must be contiguous float32 tensors of N values")
+        st = gemm_f16f32_set_layernorm(self.handle, addr(gamma), addr(beta_ln), eps)
+        if st != GEMM_OK:
+            raise GemmError(st, "gemm_f16f32_set_layernorm")
+        self._ln = (gamma, beta_ln)
+        self._ws = None if self._ws is not None and self._ws.numel() < self.workspace_bytes() else self._ws
 
     def close(self):
         if self.handle is not None:

@@ -88,6 +88,24 @@ inline int64_t workspace_bytes(int64_t split_bytes, int pack_mask, int64_t pack_
     return kCounterBytes + split_bytes + packs;
 }
 
+// Residual + LayerNorm plans (gemm_f16f32_set_layernorm) also keep the fp32
+// product Z = alpha A B in the workspace: its last ln_z_bytes, 256-byte
+// aligned, after the counters and whatever the GEMM itself needs (so at or
+// past kCounterBytes even when the GEMM needs nothing).
+inline int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// The fp32 row pass of a LayerNorm plan (gemm_layernorm.cpp's launcher, in the
+// host part of gemm_kernels.hip): Y = LayerNorm(Z + beta C + bias) gamma +
+// beta_ln over each of rows = batch * M rows of N, written into C.
+struct LayerNormArgs {
+    const float *Z;
+    void *C;                  // 16-bit (out_type) or fp32 storage
+    const float *bias, *gamma, *beta_ln;
+    int64_t N, M, ldz, sz, ldc, sc, rows;
+    float beta, eps;
+    int out_type;             // GEMM_OUT_*
+};
+
 }  // namespace mpgemm
 
 struct gemm_f16f32_plan_s {
@@ -115,5 +133,26 @@ struct gemm_f16f32_plan_s {
     // Fused epilogue (gemm_f16f32_set_epilogue): C = act(alpha A B + beta C + bias).
     const float *bias;     // device pointer to N fp32 values, or NULL
     int act;               // mpgemm::Activation
+    // Residual + LayerNorm (gemm_f16f32_set_layernorm): C = LayerNorm(alpha A B +
+    // beta C + bias) * gamma + beta_ln over each row of C.
+    int ln;                // 0 or 1
+    const float *ln_gamma, *ln_beta;
+    float ln_eps;
+    int64_t ln_ldz;        // row stride of the fp32 Z (N rounded up to 4)
+    int64_t ln_z_bytes;    // bytes of Z (batch * M * ln_ldz * 4, 256-byte multiple)
     char kernel_name[64];
 };
+
+namespace mpgemm {
+
+// Workspace bytes of a run of plan p that repacks the operands in pack_mask:
+// the GEMM's own part, then, for a LayerNorm plan, room for Z after it.
+inline int64_t plan_workspace(const gemm_f16f32_plan_s &p, int pack_mask) {
+    if (p.tile < 0) return 0;
+    const int64_t n = workspace_bytes(p.split_bytes, pack_mask, p.pack_a_bytes, p.pack_b_bytes);
+    if (!p.ln) return n;
+    return align256(n > kCounterBytes ? n : kCounterBytes) + p.ln_z_bytes;
+}
+
+}  // namespace mpgemm
+

@@ -1714,6 +1714,104 @@ bool ranges_overlap(uintptr_t a, int64_t a_bytes, uintptr_t b, int64_t b_bytes) 
     return a < b + (uintptr_t)b_bytes && b < a + (uintptr_t)a_bytes;
 }
 
+// ---------------------------------------------------------------------------
+// The row pass of the linear layer fused with its residual and LayerNorm
+// ([CATLASS] opening paragraph: the case the page's author was tuning; §3:
+// the matrix product in fp16 with fp32 accumulation, the normalisation's
+// reductions in fp32).  The GEMM kernels write Z = alpha A B in fp32 into the
+// workspace (no rounding in between); one workgroup per row then forms
+// x = Z + beta C + bias, its mean and (biased) variance over the N columns by
+// two passes over the values it holds in registers, and writes
+// (x - mean) / sqrt(var + eps) * gamma + beta_ln into C.  Rows longer than
+// 16384 are read three times instead (the second and third reads hit the L2).
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ inline float load_c_elem(const void *C, int64_t i) { return (float)((const T *)C)[i]; }
+template <typename T>
+__device__ inline void store_c_elem(void *C, int64_t i, float v) { ((T *)C)[i] = (T)v; }
+
+// Sum over the 256 threads of a workgroup (red: 4 floats of LDS).
+__device__ inline float block_sum256(float v, float *red) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    const float t = red[0] + red[1] + red[2] + red[3];
+    __syncthreads();
+    return t;
+}
+
+template <int VPT, typename T>
+__global__ __launch_bounds__(256) void gemm_layernorm_rows(LayerNormArgs a) {
+    __shared__ float red[4];
+    const int64_t r = blockIdx.x;
+    const int64_t b = r / a.M, i = r - b * a.M;
+    const float *z = a.Z + b * a.sz + i * a.ldz;
+    const int64_t cbase = b * a.sc + i * a.ldc;
+    const int t = threadIdx.x;
+    const float invn = 1.0f / (float)a.N;
+    auto input = [&](int64_t j) __attribute__((always_inline)) {
+        float x = z[j];
+        if (a.beta != 0.0f) x += a.beta * load_c_elem<T>(a.C, cbase + j);
+        if (a.bias) x += a.bias[j];
+        return x;
+    };
+    if constexpr (VPT > 0) {
+        float x[VPT];
+        float s = 0.f;
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const int64_t j = (int64_t)v * 256 + t;
+            x[v] = j < a.N ? input(j) : 0.f;
+            s += x[v];
+        }
+        const float mean = block_sum256(s, red) * invn;
+        float q = 0.f;
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const int64_t j = (int64_t)v * 256 + t;
+            const float d = x[v] - mean;
+            if (j < a.N) q += d * d;
+        }
+        const float rs = 1.0f / sqrtf(block_sum256(q, red) * invn + a.eps);
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const int64_t j = (int64_t)v * 256 + t;
+            if (j < a.N) store_c_elem<T>(a.C, cbase + j, (x[v] - mean) * rs * a.gamma[j] + a.beta_ln[j]);
+        }
+    } else {
+        float s = 0.f;
+        for (int64_t j = t; j < a.N; j += 256) s += input(j);
+        const float mean = block_sum256(s, red) * invn;
+        float q = 0.f;
+        for (int64_t j = t; j < a.N; j += 256) {
+            const float d = input(j) - mean;
+            q += d * d;
+        }
+        const float rs = 1.0f / sqrtf(block_sum256(q, red) * invn + a.eps);
+        for (int64_t j = t; j < a.N; j += 256)
+            store_c_elem<T>(a.C, cbase + j, (input(j) - mean) * rs * a.gamma[j] + a.beta_ln[j]);
+    }
+}
+
+template <typename T>
+int launch_layernorm_t(const LayerNormArgs &a, hipStream_t stream) {
+    typedef void (*Fn)(LayerNormArgs);
+    const Fn fn = a.N <= 2048 ? gemm_layernorm_rows<8, T> : a.N <= 4096 ? gemm_layernorm_rows<16, T>
+                : a.N <= 8192 ? gemm_layernorm_rows<32, T> : a.N <= 16384 ? gemm_layernorm_rows<64, T>
+                : gemm_layernorm_rows<0, T>;
+    LayerNormArgs arg = a;
+    void *args[] = {&arg};
+    return hipLaunchKernel((const void *)fn, dim3((unsigned)a.rows), dim3(256), args, 0, stream) == hipSuccess
+               ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+int launch_layernorm(const LayerNormArgs &a, hipStream_t stream) {
+    if (a.out_type == GEMM_OUT_F32) return launch_layernorm_t<float>(a, stream);
+    if (a.out_type == GEMM_OUT_BF16) return launch_layernorm_t<__bf16>(a, stream);
+    return launch_layernorm_t<_Float16>(a, stream);
+}
+
 // Zero-fills the first `words` 32-bit words of a workspace (its split-K
 // counters).  A kernel rather than hipMemsetAsync, so that the call is an
 // ordinary stream-ordered launch wherever it is made.
@@ -1731,8 +1829,7 @@ int run_plan(gemm_f16f32_plan_t plan, const void *A, const void *B, void *C, flo
     if (p.M == 0 || p.N == 0) return GEMM_OK;
     if (!C || !A || !B) return GEMM_ERR_INVALID_ARG;
     if (ws_bytes < 0 || (ws_bytes > 0 && !ws) || (uintptr_t)ws % 256 != 0) return GEMM_ERR_INVALID_ARG;
-    if (ws_bytes < workspace_bytes(p.split_bytes, p.pack, p.pack_a_bytes, p.pack_b_bytes))
-        return GEMM_ERR_INVALID_ARG;
+    if (ws_bytes < plan_workspace(p, p.K > 0 ? p.pack : 0)) return GEMM_ERR_INVALID_ARG;
     const int64_t cbytes = p.extent_c * (p.out_type == GEMM_OUT_F32 ? 4 : 2);
     if (p.K > 0 && (ranges_overlap((uintptr_t)C, cbytes, (uintptr_t)A, p.extent_a * 2) ||
                     ranges_overlap((uintptr_t)C, cbytes, (uintptr_t)B, p.extent_b * 2)))
@@ -1740,6 +1837,41 @@ int run_plan(gemm_f16f32_plan_t plan, const void *A, const void *B, void *C, flo
     if (ranges_overlap((uintptr_t)C, cbytes, (uintptr_t)ws, ws_bytes)) return GEMM_ERR_INVALID_ARG;
     if (p.bias && ranges_overlap((uintptr_t)C, cbytes, (uintptr_t)p.bias, p.N * 4))
         return GEMM_ERR_INVALID_ARG;
+
+    if (p.ln) {
+        // Z = alpha A B in fp32 into the last bytes of the workspace (the
+        // plan's kernels with an fp32 C, no epilogue), then the row pass.
+        const int64_t z_off = (ws_bytes - p.ln_z_bytes) / 256 * 256;
+        float *Z = (float *)((char *)ws + z_off);
+        gemm_f16f32_plan_s q = p;
+        q.out_type = GEMM_OUT_F32;
+        q.ldc = p.ln_ldz;
+        q.stride_c = p.M * p.ln_ldz;
+        q.extent_c = (p.batch - 1) * q.stride_c + (p.M - 1) * q.ldc + p.N;
+        q.bias = nullptr;
+        q.act = ACT_NONE;
+        q.ln = 0;
+        const int st = run_plan(&q, A, B, Z, alpha, 0.0f, ws, z_off, stream);
+        if (st != GEMM_OK) return st;
+        LayerNormArgs la;
+        la.Z = Z;
+        la.C = C;
+        la.bias = p.bias;
+        la.gamma = p.ln_gamma;
+        la.beta_ln = p.ln_beta;
+        la.N = p.N;
+        la.M = p.M;
+        la.ldz = p.ln_ldz;
+        la.sz = q.stride_c;
+        la.ldc = p.ldc;
+        la.sc = p.stride_c;
+        la.rows = p.batch * p.M;
+        la.beta = beta;
+        la.eps = p.ln_eps;
+        la.out_type = p.out_type;
+        if (la.rows > 0x7fffffff) return GEMM_ERR_UNSUPPORTED;
+        return launch_layernorm(la, (hipStream_t)stream);
+    }
 
     // Operands copied into the workspace first: those whose shape needs it,
     // and, for the direct and streaming kernels, any whose pointer is not
@@ -1936,15 +2068,13 @@ extern "C" int gemm_f16f32_run_noalloc(gemm_f16f32_plan_t plan, const void *A, c
                                        void *C, float alpha, float beta, void *stream) {
     if (!plan) return GEMM_ERR_INVALID_ARG;
     if (plan->M == 0 || plan->N == 0) return GEMM_OK;
-    if (workspace_bytes(plan->split_bytes, plan->pack, plan->pack_a_bytes, plan->pack_b_bytes) >
-        kScratchBytes)
-        return GEMM_ERR_SCRATCH;
+    if (plan_workspace(*plan, plan->pack) > kScratchBytes) return GEMM_ERR_SCRATCH;
     if (!A || !B || !C) return GEMM_ERR_INVALID_ARG;
     void *ws = nullptr;
     int64_t ws_bytes = 0;
     // Plans that need scratch, and those that repack misaligned operands into
     // it when it holds the copies, use the device's array.
-    if (plan->split_bytes > 0 || plan->pack != 0 || plan->fast) {
+    if (plan->split_bytes > 0 || plan->pack != 0 || plan->fast || plan->ln) {
         const int st = device_scratch(&ws, (hipStream_t)stream);
         if (st != GEMM_OK) return st;
         ws_bytes = kScratchBytes;

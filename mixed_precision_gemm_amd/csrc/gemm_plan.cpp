@@ -11,6 +11,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <math.h>
+
 #include <algorithm>
 #include <new>
 
@@ -206,6 +208,8 @@ int make_plan(int in_type, gemm_f16f32_plan_t *out, int64_t M, int64_t N, int64_
             return GEMM_ERR_UNSUPPORTED;
         }
     }
+    p->ln_ldz = ceil_div(N, 4) * 4;
+    p->ln_z_bytes = align256(batch * M * p->ln_ldz * 4);
     p->group_m = 4;
     const int64_t tiles = ceil_div(M, kTiles[p->tile].bm) * ceil_div(N, kTiles[p->tile].bn) * batch;
     choose_ksplit(p, tiles);
@@ -252,10 +256,29 @@ extern "C" int gemm_bf16f32_plan(gemm_f16f32_plan_t *out, int64_t M, int64_t N,
                      batch, stride_a, stride_b, stride_c);
 }
 
+extern "C" int gemm_f16f32_set_layernorm(gemm_f16f32_plan_t plan, const void *gamma,
+                                         const void *beta_ln, float eps) {
+    if (!plan) return GEMM_ERR_INVALID_ARG;
+    if (!gamma) {                      // back to the plain (or activation) epilogue
+        plan->ln = 0;
+        plan->ln_gamma = plan->ln_beta = nullptr;
+        return GEMM_OK;
+    }
+    if (!beta_ln || (uintptr_t)gamma % 4 != 0 || (uintptr_t)beta_ln % 4 != 0) return GEMM_ERR_INVALID_ARG;
+    if (!(eps >= 0.0f) || eps == INFINITY) return GEMM_ERR_INVALID_ARG;
+    if (plan->act != ACT_NONE) return GEMM_ERR_INVALID_ARG;   // the normalisation replaces it
+    plan->ln = 1;
+    plan->ln_gamma = (const float *)gamma;
+    plan->ln_beta = (const float *)beta_ln;
+    plan->ln_eps = eps;
+    return GEMM_OK;
+}
+
 extern "C" int gemm_f16f32_set_epilogue(gemm_f16f32_plan_t plan, const void *bias,
                                         int activation) {
     if (!plan) return GEMM_ERR_INVALID_ARG;
     if (activation < ACT_NONE || activation > ACT_SILU) return GEMM_ERR_INVALID_ARG;
+    if (plan->ln && activation != ACT_NONE) return GEMM_ERR_INVALID_ARG;
     if ((uintptr_t)bias % 4 != 0) return GEMM_ERR_INVALID_ARG;
     plan->bias = (const float *)bias;
     plan->act = activation;
@@ -266,8 +289,7 @@ extern "C" int gemm_f16f32_workspace_size(gemm_f16f32_plan_t plan, int flags, in
     if (!plan || !bytes || (flags & ~GEMM_WS_ANY_ALIGNMENT) != 0) return GEMM_ERR_INVALID_ARG;
     int mask = plan->pack;
     if ((flags & GEMM_WS_ANY_ALIGNMENT) && plan->fast) mask = 3;
-    *bytes = plan->tile < 0 ? 0 : workspace_bytes(plan->split_bytes, mask, plan->pack_a_bytes,
-                                                  plan->pack_b_bytes);
+    *bytes = plan_workspace(*plan, mask);
     return GEMM_OK;
 }
 

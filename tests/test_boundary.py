@@ -411,3 +411,34 @@ def test_attention_run_and_softmax_reject_bad_arguments_before_launch():
     assert sm(4, 8, base, 8, 3, base + 4096, 8, 0) == GEMM_ERR_INVALID_ARG       # type
     assert sm(4, 8, base, 8, 0, base + 8, 8, 0) == GEMM_ERR_INVALID_ARG          # partial overlap
     assert sm(0, 8, 0, 8, 0, 0, 8, 0) == GEMM_OK                                 # empty: no-op
+
+
+# ------------------------------------------------------------ residual + LayerNorm
+
+def test_set_layernorm_validation_and_workspace():
+    from mixed_precision_gemm_amd import GEMM_ACT_GELU, GEMM_ACT_NONE
+    base = 1 << 30
+    assert mpg.gemm_f16f32_set_layernorm(None, base, base + 4096, 1e-5) == GEMM_ERR_INVALID_ARG
+    with mpg.Plan(2048, 4096, 4096, layout_b=GEMM_COL_MAJOR) as p:
+        h = p.handle
+        plain = p.workspace_bytes()
+        assert plain == 0
+        assert mpg.gemm_f16f32_set_layernorm(h, base + 2, base + 4096, 1e-5) == GEMM_ERR_INVALID_ARG
+        assert mpg.gemm_f16f32_set_layernorm(h, base, None, 1e-5) == GEMM_ERR_INVALID_ARG
+        assert mpg.gemm_f16f32_set_layernorm(h, base, base + 4096, -1.0) == GEMM_ERR_INVALID_ARG
+        assert mpg.gemm_f16f32_set_layernorm(h, base, base + 4096, float("nan")) == GEMM_ERR_INVALID_ARG
+        assert mpg.gemm_f16f32_set_epilogue(h, None, GEMM_ACT_GELU) == GEMM_OK
+        assert mpg.gemm_f16f32_set_layernorm(h, base, base + 4096, 1e-5) == GEMM_ERR_INVALID_ARG
+        assert mpg.gemm_f16f32_set_epilogue(h, base + 8192, GEMM_ACT_NONE) == GEMM_OK
+        assert mpg.gemm_f16f32_set_layernorm(h, base, base + 4096, 1e-5) == GEMM_OK
+        assert mpg.gemm_f16f32_set_epilogue(h, base + 8192, GEMM_ACT_GELU) == GEMM_ERR_INVALID_ARG
+        # Z in fp32 after the reserved counter area
+        assert p.workspace_bytes() == 4096 + 2048 * 4096 * 4
+        assert mpg.gemm_f16f32_set_layernorm(h, None, None, 0.0) == GEMM_OK
+        assert p.workspace_bytes() == plain
+    with mpg.Plan(16, 4095, 4096) as p:          # split-K and a repacked B, plus Z
+        assert mpg.gemm_f16f32_set_layernorm(p.handle, base, base + 4096 * 4, 0.0) == GEMM_OK
+        gemm_part = 4096 + 8 * 32 * 65536 + (4096 * 4096 * 2)
+        z = (16 * 4096 * 4 + 255) // 256 * 256
+        assert "_sk8" in p.kernel and p.kernel.endswith("_pkb")
+        assert p.workspace_bytes() == (gemm_part + 255) // 256 * 256 + z
