@@ -8,8 +8,8 @@ with the GPU path (mixed_precision_gemm_amd) and never imports it.
 The arithmetic is in ref_gemm.c (plain fp64 triple loop, own binary16 and
 bfloat16 decoders and encoders), ref_attention.c (softmax by its
 definition and by the online recurrence, attention in fp64) and
-ref_layernorm.c (the linear layer fused with its residual and LayerNorm);
-this module only
+ref_layernorm.c (the linear layer fused with its residual and LayerNorm)
+and ref_conv.c (2-D convolution by its definition); this module only
 marshals numpy arrays through ctypes.  See the headers of the C files for what
 each function follows on the pages.
 """
@@ -70,6 +70,12 @@ def load_library(path):
                                               vp, vp, vp, dbl, dbl, vp, vp, vp, dbl, vp, i64,
                                               vp, vp, vp, ctypes.c_int]
         lib.oracle_gemm_layernorm.restype = ctypes.c_int
+    if hasattr(lib, "oracle_conv2d"):
+        lib.oracle_conv_out_dim.argtypes = [i64, i64, i64, i64, i64]
+        lib.oracle_conv_out_dim.restype = i64
+        lib.oracle_conv2d.argtypes = [i64] * 13 + [vp, vp, vp, ctypes.c_int, dbl, dbl, vp,
+                                                  ctypes.c_int, vp, i64, vp, vp, ctypes.c_int]
+        lib.oracle_conv2d.restype = ctypes.c_int
     return lib
 
 
@@ -318,3 +324,45 @@ def gemm_layernorm(M, N, K, A, B, C=None, *, gamma, beta_ln, eps, alpha=1.0, bet
     if rc != 0:
         raise RuntimeError(f"oracle_gemm_layernorm failed with {rc}")
     return y, t, stats
+
+
+# ------------------------------------------------------------ convolution
+
+def conv_out_dim(size, k, stride, pad, dil, lib=None):
+    return (lib or _load()).oracle_conv_out_dim(size, k, stride, pad, dil)
+
+
+def conv2d(N, H, W, C, K, R, S, x, w, y_old=None, *, stride=(1, 1), pad=(0, 0), dil=(1, 1),
+           alpha=1.0, beta=0.0, bias=None, activation=ACT_NONE, out_type=OUT_F16, rows=None,
+           nthreads=None, lib=None):
+    """Reference 2-D convolution: x NHWC, w KRSC (flat binary16 storage), y_old
+    NPQK (binary16 or fp32, read when beta != 0).  Returns (ref, scale), each
+    shaped (nrows, K) with nrows = N*P*Q unless rows (output pixels) is given."""
+    lib = lib or _load()
+    P = conv_out_dim(H, R, stride[0], pad[0], dil[0], lib)
+    Q = conv_out_dim(W, S, stride[1], pad[1], dil[1], lib)
+    if P < 0 or Q < 0:
+        raise ValueError("the filter window does not fit the padded input")
+    xa, wa = _as_u16(x), _as_u16(w)
+    yo = None
+    if beta != 0.0:
+        yo = np.ascontiguousarray(y_old)
+        yo = yo if out_type == OUT_F32 else _as_u16(yo)
+    bias_arr = None if bias is None else np.ascontiguousarray(np.asarray(bias, dtype=np.float32))
+    rows_arr, nrows = None, N * P * Q
+    if rows is not None:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows = rows_arr.size
+    ref = np.zeros((nrows, K))
+    scale = np.zeros((nrows, K))
+    if nthreads is None:
+        nthreads = os.cpu_count() or 1
+    ptr = lambda a: None if a is None else a.ctypes.data
+    rc = lib.oracle_conv2d(N, H, W, C, K, R, S, stride[0], stride[1], pad[0], pad[1], dil[0],
+                           dil[1], ptr(xa), ptr(wa), ptr(yo), int(out_type == OUT_F32),
+                           float(np.float32(alpha)), float(np.float32(beta)), ptr(bias_arr),
+                           int(activation), ptr(rows_arr), nrows, ptr(ref), ptr(scale),
+                           int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_conv2d failed with {rc}")
+    return ref, scale

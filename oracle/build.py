@@ -10,7 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "ref_gemm.c")              # GEMM, codecs, activations
 SRC_ATTENTION = os.path.join(HERE, "ref_attention.c")   # softmax, attention
 SRC_LAYERNORM = os.path.join(HERE, "ref_layernorm.c")   # residual + LayerNorm linear
-SOURCES = [SRC, SRC_ATTENTION, SRC_LAYERNORM]
+SRC_CONV = os.path.join(HERE, "ref_conv.c")             # 2-D convolution
+SOURCES = [SRC, SRC_ATTENTION, SRC_LAYERNORM, SRC_CONV]
 LIB = os.path.join(HERE, "liboracle.so")
 CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c11", "-Wall", "-Wextra",
           "-shared", "-fPIC", "-pthread"]

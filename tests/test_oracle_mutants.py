@@ -237,3 +237,68 @@ def test_layernorm_mutant_is_caught(tmp_path, monkeypatch, name):
     assert src.count(old) == 1, f"mutation site for {name} not unique"
     lib = _build_layernorm_variant(tmp_path, name, src.replace(old, new))
     assert not _ln_pins_pass(lib, monkeypatch), f"pins did not catch {name}"
+
+
+# ------------------------------------------------------------ convolution oracle
+
+CONV_MUTANTS = {
+    "padding_not_subtracted": ("const int64_t ih = p * j->sh - j->ph + r * j->dh;",
+                               "const int64_t ih = p * j->sh + r * j->dh;"),
+    "dilation_ignored": ("const int64_t iw = q * j->sw - j->pw + ss * j->dw;",
+                         "const int64_t iw = q * j->sw - j->pw + ss;"),
+    "stride_ignored": ("const int64_t ih = p * j->sh - j->ph + r * j->dh;",
+                       "const int64_t ih = p - j->ph + r * j->dh;"),
+    "filter_flipped": ("const uint16_t *wp = j->w + ((k * j->R + r) * j->S + ss) * j->C;",
+                       "const uint16_t *wp = j->w + ((k * j->R + (j->R - 1 - r)) * j->S + (j->S - 1 - ss)) * j->C;"),
+    "output_size_without_dilation": ("const int64_t span = dil * (k - 1) + 1;",
+                                     "const int64_t span = k;"),
+    "border_taps_kept": ("                if (ih < 0 || ih >= j->H)\n                    continue;\n", ""),
+    "scale_without_abs": ("a += fabs(prod);", "a += prod;"),
+    "beta_term_dropped": ("double v = j->alpha * s + j->beta * yo;", "double v = j->alpha * s;"),
+}
+
+
+def _conv_pins_pass(lib, monkeypatch) -> bool:
+    import test_oracle_conv as T
+    monkeypatch.setattr(oracle, "_lib", lib)
+    try:
+        for args in [(1, 5, 5, 3, 2, 3, 3, (1, 1), (0, 0), (1, 1)),
+                     (2, 9, 7, 8, 5, 3, 3, (2, 1), (1, 1), (1, 1)),
+                     (1, 12, 10, 16, 4, 3, 2, (1, 2), (2, 0), (2, 3))]:
+            T.test_conv_matches_torch(*args)
+        T.test_one_by_one_filter_is_the_gemm()
+        T.test_identity_filter_returns_the_input()
+        T.test_all_ones_count_the_taps_inside_the_image()
+        T.test_output_size()
+        T.test_epilogue_composition()
+        T.test_conv_pure_python_brute_force((1, 5, 4, 2, 2, 3, 2, (2, 1), (1, 1), (1, 2)))
+        T.test_scale_equals_value_for_nonnegative_inputs()
+    except (AssertionError, ValueError, OverflowError, RuntimeError, IndexError):
+        return False
+    finally:
+        monkeypatch.undo()
+    return True
+
+
+def _build_conv_variant(tmp_path, name, conv_src):
+    c = tmp_path / f"{name}_conv.c"
+    so = tmp_path / f"{name}.so"
+    c.write_text(conv_src)
+    subprocess.run(["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c11",
+                    "-shared", "-fPIC", "-pthread", oracle_build.SRC, str(c), "-o", str(so), "-lm"],
+                   check=True)
+    return oracle.load_library(str(so))
+
+
+def test_unmodified_conv_oracle_passes(tmp_path, monkeypatch):
+    src = open(oracle_build.SRC_CONV).read()
+    assert _conv_pins_pass(_build_conv_variant(tmp_path, "clean", src), monkeypatch)
+
+
+@pytest.mark.parametrize("name", sorted(CONV_MUTANTS))
+def test_conv_mutant_is_caught(tmp_path, monkeypatch, name):
+    old, new = CONV_MUTANTS[name]
+    src = open(oracle_build.SRC_CONV).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique"
+    lib = _build_conv_variant(tmp_path, name, src.replace(old, new))
+    assert not _conv_pins_pass(lib, monkeypatch), f"pins did not catch {name}"
