@@ -30,6 +30,10 @@ Other workloads, one GEMM configuration per run (--case picks it):
            --case qk (256 heads of 128 x 128, D = 64: the batched Q K^T shape),
            prefill (4 x 16 heads of 4096 x 4096, D = 128) or prefill_causal;
            flops 4 Sq Sk D per head (half of that, plus the diagonal, causal).
+  conv     implicit-GEMM convolution, NHWC fp16 ~ N(0,1), KRSC filters:
+           --case r50 (32 x 56 x 56 x 64 -> 64, 3x3, pad 1: a ResNet-50 stage-2
+           layer, the default) or stem (32 x 224 x 224 x 3 -> 64, 7x7, stride
+           2, pad 3); flops 2 N P Q K R S C.
   softmax  row softmax of 8192 rows x --case cols (default 4096), fp16 in
            and out, x ~ N(0, 4); HBM-bound: 4 bytes per element.
 Products bound by HBM bytes (intensity below the ridge of 2516.6 TFLOP/s /
@@ -77,7 +81,7 @@ def parse(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", choices=["square", "small", "edge", "linear", "batched",
-                                           "layernorm", "attention", "softmax"],
+                                           "layernorm", "attention", "softmax", "conv"],
                     default="square")
     ap.add_argument("--case", default=None,
                     help="edge: 0..3; linear: M,N; batched: sq64|qk")
@@ -272,8 +276,9 @@ def bench_key(args):
     if args.workload == "square":
         M, N, K = args.shape
         return f"square {args.layout} {M}x{N}x{K} {args.dtype}"
-    case = args.case if args.case is not None else {"edge": "0", "linear": "16,11008",
-                                                    "batched": "sq64"}.get(args.workload, "0")
+    case = args.case if args.case is not None else {
+        "edge": "0", "linear": "16,11008", "batched": "sq64", "layernorm": "2048,4096",
+        "attention": "prefill", "conv": "r50", "softmax": "4096"}.get(args.workload, "0")
     return f"{args.workload} {case} {args.dtype}"
 
 
@@ -382,6 +387,28 @@ def run_attention_bench(args):
         desc = (f"fused attention {B}x{H} heads, Sq=Sk={S}, D={D}{' causal' if causal else ''}, "
                 f"fp16 Q/K/V/O ~ N(0,1), scale 1/sqrt(D)")
         cfg = {"batch": B, "heads": H, "Sq": S, "Sk": S, "D": D, "causal": causal}
+    elif args.workload == "conv":
+        case = args.case or "r50"
+        N, H, W, C, K, R, S, st_, pd = {"r50": (32, 56, 56, 64, 64, 3, 3, 1, 1),
+                                        "stem": (32, 224, 224, 3, 64, 7, 7, 2, 3)}[case]
+        x = torch.randn((N, H, W, C), generator=g).half().to(dev)
+        w = (torch.randn((K, R, S, C), generator=g) / math.sqrt(R * S * C)).half().to(dev)
+        st, h = mpg.conv_f16_plan(N, H, W, C, K, R, S, (st_, st_), (pd, pd), (1, 1), 0)
+        if st != mpg.GEMM_OK:
+            raise mpg.GemmError(st, "conv_f16_plan")
+        _, P, Q = mpg.conv_f16_output_size(h)
+        y = torch.empty((N, P, Q, K), dtype=torch.float16, device=dev)
+        kernel = mpg.conv_f16_plan_kernel(h)
+        flops = 2.0 * N * P * Q * K * R * S * C
+        abytes = 2 * (x.numel() + w.numel() + y.numel())
+        unit_sets = [(x, w, y)]
+        set_bytes = abytes
+        run = lambda t: mpg.library().conv_f16_run(h, t[0].data_ptr(), t[1].data_ptr(),
+                                                   t[2].data_ptr(), 1.0, 0.0, None, 0,
+                                                   stream.cuda_stream)
+        desc = (f"implicit-GEMM conv {N}x{H}x{W}x{C} -> {K}, {R}x{S} stride {st_} pad {pd}, "
+                f"fp16 NHWC/KRSC/NPQK")
+        cfg = {"N": N, "H": H, "W": W, "C": C, "K": K, "R": R, "S": S, "stride": st_, "pad": pd}
     else:
         cols = int(args.case or 4096)
         rows = 8192
@@ -436,22 +463,27 @@ def run_attention_bench(args):
     ms = ev0.elapsed_time(ev1) / args.steps
     if args.workload == "attention":
         mpg.attn_f16_destroy(h)
+    elif args.workload == "conv":
+        mpg.conv_f16_destroy(h)
     tflops = flops / (ms * 1e-3) / 1e12
     gbs = abytes / (ms * 1e-3) / 1e9
+    traffic = profiled_traffic(bench_key(args))
     if hbm_bound:
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "algorithmic_bytes": abytes}
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic, "algorithmic_bytes": abytes}
     else:
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_F16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(tflops / PEAK_F16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(tflops / PEAK_F16_TFLOPS, 4), "traffic": traffic,
                 "algorithmic_bytes": abytes}
-    out = {"metric": f"FP16 {args.workload} {'GB/s' if hbm_bound else 'TFLOP/s'} (fp32 softmax)",
+    what = "(fp32 accumulation)" if args.workload == "conv" else "(fp32 softmax)"
+    out = {"metric": f"FP16 {args.workload} {'GB/s' if hbm_bound else 'TFLOP/s'} {what}",
            "value": round(gbs if hbm_bound else tflops, 2),
            "unit": "GB/s" if hbm_bound else "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
            "config": dict(workload=desc, kernel=kernel, input_sets=nsets,
                           timing="hip graph replay" if graph is not None else "stream launches", **cfg),
+           "tflop_per_s": round(tflops, 2), "gb_per_s": round(gbs, 1), "flop_per_step": flops,
            "roofline": roof}
     print(json.dumps(out), flush=True)
 
@@ -469,7 +501,7 @@ def main():
         copy_calibration(args.copy_bytes, args.steps)
         return
 
-    if args.workload in ("attention", "softmax"):
+    if args.workload in ("attention", "softmax", "conv"):
         run_attention_bench(args)
         return
 

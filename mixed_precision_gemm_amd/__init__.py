@@ -31,7 +31,9 @@ EXPORTED = ("gemm_f16f32_plan", "gemm_f16f32_run", "gemm_f16f32_destroy",
             "gemm_f16f32_workspace_size", "gemm_f16f32_workspace_init",
             "gemm_f16f32_run_noalloc", "gemm_f16f32_set_layernorm",
             "attn_f16_plan", "attn_f16_run", "attn_f16_destroy", "attn_f16_plan_kernel",
-            "attn_softmax_rows")
+            "attn_softmax_rows",
+            "conv_f16_plan", "conv_f16_output_size", "conv_f16_run", "conv_f16_destroy",
+            "conv_f16_plan_kernel")
 
 _lib = None
 
@@ -79,6 +81,17 @@ def library() -> ctypes.CDLL:
         lib.attn_f16_plan_kernel.restype = ctypes.c_char_p
         lib.attn_softmax_rows.argtypes = [i64, i64, vp, i64, ctypes.c_int, vp, i64, ctypes.c_int, vp]
         lib.attn_softmax_rows.restype = ctypes.c_int
+        lib.conv_f16_plan.argtypes = [ctypes.POINTER(vp)] + [i64] * 13 + [ctypes.c_int]
+        lib.conv_f16_plan.restype = ctypes.c_int
+        lib.conv_f16_output_size.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+        lib.conv_f16_output_size.restype = ctypes.c_int
+        lib.conv_f16_run.argtypes = [vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp,
+                                     ctypes.c_int, vp]
+        lib.conv_f16_run.restype = ctypes.c_int
+        lib.conv_f16_destroy.argtypes = [vp]
+        lib.conv_f16_destroy.restype = ctypes.c_int
+        lib.conv_f16_plan_kernel.argtypes = [vp]
+        lib.conv_f16_plan_kernel.restype = ctypes.c_char_p
         lib.gemm_f16f32_set_epilogue.argtypes = [vp, vp, ctypes.c_int]
         lib.gemm_f16f32_set_epilogue.restype = ctypes.c_int
         lib.gemm_f16f32_set_layernorm.argtypes = [vp, vp, vp, ctypes.c_float]
@@ -450,4 +463,70 @@ def softmax(x, out=None):
                            types[out.dtype], torch.cuda.current_stream().cuda_stream)
     if st != GEMM_OK:
         raise GemmError(st, "attn_softmax_rows")
+    return out
+
+
+# ------------------------------------------------------------ convolution
+
+def conv_f16_plan(N, H, W, C, K, R, S, stride=(1, 1), pad=(0, 0), dil=(1, 1),
+                  out_type=GEMM_OUT_F16):
+    """Returns (status, plan_handle)."""
+    h = ctypes.c_void_p()
+    st = library().conv_f16_plan(ctypes.byref(h), N, H, W, C, K, R, S, stride[0], stride[1],
+                                 pad[0], pad[1], dil[0], dil[1], out_type)
+    return st, (h.value if st == GEMM_OK else None)
+
+
+def conv_f16_output_size(plan):
+    """Returns (status, P, Q)."""
+    P, Q = ctypes.c_int64(), ctypes.c_int64()
+    st = library().conv_f16_output_size(plan, ctypes.byref(P), ctypes.byref(Q))
+    return st, P.value, Q.value
+
+
+def conv_f16_run(plan, x, w, y, alpha=1.0, beta=0.0, bias=None, activation=GEMM_ACT_NONE,
+                 stream=None):
+    """x, w, y, bias: device addresses (ints; bias may be None)."""
+    return library().conv_f16_run(plan, x, w, y, alpha, beta, bias, activation, stream)
+
+
+def conv_f16_destroy(plan):
+    return library().conv_f16_destroy(plan)
+
+
+def conv_f16_plan_kernel(plan):
+    return library().conv_f16_plan_kernel(plan).decode()
+
+
+def conv2d(x, w, stride=(1, 1), padding=(0, 0), dilation=(1, 1), bias=None,
+           activation=GEMM_ACT_NONE, out=None, alpha=1.0, beta=0.0, out_dtype=None):
+    """Convolution of a float16 NHWC CUDA tensor x (N, H, W, C) with float16
+    filters w (K, R, S, C), both contiguous.  Returns y (N, P, Q, K), float16
+    unless out_dtype is torch.float32 (or out is given)."""
+    import torch
+    if x.dtype != torch.float16 or w.dtype != torch.float16:
+        raise TypeError("x and w must be float16")
+    if not x.is_contiguous() or not w.is_contiguous():
+        raise ValueError("x (NHWC) and w (KRSC) must be contiguous")
+    N, H, W_, C = x.shape
+    K, R, S, C2 = w.shape
+    if C != C2:
+        raise ValueError("channel counts differ")
+    out_type = GEMM_OUT_F32 if (out is not None and out.dtype == torch.float32) or \
+        out_dtype == torch.float32 else GEMM_OUT_F16
+    st, h = conv_f16_plan(N, H, W_, C, K, R, S, stride, padding, dilation, out_type)
+    if st != GEMM_OK:
+        raise GemmError(st, "conv_f16_plan")
+    try:
+        _, P, Q = conv_f16_output_size(h)
+        if out is None:
+            out = torch.empty((N, P, Q, K), dtype=torch.float32 if out_type == GEMM_OUT_F32
+                              else torch.float16, device=x.device)
+        st = conv_f16_run(h, x.data_ptr(), w.data_ptr(), out.data_ptr(), alpha, beta,
+                          None if bias is None else bias.data_ptr(), activation,
+                          torch.cuda.current_stream().cuda_stream)
+        if st != GEMM_OK:
+            raise GemmError(st, "conv_f16_run")
+    finally:
+        conv_f16_destroy(h)
     return out

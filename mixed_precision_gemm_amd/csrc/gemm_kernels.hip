@@ -41,11 +41,14 @@
 // applied once per output just before its rounding and store.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdio.h>
 
 #include <algorithm>
 #include <mutex>
+#include <new>
 #include <type_traits>
 
+#include "conv_f16.h"
 #include "gemm_bf16f32.h"
 #include "gemm_f16f32.h"
 #include "gemm_internal.h"
@@ -89,6 +92,11 @@ struct GemmArgs {
     int64_t kchunk;
     float *ws;
     int *ws_count;
+    // Implicit-GEMM convolution (conv_f16_run): A is the unrolled input,
+    // read through ConvLoader with this geometry; unused by the GEMM.
+    struct {
+        int H, W, C, P, Q, R, S, sh, sw, ph, pw, dh, dw;
+    } cv;
 };
 
 typedef void (*KernelFn)(GemmArgs);
@@ -313,6 +321,111 @@ struct TileLoader {
     }
 };
 
+// Loader of the unrolled input of an implicit-GEMM convolution ([CATLASS]
+// §5.1: the tile iterator maps row m to an input position and column k to a
+// filter position, so the unrolled matrix never exists in memory).  Row m of
+// A is output pixel (n, p, q); column k = (r S + s) C + c is filter tap
+// (r, s) and channel c; A(m, k) = x[n, p sh - ph + r dh, q sw - pw + s dw, c]
+// of the NHWC input, zero outside the image.  The tile is stored like a
+// K-contiguous operand's (rows of BK, 16-byte chunks of 8 consecutive k).
+// Every chunk of a thread sits at the same k within a stage, so each thread
+// keeps one (r, s, c) position and advances it by BK per stage (no division
+// in the K loop); per unit it keeps the window's origin and the image base.
+// VEC: C is a multiple of 8, so a chunk is 8 consecutive channels of one
+// tap, one 16-byte load; otherwise each element is loaded on its own.
+template <int R, int BK, int NT, bool VEC>
+struct ConvLoader {
+    static constexpr int VPR = BK / 8;
+    static constexpr int UNITS = R * VPR;
+    static constexpr int PER_THREAD = (UNITS + NT - 1) / NT;
+    static_assert(NT % VPR == 0, "one K chunk position per thread");
+
+    u32x4 stage[PER_THREAD];
+    int ih0[PER_THREAD], iw0[PER_THREAD], pix[PER_THREAD];   // window origin, n H W
+    bool live[PER_THREAD];
+    int cr, cs, cc;      // (r, s, c) of this thread's K index in the next stage
+    int64_t kk;          // that K index
+
+    template <typename G>
+    __device__ __forceinline__ void init(int tid, int64_t m0, int64_t M, const G &g) {
+        const int kin = (tid % VPR) * 8;
+#pragma unroll
+        for (int q = 0; q < PER_THREAD; ++q) {
+            const int idx = q * NT + tid;
+            const int64_t m = m0 + idx / VPR;
+            live[q] = idx < UNITS && m < M;
+            const int64_t pq = (int64_t)g.P * g.Q;
+            const int64_t n = m / pq, rem = m - n * pq;
+            const int p = (int)(rem / g.Q), qq = (int)(rem - (int64_t)p * g.Q);
+            ih0[q] = p * g.sh - g.ph;
+            iw0[q] = qq * g.sw - g.pw;
+            pix[q] = (int)(n * g.H * g.W);
+        }
+        cc = kin;
+        cs = 0;
+        cr = 0;
+        while (cc >= g.C) {
+            cc -= g.C;
+            if (++cs == g.S) { cs = 0; ++cr; }
+        }
+        kk = kin;
+    }
+
+    // One element (or chunk) at tap (r, s), channel c of unit q: its byte
+    // offset in x, or kOutOfRange outside the image, past K or past M.
+    template <typename G>
+    __device__ __forceinline__ uint32_t offset(int q, int r, int s, int c, int64_t k, int64_t K, const G &g) const {
+        const int ih = ih0[q] + r * g.dh, iw = iw0[q] + s * g.dw;
+        const bool ok = live[q] && k < K && (unsigned)ih < (unsigned)g.H && (unsigned)iw < (unsigned)g.W;
+        return ok ? (uint32_t)(((int64_t)(pix[q] + ih * g.W + iw) * g.C + c) * 2) : kOutOfRange;
+    }
+
+    // Loads the stage at the current position, then moves it on by BK.
+    template <typename G>
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t K, const G &g) {
+#pragma unroll
+        for (int q = 0; q < PER_THREAD; ++q) {
+            if constexpr (VEC) {
+                stage[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       rs, offset(q, cr, cs, cc, kk, K, g), 0, 0));
+            } else {
+                int r = cr, s = cs, c = cc;
+                uint32_t h[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    h[e] = __builtin_amdgcn_raw_buffer_load_b16(rs, offset(q, r, s, c, kk + e, K, g), 0, 0);
+                    if (++c == g.C) {
+                        c = 0;
+                        if (++s == g.S) { s = 0; ++r; }
+                    }
+                }
+                u32x4 v;
+                v[0] = h[0] | (h[1] << 16);
+                v[1] = h[2] | (h[3] << 16);
+                v[2] = h[4] | (h[5] << 16);
+                v[3] = h[6] | (h[7] << 16);
+                stage[q] = v;
+            }
+        }
+        cc += BK;
+        while (cc >= g.C) {
+            cc -= g.C;
+            if (++cs == g.S) { cs = 0; ++cr; }
+        }
+        kk += BK;
+    }
+
+    __device__ __forceinline__ void store(u32x4 *lds, int tid) {
+#pragma unroll
+        for (int q = 0; q < PER_THREAD; ++q) {
+            const int idx = q * NT + tid;
+            if (UNITS % NT != 0 && idx >= UNITS) continue;
+            const int r = idx / VPR, kv = idx % VPR;
+            lds[r * VPR + (kv ^ swz<VPR>(r))] = stage[q];
+        }
+    }
+};
+
 // Maps a workgroup id to (batch item, tile row, tile column).  Workgroups are
 // dispatched round-robin over the 8 XCDs, each with its own L2; the id is first
 // remapped so that each XCD receives a contiguous run of logical tile ids, and
@@ -348,9 +461,9 @@ __device__ inline void tile_coords(const GemmArgs &p, int wg, int &b, int &tm, i
 // far inside the epilogue's tolerance (checked in fp32: GELU and SiLU
 // within 3e-7 |x| over |x| <= 40).
 constexpr float kLog2e = 1.44269504088896341f;
-__device__ inline float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+__device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
-__device__ inline float erfc_as7126(float z) {
+__device__ __forceinline__ float erfc_as7126(float z) {
     const float a = fabsf(z);
     const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * a);
     const float poly =
@@ -362,7 +475,7 @@ __device__ inline float erfc_as7126(float z) {
 // Fused-epilogue activations in fp32: ReLU max(x, 0); GELU x Phi(x) =
 // x/2 erfc(-x / sqrt 2) (the erfc form keeps the left tail); SiLU
 // x / (1 + e^-x), which tends to -0 as e^-x overflows (rcp(inf) = 0).
-__device__ inline float activate(int act, float x) {
+__device__ __forceinline__ float activate(int act, float x) {
     switch (act) {
     case ACT_RELU: return fmaxf(x, 0.0f);
     case ACT_GELU: return 0.5f * x * erfc_as7126(-x * 0.70710678118654752f);
@@ -372,7 +485,7 @@ __device__ inline float activate(int act, float x) {
 }
 
 // Bias of columns n..n+3 (zeros past N, or without a bias).
-__device__ inline floatx4 load_bias4(const GemmArgs &p, int64_t n) {
+__device__ __forceinline__ floatx4 load_bias4(const GemmArgs &p, int64_t n) {
     floatx4 b = {0.0f, 0.0f, 0.0f, 0.0f};
     if (p.bias) {
 #pragma unroll
@@ -388,8 +501,10 @@ __device__ inline floatx4 load_bias4(const GemmArgs &p, int64_t n) {
 // activations raised the register pressure of the whole kernel until the
 // 256 tile's accumulators spilled inside its K loop (measured 17x slower with
 // no epilogue set), and a call instead of inlining made every kernel need
-// scratch (+3 us per launch on the short split-K grids).
-__device__ inline floatx4 epilogue4(const GemmArgs &p, floatx4 v, floatx4 bias4) {
+// scratch (+3 us per launch on the short split-K grids).  Forced inline: with
+// up to 48 call sites in one kernel the compiler otherwise emits calls and
+// keeps the accumulators in a scratch frame.
+__device__ __forceinline__ floatx4 epilogue4(const GemmArgs &p, floatx4 v, floatx4 bias4) {
     v += bias4;
     if (p.act != ACT_NONE) {
 #pragma unroll
@@ -403,6 +518,45 @@ __device__ inline floatx4 epilogue4(const GemmArgs &p, floatx4 v, floatx4 bias4)
 // masked at the M and N edges.  Accumulator register r of lane l in block
 // (i, j) holds C(m, n) with m = l % 32 and n = 8*(r/4) + 4*(l/32) + r%4
 // (block-local), so each lane owns runs of 4 consecutive n of one row.
+// Four consecutive C elements from column n of one row as fp32: one vector
+// access when full, else element by element up to N (zeros beyond).
+template <typename T>
+__device__ __forceinline__ floatx4 read_c4(const T *C, bool full, int64_t left) {
+    floatx4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (sizeof(T) == 4) {
+        if (full) return *(const floatx4 *)C;
+    } else if (full) {
+        const c4_t<T> h = *(const c4_t<T> *)C;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c[e] = (float)h[e];
+        return c;
+    }
+    for (int e = 0; e < 4 && e < left; ++e) c[e] = (float)C[e];
+    return c;
+}
+
+template <typename T>
+__device__ __forceinline__ void write_c4(T *C, bool full, int64_t left, floatx4 v) {
+    if constexpr (sizeof(T) == 4) {
+        if (full) {
+            *(floatx4 *)C = v;
+            return;
+        }
+    } else if (full) {
+        *(c4_t<T> *)C = c4_t<T>{(T)v[0], (T)v[1], (T)v[2], (T)v[3]};
+        return;
+    }
+    for (int e = 0; e < 4 && e < left; ++e) C[e] = (T)v[e];
+}
+
+// Epilogue of the staged kernel: C = alpha * acc + beta * C on the wave's
+// FM x FN blocks of 32 x 32, rounded once to fp16 (RNE) or stored as fp32,
+// masked at the M and N edges.  Accumulator register r of lane l in block
+// (i, j) holds C(m, n) with m = l % 32 and n = 8*(r/4) + 4*(l/32) + r%4
+// (block-local), so each lane owns runs of 4 consecutive n of one row.  Each
+// run is read, combined and written by one straight sequence (one copy of the
+// fused activation per run): with one copy per store form the unrolled body
+// outgrew the compiler's unroll limit and the accumulators went to scratch.
 template <typename T16, bool EPI, int FM, int FN, int WTM, int WTN>
 __device__ inline void store_tile(const GemmArgs &p, const floatx16 (&acc)[FM][FN],
                                   int b, int64_t m0, int64_t n0, int wm, int wn,
@@ -420,76 +574,27 @@ __device__ inline void store_tile(const GemmArgs &p, const floatx16 (&acc)[FM][F
                 const int64_t n = n0 + wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
                 if (n >= p.N) continue;
                 const int64_t off = b * p.sc + m * p.ldc + n;
-                float v[4];
+                const int64_t left = p.N - n;
+                const bool full = p.c_vec && left >= 4;
+                floatx4 v;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = alpha * acc[i][j][4 * g + e];
-                const bool full = p.c_vec && (n + 4 <= p.N);
-                if (p.out_f32) {
-                    float *C = (float *)p.C + off;
-                    if (full) {
-                        if (beta != 0.0f) {
-                            const floatx4 c = *(const floatx4 *)C;
+                if (beta != 0.0f) {
+                    const floatx4 c = p.out_f32 ? read_c4((const float *)p.C + off, full, left)
+                                                : read_c4((const T16 *)p.C + off, full, left);
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) v[e] += beta * c[e];
-                        }
-                        floatx4 o = {v[0], v[1], v[2], v[3]};
-                        if (epi) o = epilogue4(p, o, load_bias4(p, n));
-                        *(floatx4 *)C = o;
-                    } else if (!epi) {
-                        for (int e = 0; e < 4 && n + e < p.N; ++e) {
-                            float o = v[e];
-                            if (beta != 0.0f) o += beta * C[e];
-                            C[e] = o;
-                        }
-                    } else {
-                        floatx4 o = {v[0], v[1], v[2], v[3]};
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (beta != 0.0f && n + e < p.N) o[e] += beta * C[e];
-                        o = epilogue4(p, o, load_bias4(p, n));
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (n + e < p.N) C[e] = o[e];
-                    }
-                } else {
-                    T16 *C = (T16 *)p.C + off;
-                    if (full) {
-                        if (beta != 0.0f) {
-                            const c4_t<T16> c = *(const c4_t<T16> *)C;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) v[e] += beta * (float)c[e];
-                        }
-                        if (epi) {
-                            const floatx4 w = epilogue4(p, floatx4{v[0], v[1], v[2], v[3]}, load_bias4(p, n));
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) v[e] = w[e];
-                        }
-                        c4_t<T16> o = {(T16)v[0], (T16)v[1], (T16)v[2], (T16)v[3]};
-                        *(c4_t<T16> *)C = o;
-                    } else if (!epi) {
-                        for (int e = 0; e < 4 && n + e < p.N; ++e) {
-                            float o = v[e];
-                            if (beta != 0.0f) o += beta * (float)C[e];
-                            C[e] = (T16)o;
-                        }
-                    } else {
-                        floatx4 o = {v[0], v[1], v[2], v[3]};
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (beta != 0.0f && n + e < p.N) o[e] += beta * (float)C[e];
-                        o = epilogue4(p, o, load_bias4(p, n));
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (n + e < p.N) C[e] = (T16)o[e];
-                    }
+                    for (int e = 0; e < 4; ++e) v[e] += beta * c[e];
                 }
+                if (epi) v = epilogue4(p, v, load_bias4(p, n));
+                if (p.out_f32) write_c4((float *)p.C + off, full, left, v);
+                else write_c4((T16 *)p.C + off, full, left, v);
             }
         }
     }
 }
 
 template <typename TI, int BM, int BN, int BK, int WGM, int WGN, bool AK, bool BKC, bool VEC,
-          bool EPI>
+          bool EPI, bool CONV = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_staged(GemmArgs p) {
     constexpr int NT = 64 * WGM * WGN;
     constexpr int VPR = BK / 8;
@@ -518,10 +623,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_staged(GemmArgs p) {
     const int64_t b_tile = BKC ? n0 * p.ldb : n0;
     const int64_t b_kstep = BKC ? BK : BK * p.ldb;
 
-    TileLoader<BM, BK, NT, AK, VEC> la;
+    static_assert(!CONV || AK, "the unrolled input is K-contiguous");
+    using ALoader = typename std::conditional<CONV, ConvLoader<BM, BK, NT, VEC>,
+                                              TileLoader<BM, BK, NT, AK, VEC>>::type;
+    ALoader la;
     TileLoader<BN, BK, NT, BKC, VEC> lb;
-    la.init(tid, m0, p.M, p.lda);
+    if constexpr (CONV) la.init(tid, m0, p.M, p.cv);
+    else la.init(tid, m0, p.M, p.lda);
     lb.init(tid, n0, p.N, p.ldb);
+    // The convolution's input as one range-checked buffer (NHWC, < 2^31 bytes).
+    [[maybe_unused]] const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.A, CONV ? p.extent_a * 2 : 0);
 
     floatx16 acc[FM][FN];
 #pragma unroll
@@ -536,7 +647,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_staged(GemmArgs p) {
     auto issue = [&](int64_t kt) {
         const int64_t k0 = kt * BK;
         const int64_t ao = a_tile + kt * a_kstep, bo = b_tile + kt * b_kstep;
-        la.load(Ab + ao, (p.extent_a - ao) * 2, k0, p.K, p.lda);
+        if constexpr (CONV) la.load(rx, p.K, p.cv);   // stages in order: 0, 1, 2, ...
+        else la.load(Ab + ao, (p.extent_a - ao) * 2, k0, p.K, p.lda);
         lb.load(Bb + bo, (p.extent_b - bo) * 2, k0, p.K, p.ldb);
     };
 
@@ -2080,6 +2192,179 @@ extern "C" int gemm_f16f32_run_noalloc(gemm_f16f32_plan_t plan, const void *A, c
         ws_bytes = kScratchBytes;
     }
     return run_plan(plan, A, B, C, alpha, beta, ws, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Implicit-GEMM convolution: the staged kernel with its A tile read through
+// ConvLoader (the unrolled NHWC input), B the KRSC filters as a K-contiguous
+// operand (row k of the filters is column k of B, ldb = R S C) and C the NPQK
+// output (row-major, ldc = K).
+// ---------------------------------------------------------------------------
+struct conv_f16_plan_s {
+    int64_t N, H, W, C, K, R, S, sh, sw, ph, pw, dh, dw, P, Q;
+    int out_type;
+    int tile;            // index into kConvTiles
+    char kernel_name[64];
+};
+
+namespace {
+
+int64_t conv_out_dim(int64_t in, int64_t k, int64_t stride, int64_t pad, int64_t dil) {
+    const int64_t span = dil * (k - 1) + 1;
+    if (in + 2 * pad < span) return -1;
+    return (in + 2 * pad - span) / stride + 1;
+}
+
+// Tiles of the convolution (the staged kernel's shapes, BK = 64): the 64
+// tile for small problems (fewer than 128 workgroups otherwise), and for the
+// rest a 128- or 256-row tile whose width follows the output channels (64
+// columns when K <= 64, so that no half-empty tile is computed).
+struct ConvTile {
+    int bm, bn, wgm, wgn;
+    const char *name;
+};
+constexpr ConvTile kConvTiles[] = {
+    {64, 64, 2, 2, "64x64x64"},
+    {128, 128, 2, 2, "128x128x64"},
+    {128, 64, 2, 2, "128x64x64"},
+    {256, 64, 4, 1, "256x64x64"},
+};
+constexpr int kNumConvTiles = (int)(sizeof kConvTiles / sizeof kConvTiles[0]);
+
+template <int T, bool VEC, bool EPI>
+constexpr KernelFn pick_conv() {
+    return gemm_staged<_Float16, kConvTiles[T].bm, kConvTiles[T].bn, 64, kConvTiles[T].wgm,
+                       kConvTiles[T].wgn, true, true, VEC, EPI, true>;
+}
+
+template <int T>
+constexpr void fill_conv(KernelFn (&k)[2][2]) {
+    k[0][0] = pick_conv<T, false, false>();
+    k[0][1] = pick_conv<T, false, true>();
+    k[1][0] = pick_conv<T, true, false>();
+    k[1][1] = pick_conv<T, true, true>();
+}
+
+KernelFn conv_kernel(int tile, bool vec, bool epi) {
+    static const auto table = [] {
+        struct { KernelFn k[kNumConvTiles][2][2]; } t{};
+        fill_conv<0>(t.k[0]);
+        fill_conv<1>(t.k[1]);
+        fill_conv<2>(t.k[2]);
+        fill_conv<3>(t.k[3]);
+        return t;
+    }();
+    return table.k[tile][vec][epi];
+}
+
+// Measured on the 3x3 64 -> 64 layer at 32 x 56 x 56 (25 us on 256 x 64 against
+// 27 on 64 x 64 and 35 on 128 x 128) and the 7x7 stride-2 stem with C = 3
+// (102 us on 128 x 64; its element-wise loads leave the 256-row tile no faster).
+int choose_conv_tile(int64_t M, int64_t K, int64_t C) {
+    const int t = K > 64 ? 1 : C % 8 == 0 ? 3 : 2;
+    const int64_t tiles = ((M + kConvTiles[t].bm - 1) / kConvTiles[t].bm) *
+                          ((K + kConvTiles[t].bn - 1) / kConvTiles[t].bn);
+    return tiles >= kNumCUs / 2 ? t : 0;
+}
+
+}  // namespace
+
+extern "C" int conv_f16_plan(conv_f16_plan_t *out, int64_t N, int64_t H, int64_t W, int64_t C,
+                             int64_t K, int64_t R, int64_t S, int64_t stride_h, int64_t stride_w,
+                             int64_t pad_h, int64_t pad_w, int64_t dil_h, int64_t dil_w,
+                             int out_type) {
+    if (!out) return GEMM_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (N < 0 || K < 0 || H < 1 || W < 1 || C < 1 || R < 1 || S < 1) return GEMM_ERR_INVALID_ARG;
+    if (stride_h < 1 || stride_w < 1 || dil_h < 1 || dil_w < 1 || pad_h < 0 || pad_w < 0)
+        return GEMM_ERR_INVALID_ARG;
+    if (out_type != GEMM_OUT_F16 && out_type != GEMM_OUT_F32) return GEMM_ERR_INVALID_ARG;
+    const int64_t lim = int64_t(1) << 31;
+    if (H >= lim || W >= lim || R >= lim || S >= lim || pad_h >= lim || pad_w >= lim || stride_h >= lim ||
+        stride_w >= lim || dil_h >= lim || dil_w >= lim)
+        return GEMM_ERR_UNSUPPORTED;
+    const int64_t P = conv_out_dim(H, R, stride_h, pad_h, dil_h), Q = conv_out_dim(W, S, stride_w, pad_w, dil_w);
+    if (P < 1 || Q < 1) return GEMM_ERR_INVALID_ARG;
+    const int64_t M = N * P * Q, RSC = R * S * C;
+    if (N * H * W * C * 2 >= lim || M >= lim || RSC >= lim || K >= lim || 128 * RSC * 2 >= lim)
+        return GEMM_ERR_UNSUPPORTED;
+    conv_f16_plan_s *p = new (std::nothrow) conv_f16_plan_s();
+    if (!p) return GEMM_ERR_NOMEM;
+    p->N = N; p->H = H; p->W = W; p->C = C; p->K = K; p->R = R; p->S = S;
+    p->sh = stride_h; p->sw = stride_w; p->ph = pad_h; p->pw = pad_w; p->dh = dil_h; p->dw = dil_w;
+    p->P = P; p->Q = Q;
+    p->out_type = out_type;
+    p->tile = choose_conv_tile(M, K, C);
+    if (M == 0 || K == 0)
+        snprintf(p->kernel_name, sizeof p->kernel_name, "none");
+    else
+        snprintf(p->kernel_name, sizeof p->kernel_name, "conv_implicit_%s_%s",
+                 kConvTiles[p->tile].name, C % 8 == 0 ? "vec16" : "narrow");
+    *out = p;
+    return GEMM_OK;
+}
+
+extern "C" int conv_f16_output_size(conv_f16_plan_t plan, int64_t *P, int64_t *Q) {
+    if (!plan || !P || !Q) return GEMM_ERR_INVALID_ARG;
+    *P = plan->P;
+    *Q = plan->Q;
+    return GEMM_OK;
+}
+
+extern "C" int conv_f16_run(conv_f16_plan_t plan, const void *x, const void *w, void *y, float alpha,
+                            float beta, const float *bias, int activation, void *stream) {
+    if (!plan) return GEMM_ERR_INVALID_ARG;
+    const conv_f16_plan_s &p = *plan;
+    if (activation < ACT_NONE || activation > ACT_SILU || (uintptr_t)bias % 4 != 0)
+        return GEMM_ERR_INVALID_ARG;
+    const int64_t M = p.N * p.P * p.Q, RSC = p.R * p.S * p.C;
+    if (M == 0 || p.K == 0) return GEMM_OK;
+    if (!x || !w || !y) return GEMM_ERR_INVALID_ARG;
+    const int64_t xb = p.N * p.H * p.W * p.C * 2, wb = p.K * RSC * 2;
+    const int64_t yb = M * p.K * (p.out_type == GEMM_OUT_F32 ? 4 : 2);
+    if (ranges_overlap((uintptr_t)y, yb, (uintptr_t)x, xb) || ranges_overlap((uintptr_t)y, yb, (uintptr_t)w, wb) ||
+        (bias && ranges_overlap((uintptr_t)y, yb, (uintptr_t)bias, p.K * 4)))
+        return GEMM_ERR_INVALID_ARG;
+    const bool vec = p.C % 8 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)w % 16 == 0;
+    const ConvTile &ts = kConvTiles[p.tile];
+    GemmArgs a = {};
+    a.A = (const uint16_t *)x;
+    a.B = (const uint16_t *)w;
+    a.C = y;
+    a.M = M; a.N = p.K; a.K = RSC;
+    a.lda = RSC; a.ldb = RSC; a.ldc = p.K;
+    a.sa = a.sb = a.sc = 0;
+    a.extent_a = p.N * p.H * p.W * p.C;
+    a.extent_b = p.K * RSC;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.tiles_m = (int)((M + ts.bm - 1) / ts.bm);
+    a.tiles_n = (int)((p.K + ts.bn - 1) / ts.bn);
+    a.group_m = 4;
+    a.total_tiles = a.tiles_m * a.tiles_n;
+    a.out_f32 = p.out_type == GEMM_OUT_F32;
+    a.c_vec = p.K % 4 == 0 && (uintptr_t)y % (a.out_f32 ? 16 : 8) == 0;
+    a.bias = bias;
+    a.act = activation;
+    a.epi = bias != nullptr || activation != ACT_NONE;
+    a.ksplit = 1;
+    a.kchunk = RSC;
+    a.cv.H = (int)p.H; a.cv.W = (int)p.W; a.cv.C = (int)p.C; a.cv.P = (int)p.P; a.cv.Q = (int)p.Q;
+    a.cv.R = (int)p.R; a.cv.S = (int)p.S; a.cv.sh = (int)p.sh; a.cv.sw = (int)p.sw;
+    a.cv.ph = (int)p.ph; a.cv.pw = (int)p.pw; a.cv.dh = (int)p.dh; a.cv.dw = (int)p.dw;
+    const KernelFn fn = conv_kernel(p.tile, vec, a.epi != 0);
+    void *args[] = {&a};
+    return hipLaunchKernel((const void *)fn, dim3((unsigned)a.total_tiles), dim3(64 * ts.wgm * ts.wgn),
+                           args, 0, (hipStream_t)stream) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+extern "C" int conv_f16_destroy(conv_f16_plan_t plan) {
+    delete plan;
+    return GEMM_OK;
+}
+
+extern "C" const char *conv_f16_plan_kernel(conv_f16_plan_t plan) {
+    return plan ? plan->kernel_name : "invalid";
 }
 
 #endif  // MPGEMM_HOST_PART

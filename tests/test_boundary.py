@@ -24,7 +24,7 @@ def declared_functions():
     for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
         text = open(h).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        for m in re.finditer(r"\b((?:gemm|attn)_\w+)\s*\(", text):
+        for m in re.finditer(r"\b((?:gemm|attn|conv)_\w+)\s*\(", text):
             names.add(m.group(1))
     return names
 
@@ -442,3 +442,44 @@ def test_set_layernorm_validation_and_workspace():
         z = (16 * 4096 * 4 + 255) // 256 * 256
         assert "_sk8" in p.kernel and p.kernel.endswith("_pkb")
         assert p.workspace_bytes() == (gemm_part + 255) // 256 * 256 + z
+
+
+# ------------------------------------------------------------ convolution
+
+def test_conv_plan_rules():
+    def plan(N=2, H=16, W=16, C=64, K=32, R=3, S=3, stride=(1, 1), pad=(1, 1), dil=(1, 1), out=0):
+        st, h = mpg.conv_f16_plan(N, H, W, C, K, R, S, stride, pad, dil, out)
+        res = (st, mpg.conv_f16_plan_kernel(h) if h else None,
+               mpg.conv_f16_output_size(h)[1:] if h else None)
+        if h:
+            mpg.conv_f16_destroy(h)
+        return res
+    assert plan() == (GEMM_OK, "conv_implicit_64x64x64_vec16", (16, 16))
+    # the tile's width follows the output channels; the 64 tile below 128 workgroups
+    assert plan(N=32, H=56, W=56, C=64, K=64) == (GEMM_OK, "conv_implicit_256x64x64_vec16", (56, 56))
+    assert plan(N=32, H=56, W=56, C=64, K=65)[1] == "conv_implicit_128x128x64_vec16"
+    assert plan(N=32, H=224, W=224, C=3, K=64, R=7, S=7, stride=(2, 2),
+                pad=(3, 3))[1] == "conv_implicit_128x64x64_narrow"
+    assert plan(N=16, H=32, W=32, C=16, K=64)[1] == "conv_implicit_64x64x64_vec16"    # 64 tiles
+    assert plan(N=32, H=32, W=32, C=16, K=64)[1] == "conv_implicit_256x64x64_vec16"   # 128 tiles
+    assert plan(C=3, stride=(2, 2)) == (GEMM_OK, "conv_implicit_64x64x64_narrow", (8, 8))
+    assert plan(H=224, W=224, C=3, K=64, R=7, S=7, stride=(2, 2), pad=(3, 3))[2] == (112, 112)
+    assert plan(R=5, S=5, pad=(0, 0), dil=(4, 4))[0] == GEMM_ERR_INVALID_ARG     # window too large
+    assert plan(N=0)[1] == "none" and plan(K=0)[1] == "none"
+    for kw in [dict(H=0), dict(C=0), dict(R=0), dict(stride=(0, 1)), dict(pad=(-1, 0)),
+               dict(dil=(1, 0)), dict(out=2), dict(N=-1)]:
+        assert plan(**kw)[0] == GEMM_ERR_INVALID_ARG, kw
+    assert plan(N=1 << 14, H=256, W=256, C=64)[0] == GEMM_ERR_UNSUPPORTED   # input past 2^31 bytes
+    assert mpg.conv_f16_plan_kernel(None) == "invalid"
+    assert mpg.conv_f16_destroy(None) == GEMM_OK
+    st, h = mpg.conv_f16_plan(1, 8, 8, 8, 8, 3, 3, (1, 1), (1, 1), (1, 1), 0)
+    try:
+        base = 1 << 30
+        run = lambda *a: mpg.conv_f16_run(h, *a)
+        assert run(0, base + 4096, base + 8192) == GEMM_ERR_INVALID_ARG
+        assert run(base, base + 4096, base + 100) == GEMM_ERR_INVALID_ARG   # y overlaps x
+        assert run(base, base + 4096, base + 8192, 1.0, 0.0, base + 2) == GEMM_ERR_INVALID_ARG
+        assert run(base, base + 4096, base + 8192, 1.0, 0.0, None, 7) == GEMM_ERR_INVALID_ARG
+        assert mpg.conv_f16_run(None, base, base, base) == GEMM_ERR_INVALID_ARG
+    finally:
+        mpg.conv_f16_destroy(h)
