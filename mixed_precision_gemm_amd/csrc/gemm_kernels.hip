@@ -47,6 +47,7 @@
 #include <mutex>
 #include <new>
 #include <type_traits>
+#include <utility>
 
 #include "conv_f16.h"
 #include "gemm_bf16f32.h"
@@ -1161,11 +1162,16 @@ struct DirectOperand {
 // Per-lane LDS byte offsets of one operand's 16 x 16 x 32 fragments for one
 // wave (rows or columns wb .. wb + 16 NBLK - 1 of a BK = 64 ring slot), so
 // that every fragment read is a base register plus an immediate offset.  Two
-// sets: `cur` addresses the slot of the stage being computed, `nxt` the slot
-// of the next one.  Slot s starts s slot sizes (a power of two) above slot
-// 0, which starts at 0, and every slot-0 address is below the slot size, so
-// advancing a stage is one add-and-wrap per register (one XOR for a two-slot
-// ring; advance()) and no other address arithmetic is left in the K loop.
+// sets: `cur` addresses the slot of the stage being computed (read by its
+// head K step), `nxt` the slot of the next one (read by its tail K step).
+// Slot s starts s slot sizes (a power of two) above slot 0, which starts at
+// 0, and every slot-0 address is below the slot size, so moving a base on by
+// a stage is one add-and-wrap (one XOR for a two-slot ring; step()) and no
+// other address arithmetic is left in the K loop.  The kernel moves the
+// bases one register at a time between MFMAs: each cur base during a stage's
+// tail (after the head's last read of it), each nxt base during a stage's
+// head (before the tail reads it).  Both start at stage 0; the first head
+// moves nxt to stage 1.
 //   K-contiguous: row r = wb + 16 i + l%16 keeps its K chunk kv = 4 s + l/16
 //     at kv ^ swz16(r) = (l/16 ^ swz16(l%16)) ^ 4 s (swz16 depends on r % 16
 //     only): two bases, by s, and 16 rows per block as immediates.
@@ -1184,7 +1190,7 @@ struct Frag16 {
     static constexpr int NCLS = KC ? 2 : NBLK;
     uint32_t cur[NCLS], nxt[NCLS];
 
-    // Bases for stage 0 (slot 0) in cur and stage 1 (slot 1) in nxt.
+    // Bases for stage 0 (slot 0) in cur and in nxt.
     __device__ void setup(int lane, int wb) {
         constexpr uint32_t region = (uint32_t)BASE;
         const int lr = lane & 15, lg = lane >> 4;
@@ -1201,33 +1207,37 @@ struct Frag16 {
                                              16 * ((wb / 8 + 2 * i) ^ W) + 8 * (lr & 1));
         }
 #pragma unroll
-        for (int c = 0; c < NCLS; ++c) nxt[c] = cur[c] + SLOT_BYTES;
+        for (int c = 0; c < NCLS; ++c) nxt[c] = cur[c];
     }
 
-    // Next stage: every base moves one slot on, wrapping around the ring.
-    // Two slots at BASE and BASE + SLOT_BYTES: one XOR.  Three: add and wrap.  Four (interleaved, BASE inside the
-    // first slot): add and mask.
-    __device__ static uint32_t step(uint32_t x) {
+    // Next stage: a base moves one slot on, wrapping around the ring.  Two
+    // slots at BASE and BASE + SLOT_BYTES: one XOR.  Three (at 0): the
+    // smaller of x + SLOT and x - 2 SLOT as unsigned values (the second
+    // wraps below zero unless x + SLOT has passed the ring's end).  Four
+    // (interleaved, BASE inside the first slot): add and mask.  Written as
+    // volatile assembly so that each update stays between the MFMAs the
+    // kernel places it after (plain arithmetic was gathered into one burst).
+    __device__ static void step(uint32_t &x) {
         if constexpr (NSLOT == 2) {
             // One XOR moves base + offset to base + SLOT + offset only if
             // base + offset == base | offset: a slot-aligned base.
             static_assert(BASE % SLOT_BYTES == 0, "two slots: slot-aligned base");
             constexpr uint32_t flip = (uint32_t)BASE ^ (uint32_t)(BASE + SLOT_BYTES);
-            return x ^ flip;
+            asm volatile("v_xor_b32 %0, %1, %0" : "+v"(x) : "i"(flip));
         } else if constexpr (NSLOT == 3) {
-            x += (uint32_t)SLOT_BYTES;
-            return x >= (uint32_t)(BASE + 3 * SLOT_BYTES) ? x - (uint32_t)(3 * SLOT_BYTES) : x;
+            static_assert(BASE == 0 && 3 * SLOT_BYTES < (1 << 30), "three slots from LDS address 0");
+            uint32_t t;
+            asm volatile("v_add_u32 %0, %2, %1\n\tv_add_u32 %1, %3, %1\n\tv_min_u32 %1, %0, %1"
+                         : "=&v"(t), "+v"(x)
+                         : "i"(SLOT_BYTES), "i"(-2 * SLOT_BYTES));
         } else {
-            return (x + (uint32_t)SLOT_BYTES) & (uint32_t)(NSLOT * SLOT_BYTES - 1);
+            asm volatile("v_add_u32 %0, %1, %0\n\tv_and_b32 %0, %2, %0"
+                         : "+v"(x)
+                         : "i"(SLOT_BYTES), "i"(NSLOT * SLOT_BYTES - 1));
         }
     }
-    __device__ void advance() {
-#pragma unroll
-        for (int c = 0; c < NCLS; ++c) {
-            cur[c] = step(cur[c]);
-            nxt[c] = step(nxt[c]);
-        }
-    }
+    __device__ void advance_cur(int c) { step(cur[c]); }
+    __device__ void advance_nxt(int c) { step(nxt[c]); }
 
     // Fragment of block i, K step s (32 deep) of the current (NEXT = false)
     // or next stage: lane l receives row (or column) wb + 16 i + l%16,
@@ -1249,6 +1259,80 @@ struct Frag16 {
         }
     }
 };
+
+// A buffer descriptor moved on by a fixed byte step per stage (the K-full
+// direct kernels' loads): 64-bit base, bytes left from it (negative past the
+// operand's end, where the descriptor holds zero records).  The words are
+// kept current, so a stage's loads use them as they are; advance() is four
+// scalar instructions, as volatile assembly so that it stays where the
+// kernel places it.  Callers guarantee that bytes left and the step stay
+// within +-2^31 and that the base stays below 2^48 (word 1's stride bits are
+// never touched).
+struct RunRsrc {
+    int32_t w0, w1, w2;   // base low, base high, records
+    int32_t left, step;
+    __device__ void init(const void *base, int64_t bytes_left, int64_t step_bytes) {
+        const uint64_t a = (uint64_t)base;
+        w0 = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a);
+        w1 = __builtin_amdgcn_readfirstlane((int32_t)((uint32_t)(a >> 32) & 0xffffu));
+        left = __builtin_amdgcn_readfirstlane((int32_t)bytes_left);
+        step = __builtin_amdgcn_readfirstlane((int32_t)step_bytes);
+        w2 = left > 0 ? left : 0;
+    }
+    __device__ sgpr4 words() const {
+        sgpr4 r;
+        r[0] = w0;
+        r[1] = w1;
+        r[2] = w2;
+        r[3] = kRsrcWord3;
+        return r;
+    }
+    __device__ void advance() {
+        const int32_t hi_step = step < 0 ? -1 : 0;
+        asm volatile(
+            "s_add_u32 %0, %0, %4\n\ts_addc_u32 %1, %1, %5\n\ts_sub_i32 %3, %3, %4\n\ts_max_i32 %2, %3, 0"
+            : "+s"(w0), "+s"(w1), "=s"(w2), "+s"(left)
+            : "s"(step), "s"(hi_step)
+            : "scc");
+    }
+};
+
+// Position (the MFMA it follows) of bookkeeping item t of NB in a K step of
+// NQ MFMAs: spread evenly, moved on past any position that follows a fragment
+// read (R - 1 mod R) or a load (OFF mod T, when the step loads).
+__host__ __device__ constexpr int book_pos(int t, int nb, int nq, int r, int tl, int off, int nl) {
+    const int base = (t * nq) / nb;
+    for (int d = 0; d < 4; ++d) {
+        const int q = (base + d) % nq;
+        const bool read = r >= 1 && q % r == r - 1;
+        const bool load = nl > 0 && tl >= 1 && q >= off && (q - off) % tl == 0 && (q - off) / tl < nl;
+        if (!read && !load) return q;
+    }
+    return base;
+}
+
+// For each MFMA position of a K step, the set of bookkeeping items (a bit
+// mask) placed after it, evaluated at compile time.
+template <int NB, int NQ, int R, int TL, int OFF, int NL>
+struct BookTable {
+    static_assert(NB <= 32, "item mask in one word");
+    struct Masks {
+        uint32_t at[NQ];
+    };
+    static constexpr Masks make() {
+        Masks m{};
+        for (int t = 0; t < NB; ++t) m.at[book_pos(t, NB, NQ, R, TL, OFF, NL)] |= 1u << t;
+        return m;
+    }
+    static constexpr Masks masks = make();
+};
+
+// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1 in order: a loop
+// unrolled by construction, whose index is a compile-time constant.
+template <typename F, int... I>
+__device__ __forceinline__ void unroll_seq(std::integer_sequence<int, I...>, F &&f) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
 
 // ---------------------------------------------------------------------------
 // Direct kernel on 16 x 16 x 32 MFMAs (256 x 256 and 128 x 128 tiles): the
@@ -1356,9 +1440,24 @@ void gemm_direct16(GemmArgs pin) {
         opb.issue(Bb + bo, (p.extent_b - bo) * 2, sb, wave, st * BK, p.K);
     };
 
+    // K-full kernels (launched only when both operands, and S + 2 stages past
+    // their ends, lie within 2^30 bytes of their tile bases) keep each
+    // operand's buffer descriptor for the next stage it loads and move it on
+    // by one stage after use: a 64-bit base add and a 32-bit bytes-left
+    // subtract, clamped at zero, instead of forming the stage offset and a
+    // 64-bit clamp at every stage.  Loads of each operand go out stage by
+    // stage in order (stages S, S+1, ... after the prologue's 0 .. S-1).
+    RunRsrc ra, rb;
+    if constexpr (KFULL) {
+        ra.init(Ab + a_tile + S * a_kstep, (p.extent_a - a_tile - S * a_kstep) * 2, a_kstep * 2);
+        rb.init(Bb + b_tile + S * b_kstep, (p.extent_b - b_tile - S * b_kstep) * 2, b_kstep * 2);
+    }
+
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "16-row fragment blocks");
-    Frag16<BM, BK, AK, FM, A_SLOT, SA, A_BASE> fra;
-    Frag16<BN, BK, BKC, FN, B_SLOT, S, B_BASE> frb;
+    using FragA = Frag16<BM, BK, AK, FM, A_SLOT, SA, A_BASE>;
+    using FragB = Frag16<BN, BK, BKC, FN, B_SLOT, S, B_BASE>;
+    FragA fra;
+    FragB frb;
     fra.setup(lane, wm * WTM);
     frb.setup(lane, wn * WTN);
 
@@ -1376,15 +1475,22 @@ void gemm_direct16(GemmArgs pin) {
     // KFULL (K a multiple of BK) tests nothing: every stage inside K is full,
     // and the loads of the S stages past the end (issued by the last tails)
     // are range-checked reads that land in slots no MFMA reads again.
+    // BOOK: the head's (0) or the tail's (1) bookkeeping -- the fragment
+    // bases and the running descriptors moved on one register or one
+    // descriptor at a time, each after the MFMA of its own position, so that
+    // no MFMA waits behind a burst of address arithmetic (an MFMA leaves
+    // room for three other instructions).
     constexpr int NQ = FM * FN;
     constexpr int NF = FM + FN;
     // LOADS: 0 none, 1 the A loads, 2 the B loads, 3 both, of stage dst;
     // sa and sb are the LDS byte addresses of its A and B slots.
-    auto kstep = [&](auto curc, auto nextc, auto rksc, auto loadsc, int64_t dst, uint32_t sa,
+    uint32_t a_ld = (uint32_t)(A_BASE + (2 % SA) * A_SLOT);   // split ring: A slot of stage kt+2
+    auto kstep = [&](auto curc, auto nextc, auto rksc, auto loadsc, auto bookc, int64_t dst, uint32_t sa,
                      uint32_t sb) __attribute__((always_inline)) {
         constexpr int CUR = decltype(curc)::value, RKS = decltype(rksc)::value;
         constexpr bool NEXT = decltype(nextc)::value;
         constexpr int LOADS = decltype(loadsc)::value;
+        constexpr int BOOK = decltype(bookc)::value;
         constexpr bool LA = LOADS & 1, LB = LOADS & 2;
         constexpr int na = LA ? PA : 0;
         constexpr int nl = na + (LB ? PB : 0);
@@ -1393,23 +1499,65 @@ void gemm_direct16(GemmArgs pin) {
         if constexpr (LOADS != 0) {
             const int left = (!KFULL && (AK || BKC)) ? OpA::stage_left(dst * BK, p.K) : BK;
             if constexpr (LA) {
-                const int64_t ao = a_tile + dst * a_kstep;
-                rsa = opa.stage_rsrc(Ab + ao, (p.extent_a - ao) * 2);
-                if constexpr (!KFULL && AK) ma = opa.kmask(left);
+                if constexpr (KFULL) {
+                    rsa = ra.words();
+                } else {
+                    const int64_t ao = a_tile + dst * a_kstep;
+                    rsa = opa.stage_rsrc(Ab + ao, (p.extent_a - ao) * 2);
+                    if constexpr (AK) ma = opa.kmask(left);
+                }
             }
             if constexpr (LB) {
-                const int64_t bo = b_tile + dst * b_kstep;
-                rsb = opb.stage_rsrc(Bb + bo, (p.extent_b - bo) * 2);
-                if constexpr (!KFULL && BKC) mb = opb.kmask(left);
+                if constexpr (KFULL) {
+                    rsb = rb.words();
+                } else {
+                    const int64_t bo = b_tile + dst * b_kstep;
+                    rsb = opb.stage_rsrc(Bb + bo, (p.extent_b - bo) * 2);
+                    if constexpr (BKC) mb = opb.kmask(left);
+                }
             }
         }
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            const int i = q / FN, j = q % FN;
+        // Load l follows MFMA l T + OFF (T MFMAs apart).  Fragment reads
+        // follow MFMAs R - 1, 2 R - 1, ... (R = NQ / NF); when T is a
+        // multiple of R, OFF = R/2 - 1 puts each load between two reads,
+        // so no MFMA is followed by both a load and a read.
+        constexpr int T = nl > 0 ? NQ / nl : 1;
+        constexpr int R = NQ / NF;
+        constexpr int OFF = nl > 0 && T >= 1 && R >= 2 && T % R == 0 ? R / 2 - 1 : T - 1;
+        // Bookkeeping items: the fragment bases of A then B (FragA::NCLS +
+        // FragB::NCLS), then (BOOK = head) the A descriptor and the split
+        // ring's A slot, or (BOOK = tail) the B descriptor and, with an
+        // interleaved ring, the A descriptor; item t follows MFMA book_pos(t).
+        constexpr int NBK = FragA::NCLS + FragB::NCLS + 2;
+        using Book = BookTable<NBK, NQ, R, T, OFF, nl>;
+        unroll_seq(std::make_integer_sequence<int, NQ>{}, [&](auto qc) __attribute__((always_inline)) {
+            constexpr int q = decltype(qc)::value;
+            constexpr int i = q / FN, j = q % FN;
             acc[i][j] = mfma16<TI>(fb[CUR][j], fa[CUR][i], acc[i][j]);
-#pragma unroll
-            for (int l = q * nl / NQ; l < (q + 1) * nl / NQ; ++l) {
-                if (l < na) {
+            unroll_seq(std::make_integer_sequence<int, NBK>{}, [&](auto tc) __attribute__((always_inline)) {
+                constexpr int t = decltype(tc)::value;
+                if constexpr ((Book::masks.at[q] >> t) & 1u) {
+                    if constexpr (t < FragA::NCLS) {
+                        if constexpr (BOOK == 0) fra.advance_nxt(t);
+                        else fra.advance_cur(t);
+                    } else if constexpr (t < FragA::NCLS + FragB::NCLS) {
+                        if constexpr (BOOK == 0) frb.advance_nxt(t - FragA::NCLS);
+                        else frb.advance_cur(t - FragA::NCLS);
+                    } else if constexpr (t == NBK - 2) {
+                        if constexpr (KFULL && BOOK == 0 && SPLIT) ra.advance();
+                        if constexpr (KFULL && BOOK == 1) rb.advance();
+                    } else {
+                        if constexpr (BOOK == 0 && SPLIT)
+                            a_ld = a_ld + (uint32_t)A_SLOT == (uint32_t)(A_BASE + SA * A_SLOT)
+                                       ? (uint32_t)A_BASE
+                                       : a_ld + (uint32_t)A_SLOT;
+                        if constexpr (KFULL && BOOK == 1 && !SPLIT) ra.advance();
+                    }
+                }
+            });
+            if constexpr (nl > 0 && q >= OFF && (q - OFF) % T == 0 && (q - OFF) / T < nl) {
+                constexpr int l = (q - OFF) / T;
+                if constexpr (l < na) {
                     if constexpr (AK && !KFULL) opa.issue_one_masked(l, rsa, sa, wave, ma);
                     else opa.issue_one_full(l, rsa, sa, wave);
                 } else {
@@ -1423,7 +1571,7 @@ void gemm_direct16(GemmArgs pin) {
                 else fa[CUR ^ 1][f - FN] = fra.template read<NEXT>(lds, f - FN, RKS);
             }
             __builtin_amdgcn_sched_barrier(0);
-        }
+        });
     };
     using NoLd = std::integral_constant<int, 0>;
     using LdA = std::integral_constant<int, 1>;
@@ -1437,15 +1585,12 @@ void gemm_direct16(GemmArgs pin) {
     // head's wait only the loads issued after stage kt+1's may be pending:
     // the (S-2) L of the later stages, or (split ring) the A loads of stage
     // kt+2 just issued.
-    uint32_t a_ld = (uint32_t)(A_BASE + (2 % SA) * A_SLOT);   // split ring: A slot of stage kt+2
     auto head = [&](int64_t kt) __attribute__((always_inline)) {
         if constexpr (SPLIT) {
-            kstep(Z{}, std::false_type{}, O{}, LdA{}, kt + 2, lds_base + a_ld, 0u);
-            a_ld = a_ld + (uint32_t)A_SLOT == (uint32_t)(A_BASE + SA * A_SLOT) ? (uint32_t)A_BASE
-                                                                             : a_ld + (uint32_t)A_SLOT;
+            kstep(Z{}, std::false_type{}, O{}, LdA{}, Z{}, kt + 2, lds_base + a_ld, 0u);
             wait_vmcnt<PA>();           // this lane's loads of stage kt+1
         } else {
-            kstep(Z{}, std::false_type{}, O{}, NoLd{}, 0, 0u, 0u);
+            kstep(Z{}, std::false_type{}, O{}, NoLd{}, Z{}, 0, 0u, 0u);
             wait_vmcnt<(S - 2) * L>();  // this lane's loads of stage kt+1
         }
         asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");   // reads of stage kt done
@@ -1454,10 +1599,10 @@ void gemm_direct16(GemmArgs pin) {
     auto tail = [&](int64_t kt) __attribute__((always_inline)) {
         const uint32_t sb = lds_base + (uint32_t)(B_BASE + ((kt + S) & (S - 1)) * B_SLOT);
         if constexpr (SPLIT) {
-            kstep(O{}, std::true_type{}, Z{}, LdB{}, kt + S, 0u, sb);
+            kstep(O{}, std::true_type{}, Z{}, LdB{}, O{}, kt + S, 0u, sb);
         } else {
             const uint32_t sa = lds_base + (uint32_t)(A_BASE + ((kt + S) & (S - 1)) * A_SLOT);
-            kstep(O{}, std::true_type{}, Z{}, LdAB{}, kt + S, sa, sb);
+            kstep(O{}, std::true_type{}, Z{}, LdAB{}, O{}, kt + S, sa, sb);
         }
     };
 
@@ -1474,8 +1619,6 @@ void gemm_direct16(GemmArgs pin) {
     head(0);
     for (int64_t kt = 0; kt + 1 < nk; ++kt) {
         tail(kt);
-        fra.advance();
-        frb.advance();
         head(kt + 1);
     }
     tail(nk - 1);
@@ -2095,8 +2238,16 @@ int run_plan(gemm_f16f32_plan_t plan, const void *A, const void *B, void *C, flo
     KernelFn fn = kernels().k[ti][ep][tile][ak][bkc][vec ? 1 : 0];
     // K-full variants: every stage inside K (for split-K, every slice: kchunk
     // is a multiple of BK, so K must be too).  K = 0 takes the variant with K
-    // tests, whose loads then all fail the range check.
-    if (ts.kind == KIND_DIRECT16 && p.K > 0 && p.K % ts.bk == 0) fn = kernels().kfull[ti][ep][tile][ak][bkc];
+    // tests, whose loads then all fail the range check.  They keep 32-bit
+    // byte counts from each tile's base down to S stages past the end of K,
+    // so both operands must lie well within 2^31 bytes of that.
+    auto within = [&](int64_t extent, bool kc, int64_t ld) {
+        const int64_t step = kc ? ts.bk : ts.bk * ld;
+        return (extent + (p.K / ts.bk + ts.stages + 1) * step) * 2 < (int64_t(1) << 31);
+    };
+    if (ts.kind == KIND_DIRECT16 && p.K > 0 && p.K % ts.bk == 0 && within(a.extent_a, ak, a.lda) &&
+        within(a.extent_b, bkc, a.ldb))
+        fn = kernels().kfull[ti][ep][tile][ak][bkc];
     if (!fn) return GEMM_ERR_UNSUPPORTED;
     void *args[] = {&a};
     const unsigned threads = ts.kind == KIND_STREAM ? 512u : (unsigned)(64 * ts.wgm * ts.wgn);
