@@ -183,6 +183,9 @@ class ClockSampler:
 
     def __init__(self):
         self.samples = []
+        self.power_w = []        # socket power (W) of the same readings
+        self.power_cap_w = None
+        self._power = None
         self._handle = None
         self._last_ts = None
         self.error = None
@@ -192,6 +195,11 @@ class ClockSampler:
             self._amdsmi = amdsmi
             self._handle = amdsmi.amdsmi_get_processor_handles()[0]
             self._last_ts = self._read()[0]
+            try:
+                cap = amdsmi.amdsmi_get_power_cap_info(self._handle).get("power_cap")
+                self.power_cap_w = cap / 1e6 if isinstance(cap, (int, float)) and cap > 0 else None
+            except Exception:
+                pass
         except Exception as e:   # no amdsmi, no permission, no device
             self.error = f"{type(e).__name__}: {e}"[:120]
             self._handle = None
@@ -202,6 +210,8 @@ class ClockSampler:
         if not clks and isinstance(m.get("current_gfxclk"), (int, float)):
             clks = [m["current_gfxclk"]]
         busy = m.get("average_gfx_activity")
+        power = m.get("current_socket_power")
+        self._power = power if isinstance(power, (int, float)) and power > 0 else None
         return m.get("firmware_timestamp"), (sum(clks) / len(clks) if clks else None), busy
 
     def poll(self):
@@ -217,6 +227,8 @@ class ClockSampler:
             self._last_ts = ts
             if mhz is not None and isinstance(busy, (int, float)) and busy >= 50:
                 self.samples.append(mhz)
+                if self._power is not None:
+                    self.power_w.append(self._power)
 
     @property
     def available(self):
@@ -224,6 +236,9 @@ class ClockSampler:
 
     def mean_mhz(self):
         return sum(self.samples) / len(self.samples) if self.samples else None
+
+    def mean_power_w(self):
+        return sum(self.power_w) / len(self.power_w) if self.power_w else None
 
 
 # ------------------------------------------------------------ helpers
@@ -656,6 +671,9 @@ def main():
         "gb_per_s": round(gbs, 1),
         "clock_mhz_measured": None if mhz is None else round(mhz, 1),
         "clock_samples": len(clock.samples),
+        "socket_power_w_measured": (None if clock.mean_power_w() is None
+                                    else round(clock.mean_power_w(), 1)),
+        "socket_power_cap_w": clock.power_cap_w,
         "pct_of_measured_clock_peak": (None if mhz is None else
                                        round(100.0 * tflops * 1e12 /
                                              (NUM_CUS * FLOP_PER_CLK_CU * mhz * 1e6), 2)),
