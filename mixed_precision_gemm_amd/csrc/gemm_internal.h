@@ -21,7 +21,8 @@ enum TileId : int {
     TILE_STREAM64 = 7,       // skinny M <= 64
     TILE_STREAM32W = 8,      // skinny M <= 32, wide N: 64 columns per workgroup
     TILE_128x128_D4 = 9,     // the 128 tile on a four-slot ring (one workgroup per CU)
-    NUM_TILES = 10
+    TILE_STREAM16W = 10,     // skinny M <= 16, wide N: 64 columns per workgroup
+    NUM_TILES = 11
 };
 
 // Three kernel families share the tile table:
@@ -50,6 +51,7 @@ constexpr TileShape kTiles[NUM_TILES] = {
     {64, 16, 32, 1, 1, 1, KIND_STREAM, "stream64x16"},
     {32, 64, 32, 1, 1, 1, KIND_STREAM, "stream32x64"},
     {128, 128, 64, 2, 2, 4, KIND_DIRECT16, "128x128x64m16d4"},
+    {16, 64, 32, 1, 1, 1, KIND_STREAM, "stream16x64"},
 };
 
 // Tile of the staged kernel that serves operands the direct kernel cannot

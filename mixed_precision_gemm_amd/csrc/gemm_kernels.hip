@@ -1685,8 +1685,13 @@ __global__ __launch_bounds__(512) void gemm_stream(GemmArgs pin) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
+    // With split-K, block id = slice * total_tiles + tile, and the slice's
+    // K range is a multiple of 64 (A and B are K-contiguous here).
+    const int slice = (int)(blockIdx.x / (unsigned)p.total_tiles);
+    const int tile = (int)(blockIdx.x - (unsigned)slice * (unsigned)p.total_tiles);
+    if (p.ksplit > 1) apply_k_slice(p, slice, true, true);
     int b, tm, tn;
-    tile_coords(p, blockIdx.x, b, tm, tn);
+    tile_coords(p, tile, b, tm, tn);
     const int64_t m0 = (int64_t)tm * (MB * 16), n0 = (int64_t)tn * (NB * 16);
     const uint16_t *Ab = p.A + b * p.sa;
     const uint16_t *Bb = p.B + b * p.sb;
@@ -1765,6 +1770,69 @@ __global__ __launch_bounds__(512) void gemm_stream(GemmArgs pin) {
     __syncthreads();
 
     const float alpha = p.alpha, beta = p.beta;
+    constexpr int TE = MB * 16 * NB * 16;   // outputs of the block
+    if (p.ksplit > 1) {
+        // Split-K: the block's fp32 partial (its waves summed in order) goes
+        // to the workspace, slice-major, by the ordering rules of the direct
+        // kernels' split-K (stores written through to memory and loads that
+        // miss the L2, so slices may run on different XCDs; the device-scope
+        // counter orders them); the last slice to arrive sums the partials
+        // in slice order and applies the epilogue.
+        __shared__ int s_last;
+        constexpr int kCoherent = 1 | 16;
+        const __amdgpu_buffer_rsrc_t rws = make_rsrc(p.ws, (int64_t)p.ksplit * p.total_tiles * TE * 4);
+        const uint32_t mine = (uint32_t)(((int64_t)slice * p.total_tiles + tile) * TE * 4);
+        for (int o = tid; o < TE; o += NW * 64) {
+            const int i = o / (NB * 16), j = o % (NB * 16);
+            float v = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) v += red[w][i][j];
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rws,
+                                                  mine + (uint32_t)(o * 4), 0, kCoherent);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" : : : "memory");   // this lane's partial is in memory
+        __syncthreads();
+        if (tid == 0)
+            s_last = __hip_atomic_fetch_add(&p.ws_count[tile], 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT) == p.ksplit - 1;
+        __syncthreads();
+        if (!s_last) return;
+        constexpr int KSMAX = 8;
+        const uint32_t tile0 = (uint32_t)((int64_t)tile * TE * 4);
+        const uint32_t slice_stride = (uint32_t)((int64_t)p.total_tiles * TE * 4);
+        for (int o = tid; o < TE; o += NW * 64) {
+            const int i = o / (NB * 16), j = o % (NB * 16);
+            float part[KSMAX];
+#pragma unroll
+            for (int sl = 0; sl < KSMAX; ++sl)
+                part[sl] = sl < p.ksplit
+                    ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                          rws, tile0 + (uint32_t)sl * slice_stride + (uint32_t)(o * 4), 0, kCoherent))
+                    : 0.0f;
+            float v = part[0];
+#pragma unroll
+            for (int sl = 1; sl < KSMAX; ++sl)
+                if (sl < p.ksplit) v += part[sl];
+            const int64_t m = m0 + i, nn = n0 + j;
+            if (m >= p.M || nn >= p.N) continue;
+            v *= alpha;
+            const int64_t off = b * p.sc + m * p.ldc + nn;
+            if (p.out_f32) {
+                float *C = (float *)p.C + off;
+                if (beta != 0.0f) v += beta * *C;
+                if (p.epi) v = activate(p.act, p.bias ? v + p.bias[nn] : v);
+                *C = v;
+            } else {
+                TI *C = (TI *)p.C + off;
+                if (beta != 0.0f) v += beta * (float)*C;
+                if (p.epi) v = activate(p.act, p.bias ? v + p.bias[nn] : v);
+                *C = (TI)v;
+            }
+        }
+        if (tid == 0)
+            __hip_atomic_store(&p.ws_count[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
     for (int o = tid; o < MB * 16 * NB * 16; o += NW * 64) {
         const int i = o / (NB * 16), j = o % (NB * 16);
         const int64_t m = m0 + i, nn = n0 + j;
@@ -1928,6 +1996,7 @@ void fill_type(TileKernels &k, FullKernels &kfull) {
     fill_stream<TI, EPI, TILE_STREAM32>(k[TILE_STREAM32]);
     fill_stream<TI, EPI, TILE_STREAM64>(k[TILE_STREAM64]);
     fill_stream<TI, EPI, TILE_STREAM32W>(k[TILE_STREAM32W]);
+    fill_stream<TI, EPI, TILE_STREAM16W>(k[TILE_STREAM16W]);
 }
 
 }  // namespace

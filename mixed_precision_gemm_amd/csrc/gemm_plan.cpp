@@ -48,7 +48,7 @@ int choose_tile(int64_t M, int64_t N, int64_t K, int64_t batch, bool kc_both, bo
     // on, N that yields 64 or more 128-wide tiles goes to the 128 tile
     // (split-K) instead, which shares A and B through LDS.  (Measured on the
     // K = 4096 linear shapes.)
-    if (kc_both && M <= 16) return TILE_STREAM16;
+    if (kc_both && M <= 16) return N >= 8192 ? TILE_STREAM16W : TILE_STREAM16;
     if (kc_both && M <= 32) return ceil_div(N, 64) >= 160 ? TILE_STREAM32W : TILE_STREAM32;
     if (kc_both && M <= 64 && ceil_div(N, 128) < 64) return TILE_STREAM64;
     auto count = [&](int t) {
@@ -79,9 +79,38 @@ int choose_tile(int64_t M, int64_t N, int64_t K, int64_t batch, bool kc_both, bo
 // multiple of the 64-deep stage, at most 8 slices.  Tiles that already fill
 // a quarter of the CUs are cut only when K is deep: the partial tiles and
 // their reduction cost more than they gain at K ~ 1024 (measured at 1024^3).
+//
+// K slices for the 64-column streaming tile (M <= 16, N >= 8192): up to four
+// workgroups per CU, slices at least 1024 deep (four K steps per wave), at
+// most 8.  Every streaming workgroup re-reads its rows of A from the L2, and
+// with one 16-column block per workgroup those hits (as many bytes as B)
+// held B's HBM stream to two thirds of what it reaches alone (measured on
+// 16 x 11008 x 4096 with A's or B's loads removed: 18.3 us without A's,
+// 27 with both); 64 columns per workgroup cut them by four, and the slices
+// keep the grid as large as before.  The last slice of a block to finish sums
+// the partial blocks in slice order.  Measured against one 16-column block
+// per workgroup: 16 x 11008 and 16 x 12288 (K = 4096) 4-5% faster; at N =
+// 4096 7% slower, so narrower N keeps the 16-column tile, unsplit.
+void choose_ksplit_stream(gemm_f16f32_plan_s *p, int64_t tiles) {
+    if (p->tile != TILE_STREAM16W || tiles > kMaxCounters) return;
+    int64_t ks = std::min<int64_t>(8, ceil_div(4 * kNumCUs, tiles));
+    ks = std::min<int64_t>(ks, p->K / 1024);
+    if (ks < 2) return;
+    const int64_t chunk = ceil_div(ceil_div(p->K, ks), 64) * 64;
+    const int64_t n = ceil_div(p->K, chunk);
+    if (n < 2) return;
+    p->kchunk = chunk;
+    p->ksplit = (int)n;
+    p->split_bytes = n * tiles * kTiles[p->tile].bm * kTiles[p->tile].bn * 4;
+}
+
 void choose_ksplit(gemm_f16f32_plan_s *p, int64_t tiles) {
     p->ksplit = 1;
     p->kchunk = p->K;
+    if (kTiles[p->tile].kind == KIND_STREAM && p->vec_ok) {
+        choose_ksplit_stream(p, tiles);
+        return;
+    }
     if (p->tile != TILE_128x128 || !p->vec_ok || p->batch != 1 || tiles >= kNumCUs) return;
     if (tiles >= kNumCUs / 4 && p->K < 2048) return;
     int64_t ks = std::max<int64_t>(2, kNumCUs / tiles);

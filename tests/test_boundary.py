@@ -109,7 +109,8 @@ def test_streaming_plan_with_large_column_pitch():
         assert p.kernel == "gemm_stream16x16_nt_direct"
         assert p.workspace_bytes() == 0
     with mpg.Plan(16, 152064, 8192, layout_b=GEMM_COL_MAJOR) as p:
-        assert p.kernel.startswith("gemm_stream16x16")
+        # wide N: 64 columns per workgroup, unsplit (more blocks than counters)
+        assert p.kernel == "gemm_stream16x64_nt_direct"
 
 
 def test_null_out_pointer():
@@ -136,6 +137,9 @@ def test_kernel_choice_by_regime():
     assert kern(8192, 8192, 8192, layout_b=GEMM_COL_MAJOR).endswith("nt_direct")
     # skinny, K-contiguous A and B: streaming kernel; other layouts: small tiles
     assert kern(16, 4096, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_stream16x16")
+    # M <= 16 with N >= 8192: 64 columns per workgroup, K in slices of >= 1024
+    assert kern(16, 11008, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream16x64_nt_direct_sk4"
+    assert kern(16, 8192, 1024, layout_b=GEMM_COL_MAJOR) == "gemm_stream16x64_nt_direct"
     assert kern(40, 4096, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_stream64x16")
     # wide N: 64 columns per streaming workgroup (M <= 32), else the 128 tile
     assert kern(32, 11008, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_stream32x64")

@@ -692,6 +692,38 @@ def test_split_k_repeatable_and_interleaved():
     check_bound(c_logical(c2, C2.cpu()), ref2, scale2, c2.out_type, "split-K interleaved")
 
 
+@pytest.mark.parametrize("shape,kw,frag", [
+    ((16, 11008, 4096), {}, "stream16x64_nt_direct_sk4"),
+    ((12, 12288, 4096), dict(out_type=OUT_F32, alpha=0.5, beta=-1.0), "stream16x64_nt_direct_sk4"),
+    ((16, 8200, 3000), dict(beta=1.0), "stream16x64_nt_direct_sk2"),        # ragged N, short last slice
+    ((16, 8192, 2048), dict(batch=2, out_type=OUT_F32), "stream16x64_nt_direct_sk2"),   # batched
+])
+def test_streaming_split_k(shape, kw, frag):
+    """The 64-column streaming tile with K slices summed by the last slice to
+    arrive: parity with the oracle, the same bits on a second run, and the
+    counter words zero again afterwards."""
+    M, N, K = shape
+    kw = dict(kw)
+    batch = kw.pop("batch", 1)
+    case = gi.make_case(M, N, K, layout_b=COL_MAJOR, batch=batch, seed=M + N + K, **kw)
+    with mpg.Plan(case.M, case.N, case.K, case.layout_a, case.layout_b, case.out_type, case.lda,
+                  case.ldb, case.ldc, case.batch, case.stride_a, case.stride_b, case.stride_c) as p:
+        assert frag in p.kernel, p.kernel
+        ws = torch.zeros(p.workspace_bytes(), dtype=torch.uint8, device="cuda")
+        A, B, C = to_device(case)
+        C0 = C.clone()
+        outs = []
+        for _ in range(2):
+            C.copy_(C0)
+            p.run(A, B, C, case.alpha, case.beta, workspace=ws)
+            torch.cuda.synchronize()
+            outs.append(C.clone())
+    assert torch.equal(outs[0], outs[1])
+    assert torch.count_nonzero(ws[:4096]).item() == 0
+    ref, scale = oracle_for(case)
+    check_bound(c_logical(case, outs[0].cpu()), ref, scale, case.out_type, f"{frag} {shape}")
+
+
 def test_split_k_plan_with_misaligned_pointer_repacks():
     """A split-K plan run with a misaligned A: A is copied into the padded
     area of the workspace and the split kernel runs on the copy."""
