@@ -514,6 +514,18 @@ __device__ __forceinline__ floatx4 epilogue4(const GemmArgs &p, floatx4 v, float
     return v;
 }
 
+// The same activations with the choice made at compile time (the direct
+// kernels' epilogue dispatches once per tile on the plan's activation, so no
+// branch sits between the batched loads and stores of C).
+template <int ACT>
+__device__ __forceinline__ floatx4 activate4(floatx4 v) {
+    if constexpr (ACT != ACT_NONE) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = activate(ACT, v[e]);
+    }
+    return v;
+}
+
 // Epilogue shared by both kernels: C = alpha * acc + beta * C on the wave's
 // FM x FN blocks of 32 x 32, rounded once to fp16 (RNE) or stored as fp32,
 // masked at the M and N edges.  Accumulator register r of lane l in block
@@ -830,7 +842,7 @@ __device__ inline void store_c4(const GemmArgs &p, int64_t off, int64_t n, bool 
 // conflict on banks.
 template <typename T, bool FULL, int BM, int BN, int WGM, int WGN, int LDS_BYTES, int MB,
           bool EPI, typename AccT, int FM, int FN>
-__device__ inline void store_tile_lds(const GemmArgs &p, const AccT (&acc)[FM][FN],
+__device__ __forceinline__ void store_tile_lds(const GemmArgs &p, const AccT (&acc)[FM][FN],
                                       u32x4 *lds, int b, int64_t m0, int64_t n0,
                                       int wave, int lane) {
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
@@ -895,55 +907,52 @@ __device__ inline void store_tile_lds(const GemmArgs &p, const AccT (&acc)[FM][F
         }
         asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
         barrier();
-        if constexpr (EPI) {
-            // Fused epilogue: the same batched C loads; each lane writes its
-            // pre-activation values back into its own staging slots (one
-            // reader per slot, so no other lane is affected).  Then a loop
-            // after the batched one (not inside it: a partly unrolled loop
-            // inside a fully unrolled one kept the latter rolled, and its
-            // register arrays went to scratch) activates and stores them,
-            // four row groups per iteration: 16 activations in flight, as
-            // one wave per SIMD hides no latency.
+        // The staged rows in one fully unrolled loop: C loaded in batches
+        // (the next batch in flight while one is combined), beta * C and the
+        // bias added, then either stored (no activation: one rounding per
+        // output) or, with an activation, written back to the lane's own
+        // staging slot (one reader per slot).  The activation then runs in a
+        // second, rolled loop chosen once per tile, so that no branch sits
+        // between the batched loads and stores, and the fully unrolled loop
+        // is not repeated per activation.
+        const bool act = EPI && p.act != ACT_NONE;
 #pragma unroll
-            for (int it0 = 0; it0 < IT; it0 += CB) {
-                const int buf = (it0 / CB) & 1;
-                if (it0 + CB < IT) load_batch(pass, it0 + CB, buf ^ 1);
+        for (int it0 = 0; it0 < IT; it0 += CB) {
+            const int buf = (it0 / CB) & 1;
+            if (it0 + CB < IT) load_batch(pass, it0 + CB, buf ^ 1);
 #pragma unroll
-                for (int t = 0; t < CB; ++t) {
-                    const int r = ((it0 + t) * NW + wave) * RPI + r_in;
-                    floatx4 *slot = (floatx4 *)(base + r * BN * 4 + ((g ^ (r & SW)) << 4));
-                    floatx4 v = *slot;
-                    if (beta != 0.0f) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] += beta * (float)cv[buf][t][e];
-                    }
-                    *slot = v + bias4;
-                }
-            }
-#pragma unroll 4
-            for (int it = 0; it < IT; ++it) {
-                const int r = (it * NW + wave) * RPI + r_in;
+            for (int t = 0; t < CB; ++t) {
+                const int r = ((it0 + t) * NW + wave) * RPI + r_in;
                 const int64_t m = m0 + pass * PR + r;
-                floatx4 v = *(const floatx4 *)(base + r * BN * 4 + ((g ^ (r & SW)) << 4));
-                v = epilogue4(p, v, floatx4{0.0f, 0.0f, 0.0f, 0.0f});
-                if (FULL || (m < p.M && n_ok)) store_c4<T>(p, cbase + m * p.ldc, n, vec, v);
+                floatx4 *slot = (floatx4 *)(base + r * BN * 4 + ((g ^ (r & SW)) << 4));
+                floatx4 v = *slot;
+                if (beta != 0.0f) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] += beta * (float)cv[buf][t][e];
+                }
+                if constexpr (EPI) v += bias4;
+                if (act)
+                    *slot = v;
+                else if (FULL || (m < p.M && n_ok))
+                    store_c4<T>(p, cbase + m * p.ldc, n, vec, v);
             }
-        } else {
-#pragma unroll
-            for (int it0 = 0; it0 < IT; it0 += CB) {
-                const int buf = (it0 / CB) & 1;
-                if (it0 + CB < IT) load_batch(pass, it0 + CB, buf ^ 1);
-#pragma unroll
-                for (int t = 0; t < CB; ++t) {
-                    const int r = ((it0 + t) * NW + wave) * RPI + r_in;
+        }
+        if constexpr (EPI) {
+            auto act_rows = [&](auto actc) __attribute__((always_inline)) {
+                constexpr int ACT = decltype(actc)::value;
+#pragma unroll 4
+                for (int it = 0; it < IT; ++it) {
+                    const int r = (it * NW + wave) * RPI + r_in;
                     const int64_t m = m0 + pass * PR + r;
-                    floatx4 v = *(const floatx4 *)(base + r * BN * 4 + ((g ^ (r & SW)) << 4));
-                    if (beta != 0.0f) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] += beta * (float)cv[buf][t][e];
-                    }
+                    const floatx4 v = activate4<ACT>(*(const floatx4 *)(base + r * BN * 4 + ((g ^ (r & SW)) << 4)));
                     if (FULL || (m < p.M && n_ok)) store_c4<T>(p, cbase + m * p.ldc, n, vec, v);
                 }
+            };
+            switch (p.act) {
+            case ACT_RELU: act_rows(std::integral_constant<int, ACT_RELU>{}); break;
+            case ACT_GELU: act_rows(std::integral_constant<int, ACT_GELU>{}); break;
+            case ACT_SILU: act_rows(std::integral_constant<int, ACT_SILU>{}); break;
+            default: break;
             }
         }
         if (pass + 1 < NPASS) {
@@ -963,7 +972,7 @@ __device__ inline void store_tile_lds(const GemmArgs &p, const AccT (&acc)[FM][F
 // resets the counter for the next launch.
 template <typename T, int BM, int BN, int WGM, int WGN, int LDS_BYTES, int MB,
           typename AccT, int FM, int FN>
-__device__ inline void store_tile_splitk(const GemmArgs &p, const AccT (&acc)[FM][FN],
+__device__ __forceinline__ void store_tile_splitk(const GemmArgs &p, const AccT (&acc)[FM][FN],
                                          u32x4 *lds, int tile, int slice, int b,
                                          int64_t m0, int64_t n0, int wave, int lane) {
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
@@ -1264,8 +1273,7 @@ struct Frag16 {
 // direct kernels' loads): 64-bit base, bytes left from it (negative past the
 // operand's end, where the descriptor holds zero records).  The words are
 // kept current, so a stage's loads use them as they are; advance() is four
-// scalar instructions, as volatile assembly so that it stays where the
-// kernel places it.  Callers guarantee that bytes left and the step stay
+// scalar instructions.  Callers guarantee that bytes left and the step stay
 // within +-2^31 and that the base stays below 2^48 (word 1's stride bits are
 // never touched).
 struct RunRsrc {
@@ -1288,12 +1296,14 @@ struct RunRsrc {
         return r;
     }
     __device__ void advance() {
-        const int32_t hi_step = step < 0 ? -1 : 0;
-        asm volatile(
-            "s_add_u32 %0, %0, %4\n\ts_addc_u32 %1, %1, %5\n\ts_sub_i32 %3, %3, %4\n\ts_max_i32 %2, %3, 0"
-            : "+s"(w0), "+s"(w1), "=s"(w2), "+s"(left)
-            : "s"(step), "s"(hi_step)
-            : "scc");
+        // Plain scalar arithmetic; readfirstlane keeps every word provably
+        // uniform (free when it already is), whatever register the compiler
+        // picked for an intermediate, so the loads' descriptor stays scalar.
+        const uint64_t a = (((uint64_t)(uint32_t)w1 << 32) | (uint32_t)w0) + (uint64_t)(int64_t)step;
+        w0 = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a);
+        w1 = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(a >> 32));
+        left = __builtin_amdgcn_readfirstlane(left - step);
+        w2 = __builtin_amdgcn_readfirstlane(left > 0 ? left : 0);
     }
 };
 
