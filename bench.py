@@ -181,7 +181,7 @@ class ClockSampler:
     a new firmware timestamp and the engine at least half busy are kept.  Inert where
     amdsmi or the metrics are unavailable."""
 
-    def __init__(self):
+    def __init__(self, enabled=True):
         self.samples = []
         self.power_w = []        # socket power (W) of the same readings
         self.power_cap_w = None
@@ -189,6 +189,8 @@ class ClockSampler:
         self._handle = None
         self._last_ts = None
         self.error = None
+        if not enabled:         # --clock-window 0: amdsmi is not touched at all
+            return
         try:
             import amdsmi
             amdsmi.amdsmi_init()
@@ -604,7 +606,7 @@ def main():
 
     # Clock under sustained load of the same step, after the timed region.
     # Bursts of about 25 ms of steps, two in flight, so the engine never idles.
-    clock = ClockSampler()
+    clock = ClockSampler(args.clock_window > 0)
     if clock.available and args.clock_window > 0:
         per_step = ev0.elapsed_time(ev1) / args.steps * 1e-3
         burst = max(1, int(25e-3 / max(per_step, 1e-7)))
