@@ -31,8 +31,9 @@ enum TileId : int {
 //                for 16-byte-aligned operands; split-K capable;
 //   KIND_STAGED: a two-slot ring filled through registers (global -> VGPR ->
 //                LDS), used for the small tiles and for the narrow-load path;
-//   KIND_STREAM:  skinny M with K-contiguous A and B: fragments loaded from
-//                global memory straight into registers, K split over 8 waves.
+//   KIND_STREAM:  skinny M with K-contiguous A and B: K split over 8 waves,
+//                each streaming its B rows through its own LDS region
+//                (direct-to-LDS loads) and its A fragments into registers.
 enum KernelKind : int { KIND_STAGED = 1, KIND_STREAM = 2, KIND_DIRECT16 = 3 };
 
 struct TileShape {

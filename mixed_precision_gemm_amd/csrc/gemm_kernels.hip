@@ -1671,12 +1671,19 @@ void gemm_direct16(GemmArgs pin) {
 // the kernel is built to keep many bytes in flight rather than to reuse tiles:
 //   * a workgroup owns NB x 16 columns of C (all M rows, MB blocks of 16) and
 //     splits K over its 8 waves, so even N = 4096 yields 256 workgroups;
-//   * MFMA fragments of v_mfma_f32_16x16x32_f16 are loaded straight from
-//     global memory (lane l holds 8 consecutive k of row/column l % 16 --
-//     16 contiguous bytes of a K-contiguous operand), UNROLL K steps at a
-//     time, with the range check zero-filling rows >= M, columns >= N and
-//     k >= K; each A fragment feeds NB MFMAs, so A (re-read by every
-//     workgroup from L2) costs 1/NB of the load instructions it would;
+//   * each wave streams its K range in batches of U steps of 32 (U = 2 for
+//     64-column workgroups, else 4): the batch's B rows go straight to the
+//     wave's own LDS region by direct-to-LDS loads, each load covering whole
+//     128-byte lines of 16/U rows (a load shaped as one MFMA fragment, 16
+//     rows x 64 bytes, touches twice the lines for the same bytes and
+//     streamed HBM 8-20 % slower), and come back as fragments by
+//     ds_read_b128; the next batch's loads are issued as soon as the
+//     fragments are in registers, before this batch's MFMAs;
+//   * A fragments of v_mfma_f32_16x16x32_f16 (lane l: 8 consecutive k of
+//     row l % 16, 16 contiguous bytes of the K-contiguous operand) are
+//     loaded from global memory into registers (A is small and stays in L2);
+//     each feeds NB MFMAs.  The range check zero-fills rows >= M, columns
+//     >= N and k >= K on both operands;
 //   * the 8 partial tiles are summed through LDS and the alpha/beta epilogue
 //     is applied once per output.
 // ---------------------------------------------------------------------------
@@ -1687,9 +1694,18 @@ __global__ __launch_bounds__(512) void gemm_stream(GemmArgs pin) {
     GemmArgs p = pin;
     if constexpr (!EPI) p.epi = 0;   // no epilogue code in this instantiation
     constexpr int NW = 8;
-    constexpr int UNROLL = 4;   // K steps whose loads are issued together (8: 1-3% slower)
-    static_assert(MB * NB <= 8, "reduction buffer within 64 KiB");
-    __shared__ float red[NW][MB * 16][NB * 16];
+    // K steps (32 deep) per batch: a batch of B is NB*16 rows x U*64 bytes,
+    // NB*U loads of 1 KiB, each covering 16/U whole rows of U*64 bytes.
+    constexpr int U = NB >= 4 ? 2 : 4;
+    constexpr int ROWB = U * 64;                 // bytes of one B row in a batch
+    constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
+    constexpr int NLD = NB * U;                  // loads per batch
+    constexpr int WAVE_BYTES = NLD * 1024;       // LDS of one wave's batch
+    constexpr int RED_BYTES = NW * MB * 16 * NB * 16 * 4;
+    constexpr int LDS_BYTES = NW * WAVE_BYTES > RED_BYTES ? NW * WAVE_BYTES : RED_BYTES;
+    static_assert(LDS_BYTES <= 64 * 1024, "two workgroups per CU");
+    __shared__ u32x4 lds_raw[LDS_BYTES / 16];
+    auto red = reinterpret_cast<float (*)[MB * 16][NB * 16]>(lds_raw);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1710,28 +1726,49 @@ __global__ __launch_bounds__(512) void gemm_stream(GemmArgs pin) {
     const int64_t steps = (p.K + 31) / 32;
     const int64_t s_lo = steps * wave / NW, s_hi = steps * (wave + 1) / NW;
 
-    const int r16 = lane & 15;            // row of A / column of B this lane loads
+    const int r16 = lane & 15;            // row of A this lane loads
     const int kq = 8 * (lane >> 4);       // first of its 8 consecutive k
     // Descriptors based at the workgroup's first row of A and first column
     // of B, so that lane offsets span only MB*16 rows (NB*16 columns) of at
     // most 2^22 elements plus K: below 2^31 bytes however large N * ldb is.
     const int64_t a_base = m0 * p.lda, b_base = n0 * p.ldb;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + a_base, (p.extent_a - a_base) * 2);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + b_base, (p.extent_b - b_base) * 2);
-    bool a_ok[MB], b_ok[NB];
-    uint32_t a_off[MB], b_off[NB];
+    const sgpr4 rb = make_rsrc_words(Bb + b_base, (p.extent_b - b_base) * 2);
+    bool a_ok[MB];
+    uint32_t a_off[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
         const int64_t ml = mb * 16 + r16;   // row within the workgroup's rows
         a_ok[mb] = m0 + ml < p.M;
         a_off[mb] = (uint32_t)((ml * p.lda + kq) * 2);
     }
+    // B rows (columns of the product) are staged in LDS: load j of a batch
+    // brings rows j*16/U .. (j+1)*16/U - 1, lane t row j*16/U + t/CPR, its
+    // 16-byte slot t%CPR holding chunk (slot ^ bswz(row)) of the row's batch
+    // bytes, so that one load reads whole 128-byte lines of whole rows.  The
+    // XOR makes the fragment reads (16 rows at one chunk per 16 lanes)
+    // free of bank conflicts.
+    auto bswz = [](int r) {
+        if constexpr (U == 2) return swz16(r);                  // 8 chunks a row
+        else return (r & 1) | ((r & 6) << 1);                   // 16 chunks a row
+    };
+    bool b_ok[NLD];
+    uint32_t b_off[NLD];
+    int b_k[NLD];                          // first k of the lane's chunk in the batch
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const int64_t nl = nb * 16 + r16;   // column within the workgroup's columns
-        b_ok[nb] = n0 + nl < p.N;
-        b_off[nb] = (uint32_t)((nl * p.ldb + kq) * 2);
+    for (int j = 0; j < NLD; ++j) {
+        const int r = j * (16 / U) + lane / CPR;
+        const int c = (lane % CPR) ^ bswz(r & 15);
+        b_ok[j] = n0 + r < p.N;
+        b_k[j] = 8 * c;
+        b_off[j] = (uint32_t)(((int64_t)r * p.ldb + 8 * c) * 2);
     }
+    const uint32_t wave_lds = lds_offset(lds_raw) + (uint32_t)(wave * WAVE_BYTES);
+    // Fragment (u, nb): row nb*16 + l%16, chunk 4u + l/16 of the batch.
+    uint32_t frag_addr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        frag_addr[u] = (uint32_t)(wave * WAVE_BYTES + r16 * ROWB + 16 * ((4 * u + (lane >> 4)) ^ bswz(r16)));
 
     floatx4v acc[MB][NB];
 #pragma unroll
@@ -1739,34 +1776,87 @@ __global__ __launch_bounds__(512) void gemm_stream(GemmArgs pin) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = floatx4v{0.f, 0.f, 0.f, 0.f};
 
-    for (int64_t s0 = s_lo; s0 < s_hi; s0 += UNROLL) {
-        half8 fa[UNROLL][MB], fb[UNROLL][NB];
+    // A fragments of the batch in flight.  With one row block (MB = 1)
+    // they are double-buffered and issued with the batch's B loads; with
+    // more, the next batch's A loads wait for this batch's MFMAs, so that
+    // one set of fragment registers suffices (A comes from L2, whose latency
+    // the B stream's hides).
+    constexpr bool A_EARLY = MB == 1;
+    half8 fa[U][MB];
+    // A chunk of the batch starting at step s is loaded when its step is
+    // below s_hi and its first k below K (both limits taken relative to s,
+    // so that the per-lane tests are 32-bit).
+    auto steps_left = [&](int64_t s) { return (int)(s_hi - s < U ? s_hi - s : U); };
+    auto k_left = [&](int64_t s) { return (int)(p.K - s * 32 < 32 * U ? p.K - s * 32 : 32 * U); };
+    auto issue_b = [&](int64_t s) __attribute__((always_inline)) {
+        const uint32_t kb = (uint32_t)(s * 64);
+        const int sl = steps_left(s), kl = k_left(s);
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const int64_t k = (s0 + u) * 32 + kq;
-            const bool kin = (s0 + u < s_hi) && (k < p.K);
-            const uint32_t kb = (uint32_t)((s0 + u) * 64);
+        for (int j = 0; j < NLD; ++j) {
+            const bool in = b_k[j] < 32 * sl && b_k[j] < kl;
+            lds_dma16(rb, wave_lds + (uint32_t)(j * 1024), (b_ok[j] && in) ? b_off[j] + kb : kOutOfRange);
+        }
+    };
+    auto issue_a = [&](int64_t s) __attribute__((always_inline)) {
+        const uint32_t kb = (uint32_t)(s * 64);
+        const int sl = steps_left(s), kl = k_left(s);
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-                fb[u][nb] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(
-                    rb, (b_ok[nb] && kin) ? b_off[nb] + kb : kOutOfRange, 0, 0));
+        for (int u = 0; u < U; ++u) {
+            const bool kin = u < sl && 32 * u + kq < kl;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
                 fa[u][mb] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(
-                    ra, (a_ok[mb] && kin) ? a_off[mb] + kb : kOutOfRange, 0, 0));
+                    ra, (a_ok[mb] && kin) ? a_off[mb] + kb + (uint32_t)(u * 64) : kOutOfRange, 0, 0));
         }
-        // All UNROLL steps' loads are issued before the first MFMA waits on
-        // one (the scheduler would otherwise interleave them and keep fewer
-        // bytes in flight).
+    };
+
+    if (s_lo < s_hi) {
+        issue_b(s_lo);
+        issue_a(s_lo);
+    }
+    for (int64_t s0 = s_lo; s0 < s_hi; s0 += U) {
+        // The batch's loads (the only ones outstanding) have landed.  The
+        // empty statement naming its A fragments is their first use: the
+        // compiler's own wait for them goes here, not after the next batch's
+        // B loads.  With early A loads the fragments move to fc, freeing fa.
+        asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+        half8 fb[U][NB], fc[U][MB];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                asm volatile("" : "+v"(fa[u][mb]));
+                fc[u][mb] = fa[u][mb];
+            }
+        const char *base = (const char *)lds_raw;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                fb[u][nb] = *(const half8 *)(base + frag_addr[u] + nb * 16 * ROWB);
+        // The region is free once its fragments are in registers: the next
+        // batch's B loads go out before this batch's MFMAs.
+        asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+        const bool more = s0 + U < s_hi;
+        if (more) {
+            issue_b(s0 + U);
+            if constexpr (A_EARLY) issue_a(s0 + U);
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
+        for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
-                    acc[mb][nb] = mfma16<TI>(fa[u][mb], fb[u][nb], acc[mb][nb]);
+                    acc[mb][nb] = mfma16<TI>(A_EARLY ? fc[u][mb] : fa[u][mb], fb[u][nb], acc[mb][nb]);
+        if constexpr (!A_EARLY) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (more) issue_a(s0 + U);
+        }
     }
+    // Every wave is done with its LDS region before the reduction reuses it.
+    __syncthreads();
 
     // Accumulator register r of lane l holds row 4*(l/16) + r, column l % 16
     // of each 16 x 16 block.

@@ -42,14 +42,14 @@ int64_t operand_extent(int64_t rows, int64_t cols, int64_t ld, int64_t batch,
 // small staged tiles, the 32-row one for skinny M (token counts of a linear
 // layer).
 int choose_tile(int64_t M, int64_t N, int64_t K, int64_t batch, bool kc_both, bool vec_ok) {
-    // Skinny M with K-contiguous A and B streams B through registers.  Every
-    // workgroup re-reads its rows of A, so wide N (at least 160 workgroups of
-    // 64 columns) takes 64 columns per workgroup from M = 17 on; from M = 33
-    // on, N that yields 64 or more 128-wide tiles goes to the 128 tile
-    // (split-K) instead, which shares A and B through LDS.  (Measured on the
-    // K = 4096 linear shapes.)
+    // Skinny M with K-contiguous A and B streams B through LDS.  Every
+    // workgroup re-reads its rows of A, so N >= 8192 (128 or more workgroups
+    // of 64 columns, split-K below 160) takes 64 columns per workgroup; from
+    // M = 33 on, N that yields 64 or more 128-wide tiles goes to the 128
+    // tile (split-K) instead, which shares A and B through LDS.  (Measured on
+    // the K = 4096 linear shapes.)
     if (kc_both && M <= 16) return N >= 8192 ? TILE_STREAM16W : TILE_STREAM16;
-    if (kc_both && M <= 32) return ceil_div(N, 64) >= 160 ? TILE_STREAM32W : TILE_STREAM32;
+    if (kc_both && M <= 32) return N >= 8192 ? TILE_STREAM32W : TILE_STREAM32;
     if (kc_both && M <= 64 && ceil_div(N, 128) < 64) return TILE_STREAM64;
     auto count = [&](int t) {
         return ceil_div(M, kTiles[t].bm) * ceil_div(N, kTiles[t].bn) * batch;
@@ -80,21 +80,19 @@ int choose_tile(int64_t M, int64_t N, int64_t K, int64_t batch, bool kc_both, bo
 // a quarter of the CUs are cut only when K is deep: the partial tiles and
 // their reduction cost more than they gain at K ~ 1024 (measured at 1024^3).
 //
-// K slices for the 64-column streaming tile (M <= 16, N >= 8192): up to four
-// workgroups per CU, slices at least 1024 deep (four K steps per wave), at
-// most 8.  Every streaming workgroup re-reads its rows of A from the L2, and
-// with one 16-column block per workgroup those hits (as many bytes as B)
-// held B's HBM stream to two thirds of what it reaches alone (measured on
-// 16 x 11008 x 4096 with A's or B's loads removed: 18.3 us without A's,
-// 27 with both); 64 columns per workgroup cut them by four, and the slices
-// keep the grid as large as before.  The last slice of a block to finish sums
-// the partial blocks in slice order.  Measured against one 16-column block
-// per workgroup: 16 x 11008 and 16 x 12288 (K = 4096) 4-5% faster; at N =
-// 4096 7% slower, so narrower N keeps the 16-column tile, unsplit.
+// K slices for the 64-column streaming tiles (M <= 32, N >= 8192).  With
+// 160 or more workgroups (N >= 10240) a tile is not split: its waves keep
+// their batches streaming back to back, and a split only adds the partial
+// sums' round trips at the end (16 x 11008 x 4096: 20.9 us unsplit, 22.0 in
+// four slices, 24.7 in two; 16 x 16384: 28.2 against 34.9).  Fewer
+// workgroups (128 to 159: N from 8192) are cut into four slices of at least
+// 1024 (16 x 8192 x 4096: 16.7 us against 19.9 unsplit, 18.9 in two, 21.5
+// in eight; 32 x 8192: 20.6 against 25.3 on the 16-column tile).  The last
+// slice of a block to finish sums the partial blocks in slice order.
 void choose_ksplit_stream(gemm_f16f32_plan_s *p, int64_t tiles) {
-    if (p->tile != TILE_STREAM16W || tiles > kMaxCounters) return;
-    int64_t ks = std::min<int64_t>(8, ceil_div(4 * kNumCUs, tiles));
-    ks = std::min<int64_t>(ks, p->K / 1024);
+    if (p->tile != TILE_STREAM16W && p->tile != TILE_STREAM32W) return;
+    if (tiles >= kNumCUs * 5 / 8 || tiles > kMaxCounters) return;
+    int64_t ks = std::min<int64_t>(4, p->K / 1024);
     if (ks < 2) return;
     const int64_t chunk = ceil_div(ceil_div(p->K, ks), 64) * 64;
     const int64_t n = ceil_div(p->K, chunk);

@@ -137,12 +137,20 @@ def test_kernel_choice_by_regime():
     assert kern(8192, 8192, 8192, layout_b=GEMM_COL_MAJOR).endswith("nt_direct")
     # skinny, K-contiguous A and B: streaming kernel; other layouts: small tiles
     assert kern(16, 4096, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_stream16x16")
-    # M <= 16 with N >= 8192: 64 columns per workgroup, K in slices of >= 1024
-    assert kern(16, 11008, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream16x64_nt_direct_sk4"
+    # M <= 32 with N >= 8192: 64 columns per workgroup; fewer than 160
+    # workgroups take four K slices of >= 1024, more are not split
+    assert kern(16, 11008, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream16x64_nt_direct"
+    assert kern(16, 8192, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream16x64_nt_direct_sk4"
+    assert kern(16, 10176, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream16x64_nt_direct_sk4"
+    assert kern(16, 10240, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream16x64_nt_direct"
     assert kern(16, 8192, 1024, layout_b=GEMM_COL_MAJOR) == "gemm_stream16x64_nt_direct"
+    assert kern(16, 8192, 3000, layout_b=GEMM_COL_MAJOR) == "gemm_stream16x64_nt_direct_sk2"
+    assert kern(16, 8192, 4096, layout_b=GEMM_COL_MAJOR, batch=2, stride_a=16 * 4096,
+                stride_b=8192 * 4096, stride_c=16 * 8192) == "gemm_stream16x64_nt_direct"
     assert kern(40, 4096, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_stream64x16")
     # wide N: 64 columns per streaming workgroup (M <= 32), else the 128 tile
-    assert kern(32, 11008, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_stream32x64")
+    assert kern(32, 11008, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream32x64_nt_direct"
+    assert kern(32, 8192, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream32x64_nt_direct_sk4"
     assert kern(32, 4096, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_stream32x16")
     assert kern(64, 11008, 4096, layout_b=GEMM_COL_MAJOR).endswith("d4_nt_direct_sk2")
     # skinny with row-major B: too few tiles for the CUs, so the 128 tile with

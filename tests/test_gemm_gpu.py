@@ -693,10 +693,11 @@ def test_split_k_repeatable_and_interleaved():
 
 
 @pytest.mark.parametrize("shape,kw,frag", [
-    ((16, 11008, 4096), {}, "stream16x64_nt_direct_sk4"),
-    ((12, 12288, 4096), dict(out_type=OUT_F32, alpha=0.5, beta=-1.0), "stream16x64_nt_direct_sk4"),
+    ((16, 8192, 4096), {}, "stream16x64_nt_direct_sk4"),
+    ((12, 9000, 4096), dict(out_type=OUT_F32, alpha=0.5, beta=-1.0), "stream16x64_nt_direct_sk4"),
     ((16, 8200, 3000), dict(beta=1.0), "stream16x64_nt_direct_sk2"),        # ragged N, short last slice
-    ((16, 8192, 2048), dict(batch=2, out_type=OUT_F32), "stream16x64_nt_direct_sk2"),   # batched
+    ((32, 8192, 4096), dict(out_type=OUT_F32), "stream32x64_nt_direct_sk4"),  # two row blocks
+    ((27, 8256, 2048), dict(beta=1.0), "stream32x64_nt_direct_sk2"),        # rows of A past M
 ])
 def test_streaming_split_k(shape, kw, frag):
     """The 64-column streaming tile with K slices summed by the last slice to
