@@ -1041,8 +1041,11 @@ __device__ __forceinline__ void store_tile_splitk(const GemmArgs &p, const AccT 
     const uint32_t slice_stride = (uint32_t)((int64_t)p.total_tiles * tile_elems * 4);
     // All slices of RB row groups (and their C) are requested before any is
     // summed: the partials come from memory, so the reduction is latency
-    // bound unless many loads are in flight.  Slices are summed in order.
-    constexpr int KSMAX = 8, RB = 2;
+    // bound unless many loads are in flight (half the 128 tile's rows at a
+    // time: against a quarter, 3-9 % faster on the split-K shapes, e.g.
+    // 128 x 4096 x 4096 in eight slices 25.9 -> 23.5 us).  Slices are summed
+    // in order.
+    constexpr int KSMAX = 8, RB = IT >= 8 ? 8 : IT;
     static_assert(IT % RB == 0, "row batches");
 #pragma unroll 1
     for (int it0 = 0; it0 < IT; it0 += RB) {
