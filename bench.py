@@ -431,7 +431,8 @@ def run_attention_bench(args):
         rows = 8192
         x = (torch.randn((rows, cols), generator=g) * 4).half().to(dev)
         y = torch.empty_like(x)
-        kernel = "softmax_rows_reg" if cols <= 8192 else "softmax_rows_online"
+        kernel = ("softmax_rows_online" if cols > 8192 else
+                  "softmax_rows_vec" if cols % 8 == 0 else "softmax_rows_reg")
         flops = 0.0
         abytes = rows * cols * 4
         unit_sets = [(x, y)]

@@ -399,6 +399,73 @@ __global__ __launch_bounds__(256) void softmax_rows_reg(SmArgs a) {
     }
 }
 
+// Rows held in registers, read and written 16 bytes (fp16) or 32 bytes
+// (fp32) at a time: NCH chunks of 8 elements per thread, chunk c of thread t
+// covering elements 8 (256 c + t) .. + 7.  For rows whose length, leading
+// dimensions and base addresses are multiples of 8 elements and 16 bytes:
+// every chunk is then wholly inside or wholly outside the row.  Element-wide
+// accesses (the kernel above) move 128 bytes per wave instruction and ran
+// at 0.30 of HBM bandwidth on 8192 rows of 4096.
+template <int NCH, bool IN32, bool OUT32>
+__global__ __launch_bounds__(256) void softmax_rows_vec(SmArgs a) {
+    __shared__ float red[8];
+    const int64_t row = blockIdx.x;
+    const int t = threadIdx.x;
+    float v[NCH][8];
+    float m = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int64_t j0 = ((int64_t)c * 256 + t) * 8;
+        if (j0 < a.cols) {
+            if constexpr (IN32) {
+                const floatx4 *src = (const floatx4 *)((const float *)a.x + row * a.ldx + j0);
+                const floatx4 lo = src[0], hi = src[1];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[c][e] = lo[e] * kLog2e;
+                    v[c][4 + e] = hi[e] * kLog2e;
+                }
+            } else {
+                const half8 h = *(const half8 *)((const _Float16 *)a.x + row * a.ldx + j0);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[c][e] = (float)h[e] * kLog2e;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[c][e] = -INFINITY;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, v[c][e]);
+    }
+    float s = 0.f;
+    const float ms = m == -INFINITY ? 0.f : m;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += __builtin_amdgcn_exp2f(v[c][e] - ms);
+    block_merge(m, s, red);
+    const float mm = m == -INFINITY ? 0.f : m;
+    const float inv = s > 0.f ? __builtin_amdgcn_rcpf(s) : 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int64_t j0 = ((int64_t)c * 256 + t) * 8;
+        if (j0 >= a.cols) continue;
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = __builtin_amdgcn_exp2f(v[c][e] - mm) * inv;
+        if constexpr (OUT32) {
+            floatx4 *dst = (floatx4 *)((float *)a.y + row * a.ldy + j0);
+            dst[0] = floatx4{y[0], y[1], y[2], y[3]};
+            dst[1] = floatx4{y[4], y[5], y[6], y[7]};
+        } else {
+            half8 h;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[e] = (_Float16)y[e];
+            *(half8 *)((_Float16 *)a.y + row * a.ldy + j0) = h;
+        }
+    }
+}
+
 // Long rows: pass 1 keeps (m, s) per thread with the online rule, element by
 // element; the workgroup merges them; pass 2 re-reads and writes.
 template <bool IN32, bool OUT32>
@@ -580,7 +647,19 @@ extern "C" int attn_softmax_rows(int64_t rows, int64_t cols, const void *x, int6
                                          {softmax_rows_reg<32, true, false>, softmax_rows_reg<32, true, true>}};
     static const SmKernel klong[2][2] = {{softmax_rows_online<false, false>, softmax_rows_online<false, true>},
                                          {softmax_rows_online<true, false>, softmax_rows_online<true, true>}};
-    const SmKernel fn = (cols <= 2048 ? k2048 : cols <= 4096 ? k4096 : cols <= 8192 ? k8192 : klong)[i32][o32];
+    static const SmKernel v2048[2][2] = {{softmax_rows_vec<1, false, false>, softmax_rows_vec<1, false, true>},
+                                         {softmax_rows_vec<1, true, false>, softmax_rows_vec<1, true, true>}};
+    static const SmKernel v4096[2][2] = {{softmax_rows_vec<2, false, false>, softmax_rows_vec<2, false, true>},
+                                         {softmax_rows_vec<2, true, false>, softmax_rows_vec<2, true, true>}};
+    static const SmKernel v8192[2][2] = {{softmax_rows_vec<4, false, false>, softmax_rows_vec<4, false, true>},
+                                         {softmax_rows_vec<4, true, false>, softmax_rows_vec<4, true, true>}};
+    // Whole 16-byte chunks: row length, leading dimensions and bases multiples
+    // of 8 elements and 16 bytes.
+    const bool vec = cols % 8 == 0 && ldx % 8 == 0 && ldy % 8 == 0 && (uintptr_t)x % 16 == 0 &&
+                     (uintptr_t)y % 16 == 0;
+    const SmKernel fn = vec && cols <= 8192
+        ? (cols <= 2048 ? v2048 : cols <= 4096 ? v4096 : v8192)[i32][o32]
+        : (cols <= 2048 ? k2048 : cols <= 4096 ? k4096 : cols <= 8192 ? k8192 : klong)[i32][o32];
     void *args[] = {&a};
     return hipLaunchKernel((const void *)fn, dim3((unsigned)rows), dim3(256), args, 0,
                            (hipStream_t)stream) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;

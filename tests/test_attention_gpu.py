@@ -158,8 +158,13 @@ def softmax_bound(ref, x, m, n, out_f32):
 
 @pytest.mark.parametrize("cols", [1, 100, 2048, 2049, 4096, 8192, 8193, 20000])
 @pytest.mark.parametrize("in32,out32", [(False, False), (True, True), (False, True)])
-def test_softmax_rows_parity(cols, in32, out32):
-    rows, ld = 37, cols + 5
+@pytest.mark.parametrize("aligned", [False, True])
+def test_softmax_rows_parity(cols, in32, out32, aligned):
+    """Rows of any length; with aligned rows (length, leading dimension and
+    bases multiples of 8 elements and 16 bytes) the 16-byte-access kernel
+    takes rows of up to 8192."""
+    rows = 37
+    ld = (cols + 7) // 8 * 8 + 8 if aligned else cols + 5
     g = torch.Generator("cpu").manual_seed(cols)
     x = torch.randn(rows, ld, generator=g) * 6
     x[:, : cols // 3] -= 40.0                                 # maximum late in the row
