@@ -251,8 +251,12 @@ def test_integer_inputs_bit_exact_direct_tiles(shape, prefix, sampled, la, lb):
     assert bad.size == 0, f"{kernel}: {len(bad)} inexact, first {bad[:4].tolist()}"
 
 
-@pytest.mark.parametrize("M,N", [(16, 4096), (32, 11008), (64, 4096)])
+@pytest.mark.parametrize("M,N", [(16, 4096), (32, 11008), (64, 4096), (16, 11008), (16, 8192),
+                                 (27, 8200)])
 def test_integer_inputs_bit_exact_streaming(M, N):
+    """Every streaming form: 16 and 64 columns, A staged through LDS (M <=
+    16) or loaded into registers, unsplit and in K slices (16 x 8192, 27 x
+    8200); integer sums stay below 2^24, exact in fp32 in any order."""
     case = gi.make_case(M, N, 4096, layout_b=COL_MAJOR, out_type=OUT_F32,
                         dist_a="integer", dist_b="integer", int_range=(-8, 8), seed=7)
     kernel = plan_kernel(case)
