@@ -218,18 +218,17 @@ void attn_fwd(AttnArgs p) {
         if (active) {
             const _Float16 *kt_lds = lds[buf][0];
             const _Float16 *vt_lds = lds[buf][1];
+            // The first d step starts from a zero accumulator operand
+            // (no register clearing per tile).
             floatx4 s[4][2];
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) s[kb][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int dc = 0; dc < NDC; ++dc)
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
                     const half8 kf = *(const half8 *)&kt_lds[(16 * kb + li) * D + 8 * ((4 * dc + g) ^ kx)];
 #pragma unroll
-                    for (int qb = 0; qb < 2; ++qb) s[kb][qb] = mfma16(kf, qf[qb][dc], s[kb][qb]);
+                    for (int qb = 0; qb < 2; ++qb)
+                        s[kb][qb] = mfma16(kf, qf[qb][dc], dc == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : s[kb][qb]);
                 }
             // Online softmax per query block: lane l's query is row 16 qb +
             // l%16; its keys are k0 + 16 kb + 4 g + r.
@@ -270,8 +269,12 @@ void attn_fwd(AttnArgs p) {
                     }
                 l[qb] = l[qb] * alpha + rs;
                 m[qb] = mnew;
+                // Rescaling by 1 changes nothing: skipped when no row of the
+                // block has a new maximum (most tiles once the maxima settle).
+                if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) o[cb][qb] *= alpha;
+                    for (int cb = 0; cb < NCB; ++cb) o[cb][qb] *= alpha;
+                }
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc)
                     pf[kc][qb] = half8{ph[2 * kc][0], ph[2 * kc][1], ph[2 * kc][2], ph[2 * kc][3],
