@@ -22,7 +22,8 @@ enum TileId : int {
     TILE_STREAM32W = 8,      // skinny M <= 32, wide N: 64 columns per workgroup
     TILE_128x128_D4 = 9,     // the 128 tile on a four-slot ring (one workgroup per CU)
     TILE_STREAM16W = 10,     // skinny M <= 16, wide N: 64 columns per workgroup
-    NUM_TILES = 11
+    TILE_ROWVEC = 11,        // M <= 4, row-major A and B: B streamed into registers, fp32 FMAs
+    NUM_TILES = 12
 };
 
 // Three kernel families share the tile table:
@@ -53,6 +54,7 @@ constexpr TileShape kTiles[NUM_TILES] = {
     {32, 64, 32, 1, 1, 1, KIND_STREAM, "stream32x64"},
     {128, 128, 64, 2, 2, 4, KIND_DIRECT16, "128x128x64m16d4"},
     {16, 64, 32, 1, 1, 1, KIND_STREAM, "stream16x64"},
+    {4, 64, 32, 1, 1, 1, KIND_STREAM, "rowvec4x64"},
 };
 
 // Tile of the staged kernel that serves operands the direct kernel cannot

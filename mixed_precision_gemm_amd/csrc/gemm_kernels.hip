@@ -1993,6 +1993,169 @@ __global__ __launch_bounds__(512) void gemm_stream(GemmArgs pin) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Row-vector kernel: M <= 4 with row-major A and B (B N-contiguous, the NN
+// layout of a matrix-vector product).  Such a product is bound by reading B
+// once ([OPS] §1.2, [GEMM] §2.4), and with at most 4 rows of A an MFMA tile
+// would be almost all padding, so B is streamed into registers and the dot
+// products are fp32 FMAs:
+//   * a workgroup owns 64 columns of C (all M rows) and K (or its K slice);
+//     each of its 8 waves takes 128 rows of B per round of 1024;
+//   * lane t reads 16 consecutive rows (16 (t / 8) + j) at columns
+//     8 (t % 8) .. + 7: every load instruction covers 8 rows x 128 bytes,
+//     whole lines, and the lane's 16 values of each A row are two 16-byte
+//     loads (A is tiny and stays in L1/L2);
+//   * the 8 lanes that share columns are summed by lane exchanges, the 8
+//     waves through LDS in wave order; split-K partials as in the streaming
+//     kernel (the last slice to arrive sums them in slice order).
+// ---------------------------------------------------------------------------
+template <typename TI>
+__device__ inline float elem_f32(uint32_t w, int hi) {
+    const uint32_t h = hi ? (w >> 16) : (w & 0xffffu);
+    if constexpr (std::is_same<TI, __bf16>::value) return __builtin_bit_cast(float, h << 16);
+    else return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+template <typename TI, int MB, int NB, bool EPI>
+__global__ __launch_bounds__(512) void gemm_rowvec(GemmArgs pin) {
+    GemmArgs p = pin;
+    if constexpr (!EPI) p.epi = 0;
+    constexpr int MR = 4, NW = 8, COLS = 64;
+    static_assert(MB == 1 && NB == 4, "4 rows x 64 columns");
+    __shared__ float red[NW][MR][COLS];
+    __shared__ int s_last;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    const int slice = (int)(blockIdx.x / (unsigned)p.total_tiles);
+    const int tile = (int)(blockIdx.x - (unsigned)slice * (unsigned)p.total_tiles);
+    if (p.ksplit > 1) apply_k_slice(p, slice, true, false);
+    int b, tm, tn;
+    tile_coords(p, tile, b, tm, tn);
+    const int64_t n0 = (int64_t)tn * COLS;
+    const uint16_t *Ab = p.A + b * p.sa;
+    const uint16_t *Bb = p.B + b * p.sb;
+    // B's descriptor starts at the workgroup's first column (offsets span
+    // K rows of ldb elements: below 2^31 bytes for the ld limit and K).
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + n0, (p.extent_b - n0) * 2);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab, p.extent_a * 2);
+
+    const int cg = lane & 7, rg = lane >> 3;            // column group, row group
+    const bool col_ok = n0 + 8 * cg < p.N;
+    float acc[MR][8];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[m][e] = 0.f;
+
+    for (int64_t k0 = (int64_t)wave * 128; k0 < p.K; k0 += NW * 128) {
+        const int64_t kr = k0 + 16 * rg;                // this lane's first row
+        u32x4 bv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const bool ok = col_ok && kr + j < p.K;
+            bv[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                rb, ok ? (uint32_t)(((kr + j) * p.ldb + 8 * cg) * 2) : kOutOfRange, 0, 0));
+        }
+        u32x4 av[MR][2];
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                // Rows of A are 16-byte aligned and K a multiple of 8 here,
+                // so an 8-element chunk is wholly inside or outside K.
+                const bool ok = m < p.M && kr + 8 * h < p.K;
+                av[m][h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                    ra, ok ? (uint32_t)((m * p.lda + kr + 8 * h) * 2) : kOutOfRange, 0, 0));
+            }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            float bf[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bf[e] = elem_f32<TI>(bv[j][e >> 1], e & 1);
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                const float a = elem_f32<TI>(av[m][j >> 3][(j & 7) >> 1], j & 1);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[m][e] = __builtin_fmaf(a, bf[e], acc[m][e]);
+            }
+        }
+    }
+
+    // Lanes t, t ^ 8, t ^ 16, ... share columns: fixed-order pairwise sums.
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float v = acc[m][e];
+            v += __shfl_xor(v, 8);
+            v += __shfl_xor(v, 16);
+            v += __shfl_xor(v, 32);
+            acc[m][e] = v;
+        }
+    if (rg == 0) {
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red[wave][m][8 * cg + e] = acc[m][e];
+    }
+    __syncthreads();
+
+    // Thread o < 256 owns output (o / 64, o % 64): its sum over the waves.
+    const int o = tid, om = o >> 6, oc = o & 63;
+    float v = 0.f;
+    if (o < MR * COLS) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) v += red[w][om][oc];
+    }
+    const int64_t nn = n0 + oc;
+    const float alpha = p.alpha, beta = p.beta;
+    constexpr int TE = MR * COLS;
+    if (p.ksplit > 1) {
+        constexpr int kCoherent = 1 | 16;
+        const __amdgpu_buffer_rsrc_t rws = make_rsrc(p.ws, (int64_t)p.ksplit * p.total_tiles * TE * 4);
+        if (o < TE)
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rws,
+                                                  (uint32_t)((((int64_t)slice * p.total_tiles + tile) * TE + o) * 4),
+                                                  0, kCoherent);
+        asm volatile("s_waitcnt vmcnt(0)" : : : "memory");   // this lane's partial is in memory
+        __syncthreads();
+        if (tid == 0)
+            s_last = __hip_atomic_fetch_add(&p.ws_count[tile], 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT) == p.ksplit - 1;
+        __syncthreads();
+        if (!s_last) return;
+        constexpr int KSMAX = 8;
+        float part[KSMAX];
+#pragma unroll
+        for (int sl = 0; sl < KSMAX; ++sl)
+            part[sl] = (sl < p.ksplit && o < TE)
+                ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                      rws, (uint32_t)((((int64_t)sl * p.total_tiles + tile) * TE + o) * 4), 0, kCoherent))
+                : 0.0f;
+        v = part[0];
+#pragma unroll
+        for (int sl = 1; sl < KSMAX; ++sl)
+            if (sl < p.ksplit) v += part[sl];
+        if (tid == 0)
+            __hip_atomic_store(&p.ws_count[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (o >= TE || om >= p.M || nn >= p.N) return;
+    v *= alpha;
+    const int64_t off = b * p.sc + om * p.ldc + nn;
+    if (p.out_f32) {
+        float *C = (float *)p.C + off;
+        if (beta != 0.0f) v += beta * *C;
+        if (p.epi) v = activate(p.act, p.bias ? v + p.bias[nn] : v);
+        *C = v;
+    } else {
+        TI *C = (TI *)p.C + off;
+        if (beta != 0.0f) v += beta * (float)*C;
+        if (p.epi) v = activate(p.act, p.bias ? v + p.bias[nn] : v);
+        *C = (TI)v;
+    }
+}
+
 #if MPGEMM_HOST_PART
 // ---------------------------------------------------------------------------
 // Repacking of an operand whose rows are not 16-byte aligned ([GEMM] §3.4:
@@ -2116,6 +2279,14 @@ void fill_stream(KernelFn (&t)[2][2][2]) {
     t[1][1][1] = gemm_stream<TI, kTiles[T].bm / 16, kTiles[T].bn / 16, EPI>;
 }
 
+template <typename TI, bool EPI, int T>
+void fill_rowvec(KernelFn (&t)[2][2][2]) {
+    // Only row-major A and B (A K-contiguous, B N-contiguous), 128-bit form.
+    t[0][0][0] = t[0][0][1] = t[0][1][0] = t[0][1][1] = nullptr;
+    t[1][0][0] = t[1][1][0] = t[1][1][1] = nullptr;
+    t[1][0][1] = gemm_rowvec<TI, kTiles[T].bm / 4, kTiles[T].bn / 16, EPI>;
+}
+
 template <typename TI, bool EPI>
 void fill_type(TileKernels &k, FullKernels &kfull) {
     for (auto &t : kfull)
@@ -2134,6 +2305,7 @@ void fill_type(TileKernels &k, FullKernels &kfull) {
     fill_stream<TI, EPI, TILE_STREAM64>(k[TILE_STREAM64]);
     fill_stream<TI, EPI, TILE_STREAM32W>(k[TILE_STREAM32W]);
     fill_stream<TI, EPI, TILE_STREAM16W>(k[TILE_STREAM16W]);
+    fill_rowvec<TI, EPI, TILE_ROWVEC>(k[TILE_ROWVEC]);
 }
 
 }  // namespace

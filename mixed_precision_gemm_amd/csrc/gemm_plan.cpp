@@ -41,7 +41,11 @@ int64_t operand_extent(int64_t rows, int64_t cols, int64_t ld, int64_t batch,
 // the 128 x 128 tile (two workgroups per CU) a quarter of one; otherwise the
 // small staged tiles, the 32-row one for skinny M (token counts of a linear
 // layer).
-int choose_tile(int64_t M, int64_t N, int64_t K, int64_t batch, bool kc_both, bool vec_ok) {
+int choose_tile(int64_t M, int64_t N, int64_t K, int64_t batch, bool kc_both, bool nn,
+                bool vec_ok) {
+    // At most 4 rows with row-major A and B (a matrix-vector product in the
+    // NN layout): B streamed into registers, fp32 dot products.
+    if (nn && M <= 4 && K > 0) return TILE_ROWVEC;
     // Skinny M with K-contiguous A and B streams B through LDS.  Every
     // workgroup re-reads its rows of A, so N >= 8192 (128 or more workgroups
     // of 64 columns, split-K below 160) takes 64 columns per workgroup; from
@@ -90,6 +94,19 @@ int choose_tile(int64_t M, int64_t N, int64_t K, int64_t batch, bool kc_both, bo
 // in eight; 32 x 8192: 20.6 against 25.3 on the 16-column tile).  The last
 // slice of a block to finish sums the partial blocks in slice order.
 void choose_ksplit_stream(gemm_f16f32_plan_s *p, int64_t tiles) {
+    if (p->tile == TILE_ROWVEC) {
+        // Row vectors: enough K slices of at least 1024 for about 256
+        // workgroups, at most 8.
+        int64_t ks = std::min<int64_t>(8, std::min<int64_t>(ceil_div(kNumCUs, tiles), p->K / 1024));
+        if (ks < 2 || tiles > kMaxCounters) return;
+        const int64_t chunk = ceil_div(ceil_div(p->K, ks), 64) * 64;
+        const int64_t n = ceil_div(p->K, chunk);
+        if (n < 2) return;
+        p->kchunk = chunk;
+        p->ksplit = (int)n;
+        p->split_bytes = n * tiles * kTiles[p->tile].bm * kTiles[p->tile].bn * 4;
+        return;
+    }
     if (p->tile != TILE_STREAM16W && p->tile != TILE_STREAM32W) return;
     if (tiles >= kNumCUs * 5 / 8 || tiles > kMaxCounters) return;
     int64_t ks = std::min<int64_t>(4, p->K / 1024);
@@ -186,6 +203,7 @@ int make_plan(int in_type, gemm_f16f32_plan_t *out, int64_t M, int64_t N, int64_
     const bool a_ok = (contig_a % 8 == 0) && (lda % 8 == 0) && (stride_a % 8 == 0);
     const bool b_ok = (contig_b % 8 == 0) && (ldb % 8 == 0) && (stride_b % 8 == 0);
     const bool kc_both = layout_a == GEMM_ROW_MAJOR && layout_b == GEMM_COL_MAJOR;
+    const bool nn = layout_a == GEMM_ROW_MAJOR && layout_b == GEMM_ROW_MAJOR;
     // Copies padded to 8-element rows; sized here, made only by a run that
     // packs (an operand of this shape, or a misaligned pointer).
     p->ld8_a = ceil_div(contig_a, 8) * 8;
@@ -206,7 +224,10 @@ int make_plan(int in_type, gemm_f16f32_plan_t *out, int64_t M, int64_t N, int64_
         delete p;
         return GEMM_ERR_UNSUPPORTED;
     }
-    p->tile = choose_tile(M, N, K, batch, kc_both, true);
+    // The row-vector kernel's B offsets span K rows of ldb elements in 32 bits.
+    const bool rv_ok = (K + 1) * std::max(ldb, p->ld8_b) * 2 < (int64_t(1) << 31) &&
+                       M * std::max(lda, p->ld8_a) * 2 < (int64_t(1) << 30);
+    p->tile = choose_tile(M, N, K, batch, kc_both, nn && rv_ok, true);
     if (huge_ld) {
         p->vec_ok = 1;
         p->pack = 3;
@@ -222,7 +243,7 @@ int make_plan(int in_type, gemm_f16f32_plan_t *out, int64_t M, int64_t N, int64_
         // Small products keep the operands in place: the staged kernel with
         // element-wide loads, whose largest tile is 128.
         p->vec_ok = 0;
-        p->tile = choose_tile(M, N, K, batch, kc_both, false);
+        p->tile = choose_tile(M, N, K, batch, kc_both, nn && rv_ok, false);
     }
     // Operands given at misaligned addresses are repacked at run time only
     // for the direct and streaming kernels (and only when the workspace

@@ -137,6 +137,13 @@ def test_kernel_choice_by_regime():
     assert kern(8192, 8192, 8192, layout_b=GEMM_COL_MAJOR).endswith("nt_direct")
     # skinny, K-contiguous A and B: streaming kernel; other layouts: small tiles
     assert kern(16, 4096, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_stream16x16")
+    # at most 4 rows with row-major A and B: the row-vector kernel, K slices of
+    # at least 1024 for about 256 workgroups; other layouts keep the tiles
+    assert kern(1, 4096, 4096) == "gemm_rowvec4x64_nn_direct_sk4"
+    assert kern(4, 11008, 4096) == "gemm_rowvec4x64_nn_direct_sk2"
+    assert kern(3, 4096, 512) == "gemm_rowvec4x64_nn_direct"
+    assert kern(5, 4096, 4096).startswith("gemm_128x128")
+    assert kern(1, 4096, 4096, layout_a=GEMM_COL_MAJOR).startswith("gemm_128x128")
     # M <= 32 with N >= 8192: 64 columns per workgroup; fewer than 160
     # workgroups take four K slices of >= 1024, more are not split
     assert kern(16, 11008, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream16x64_nt_direct"

@@ -76,6 +76,40 @@ def test_streaming_wide_ragged(shape):
     parity(case, what=f"streaming {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("shape,kw,frag", [
+    ((1, 4096, 4096), {}, "rowvec4x64_nn_direct_sk4"),                    # the edge shape, split
+    ((4, 1000, 2048), dict(alpha=-0.75, beta=1.0), "rowvec4x64_nn_direct_sk2"),
+    ((3, 200, 77), dict(out_type=OUT_F32, beta=0.5), "rowvec4x64_nn_direct_pka"),   # ragged K
+    ((2, 33, 1030), {}, "rowvec4x64_nn_direct_pkab"),                     # ragged N and K, repacked
+    ((1, 4104, 8192), dict(batch=3, out_type=OUT_F32), "rowvec4x64_nn_direct_sk2"),  # batched, split
+])
+def test_row_vector_kernel(shape, kw, frag):
+    """M <= 4 with row-major A and B: the row-vector kernel (fp32 FMA dot
+    products over B streamed once), unsplit, in K slices, repacked, batched."""
+    M, N, K = shape
+    kw = dict(kw)
+    batch = kw.pop("batch", 1)
+    case = gi.make_case(M, N, K, batch=batch, seed=M * 7 + N + K, dist_c="normal", **kw)
+    kernel = plan_kernel(case)
+    assert frag in kernel, kernel
+    parity(case, what=f"row vector {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_row_vector_bit_exact_and_repeatable(M):
+    """Integer inputs: exact in fp32 in any summation order; two runs give the
+    same bits (the split-K slices are summed in slice order)."""
+    case = gi.make_case(M, 4096, 4096, out_type=OUT_F32, dist_a="integer", dist_b="integer",
+                        int_range=(-8, 8), seed=11)
+    kernel = plan_kernel(case)
+    assert "rowvec" in kernel and "_sk" in kernel, kernel
+    d1 = run_case(case)
+    d2 = run_case(case)
+    ref, _ = oracle_for(case)
+    assert np.array_equal(c_logical(case, d1.cpu()), ref), kernel
+    assert torch.equal(d1, d2)
+
+
 @pytest.mark.parametrize("kind", ["sq64", "qk"])
 def test_batched_small(kind):
     case = gi.batched_case(kind)
