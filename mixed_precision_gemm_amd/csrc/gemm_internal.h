@@ -19,7 +19,7 @@ enum TileId : int {
     TILE_STREAM16 = 5,       // skinny M <= 16, K-contiguous A and B
     TILE_STREAM32 = 6,       // skinny M <= 32
     TILE_STREAM64 = 7,       // skinny M <= 64
-    TILE_STREAM32W = 8,      // skinny M <= 32, wide N: 64 columns per workgroup
+    TILE_STREAM32W = 8,      // skinny M <= 32, wide N: 64 columns per workgroup; M <= 128 as row tiles
     TILE_128x128_D4 = 9,     // the 128 tile on a four-slot ring (one workgroup per CU)
     TILE_STREAM16W = 10,     // skinny M <= 16, wide N: 64 columns per workgroup
     TILE_ROWVEC = 11,        // M <= 4, row-major A and B: B streamed into registers, fp32 FMAs

@@ -1667,13 +1667,15 @@ void gemm_direct16(GemmArgs pin) {
 }
 
 // ---------------------------------------------------------------------------
-// Streaming kernel for skinny problems (M <= 64) whose A and B are both
+// Streaming kernel for skinny problems (M <= 128) whose A and B are both
 // K-contiguous (row-major A, column-major B: the linear-layer layout, with W
 // stored N x K).  Such a GEMM is bound by reading B once from HBM
 // ([OPS] §1.2 and [GEMM] §2.4: classify by arithmetic intensity first), so
 // the kernel is built to keep many bytes in flight rather than to reuse tiles:
-//   * a workgroup owns NB x 16 columns of C (all M rows, MB blocks of 16) and
-//     splits K over its 8 waves, so even N = 4096 yields 256 workgroups;
+//   * a workgroup owns NB x 16 columns of C and MB blocks of 16 rows (all M
+//     rows up to 64; from 33 rows on the 32 x 64 form also runs as several
+//     row tiles) and splits K over its 8 waves, so even N = 4096 yields 256
+//     workgroups;
 //   * each wave streams its K range in batches of U steps of 32 (U = 2 for
 //     64-column workgroups, else 4): the batch's B rows go straight to the
 //     wave's own LDS region by direct-to-LDS loads, each load covering whole

@@ -54,6 +54,15 @@ int choose_tile(int64_t M, int64_t N, int64_t K, int64_t batch, bool kc_both, bo
     // the K = 4096 linear shapes.)
     if (kc_both && M <= 16) return N >= 8192 ? TILE_STREAM16W : TILE_STREAM16;
     if (kc_both && M <= 32) return N >= 8192 ? TILE_STREAM32W : TILE_STREAM32;
+    // Up to 128 rows, the 32 x 64 streaming tile while its grid fits one
+    // workgroup per CU and K is at most 8192: more workgroups stream B than
+    // the 128 tile's split-K grid, without its partial tiles.  (Measured at
+    // K = 4096: 64 x 4096 18.2 against 22.0 us, 128 x 4096 21.8 against
+    // 29.0, 96 x 2048 17.2 against 21.0; beyond one pass, 128 x 6144 36.2
+    // against 27.2; at K = 16384, 128 x 2048 41.6 against 38.5.)
+    if (kc_both && M <= 128 && K <= 8192 &&
+        ceil_div(M, 32) * ceil_div(N, 64) * batch <= kNumCUs)
+        return TILE_STREAM32W;
     if (kc_both && M <= 64 && ceil_div(N, 128) < 64) return TILE_STREAM64;
     auto count = [&](int t) {
         return ceil_div(M, kTiles[t].bm) * ceil_div(N, kTiles[t].bn) * batch;

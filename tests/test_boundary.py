@@ -154,7 +154,18 @@ def test_kernel_choice_by_regime():
     assert kern(16, 8192, 3000, layout_b=GEMM_COL_MAJOR) == "gemm_stream16x64_nt_direct_sk2"
     assert kern(16, 8192, 4096, layout_b=GEMM_COL_MAJOR, batch=2, stride_a=16 * 4096,
                 stride_b=8192 * 4096, stride_c=16 * 8192) == "gemm_stream16x64_nt_direct"
-    assert kern(40, 4096, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_stream64x16")
+    # up to 128 rows: the 32 x 64 streaming tile while ceil(M/32) x ceil(N/64)
+    # workgroups fit one per CU and K <= 8192 (split as above below 160)
+    assert kern(40, 4096, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream32x64_nt_direct_sk4"
+    assert kern(128, 4096, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream32x64_nt_direct"
+    assert kern(64, 8192, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream32x64_nt_direct"
+    assert kern(96, 2048, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream32x64_nt_direct_sk4"
+    assert kern(128, 4096, 8192, layout_b=GEMM_COL_MAJOR) == "gemm_stream32x64_nt_direct"
+    assert kern(128, 6144, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_128x128")
+    assert kern(128, 2048, 16384, layout_b=GEMM_COL_MAJOR).startswith("gemm_128x128")
+    assert kern(64, 4096, 4096, layout_b=GEMM_COL_MAJOR, batch=3, stride_a=64 * 4096,
+                stride_b=4096 * 4096, stride_c=64 * 4096).startswith("gemm_stream64x16")
+    assert kern(40, 4096, 16384, layout_b=GEMM_COL_MAJOR).startswith("gemm_stream64x16")
     # wide N: 64 columns per streaming workgroup (M <= 32), else the 128 tile
     assert kern(32, 11008, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream32x64_nt_direct"
     assert kern(32, 8192, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream32x64_nt_direct_sk4"

@@ -65,7 +65,8 @@ def test_linear_layer_shapes(M, N):
     parity(case, rows=rows, what=f"linear M={M} N={N}")
 
 
-@pytest.mark.parametrize("shape", [(24, 10250, 1000), (5, 10260, 77), (31, 16384, 4104)])
+@pytest.mark.parametrize("shape", [(24, 10250, 1000), (5, 10260, 77), (31, 16384, 4104),
+                                   (77, 3000, 4104), (33, 130, 200)])
 def test_streaming_wide_ragged(shape):
     """The 64-column streaming workgroup with N off its grid, K off the
     32-deep step, and rows of A past M."""
@@ -286,11 +287,12 @@ def test_integer_inputs_bit_exact_direct_tiles(shape, prefix, sampled, la, lb):
 
 
 @pytest.mark.parametrize("M,N", [(16, 4096), (32, 11008), (64, 4096), (16, 11008), (16, 8192),
-                                 (27, 8200)])
+                                 (27, 8200), (128, 4096), (100, 2048), (48, 512)])
 def test_integer_inputs_bit_exact_streaming(M, N):
     """Every streaming form: 16 and 64 columns, A staged through LDS (M <=
     16) or loaded into registers, unsplit and in K slices (16 x 8192, 27 x
-    8200); integer sums stay below 2^24, exact in fp32 in any order."""
+    8200, 100 x 2048), several 32-row tiles (128, 100 and 48 rows); integer
+    sums stay below 2^24, exact in fp32 in any order."""
     case = gi.make_case(M, N, 4096, layout_b=COL_MAJOR, out_type=OUT_F32,
                         dist_a="integer", dist_b="integer", int_range=(-8, 8), seed=7)
     kernel = plan_kernel(case)
@@ -707,7 +709,7 @@ def test_split_k_repeatable_and_interleaved():
     """The arrival counters return to zero after every launch: a split-K plan
     run twice gives the same bits, also with another split-K plan launched in
     between on the same stream."""
-    c1 = gi.linear_case(128, 4096)
+    c1 = gi.linear_case(128, 6144)
     c2 = gi.make_case(16, 4096, 4096, seed=33)
     p1 = mpg.Plan(c1.M, c1.N, c1.K, c1.layout_a, c1.layout_b, c1.out_type, c1.lda, c1.ldb, c1.ldc)
     p2 = mpg.Plan(c2.M, c2.N, c2.K, c2.layout_a, c2.layout_b, c2.out_type, c2.lda, c2.ldb, c2.ldc)
@@ -736,6 +738,8 @@ def test_split_k_repeatable_and_interleaved():
     ((16, 8200, 3000), dict(beta=1.0), "stream16x64_nt_direct_sk2"),        # ragged N, short last slice
     ((32, 8192, 4096), dict(out_type=OUT_F32), "stream32x64_nt_direct_sk4"),  # two row blocks
     ((27, 8256, 2048), dict(beta=1.0), "stream32x64_nt_direct_sk2"),        # rows of A past M
+    ((96, 2048, 4096), {}, "stream32x64_nt_direct_sk4"),                    # three row tiles
+    ((100, 1000, 3000), dict(beta=1.0, out_type=OUT_F32), "stream32x64_nt_direct_sk2"),  # ragged
 ])
 def test_streaming_split_k(shape, kw, frag):
     """The 64-column streaming tile with K slices summed by the last slice to

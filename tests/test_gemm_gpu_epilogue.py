@@ -59,7 +59,8 @@ FAMILIES = [
     ((1000, 1000, 1000), dict(layout_a=COL_MAJOR), "m16d4_tn", False),
     ((256, 256, 32768), {}, "_sk8", False),
     ((16, 4096, 4096), dict(layout_b=COL_MAJOR), "stream16x16", False),
-    ((40, 4096, 1024), dict(layout_b=COL_MAJOR), "stream64x16", False),
+    ((40, 4096, 1024), dict(layout_b=COL_MAJOR), "stream32x64", False),
+    ((40, 512, 8448), dict(layout_b=COL_MAJOR), "stream64x16", False),
     ((127, 257, 33), {}, "narrow", False),
     ((64, 96, 200), dict(layout_a=COL_MAJOR, layout_b=COL_MAJOR), "vec16", False),
     ((4097, 63, 1025), {}, "_sk2_pkab", False),                   # repacked, split-K

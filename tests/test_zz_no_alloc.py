@@ -62,7 +62,7 @@ def test_noalloc_matches_run_on_calls_in_a_row():
     """Split-K plans (counters and 16, then 4 MiB of partial tiles in the
     scratch), a repacked one, a bfloat16 one and a plain one, in a row,
     each smaller than the first."""
-    k1 = _check(gi.make_case(128, 4096, 4096, layout_b=COL_MAJOR, beta=1.0, seed=201), "split-K 8")
+    k1 = _check(gi.make_case(128, 4096, 4096, beta=1.0, seed=201), "split-K 8")
     assert "_sk8" in k1, k1
     k2 = _check(gi.make_case(64, 2048, 2048, beta=0.5, alpha=-1.25, seed=202), "split-K 4")
     assert "_sk4" in k2, k2
