@@ -21,9 +21,10 @@ enum TileId : int {
     TILE_STREAM64 = 7,       // skinny M <= 64
     TILE_STREAM32W = 8,      // skinny M <= 32, wide N: 64 columns per workgroup; M <= 128 as row tiles
     TILE_128x128_D4 = 9,     // the 128 tile on a four-slot ring (one workgroup per CU)
-    TILE_STREAM16W = 10,     // skinny M <= 16, wide N: 64 columns per workgroup
+    TILE_STREAM16W = 10,     // skinny M <= 16, wide N: 48 columns per workgroup
     TILE_ROWVEC = 11,        // M <= 4, row-major A and B: B streamed into registers, fp32 FMAs
-    NUM_TILES = 12
+    TILE_STREAM32N = 12,     // skinny M <= 32, N >= 10240: 48 columns per workgroup
+    NUM_TILES = 13
 };
 
 // Three kernel families share the tile table:
@@ -53,8 +54,9 @@ constexpr TileShape kTiles[NUM_TILES] = {
     {64, 16, 32, 1, 1, 1, KIND_STREAM, "stream64x16"},
     {32, 64, 32, 1, 1, 1, KIND_STREAM, "stream32x64"},
     {128, 128, 64, 2, 2, 4, KIND_DIRECT16, "128x128x64m16d4"},
-    {16, 64, 32, 1, 1, 1, KIND_STREAM, "stream16x64"},
+    {16, 48, 32, 1, 1, 1, KIND_STREAM, "stream16x48"},
     {4, 64, 32, 1, 1, 1, KIND_STREAM, "rowvec4x64"},
+    {32, 48, 32, 1, 1, 1, KIND_STREAM, "stream32x48"},
 };
 
 // Tile of the staged kernel that serves operands the direct kernel cannot

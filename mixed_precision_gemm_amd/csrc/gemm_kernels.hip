@@ -1677,7 +1677,7 @@ void gemm_direct16(GemmArgs pin) {
 //     row tiles) and splits K over its 8 waves, so even N = 4096 yields 256
 //     workgroups;
 //   * each wave streams its K range in batches of U steps of 32 (U = 2 for
-//     64-column workgroups, else 4): the batch's B rows go straight to the
+//     48- and 64-column workgroups, else 4): the batch's B rows go straight to the
 //     wave's own LDS region by direct-to-LDS loads, each load covering whole
 //     128-byte lines of 16/U rows (a load shaped as one MFMA fragment, 16
 //     rows x 64 bytes, touches twice the lines for the same bytes and
@@ -1704,7 +1704,7 @@ __global__ __launch_bounds__(512) void gemm_stream(GemmArgs pin) {
     constexpr int NW = 8;
     // K steps (32 deep) per batch: a batch of B is NB*16 rows x U*64 bytes,
     // NB*U loads of 1 KiB, each covering 16/U whole rows of U*64 bytes.
-    constexpr int U = NB >= 4 ? 2 : 4;
+    constexpr int U = NB >= 3 ? 2 : 4;
     constexpr int ROWB = U * 64;                 // bytes of one B row in a batch
     constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
     constexpr int NLD = NB * U;                  // B loads per batch
@@ -2307,6 +2307,7 @@ void fill_type(TileKernels &k, FullKernels &kfull) {
     fill_stream<TI, EPI, TILE_STREAM64>(k[TILE_STREAM64]);
     fill_stream<TI, EPI, TILE_STREAM32W>(k[TILE_STREAM32W]);
     fill_stream<TI, EPI, TILE_STREAM16W>(k[TILE_STREAM16W]);
+    fill_stream<TI, EPI, TILE_STREAM32N>(k[TILE_STREAM32N]);
     fill_rowvec<TI, EPI, TILE_ROWVEC>(k[TILE_ROWVEC]);
 }
 

@@ -47,13 +47,17 @@ int choose_tile(int64_t M, int64_t N, int64_t K, int64_t batch, bool kc_both, bo
     // NN layout): B streamed into registers, fp32 dot products.
     if (nn && M <= 4 && K > 0) return TILE_ROWVEC;
     // Skinny M with K-contiguous A and B streams B through LDS.  Every
-    // workgroup re-reads its rows of A, so N >= 8192 (128 or more workgroups
-    // of 64 columns, split-K below 160) takes 64 columns per workgroup; from
-    // M = 33 on, N that yields 64 or more 128-wide tiles goes to the 128
-    // tile (split-K) instead, which shares A and B through LDS.  (Measured on
-    // the K = 4096 linear shapes.)
+    // workgroup re-reads its rows of A, so wide N takes more columns per
+    // workgroup: 48 for M <= 16 from N = 8192 and for M <= 32 from N = 10240
+    // (171 or more workgroups, about one per CU, none split), 64 for
+    // 16 < M <= 32 at N = 8192 .. 10239 (128 to 159 workgroups, split-K
+    // below).  48 columns against 64: 16 x 11008 19.3 against 20.7 us,
+    // 16 x 12288 20.8 against 21.8, 32 x 11008 23.4 against 27.0; at
+    // N = 8192, 16 rows 16.7 (unsplit) against 16.9 (four slices), 32 rows
+    // 21.6 against 20.6.  (Measured on the K = 4096 linear shapes.)
     if (kc_both && M <= 16) return N >= 8192 ? TILE_STREAM16W : TILE_STREAM16;
-    if (kc_both && M <= 32) return N >= 8192 ? TILE_STREAM32W : TILE_STREAM32;
+    if (kc_both && M <= 32)
+        return N >= 10240 ? TILE_STREAM32N : N >= 8192 ? TILE_STREAM32W : TILE_STREAM32;
     // Up to 128 rows, the 32 x 64 streaming tile while its grid fits one
     // workgroup per CU and K is at most 8192: more workgroups stream B than
     // the 128 tile's split-K grid, without its partial tiles.  (Measured at
@@ -93,15 +97,16 @@ int choose_tile(int64_t M, int64_t N, int64_t K, int64_t batch, bool kc_both, bo
 // a quarter of the CUs are cut only when K is deep: the partial tiles and
 // their reduction cost more than they gain at K ~ 1024 (measured at 1024^3).
 //
-// K slices for the 64-column streaming tiles (M <= 32, N >= 8192).  With
-// 160 or more workgroups (N >= 10240) a tile is not split: its waves keep
-// their batches streaming back to back, and a split only adds the partial
-// sums' round trips at the end (16 x 11008 x 4096: 20.9 us unsplit, 22.0 in
-// four slices, 24.7 in two; 16 x 16384: 28.2 against 34.9).  Fewer
-// workgroups (128 to 159: N from 8192) are cut into four slices of at least
-// 1024 (16 x 8192 x 4096: 16.7 us against 19.9 unsplit, 18.9 in two, 21.5
-// in eight; 32 x 8192: 20.6 against 25.3 on the 16-column tile).  The last
-// slice of a block to finish sums the partial blocks in slice order.
+// K slices for the 48- and 64-column streaming tiles.  With 160 or more
+// workgroups a tile is not split: its waves keep their batches streaming
+// back to back, and a split only adds the partial sums' round trips at the
+// end (16 x 11008 x 4096 on 64 columns: 20.9 us unsplit, 22.0 in four
+// slices, 24.7 in two; 16 x 16384: 28.2 against 34.9).  Fewer workgroups
+// (the 64-column tiles from N = 8192, and the many-row tiles of up to 128
+// rows) are cut into up to four slices of at least 1024 (16 x 8192 x 4096
+// on 64 columns: 16.7 us against 19.9 unsplit, 18.9 in two, 21.5 in eight;
+// 32 x 8192: 20.6 against 25.3 on the 16-column tile).  The last slice of a
+// block to finish sums the partial blocks in slice order.
 void choose_ksplit_stream(gemm_f16f32_plan_s *p, int64_t tiles) {
     if (p->tile == TILE_ROWVEC) {
         // Row vectors: enough K slices of at least 1024 for about 256
@@ -116,7 +121,7 @@ void choose_ksplit_stream(gemm_f16f32_plan_s *p, int64_t tiles) {
         p->split_bytes = n * tiles * kTiles[p->tile].bm * kTiles[p->tile].bn * 4;
         return;
     }
-    if (p->tile != TILE_STREAM16W && p->tile != TILE_STREAM32W) return;
+    if (p->tile != TILE_STREAM16W && p->tile != TILE_STREAM32W && p->tile != TILE_STREAM32N) return;
     if (tiles >= kNumCUs * 5 / 8 || tiles > kMaxCounters) return;
     int64_t ks = std::min<int64_t>(4, p->K / 1024);
     if (ks < 2) return;

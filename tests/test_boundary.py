@@ -109,8 +109,8 @@ def test_streaming_plan_with_large_column_pitch():
         assert p.kernel == "gemm_stream16x16_nt_direct"
         assert p.workspace_bytes() == 0
     with mpg.Plan(16, 152064, 8192, layout_b=GEMM_COL_MAJOR) as p:
-        # wide N: 64 columns per workgroup, unsplit (more blocks than counters)
-        assert p.kernel == "gemm_stream16x64_nt_direct"
+        # wide N: 48 columns per workgroup, unsplit
+        assert p.kernel == "gemm_stream16x48_nt_direct"
 
 
 def test_null_out_pointer():
@@ -144,16 +144,19 @@ def test_kernel_choice_by_regime():
     assert kern(3, 4096, 512) == "gemm_rowvec4x64_nn_direct"
     assert kern(5, 4096, 4096).startswith("gemm_128x128")
     assert kern(1, 4096, 4096, layout_a=GEMM_COL_MAJOR).startswith("gemm_128x128")
-    # M <= 32 with N >= 8192: 64 columns per workgroup; fewer than 160
-    # workgroups take four K slices of >= 1024, more are not split
-    assert kern(16, 11008, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream16x64_nt_direct"
-    assert kern(16, 8192, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream16x64_nt_direct_sk4"
-    assert kern(16, 10176, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream16x64_nt_direct_sk4"
-    assert kern(16, 10240, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream16x64_nt_direct"
-    assert kern(16, 8192, 1024, layout_b=GEMM_COL_MAJOR) == "gemm_stream16x64_nt_direct"
-    assert kern(16, 8192, 3000, layout_b=GEMM_COL_MAJOR) == "gemm_stream16x64_nt_direct_sk2"
+    # M <= 16 with N >= 8192: 48 columns per workgroup (171 or more), not split
+    assert kern(16, 11008, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream16x48_nt_direct"
+    assert kern(16, 8192, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream16x48_nt_direct"
+    assert kern(16, 8192, 3000, layout_b=GEMM_COL_MAJOR) == "gemm_stream16x48_nt_direct"
     assert kern(16, 8192, 4096, layout_b=GEMM_COL_MAJOR, batch=2, stride_a=16 * 4096,
-                stride_b=8192 * 4096, stride_c=16 * 8192) == "gemm_stream16x64_nt_direct"
+                stride_b=8192 * 4096, stride_c=16 * 8192) == "gemm_stream16x48_nt_direct"
+    # 16 < M <= 32: 64 columns for N = 8192 .. 10239, fewer than 160
+    # workgroups in K slices of >= 1024; 48 columns from N = 10240
+    assert kern(32, 10176, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream32x64_nt_direct_sk4"
+    assert kern(20, 8192, 3000, layout_b=GEMM_COL_MAJOR) == "gemm_stream32x64_nt_direct_sk2"
+    assert kern(20, 8192, 1024, layout_b=GEMM_COL_MAJOR) == "gemm_stream32x64_nt_direct"
+    assert kern(20, 10239, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream32x64_nt_direct"
+    assert kern(32, 10240, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream32x48_nt_direct"
     # up to 128 rows: the 32 x 64 streaming tile while ceil(M/32) x ceil(N/64)
     # workgroups fit one per CU and K <= 8192 (split as above below 160)
     assert kern(40, 4096, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream32x64_nt_direct_sk4"
@@ -167,7 +170,7 @@ def test_kernel_choice_by_regime():
                 stride_b=4096 * 4096, stride_c=64 * 4096).startswith("gemm_stream64x16")
     assert kern(40, 4096, 16384, layout_b=GEMM_COL_MAJOR).startswith("gemm_stream64x16")
     # wide N: 64 columns per streaming workgroup (M <= 32), else the 128 tile
-    assert kern(32, 11008, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream32x64_nt_direct"
+    assert kern(32, 11008, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream32x48_nt_direct"
     assert kern(32, 8192, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream32x64_nt_direct_sk4"
     assert kern(32, 4096, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_stream32x16")
     assert kern(64, 11008, 4096, layout_b=GEMM_COL_MAJOR).endswith("d4_nt_direct_sk2")

@@ -68,7 +68,7 @@ def test_linear_layer_shapes(M, N):
 @pytest.mark.parametrize("shape", [(24, 10250, 1000), (5, 10260, 77), (31, 16384, 4104),
                                    (77, 3000, 4104), (33, 130, 200)])
 def test_streaming_wide_ragged(shape):
-    """The 64-column streaming workgroup with N off its grid, K off the
+    """The 48- and 64-column streaming workgroups with N off their grid, K off the
     32-deep step, and rows of A past M."""
     M, N, K = shape
     case = gi.make_case(M, N, K, layout_b=COL_MAJOR, alpha=1.5, beta=-1.0, seed=70)
@@ -289,10 +289,10 @@ def test_integer_inputs_bit_exact_direct_tiles(shape, prefix, sampled, la, lb):
 @pytest.mark.parametrize("M,N", [(16, 4096), (32, 11008), (64, 4096), (16, 11008), (16, 8192),
                                  (27, 8200), (128, 4096), (100, 2048), (48, 512)])
 def test_integer_inputs_bit_exact_streaming(M, N):
-    """Every streaming form: 16 and 64 columns, A staged through LDS (M <=
-    16) or loaded into registers, unsplit and in K slices (16 x 8192, 27 x
-    8200, 100 x 2048), several 32-row tiles (128, 100 and 48 rows); integer
-    sums stay below 2^24, exact in fp32 in any order."""
+    """Every streaming form: 16, 48 and 64 columns, A staged through LDS (M
+    <= 16) or loaded into registers, unsplit and in K slices (27 x 8200, 100
+    x 2048), several 32-row tiles (128, 100 and 48 rows); integer sums stay
+    below 2^24, exact in fp32 in any order."""
     case = gi.make_case(M, N, 4096, layout_b=COL_MAJOR, out_type=OUT_F32,
                         dist_a="integer", dist_b="integer", int_range=(-8, 8), seed=7)
     kernel = plan_kernel(case)
@@ -733,9 +733,9 @@ def test_split_k_repeatable_and_interleaved():
 
 
 @pytest.mark.parametrize("shape,kw,frag", [
-    ((16, 8192, 4096), {}, "stream16x64_nt_direct_sk4"),
-    ((12, 9000, 4096), dict(out_type=OUT_F32, alpha=0.5, beta=-1.0), "stream16x64_nt_direct_sk4"),
-    ((16, 8200, 3000), dict(beta=1.0), "stream16x64_nt_direct_sk2"),        # ragged N, short last slice
+    ((20, 8192, 4096), {}, "stream32x64_nt_direct_sk4"),
+    ((17, 9000, 4096), dict(out_type=OUT_F32, alpha=0.5, beta=-1.0), "stream32x64_nt_direct_sk4"),
+    ((24, 8200, 3000), dict(beta=1.0), "stream32x64_nt_direct_sk2"),        # ragged N, short last slice
     ((32, 8192, 4096), dict(out_type=OUT_F32), "stream32x64_nt_direct_sk4"),  # two row blocks
     ((27, 8256, 2048), dict(beta=1.0), "stream32x64_nt_direct_sk2"),        # rows of A past M
     ((96, 2048, 4096), {}, "stream32x64_nt_direct_sk4"),                    # three row tiles

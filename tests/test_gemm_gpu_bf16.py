@@ -68,7 +68,7 @@ def test_bf16_headline_sampled(lb):
 
 
 @pytest.mark.parametrize("M,N,tile", [
-    (16, 4096, "stream16x16"), (32, 4096, "stream32x16"), (32, 11008, "stream32x64"),
+    (16, 4096, "stream16x16"), (32, 4096, "stream32x16"), (32, 11008, "stream32x48"),
     (64, 4096, "stream32x64"), (128, 4096, "stream32x64"), (64, 11008, "128x128x64m16d4"),
     (128, 11008, "128x128x64m16d4"),
     (2048, 4096, "128x128x64m16_"),
