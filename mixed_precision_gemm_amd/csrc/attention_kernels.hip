@@ -11,9 +11,11 @@
 // chip).  One workgroup of four 64-lane waves owns 128 query rows of one
 // (batch, head); each wave owns 32 of them as two blocks of 16.  The keys are
 // walked in tiles of 64:
-//   * K and V tiles go global -> registers -> LDS, double buffered: tile t+1
-//     is loaded into registers while tile t is consumed from LDS, then
-//     written to the other LDS buffer; one barrier per tile;
+//   * K and V tiles go straight to LDS by direct-to-LDS loads, double
+//     buffered: tile t+1 is loaded into the other buffer while tile t is
+//     consumed; one wait and one barrier per tile.  Each load instruction
+//     fills 1 KiB of whole LDS rows, lane l the 16-byte slot l of them, and
+//     fetches the global chunk that the row's swizzle puts in that slot;
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_f16 (K fragments from LDS with
 //     ds_read_b128, Q fragments held in registers for the whole walk), fp32
 //     accumulation.  Computing the transpose puts, in each lane, four keys of
@@ -72,6 +74,38 @@ __device__ inline floatx4 mfma16(half8 a, half8 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Byte offset of a __shared__ object within the workgroup's LDS allocation.
+__device__ inline uint32_t lds_offset(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// Buffer descriptor as four scalar words, for inline assembly.
+typedef int32_t sgpr4 __attribute__((ext_vector_type(4)));
+
+__device__ inline sgpr4 make_rsrc_words(const void *base, int64_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    const int32_t n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int32_t)bytes);
+    sgpr4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(a >> 32) & 0xffff);  // stride 0
+    r[2] = __builtin_amdgcn_readfirstlane(n);
+    r[3] = kRsrcWord3;
+    return r;
+}
+
+// One 16-byte-per-lane direct-to-LDS load: lane t's data lands at LDS byte
+// address lds_addr + 16 t (lds_addr taken from the first lane).  Assembly,
+// so the compiler's wait-count insertion does not tie the fragment reads of
+// the other buffer to it; the kernel waits for it explicitly before its
+// barrier.
+__device__ inline void lds_dma16(sgpr4 rs, uint32_t lds_addr, uint32_t voff) {
+    const uint32_t m0v = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr);
+    asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(m0v), "s"(rs)
+                 : "m0");
+}
+
 struct AttnArgs {
     const uint16_t *Q, *K, *V;
     void *O;
@@ -111,7 +145,8 @@ void attn_fwd(AttnArgs p) {
     constexpr int NCB = D / 16;          // 16-wide column blocks of O
     constexpr int CPR = D / 8;           // 16-byte chunks per LDS row
     constexpr int TILE = BN * D;         // halves per K (or V) tile
-    constexpr int KCH = BN * CPR / 256;  // chunks per thread per tile
+    constexpr int RPI = 1024 / (2 * D);  // rows of a tile per 1 KiB load
+    constexpr int NLW = BN / RPI / 4;    // loads per wave per tile, each of K and V
     static_assert(D == 64 || D == 128, "head dimension");
     __shared__ __attribute__((aligned(16))) _Float16 lds[2][2][TILE];   // [buffer][K, V]
 
@@ -146,8 +181,8 @@ void attn_fwd(AttnArgs p) {
     const uint16_t *Kb = p.K + b * p.k_sb + h * p.k_sh;
     const uint16_t *Vb = p.V + b * p.v_sb + h * p.v_sh;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qb, Sq > 0 ? ((Sq - 1) * p.q_ld + D) * 2 : 0);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb, Sk > 0 ? ((Sk - 1) * p.k_ld + D) * 2 : 0);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb, Sk > 0 ? ((Sk - 1) * p.v_ld + D) * 2 : 0);
+    const sgpr4 rk = make_rsrc_words(Kb, Sk > 0 ? ((Sk - 1) * p.k_ld + D) * 2 : 0);
+    const sgpr4 rv = make_rsrc_words(Vb, Sk > 0 ? ((Sk - 1) * p.v_ld + D) * 2 : 0);
 
     // Q fragments (second MFMA operand of S^T): lane l holds query row
     // 16 qb + l%16 of the wave's rows, d = 32 dc + 8 (l/16) .. + 7.
@@ -162,26 +197,22 @@ void attn_fwd(AttnArgs p) {
         }
     }
 
-    // Staging of one K and one V tile: thread t moves chunks t + 256 q.
-    u32x4 stk[KCH], stv[KCH];
-    auto gload = [&](int kt) __attribute__((always_inline)) {
+    // Loads of one K and one V tile into buffer buf: wave w's load j fills
+    // rows r0 = (NLW w + j) RPI .. + RPI - 1; lane l lands in row r0 + l /
+    // CPR, slot l % CPR, which holds the row's chunk slot ^ swizzle (the XOR
+    // is its own inverse).  Keys past Sk read zeros (range check).
+    const uint32_t lds0 = lds_offset(lds);
+    auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < KCH; ++q) {
-            const int id = tid + 256 * q, row = id / CPR, c = id % CPR;
+        for (int j = 0; j < NLW; ++j) {
+            const int r0 = (NLW * wave + j) * RPI;
+            const int row = r0 + lane / CPR, slot = lane % CPR;
             const int64_t key = (int64_t)kt * BN + row;
             const bool ok = key < Sk;
-            const uint32_t ok_k = ok ? (uint32_t)((key * p.k_ld + 8 * c) * 2) : kOutOfRange;
-            const uint32_t ok_v = ok ? (uint32_t)((key * p.v_ld + 8 * c) * 2) : kOutOfRange;
-            stk[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ok_k, 0, 0));
-            stv[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, ok_v, 0, 0));
-        }
-    };
-    auto lstore = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-        for (int q = 0; q < KCH; ++q) {
-            const int id = tid + 256 * q, row = id / CPR, c = id % CPR;
-            *(u32x4 *)&lds[buf][0][row * D + 8 * (c ^ kswz<D>(row))] = stk[q];
-            *(u32x4 *)&lds[buf][1][row * D + 8 * (c ^ vswz<D>(row))] = stv[q];
+            const int ck = slot ^ kswz<D>(row), cv = slot ^ vswz<D>(row);
+            const uint32_t dst = lds0 + (uint32_t)((buf * 2 * TILE + r0 * D) * 2);
+            lds_dma16(rk, dst, ok ? (uint32_t)((key * p.k_ld + 8 * ck) * 2) : kOutOfRange);
+            lds_dma16(rv, dst + (uint32_t)(TILE * 2), ok ? (uint32_t)((key * p.v_ld + 8 * cv) * 2) : kOutOfRange);
         }
     };
 
@@ -202,15 +233,15 @@ void attn_fwd(AttnArgs p) {
         for (int qb = 0; qb < 2; ++qb) o[cb][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
 
-    if (nkv > 0) {
-        gload(0);
-        lstore(0);
-    }
+    if (nkv > 0) issue(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");   // Q fragments and tile 0
     __syncthreads();
 
     for (int kt = 0; kt < nkv; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < nkv) gload(kt + 1);
+        // The other buffer was last read in tile kt - 1, before the barrier
+        // that ended it.
+        if (kt + 1 < nkv) issue(kt + 1, buf ^ 1);
         const int64_t k0 = (int64_t)kt * BN;
         // Tiles wholly past this wave's causal limit (or waves past Sq) skip
         // the arithmetic but keep loading and meeting the barrier.
@@ -300,7 +331,9 @@ void attn_fwd(AttnArgs p) {
                     for (int qb = 0; qb < 2; ++qb) o[cb][qb] = mfma16(vf, pf[kc][qb], o[cb][qb]);
                 }
         }
-        if (kt + 1 < nkv) lstore(buf ^ 1);
+        // This wave's loads of tile kt + 1 have landed; after the barrier,
+        // every wave's have, and no wave still reads buffer buf.
+        asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
         __syncthreads();
     }
 
