@@ -169,7 +169,8 @@ def test_kernel_choice_by_regime():
     assert kern(64, 4096, 4096, layout_b=GEMM_COL_MAJOR, batch=3, stride_a=64 * 4096,
                 stride_b=4096 * 4096, stride_c=64 * 4096).startswith("gemm_stream64x16")
     assert kern(40, 4096, 16384, layout_b=GEMM_COL_MAJOR).startswith("gemm_stream64x16")
-    # wide N: 64 columns per streaming workgroup (M <= 32), else the 128 tile
+    # wide N: 48 or 64 columns per streaming workgroup (M <= 32); past one pass
+    # of 32 x 64 tiles, more rows go to the 128 tile
     assert kern(32, 11008, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream32x48_nt_direct"
     assert kern(32, 8192, 4096, layout_b=GEMM_COL_MAJOR) == "gemm_stream32x64_nt_direct_sk4"
     assert kern(32, 4096, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_stream32x16")
