@@ -13,8 +13,8 @@ import torch
 
 import gemm_inputs as gi
 import mixed_precision_gemm_amd as mpg
-from gemm_inputs import COL_MAJOR, OUT_F16, OUT_F32, ROW_MAJOR
-from parity import (c_logical, check_bound, oracle_for, parity, run_case,
+from gemm_inputs import COL_MAJOR, OUT_BF16, OUT_F16, OUT_F32, ROW_MAJOR
+from parity import (c_logical, check_bound, in_dtype, oracle_for, parity, run_case,
                     sample_rows, to_device)
 
 pytestmark = [pytest.mark.gpu,
@@ -94,6 +94,31 @@ def test_row_vector_kernel(shape, kw, frag):
     kernel = plan_kernel(case)
     assert frag in kernel, kernel
     parity(case, what=f"row vector {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("shape,kw,frag", [
+    ((16, 8200, 1024), dict(batch=3, beta=1.0), "stream16x48_nt_direct"),              # batched, ragged N
+    ((30, 10300, 640), dict(batch=2, out_type=OUT_F32), "stream32x48_nt_direct"),
+    ((100, 1000, 2048), dict(batch=2, alpha=0.5, beta=-1.0), "stream32x64_nt_direct_sk2"),  # row tiles, split
+    ((16, 9000, 2048), dict(in_dtype="bf16", out_type=OUT_BF16), "gemm_bf16_stream16x48"),
+    ((70, 2048, 4096), dict(in_dtype="bf16", out_type=OUT_BF16, beta=1.0), "gemm_bf16_stream32x64"),
+])
+def test_streaming_wide_and_row_tiles_batched(shape, kw, frag):
+    """The 48-column streaming tiles and the 32 x 64 tile in several row tiles
+    over batch items (each item's blocks on their own descriptors), and in
+    bfloat16."""
+    M, N, K = shape
+    kw = dict(kw)
+    batch = kw.pop("batch", 1)
+    case = gi.make_case(M, N, K, layout_b=COL_MAJOR, batch=batch, seed=M + N + K + 5,
+                        dist_c="normal", **kw)
+    with mpg.Plan(case.M, case.N, case.K, case.layout_a, case.layout_b, case.out_type,
+                  case.lda, case.ldb, case.ldc, case.batch, case.stride_a, case.stride_b,
+                  case.stride_c, dtype=in_dtype(case)) as p:
+        kernel = p.kernel
+    assert frag in kernel, kernel
+    rows = sample_rows(M, n_random=32) if M > 64 else None
+    parity(case, rows=rows, what=f"streaming {M}x{N}x{K} batch {batch}")
 
 
 @pytest.mark.parametrize("M", [1, 4])
