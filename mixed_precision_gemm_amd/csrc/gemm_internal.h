@@ -24,7 +24,8 @@ enum TileId : int {
     TILE_STREAM16W = 10,     // skinny M <= 16, wide N: 48 columns per workgroup
     TILE_ROWVEC = 11,        // M <= 4, row-major A and B: B streamed into registers, fp32 FMAs
     TILE_STREAM32N = 12,     // skinny M <= 32, N >= 10240: 48 columns per workgroup
-    NUM_TILES = 13
+    TILE_SMALL64 = 13,       // batched products of at most 64 x 64 x 64, NN: one wave each
+    NUM_TILES = 14
 };
 
 // Three kernel families share the tile table:
@@ -35,8 +36,9 @@ enum TileId : int {
 //                LDS), used for the small tiles and for the narrow-load path;
 //   KIND_STREAM:  skinny M with K-contiguous A and B: K split over 8 waves,
 //                each streaming its B rows through its own LDS region
-//                (direct-to-LDS loads) and its A fragments into registers.
-enum KernelKind : int { KIND_STAGED = 1, KIND_STREAM = 2, KIND_DIRECT16 = 3 };
+//                (direct-to-LDS loads) and its A fragments into registers;
+//   KIND_SMALL:   a batch of products of at most 64 x 64 x 64, one wave each.
+enum KernelKind : int { KIND_STAGED = 1, KIND_STREAM = 2, KIND_DIRECT16 = 3, KIND_SMALL = 4 };
 
 struct TileShape {
     int bm, bn, bk, wgm, wgn, stages, kind;
@@ -57,12 +59,14 @@ constexpr TileShape kTiles[NUM_TILES] = {
     {16, 48, 32, 1, 1, 1, KIND_STREAM, "stream16x48"},
     {4, 64, 32, 1, 1, 1, KIND_STREAM, "rowvec4x64"},
     {32, 48, 32, 1, 1, 1, KIND_STREAM, "stream32x48"},
+    {64, 64, 64, 1, 1, 1, KIND_SMALL, "small64"},
 };
 
 // Tile of the staged kernel that serves operands the direct kernel cannot
 // take (unaligned rows or pointers).
 constexpr int narrow_tile(int t) {
     return kTiles[t].kind == KIND_STREAM ? (kTiles[t].bm <= 32 ? TILE_32x64 : TILE_64x64)
+           : kTiles[t].kind == KIND_SMALL ? TILE_64x64
            : kTiles[t].kind != KIND_STAGED ? TILE_128x128_STAGED : t;
 }
 

@@ -2011,6 +2011,116 @@ __global__ __launch_bounds__(512) void gemm_stream(GemmArgs pin) {
 //     waves through LDS in wave order; split-K partials as in the streaming
 //     kernel (the last slice to arrive sums them in slice order).
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// Batched small products (M, N, K <= 64; A and B row-major): one wave per
+// product.  Such products are bound by moving their operands ([GEMM] §2.4,
+// [CATLASS] §3.1); with the staged tile's four waves per product, a batch of
+// 512 spent about a fifth of its time having its waves dispatched, and the
+// waves of one product wait for each other at every barrier.  Here:
+//   * A's fragments of v_mfma_f32_16x16x32 (lane l: row l % 16 of a 16-row
+//     block, 8 consecutive k from 8 (l / 16)) are 16 contiguous bytes of a
+//     row of A, loaded straight into registers, 8 per lane;
+//   * B (rows of k, N-contiguous) goes to LDS by 16-byte loads, 8 per lane,
+//     issued with A's, and comes back transposed by ds_read_b64_tr_b16, two
+//     reads per fragment (lane j of a 16-lane group addresses row k0 + j / 4
+//     at column n0 + 4 (j % 4); lane i receives column n0 + i of rows
+//     k0 .. k0 + 3);
+//   * the wave accumulates C^T (B's fragment as the first operand), so each
+//     lane ends with runs of 4 consecutive n of one row of C, stored as one
+//     vector each.
+// Rows past M, chunks past K and chunks past N read zeros (range check on
+// each 8-element chunk; K and N are multiples of 8, or the operands are
+// padded copies whose padding is zero).
+template <typename TI, bool EPI>
+__global__ __launch_bounds__(64) void gemm_small64(GemmArgs pin) {
+    GemmArgs p = pin;
+    if constexpr (!EPI) p.epi = 0;   // no epilogue code in this instantiation
+    __shared__ u32x4 bl[64 * 8];     // B: 64 rows of k, 8 chunks of 8 n
+    const int lane = threadIdx.x;
+    const int64_t b = blockIdx.x;    // one tile per product: the batch item
+    const uint16_t *Ab = p.A + b * p.sa;
+    const uint16_t *Bb = p.B + b * p.sb;
+    // extent_a / extent_b: elements of one batch item reachable from its base.
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab, p.extent_a * 2);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb, p.extent_b * 2);
+    const int li = lane & 15, g = lane >> 4;
+
+    // B chunk q of this lane: row 8 q + lane / 8, columns 8 (lane % 8) .. + 7.
+    u32x4 bv[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int row = 8 * q + (lane >> 3), c = lane & 7;
+        const bool ok = row < p.K && 8 * c < p.N;
+        bv[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                    rb, ok ? (uint32_t)(((int64_t)row * p.ldb + 8 * c) * 2) : kOutOfRange, 0, 0));
+    }
+    // A fragment (mb, ks): row 16 mb + l % 16, k = 32 ks + 8 (l / 16) .. + 7.
+    half8 af[4][2];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int row = 16 * mb + li, k = 32 * ks + 8 * g;
+            const bool ok = row < p.M && k < p.K;
+            af[mb][ks] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(
+                             ra, ok ? (uint32_t)(((int64_t)row * p.lda + k) * 2) : kOutOfRange, 0, 0));
+        }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) bl[(8 * q + (lane >> 3)) * 8 + (lane & 7)] = bv[q];
+    __syncthreads();
+
+    floatx4 acc[4][4];   // [nb][mb]
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const char *lb = (const char *)bl;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            // Columns 16 nb + l % 16 of rows 32 ks + 8 g .. + 7.
+            v4i16 hv[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int row = 32 * ks + 8 * g + 4 * t + (li >> 2);
+                hv[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4i16 *)(const void *)(lb + row * 128 + 32 * nb +
+                                                                               8 * (li & 3)));
+            }
+            const half8 bf = __builtin_bit_cast(half8, __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3,
+                                                                               4, 5, 6, 7));
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = mfma16<TI>(bf, af[mb][ks], acc[nb][mb]);
+        }
+
+    // acc[nb][mb][r] = C(16 mb + l % 16, 16 nb + 4 (l / 16) + r).
+    const float alpha = p.alpha, beta = p.beta;
+    const bool epi = EPI && p.epi;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+        const int64_t m = 16 * mb + li;
+        if (m >= p.M) continue;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const int64_t n = 16 * nb + 4 * g;
+            if (n >= p.N) continue;
+            const int64_t off = b * p.sc + m * p.ldc + n;
+            const int64_t left = p.N - n;
+            const bool full = p.c_vec && left >= 4;
+            floatx4 v = acc[nb][mb] * alpha;
+            if (beta != 0.0f) {
+                const floatx4 c = p.out_f32 ? read_c4((const float *)p.C + off, full, left)
+                                            : read_c4((const TI *)p.C + off, full, left);
+                v += beta * c;
+            }
+            if (epi) v = epilogue4(p, v, load_bias4(p, n));
+            if (p.out_f32) write_c4((float *)p.C + off, full, left, v);
+            else write_c4((TI *)p.C + off, full, left, v);
+        }
+    }
+}
+
 template <typename TI>
 __device__ inline float elem_f32(uint32_t w, int hi) {
     const uint32_t h = hi ? (w >> 16) : (w & 0xffffu);
@@ -2290,6 +2400,14 @@ void fill_rowvec(KernelFn (&t)[2][2][2]) {
 }
 
 template <typename TI, bool EPI>
+void fill_small(KernelFn (&t)[2][2][2]) {
+    // Only row-major A and B, 128-bit form.
+    t[0][0][0] = t[0][0][1] = t[0][1][0] = t[0][1][1] = nullptr;
+    t[1][0][0] = t[1][1][0] = t[1][1][1] = nullptr;
+    t[1][0][1] = gemm_small64<TI, EPI>;
+}
+
+template <typename TI, bool EPI>
 void fill_type(TileKernels &k, FullKernels &kfull) {
     for (auto &t : kfull)
         t[0][0] = t[0][1] = t[1][0] = t[1][1] = nullptr;
@@ -2308,6 +2426,7 @@ void fill_type(TileKernels &k, FullKernels &kfull) {
     fill_stream<TI, EPI, TILE_STREAM32W>(k[TILE_STREAM32W]);
     fill_stream<TI, EPI, TILE_STREAM16W>(k[TILE_STREAM16W]);
     fill_stream<TI, EPI, TILE_STREAM32N>(k[TILE_STREAM32N]);
+    fill_small<TI, EPI>(k[TILE_SMALL64]);
     fill_rowvec<TI, EPI, TILE_ROWVEC>(k[TILE_ROWVEC]);
 }
 

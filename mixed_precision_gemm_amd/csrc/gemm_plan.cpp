@@ -46,6 +46,10 @@ int choose_tile(int64_t M, int64_t N, int64_t K, int64_t batch, bool kc_both, bo
     // At most 4 rows with row-major A and B (a matrix-vector product in the
     // NN layout): B streamed into registers, fp32 dot products.
     if (nn && M <= 4 && K > 0) return TILE_ROWVEC;
+    // Batches of products of at most 64 x 64 x 64 with row-major A and B:
+    // one wave per product, its loads all in flight at once (512 x 64^3:
+    // see the kernel).
+    if (nn && vec_ok && batch > 1 && M <= 64 && N <= 64 && K <= 64 && K > 0) return TILE_SMALL64;
     // Skinny M with K-contiguous A and B streams B through LDS.  Every
     // workgroup re-reads its rows of A, so wide N takes more columns per
     // workgroup: 48 for M <= 16 from N = 8192 and for M <= 32 from N = 10240
@@ -59,12 +63,12 @@ int choose_tile(int64_t M, int64_t N, int64_t K, int64_t batch, bool kc_both, bo
     if (kc_both && M <= 32)
         return N >= 10240 ? TILE_STREAM32N : N >= 8192 ? TILE_STREAM32W : TILE_STREAM32;
     // Up to 128 rows, the 32 x 64 streaming tile while its grid fits one
-    // workgroup per CU and K is at most 8192: more workgroups stream B than
+    // workgroup per CU and K is 1024 to 8192: more workgroups stream B than
     // the 128 tile's split-K grid, without its partial tiles.  (Measured at
     // K = 4096: 64 x 4096 18.2 against 22.0 us, 128 x 4096 21.8 against
     // 29.0, 96 x 2048 17.2 against 21.0; beyond one pass, 128 x 6144 36.2
     // against 27.2; at K = 16384, 128 x 2048 41.6 against 38.5.)
-    if (kc_both && M <= 128 && K <= 8192 &&
+    if (kc_both && M <= 128 && K >= 1024 && K <= 8192 &&
         ceil_div(M, 32) * ceil_div(N, 64) * batch <= kNumCUs)
         return TILE_STREAM32W;
     if (kc_both && M <= 64 && ceil_div(N, 128) < 64) return TILE_STREAM64;
@@ -247,22 +251,25 @@ int make_plan(int in_type, gemm_f16f32_plan_t *out, int64_t M, int64_t N, int64_
         p->pack = 3;
     } else if (a_ok && b_ok) {
         p->vec_ok = 1;
-    } else if (kTiles[p->tile].kind != KIND_STAGED && K > 0 && chunks_ok) {
+    } else if (kTiles[p->tile].kind != KIND_STAGED && kTiles[p->tile].kind != KIND_SMALL && K > 0 &&
+               chunks_ok) {
         // Shapes for the direct or streaming kernels repack the unaligned
         // operands: one extra pass over them instead of element-wide loads
         // for the whole K loop (copies of A and B below 2^31 16-byte chunks).
         p->vec_ok = 1;
         p->pack = (a_ok ? 0 : 1) | (b_ok ? 0 : 2);
     } else {
-        // Small products keep the operands in place: the staged kernel with
-        // element-wide loads, whose largest tile is 128.
+        // Small and batched-small products keep the operands in place: the
+        // staged kernel with element-wide loads, whose largest tile is 128.
         p->vec_ok = 0;
         p->tile = choose_tile(M, N, K, batch, kc_both, nn && rv_ok, false);
     }
     // Operands given at misaligned addresses are repacked at run time only
     // for the direct and streaming kernels (and only when the workspace
-    // holds the copies); the staged tiles read them with element-wide loads.
-    p->fast = p->vec_ok && kTiles[p->tile].kind != KIND_STAGED && K > 0 && chunks_ok;
+    // holds the copies); the staged tiles read them with element-wide loads,
+    // and so do batched small products (their staged tile).
+    p->fast = p->vec_ok && kTiles[p->tile].kind != KIND_STAGED && kTiles[p->tile].kind != KIND_SMALL &&
+              K > 0 && chunks_ok;
     for (int cand : {p->tile, narrow_tile(p->tile)}) {
         const TileShape &c = kTiles[cand];
         if (ceil_div(M, c.bm) * ceil_div(N, c.bn) * batch > 0x7fffffff) {

@@ -166,6 +166,7 @@ def test_kernel_choice_by_regime():
     assert kern(128, 4096, 8192, layout_b=GEMM_COL_MAJOR) == "gemm_stream32x64_nt_direct"
     assert kern(128, 6144, 4096, layout_b=GEMM_COL_MAJOR).startswith("gemm_128x128")
     assert kern(128, 2048, 16384, layout_b=GEMM_COL_MAJOR).startswith("gemm_128x128")
+    assert not kern(128, 4096, 512, layout_b=GEMM_COL_MAJOR).startswith("gemm_stream")
     assert kern(64, 4096, 4096, layout_b=GEMM_COL_MAJOR, batch=3, stride_a=64 * 4096,
                 stride_b=4096 * 4096, stride_c=64 * 4096).startswith("gemm_stream64x16")
     assert kern(40, 4096, 16384, layout_b=GEMM_COL_MAJOR).startswith("gemm_stream64x16")
@@ -182,9 +183,19 @@ def test_kernel_choice_by_regime():
     # 2048^2 already fills the CUs with 128 tiles; short K is not cut
     assert not kern(2048, 2048, 2048).endswith(tuple(f"_sk{k}" for k in range(2, 9)))
     assert "_sk" not in kern(16, 4096, 512)
-    # batched small products are not put on tiles far larger than themselves
+    # batched small products are not put on tiles far larger than themselves:
+    # at most 64 x 64 x 64 with row-major A and B, one wave per product
     assert mpg.Plan(64, 64, 64, batch=512, stride_a=4096, stride_b=4096,
-                    stride_c=4096).kernel.startswith("gemm_64x64")
+                    stride_c=4096).kernel == "gemm_small64_nn_direct"
+    assert mpg.Plan(50, 40, 32, batch=3, stride_a=50 * 32, stride_b=32 * 40,
+                    stride_c=2000).kernel == "gemm_small64_nn_direct"
+    assert mpg.Plan(50, 40, 33, batch=3, stride_a=50 * 33, stride_b=33 * 40,
+                    stride_c=2000).kernel == "gemm_64x64x64_nn_narrow"    # no copies
+    assert mpg.Plan(64, 64, 64).kernel.startswith("gemm_64x64")              # one product
+    assert mpg.Plan(65, 64, 64, batch=4, stride_a=65 * 64, stride_b=4096,
+                    stride_c=65 * 64).kernel.startswith("gemm_64x64")        # 65 rows
+    assert not mpg.Plan(64, 64, 64, layout_b=GEMM_COL_MAJOR, batch=4, stride_a=4096,
+                        stride_b=4096, stride_c=4096).kernel.startswith("gemm_small")   # NT
     assert kern(1024, 1024, 1024).startswith("gemm_128x128")
     # the 128 tile on a four-slot ring when its grid is one wave at one
     # workgroup per CU, with four or more stages

@@ -136,6 +136,46 @@ def test_row_vector_bit_exact_and_repeatable(M):
     assert torch.equal(d1, d2)
 
 
+@pytest.mark.parametrize("shape,kw", [
+    ((64, 64, 64), dict(batch=512, out_type=OUT_F32)),                        # the batched workload
+    ((37, 40, 24), dict(batch=5, beta=1.0)),                                  # ragged M, N, K
+    ((64, 64, 64), dict(batch=3, alpha=-0.5, beta=0.5)),                      # fp16 C, alpha, beta
+    ((5, 8, 8), dict(batch=2, out_type=OUT_F32)),                             # smallest rows
+    ((64, 64, 64), dict(batch=4, in_dtype="bf16", out_type=OUT_BF16, beta=1.0)),
+    ((64, 48, 64), dict(batch=6, lda=72, ldb=56)),                            # padded rows
+])
+def test_small_batched_kernel(shape, kw):
+    """Batched products of at most 64 x 64 x 64 with row-major A and B: one
+    wave per product (A's fragments from global memory, B transposed out of
+    LDS, C^T accumulated)."""
+    M, N, K = shape
+    kw = dict(kw)
+    batch = kw.pop("batch")
+    case = gi.make_case(M, N, K, batch=batch, seed=M * 3 + N + K + batch, dist_c="normal", **kw)
+    with mpg.Plan(case.M, case.N, case.K, case.layout_a, case.layout_b, case.out_type,
+                  case.lda, case.ldb, case.ldc, case.batch, case.stride_a, case.stride_b,
+                  case.stride_c, dtype=in_dtype(case)) as p:
+        assert "small64_nn_direct" in p.kernel, p.kernel
+    parity(case, what=f"small batched {M}x{N}x{K} x {batch}")
+
+
+def test_small_batched_bit_exact_and_misaligned_fallback():
+    """Integer inputs give exact fp32 sums (fragment layouts and the
+    transposed B read pinned bit for bit); an A at an odd address takes the
+    staged tile's element loads instead, with the same result."""
+    case = gi.make_case(64, 64, 64, batch=8, out_type=OUT_F32, dist_a="integer",
+                        dist_b="integer", int_range=(-8, 8), seed=12)
+    assert "small64" in plan_kernel(case)
+    ref, _ = oracle_for(case)
+    dC = run_case(case)
+    assert np.array_equal(c_logical(case, dC.cpu()), ref)
+    A = torch.zeros(case.A.numel() + 1, dtype=torch.float16, device="cuda")
+    A[1:] = case.A.cuda()
+    B, C = case.B.cuda(), case.C.cuda()
+    run_case(case, A[1:], B, C)
+    assert np.array_equal(c_logical(case, C.cpu()), ref)
+
+
 @pytest.mark.parametrize("kind", ["sq64", "qk"])
 def test_batched_small(kind):
     case = gi.batched_case(kind)

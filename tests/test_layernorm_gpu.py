@@ -99,7 +99,8 @@ def test_layernorm_linear_layer_shapes(M, N):
     ((300, 260, 1500), dict(layout_a=COL_MAJOR), "128x128"),        # two-slot 128 tile
     ((16, 2048, 4096), {}, "_sk"),                                   # split-K
     ((1000, 1001, 999), {}, "_pk"),                                  # repacked operands
-    ((64, 64, 64), dict(batch=8), "64x64"),                          # batched staged tile
+    ((64, 64, 64), dict(batch=8), "small64"),                        # one wave per product
+    ((64, 64, 64), dict(batch=8, layout_a=COL_MAJOR), "64x64"),      # batched staged tile
     ((127, 257, 33), {}, "narrow"),                                  # element-wide loads
     ((4096, 4096, 4096), dict(layout_b=COL_MAJOR), "256x256"),       # the 256 tile
 ])
