@@ -159,6 +159,31 @@ def test_small_batched_kernel(shape, kw):
     parity(case, what=f"small batched {M}x{N}x{K} x {batch}")
 
 
+def test_small_batched_writes_stay_inside_c_and_skip_nan_c():
+    """One wave per product with C's rows padded (ldc > N) and a gap between
+    batch items: sentinels outside the logical C survive; with beta = 0 a
+    NaN-filled C is never read."""
+    M, N, K, ldc, batch = 40, 56, 64, 72, 3
+    stride_c = (M + 2) * ldc
+    case = gi.make_case(M, N, K, batch=batch, out_type=OUT_F32, seed=13)
+    sentinel = -1234.0
+    C = torch.full((batch * stride_c,), float("nan"), dtype=torch.float32, device="cuda")
+    Cv = C.view(batch, M + 2, ldc)
+    Cv[:, :, N:] = sentinel
+    Cv[:, M:, :] = sentinel
+    with mpg.Plan(M, N, K, ROW_MAJOR, ROW_MAJOR, OUT_F32, case.lda, case.ldb, ldc, batch,
+                  case.stride_a, case.stride_b, stride_c) as p:
+        assert "small64" in p.kernel, p.kernel
+        p.run(case.A.cuda(), case.B.cuda(), C, 1.0, 0.0)
+    torch.cuda.synchronize()
+    Cv = C.cpu().view(batch, M + 2, ldc)
+    assert torch.all(Cv[:, :, N:] == sentinel) and torch.all(Cv[:, M:, :] == sentinel)
+    got = Cv[:, :M, :N].double().numpy()
+    ref, scale = oracle_for(case)
+    assert not np.isnan(got).any()
+    check_bound(got, ref, scale, OUT_F32, "small batched, padded C")
+
+
 def test_small_batched_bit_exact_and_misaligned_fallback():
     """Integer inputs give exact fp32 sums (fragment layouts and the
     transposed B read pinned bit for bit); an A at an odd address takes the
