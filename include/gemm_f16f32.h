@@ -47,7 +47,8 @@
  * every run (gemm_f16f32_workspace_size gives the bytes; 0 means none):
  *   - split-K (kernel name contains "_sk<slices>"): one word per output tile,
  *     counting the K slices that have finished it, in the first 4096 bytes,
- *     then slices x tiles x 64 KiB of fp32 partial tiles;
+ *     then slices x tiles fp32 partial tiles (64 KiB each on the 128 x 128
+ *     tile, one 32 x 64, 16 x 48 ... block each on the streaming kernels);
  *   - repacking (kernel name ends in "_pka", "_pkb" or "_pkab"): dense copies
  *     of the operands whose rows do not allow 128-bit loads, rows padded to a
  *     multiple of 8 elements.
